@@ -1,0 +1,221 @@
+"""CPU fp64 oracle for the q4_0 decode hot path.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import this module;
+only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` use it. It shares no code with the HIP library: it reads the
+interchange formats produced by ``synth`` (int8 codes, fp16 / bf16 bit
+patterns, int8 tables, int32 ids) and evaluates the plain definitions in fp64.
+
+Sources (titles of the pages, with the section each function follows):
+
+* [CARD] "visible-cx/gemma-4-E2B-CoreAI" model card: Provenance table (weight
+  format: int4 per-block-32, the ggml q4_0 grid), the PLE gather-table sidecar
+  section (int8 table, fp32 per-row scale, multiplier 16.0 = sqrt(256)) and the
+  engine contract (int32 ids, int8 table, fp32 scale).
+* [E2B] "Gemma 4 E2B (text decoder) - Core AI" model-zoo card: signature
+  features (final logit softcap tanh(z/30)*30), "QAT weights" section (q4_0 is
+  per-block-32 absmax symmetric int4), "What it took" (fused head with an
+  in-kernel argmax returning (value, index)).
+* [E4B] "Gemma 4 E4B" model-zoo card: architecture paragraph (softcap 30,
+  vocabulary 262,144).
+* [MIX] "Gemma-4 E2B mobile mixed-bit QAT weights" knowledge page: P6 section
+  (official packing stores the UNSIGNED code minus the midpoint, -8 for int4)
+  and the receiving-end design (q_u = q_s + 8; the fused gate/up kernel uses a
+  precise fp32 tanh GELU).
+
+Every function is pinned by ``tests/test_oracle_pins.py`` to values that do
+not come from this file: hand-derived worked examples, exact rational
+arithmetic, closed forms, invariants and brute force. No function here is
+"parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Rows of the weight matrix processed per numpy call; bounds peak memory of the
+# fp64 dequantised slab (ROW_CHUNK * K * 8 bytes).
+ROW_CHUNK = 8192
+
+
+# ---------------------------------------------------------------- decoding --
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns -> fp64, exactly (bf16 is the upper half of fp32)."""
+    b = np.ascontiguousarray(bits).view(np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def f16_bits_to_f64(bits) -> np.ndarray:
+    """fp16 bit patterns -> fp64, exactly."""
+    return np.ascontiguousarray(bits).view(np.uint16).view(np.float16).astype(np.float64)
+
+
+def codes_from_nibbles(nibbles) -> np.ndarray:
+    """Stored unsigned nibble -> signed code: c = n - 8, so c is in [-8, 7].
+
+    [MIX] P6 section: the official int4 packing is the unsigned code minus the
+    midpoint 8; the receiving-end design maps q_u = q_s + 8.
+    """
+    n = np.asarray(nibbles).astype(np.int16)
+    if ((n < 0) | (n > 15)).any():
+        raise ValueError("nibbles must be in [0, 15]")
+    return (n - 8).astype(np.int8)
+
+
+def nibbles_from_codes(codes) -> np.ndarray:
+    """Signed code -> stored unsigned nibble n = c + 8 ([MIX] P6 section)."""
+    c = np.asarray(codes).astype(np.int16)
+    if ((c < -8) | (c > 7)).any():
+        raise ValueError("codes must be in [-8, 7]")
+    return (c + 8).astype(np.uint8)
+
+
+# ----------------------------------------------------------------- dequant --
+def dequant(codes, scale_bits) -> np.ndarray:
+    """q4_0 dequantisation in fp64: w[n, k] = c[n, k] * d[n, k // 32].
+
+    [CARD] Provenance table: int4 weights, one scale per block of 32 along the
+    input dimension; [E2B] "QAT weights": per-block-32 absmax symmetric int4.
+    Exact in fp64 (a 4-bit integer times an 11-bit fp16 significand).
+    """
+    codes = np.asarray(codes)
+    n, k = codes.shape
+    if k % 32:
+        raise ValueError("K must be a multiple of 32")
+    d = f16_bits_to_f64(scale_bits).reshape(n, k // 32)
+    return codes.astype(np.float64) * np.repeat(d, 32, axis=1)
+
+
+# -------------------------------------------------------------------- GEMV --
+def gemv(codes, scale_bits, x_bits):
+    """y[n] = sum_k w[n, k] * x[k] in fp64, plus A[n] = sum_k |w[n, k] x[k]|.
+
+    A is the magnitude sum the tolerance |y_gpu - y| <= 1e-4 * A + 1e-6 is
+    measured against. Row-chunked so large heads fit in memory.
+    """
+    codes = np.asarray(codes)
+    n, k = codes.shape
+    x = bf16_bits_to_f64(x_bits).reshape(k)
+    ax = np.abs(x)
+    y = np.empty(n, dtype=np.float64)
+    a = np.empty(n, dtype=np.float64)
+    for r0 in range(0, n, ROW_CHUNK):
+        w = dequant(codes[r0:r0 + ROW_CHUNK], np.asarray(scale_bits)[r0:r0 + ROW_CHUNK])
+        y[r0:r0 + len(w)] = w @ x
+        a[r0:r0 + len(w)] = np.abs(w) @ ax
+    return y, a
+
+
+def gemm(codes, scale_bits, x_bits):
+    """Y[s, n] = sum_k w[n, k] * X[s, k] in fp64 (X rows are tokens of one
+    prefill chunk, [CARD] "prefill (S=64 chunked prefill)"), plus the
+    magnitude sums A[s, n] = sum_k |w[n, k] X[s, k]|."""
+    codes = np.asarray(codes)
+    n, k = codes.shape
+    xs = bf16_bits_to_f64(x_bits).reshape(-1, k)
+    s = xs.shape[0]
+    axs = np.abs(xs)
+    y = np.empty((s, n), dtype=np.float64)
+    a = np.empty((s, n), dtype=np.float64)
+    for r0 in range(0, n, ROW_CHUNK):
+        w = dequant(codes[r0:r0 + ROW_CHUNK], np.asarray(scale_bits)[r0:r0 + ROW_CHUNK])
+        y[:, r0:r0 + len(w)] = xs @ w.T
+        a[:, r0:r0 + len(w)] = axs @ np.abs(w).T
+    return y, a
+
+
+# ----------------------------------------------------------------- LM head --
+def softcap(z, cap: float = 30.0):
+    """Final logit softcap cap * tanh(z / cap) in fp64 ([E2B] signature
+    features: tanh(z/30)*30; [E4B] softcap 30). cap <= 0 disables it."""
+    z = np.asarray(z, dtype=np.float64)
+    if cap <= 0:
+        return z.copy()
+    return cap * np.tanh(z / cap)
+
+
+def first_argmax(v) -> int:
+    """Index of the maximum; among equal maxima the lowest index wins."""
+    v = np.asarray(v)
+    return int(np.argmax(v))
+
+
+def top2_margin(v) -> float:
+    """Largest value minus the largest value at any other index."""
+    v = np.asarray(v, dtype=np.float64)
+    if v.size < 2:
+        return float("inf")
+    i = int(np.argmax(v))
+    rest = np.delete(v, i)
+    return float(v[i] - rest.max())
+
+
+def lmhead(codes, scale_bits, x_bits, cap: float = 30.0):
+    """Head GEMV, softcap, then argmax over the capped logits ([E2B] "What it
+    took": fused head with a two-level argmax that returns (value, index);
+    signature features: softcap).
+
+    Returns dict(idx, val, margin, a_idx, z, capped) where ``margin`` is the
+    top-2 margin of the capped logits and ``a_idx`` the magnitude sum of the
+    winning row (for the value tolerance).
+    """
+    z, a = gemv(codes, scale_bits, x_bits)
+    c = softcap(z, cap)
+    i = first_argmax(c)
+    return dict(idx=i, val=float(c[i]), margin=top2_margin(c), a_idx=float(a[i]),
+                z=z, capped=c)
+
+
+# -------------------------------------------------------------- PLE gather --
+def ple_gather(table, row_scale, ids, mult: float = 16.0):
+    """Per-Layer-Embedding gather: out[t, j] = RN_fp32(q[id_t, j] * s[id_t] * mult).
+
+    [CARD] sidecar section: int8 table [V, L*ld], fp32 per-row scale [V],
+    multiplier embed_scale_pl 16.0. The product of the int8 code, the fp32
+    scale and the fp32 multiplier is formed exactly in 80-bit extended
+    precision (at most 8 + 24 + 24 = 56 significant bits) and rounded once to
+    fp32. Ids outside [0, V) give a zero row and set the returned error flag.
+    Returns (out float32 [T, D], err int).
+    """
+    table = np.asarray(table)
+    v, dim = table.shape
+    ids = np.asarray(ids, dtype=np.int64).reshape(-1)
+    out = np.zeros((ids.size, dim), dtype=np.float32)
+    ok = (ids >= 0) & (ids < v)
+    err = int((~ok).any())
+    if ok.any():
+        rows = ids[ok]
+        q = table[rows].astype(np.longdouble)
+        s = np.asarray(row_scale, dtype=np.float32)[rows].astype(np.longdouble)
+        m = np.longdouble(np.float32(mult))
+        out[ok] = (q * s[:, None] * m).astype(np.float32)
+    return out, err
+
+
+# --------------------------------------------------------- FFN host glue --
+def gelu_tanh_f32(g):
+    """tanh-approximation GELU evaluated in fp32 ([MIX] fused gate/up kernel:
+    precise fp32 tanh GELU in the epilogue):
+    0.5 * g * (1 + tanh(sqrt(2/pi) * (g + 0.044715 * g^3)))."""
+    g = np.asarray(g, dtype=np.float32)
+    k0 = np.float32(np.sqrt(2.0 / np.pi))
+    k1 = np.float32(0.044715)
+    inner = k0 * (g + k1 * g * g * g)
+    return (np.float32(0.5) * g * (np.float32(1.0) + np.tanh(inner))).astype(np.float32)
+
+
+def ffn_down_input_bits(g, u):
+    """Host step between the fused gate+up GEMV and the down GEMV:
+    a = gelu_tanh(g) * u in fp32, rounded to bf16 (torch's round to nearest
+    even). Returns uint16 bf16 bit patterns."""
+    import torch
+
+    a = gelu_tanh_f32(np.asarray(g, dtype=np.float32)) * np.asarray(u, dtype=np.float32)
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+# ------------------------------------------------------------- tolerances --
+def gemv_tolerance(a):
+    """Per-output tolerance for fp32-accumulated GEMV results:
+    1e-4 * sum_k |w x| + 1e-6."""
+    return 1e-4 * np.asarray(a, dtype=np.float64) + 1e-6

@@ -1,0 +1,378 @@
+"""Pins for the fp64 oracle against values that do not come from the oracle.
+
+Each test fixes the oracle to something independent of its own code: the
+hand-derived worked examples under tests/golden/, exact rational arithmetic
+(fractions.Fraction over independently decoded fp16/bf16 bit patterns), closed
+forms evaluated with the decimal module, invariants, and brute-force loops.
+The cases are chosen so that a dropped scale, a wrong block index, a
+transposed operand, a wrong sign or offset, a missing softcap factor or a
+wrong tie-break each fail at least one of them.
+"""
+import decimal
+import math
+import os
+import struct
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# -------------------------------------------------- independent decoders --
+def f16_exact(bits: int) -> Fraction:
+    """fp16 bit pattern -> exact rational, decoded by struct (not numpy)."""
+    return Fraction(struct.unpack("<e", struct.pack("<H", int(bits)))[0])
+
+
+def bf16_exact(bits: int) -> Fraction:
+    return Fraction(struct.unpack("<f", struct.pack("<I", int(bits) << 16))[0])
+
+
+def f32_bits(x: float) -> int:
+    return struct.unpack("<I", struct.pack("<f", x))[0]
+
+
+def rn32(fr: Fraction) -> float:
+    """Exact round-half-even of a rational to fp32 (normal range)."""
+    if fr == 0:
+        return 0.0
+    sign = -1 if fr < 0 else 1
+    a = abs(fr)
+    e = 0
+    while a >= 2:
+        a /= 2
+        e += 1
+    while a < 1:
+        a *= 2
+        e -= 1
+    m = a * (1 << 23)
+    fl = m.numerator // m.denominator
+    rem = m - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sign * float(Fraction(fl, 1 << 23) * Fraction(2) ** e)
+
+
+def exact_gemv(codes, sbits, xbits):
+    n, k = codes.shape
+    xs = [bf16_exact(b) for b in xbits]
+    y, a = [], []
+    for r in range(n):
+        acc = Fraction(0)
+        mag = Fraction(0)
+        for b in range(k // 32):
+            d = f16_exact(sbits[r, b])
+            for j in range(32):
+                t = int(codes[r, 32 * b + j]) * d * xs[32 * b + j]
+                acc += t
+                mag += abs(t)
+        y.append(acc)
+        a.append(mag)
+    return y, a
+
+
+def fp16_bits(v: float) -> int:
+    return struct.unpack("<H", struct.pack("<e", v))[0]
+
+
+def bf16_bits(v: float) -> int:
+    b = f32_bits(v)
+    assert b & 0xFFFF == 0, "value must be exactly representable in bf16"
+    return b >> 16
+
+
+# ---------------------------------------------------------- worked example --
+def _worked_inputs():
+    codes = np.zeros((2, 32), dtype=np.int8)
+    codes[0] = [(j % 16) - 8 for j in range(32)]
+    codes[1] = 7
+    scales = np.array([[fp16_bits(0.5)], [fp16_bits(0.25)]], dtype=np.uint16)
+    assert scales[0, 0] == 0x3800 and scales[1, 0] == 0x3400
+    xs = {
+        "ramp": [float(j) for j in range(32)],
+        "alt": [(-1.0) ** j for j in range(32)],
+        "e5": [1.0 if j == 5 else 0.0 for j in range(32)],
+        "e21": [1.0 if j == 21 else 0.0 for j in range(32)],
+    }
+    return codes, scales, {k: np.array([bf16_bits(v) for v in vals], dtype=np.uint16)
+                           for k, vals in xs.items()}
+
+
+def _golden_rows(name):
+    rows = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def test_worked_example_2x32():
+    codes, scales, xs = _worked_inputs()
+    rows = _golden_rows("gemv_worked_2x32.txt")
+    assert len(rows) == 4
+    for case, y0, y1, a0, a1 in rows:
+        y, a = oracle.gemv(codes, scales, xs[case])
+        assert y.tolist() == [float(y0), float(y1)], case
+        assert a.tolist() == [float(a0), float(a1)], case
+    head = oracle.lmhead(codes, scales, xs["ramp"])
+    assert head["idx"] == 1
+
+
+def test_nibble_convention():
+    # stored unsigned nibble minus the midpoint 8
+    assert oracle.codes_from_nibbles([0, 8, 15]).tolist() == [-8, 0, 7]
+    allc = np.arange(-8, 8)
+    assert oracle.codes_from_nibbles(oracle.nibbles_from_codes(allc)).tolist() == allc.tolist()
+    with pytest.raises(ValueError):
+        oracle.nibbles_from_codes([8])
+    with pytest.raises(ValueError):
+        oracle.codes_from_nibbles([16])
+
+
+# ----------------------------------------------------- exact arithmetic --
+def test_dequant_exact_rational():
+    rng = np.random.default_rng(11)
+    codes, sb = synth.q4_weights(rng, 3, 96)
+    w = oracle.dequant(codes, sb)
+    for r in range(3):
+        for k in range(96):
+            assert Fraction(w[r, k]) == int(codes[r, k]) * f16_exact(sb[r, k // 32])
+
+
+def test_gemv_bruteforce_fraction_nonsquare():
+    # 5 x 96: non-square so a transposed operand cannot pass; three blocks
+    # with different scales so a wrong block index cannot pass.
+    rng = np.random.default_rng(3)
+    codes, sb = synth.q4_weights(rng, 5, 96)
+    x = synth.bf16_normal(rng, 96)
+    y, a = oracle.gemv(codes, sb, x)
+    ye, ae = exact_gemv(codes, sb, x)
+    for r in range(5):
+        assert abs(Fraction(y[r]) - ye[r]) <= Fraction(1, 10 ** 12) * ae[r]
+        assert abs(Fraction(a[r]) - ae[r]) <= Fraction(1, 10 ** 12) * ae[r]
+
+
+def test_gemv_integer_inputs_exact():
+    # power-of-two scales and integer x: every partial sum is an exact
+    # multiple of 2^-8, so the fp64 oracle must equal the integer result.
+    rng = np.random.default_rng(5)
+    n, k = 24, 512
+    codes = rng.integers(-8, 8, size=(n, k), dtype=np.int8)
+    pw = rng.integers(6, 9, size=(n, k // 32))
+    sb = np.vectorize(lambda p: fp16_bits(2.0 ** -int(p)))(pw).astype(np.uint16)
+    xi = rng.integers(-8, 9, size=k)
+    xb = np.array([bf16_bits(float(v)) for v in xi], dtype=np.uint16)
+    y, _ = oracle.gemv(codes, sb, xb)
+    for r in range(n):
+        tot = 0
+        for kk in range(k):
+            tot += int(codes[r, kk]) * int(xi[kk]) * (1 << (8 - int(pw[r, kk // 32])))
+        assert y[r] == tot / 256.0
+
+
+def test_gemv_onehot_selects_column():
+    rng = np.random.default_rng(7)
+    n, k = 6, 128
+    codes, sb = synth.q4_weights(rng, n, k)
+    for kk in range(k):
+        x = np.zeros(k, dtype=np.uint16)
+        x[kk] = bf16_bits(1.0)
+        y, _ = oracle.gemv(codes, sb, x)
+        for r in range(n):
+            assert Fraction(y[r]) == int(codes[r, kk]) * f16_exact(sb[r, kk // 32])
+
+
+def test_gemv_zero_codes_and_zero_x():
+    rng = np.random.default_rng(8)
+    codes, sb = synth.q4_weights(rng, 4, 64)
+    x = synth.bf16_normal(rng, 64)
+    y, a = oracle.gemv(np.zeros_like(codes), sb, x)
+    assert (y == 0).all() and (a == 0).all()
+    y, a = oracle.gemv(codes, sb, np.zeros(64, dtype=np.uint16))
+    assert (y == 0).all() and (a == 0).all()
+
+
+def test_gemm_bruteforce_fraction():
+    rng = np.random.default_rng(9)
+    s, n, k = 3, 4, 64
+    codes, sb = synth.q4_weights(rng, n, k)
+    xs = synth.bf16_normal(rng, (s, k))
+    y, a = oracle.gemm(codes, sb, xs)
+    assert y.shape == (s, n)
+    for t in range(s):
+        ye, ae = exact_gemv(codes, sb, xs[t])
+        for r in range(n):
+            assert abs(Fraction(y[t, r]) - ye[r]) <= Fraction(1, 10 ** 12) * ae[r]
+            assert abs(Fraction(a[t, r]) - ae[r]) <= Fraction(1, 10 ** 12) * ae[r]
+
+
+def test_gemm_rows_equal_gemv():
+    rng = np.random.default_rng(10)
+    codes, sb = synth.q4_weights(rng, 33, 160)
+    xs = synth.bf16_normal(rng, (5, 160))
+    y, _ = oracle.gemm(codes, sb, xs)
+    for t in range(5):
+        yv, _ = oracle.gemv(codes, sb, xs[t])
+        np.testing.assert_allclose(y[t], yv, rtol=1e-13, atol=0)
+
+
+# ----------------------------------------------------------------- softcap --
+def _tanh_decimal(u: Fraction) -> decimal.Decimal:
+    with decimal.localcontext() as ctx:
+        ctx.prec = 40
+        e = (decimal.Decimal(u.numerator) / decimal.Decimal(u.denominator) * 2).exp()
+        return (e - 1) / (e + 1)
+
+
+def test_softcap_closed_forms():
+    assert oracle.softcap(0.0) == 0.0
+    z = np.linspace(-300, 300, 1201)
+    c = oracle.softcap(z)
+    np.testing.assert_array_equal(oracle.softcap(-z), -c)  # odd
+    assert (np.abs(c) <= 30.0).all() and (np.diff(c) > 0)[np.abs(z[1:]) < 200].all()
+    for zz in (10, 216, 1, -7.5):
+        ref = float(30 * _tanh_decimal(Fraction(zz) / 30))
+        assert abs(float(oracle.softcap(float(zz))) - ref) <= 1e-14 * 30
+    assert abs(float(oracle.softcap(10.0)) - 9.64538212594903) < 1e-13
+    assert float(oracle.softcap(868.0)) == 30.0
+    # slope 1 at the origin: the cap divides then multiplies by 30
+    assert abs(float(oracle.softcap(1e-6)) - 1e-6) < 1e-18
+    # cap <= 0 disables
+    assert oracle.softcap(123.0, cap=0).item() == 123.0
+    # another cap value scales both sides
+    assert abs(float(oracle.softcap(10.0, cap=15.0)) - float(15 * _tanh_decimal(Fraction(10, 15)))) < 1e-13
+
+
+# ------------------------------------------------------------------ argmax --
+def _brute_argmax(v):
+    best, bi = None, -1
+    for i, x in enumerate(v):
+        if best is None or x > best:
+            best, bi = x, i
+    return bi
+
+
+def test_argmax_and_margin_bruteforce():
+    rng = np.random.default_rng(12)
+    for trial in range(20):
+        v = rng.standard_normal(4096)
+        if trial % 4 == 1:
+            v[0] = v.max() + 1.0
+        if trial % 4 == 2:
+            v[-1] = v.max() + 1.0
+        if trial % 4 == 3:
+            m = v.max() + 0.5
+            v[[17, 1000, 4095]] = m
+        i = oracle.first_argmax(v)
+        assert i == _brute_argmax(v.tolist())
+        srt = sorted(v.tolist(), reverse=True)
+        assert oracle.top2_margin(v) == srt[0] - srt[1]
+
+
+def test_lmhead_exact_ties_take_lowest_index():
+    # integer inputs make rows 5, 77 and 299 produce exactly equal logits
+    rng = np.random.default_rng(13)
+    v, k = 300, 64
+    codes = rng.integers(-2, 3, size=(v, k), dtype=np.int8)
+    sb = np.full((v, k // 32), fp16_bits(2.0 ** -7), dtype=np.uint16)
+    xi = rng.integers(-3, 4, size=k)
+    x = np.array([bf16_bits(float(t)) for t in xi], dtype=np.uint16)
+    planted = np.where(xi > 0, 7, np.where(xi < 0, -8, 0)).astype(np.int8)
+    for r in (5, 77, 299):
+        codes[r] = planted
+    out = oracle.lmhead(codes, sb, x)
+    assert out["idx"] == 5
+    assert out["margin"] == 0.0
+    exact = sum(int(planted[j]) * int(xi[j]) for j in range(k)) * Fraction(1, 128)
+    assert Fraction(out["z"][5]) == exact
+    assert abs(out["val"] - float(30 * _tanh_decimal(exact / 30))) < 1e-13
+
+
+# -------------------------------------------------------------------- PLE --
+def test_ple_golden_bits():
+    q = np.array([[-127, -1, 0, 1, 127]], dtype=np.int8)
+    rows = _golden_rows("ple_bits.txt")
+    assert len(rows) == 3
+    for row in rows:
+        s = struct.unpack("<f", struct.pack("<I", int(row[0], 16)))[0]
+        out, err = oracle.ple_gather(q, np.array([s], dtype=np.float32),
+                                     np.array([0], dtype=np.int32), 16.0)
+        assert err == 0
+        got = ["%08x" % v for v in out.view(np.uint32)[0]]
+        assert got == row[1:]
+
+
+def test_ple_bruteforce_general_multiplier():
+    # multiplier fp32(sqrt(1536)): the token-embedding normaliser quoted on
+    # the mixed-bit page; the exact product needs up to 56 bits.
+    rng = np.random.default_rng(14)
+    table, scale, _ = synth.ple_inputs(rng, 50, 40, 1)
+    ids = np.array([0, 49, 7, 7], dtype=np.int32)
+    for mult in (16.0, float(np.float32(math.sqrt(1536))), 0.3):
+        out, err = oracle.ple_gather(table, scale, ids, mult)
+        assert err == 0
+        m = Fraction(float(np.float32(mult)))
+        for t, i in enumerate(ids):
+            for j in range(40):
+                ref = rn32(int(table[i, j]) * Fraction(float(scale[i])) * m)
+                assert f32_bits(float(out[t, j])) == f32_bits(ref), (mult, t, j)
+
+
+def test_ple_out_of_range_ids():
+    rng = np.random.default_rng(15)
+    table, scale, _ = synth.ple_inputs(rng, 10, 16, 1)
+    out, err = oracle.ple_gather(table, scale, np.array([3, -1, 10, 9], dtype=np.int32))
+    assert err == 1
+    assert (out[1] == 0).all() and (out[2] == 0).all()
+    assert (out[0] != 0).any() or (table[3] == 0).all()
+
+
+def test_page_shape_constants():
+    # sidecar file sizes on the Core AI card equal V x row bytes exactly
+    assert synth.VOCAB * synth.SHAPES["ple_e2b"]["dim"] == 2_348_810_240
+    assert synth.VOCAB * 4 == 1_048_576
+    assert synth.SHAPES["ple_e2b"]["dim"] == 8960
+    assert synth.SHAPES["ple_e4b"]["dim"] == 10752
+    assert 16.0 == math.sqrt(256)
+    assert f"{np.float32(math.sqrt(1536)):.6f}" == "39.191837"
+    # E4B decode step weight bytes at 0.5625 B per weight
+    mats = synth.stack_e4b_matrices()
+    assert len(mats) == 42 * 4 + 1
+    total = sum(n * k // 2 + n * (k // 32) * 2 for _, n, k in mats)
+    assert total == 2_545_090_560
+
+
+# ------------------------------------------------------------------- GELU --
+def test_gelu_tanh_identities():
+    import torch
+
+    g = np.linspace(-12, 12, 4001, dtype=np.float32)
+    f = oracle.gelu_tanh_f32(g)
+    assert f[np.argmin(np.abs(g))] == 0.0
+    # gelu(x) - gelu(-x) = x for the tanh form (tanh is odd)
+    np.testing.assert_allclose(f - oracle.gelu_tanh_f32(-g), g, atol=2e-6, rtol=1e-6)
+    ref = torch.nn.functional.gelu(torch.from_numpy(g), approximate="tanh").numpy()
+    np.testing.assert_allclose(f, ref, atol=2e-6, rtol=2e-6)
+    # sanity of the bf16 host rounding used for the down GEMV input
+    bits = oracle.ffn_down_input_bits(np.array([1.0], np.float32), np.array([2.0], np.float32))
+    gel1 = float(oracle.gelu_tanh_f32(np.array([1.0], np.float32))[0])
+    assert float(oracle.bf16_bits_to_f64(bits)[0]) == float(
+        torch.tensor(gel1 * 2.0, dtype=torch.float32).to(torch.bfloat16).float())
+
+
+def test_decoders_exact():
+    for v in (0.0, 1.0, -2.5, 65504.0, 2.0 ** -24, 6.1e-5):
+        b = fp16_bits(v)
+        assert oracle.f16_bits_to_f64(np.array([b], np.uint16))[0] == float(f16_exact(b))
+    rng = np.random.default_rng(16)
+    xb = synth.bf16_normal(rng, 1000)
+    got = oracle.bf16_bits_to_f64(xb)
+    for i in range(0, 1000, 37):
+        assert got[i] == float(bf16_exact(xb[i]))
