@@ -1,0 +1,147 @@
+/*
+ * libq4dec: q4_0 decode hot path for one MI355X (gfx950).
+ *
+ * The operations follow these pages:
+ *  - "visible-cx/gemma-4-E2B-CoreAI" model card: Provenance table (weights are
+ *    int4 per-block-32, the ggml q4_0 grid; S=1 decode and S=64 chunked
+ *    prefill entry points), the PLE gather-table sidecar section (int8 table,
+ *    fp32 per-row scale, multiplier 16.0) and the engine contract (int32 ids,
+ *    int8 table, fp32 scale; statics bound over the caller's buffer).
+ *  - "Gemma 4 E2B (text decoder) - Core AI" model-zoo card: signature features
+ *    (final logit softcap tanh(z/30)*30), "What it took" (fused head with an
+ *    in-kernel two-level argmax returning (value, index) with no logit
+ *    readback), "QAT weights" (q4_0 = per-block-32 absmax symmetric int4).
+ *  - "Gemma-4 E2B mobile mixed-bit QAT weights" knowledge page, P6 section
+ *    (stored int4 code = unsigned nibble minus the midpoint 8).
+ *
+ * Conventions for every call:
+ *  - All data pointers are device memory owned by the caller. The library
+ *    never allocates, frees, copies to the host or synchronises; each call
+ *    validates its arguments on the host, enqueues its kernels on `stream`
+ *    (a hipStream_t; NULL means the default stream) and returns. Results are
+ *    ready once the caller's stream has been synchronised.
+ *  - Return value: Q4DEC_OK (0) on success or a negative Q4DEC_ERR_* code.
+ *    Validation errors return before anything is enqueued.
+ *    q4dec_last_error() then names the offending argument (thread-local).
+ *  - Calls are stateless and thread-safe; the only library state is a cache
+ *    of per-device properties (compute-unit count).
+ *  - Activations are bf16 bit patterns (uint16), outputs fp32.
+ *  - q4_0 weights enter as unpacked int8 codes c in [-8, 7] plus fp16 scale
+ *    bit patterns, one per 32 consecutive weights of a row; q4_pack converts
+ *    them into the library's packed layout. The packed layout is opaque and
+ *    versioned by Q4DEC_ABI_VERSION; its size is q4_packed_bytes(n, k).
+ */
+#ifndef Q4DEC_H
+#define Q4DEC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define Q4DEC_ABI_VERSION 1
+
+#define Q4DEC_OK 0
+#define Q4DEC_ERR_NULL -1        /* a required pointer is NULL */
+#define Q4DEC_ERR_SHAPE -2       /* n, k, vocab, dim, s or n_ids out of range */
+#define Q4DEC_ERR_ALIGN -3       /* pointer misaligned (see each call) */
+#define Q4DEC_ERR_WORKSPACE -4   /* workspace smaller than required */
+#define Q4DEC_ERR_UNSUPPORTED -5 /* valid request this build does not handle */
+#define Q4DEC_ERR_HIP -6         /* HIP runtime error at launch */
+
+/* Largest K (input dimension) the GEMV, head and GEMM kernels accept. */
+#define Q4DEC_MAX_K 16384
+
+/* Library ABI version (Q4DEC_ABI_VERSION of the built library). */
+int32_t q4dec_abi_version(void);
+
+/* Text of the last error raised on the calling thread ("" if none). The
+ * pointer stays valid until the next failing call on this thread. */
+const char* q4dec_last_error(void);
+
+/* Bytes of device memory a packed [n, k] q4_0 matrix occupies:
+ * a nibble plane of n*k/2 bytes and an fp16 scale plane of n*(k/32)*2 bytes,
+ * each padded to 256 bytes. Returns 0 if n <= 0, k <= 0 or k % 32 != 0. */
+size_t q4_packed_bytes(int64_t n, int64_t k);
+
+/* q4_pack: q4_0 codes and scales -> packed layout (load time, not per token).
+ *   codes   int8 [n, k] row-major, values in [-8, 7]; stored nibble = c + 8
+ *           (mixed-bit page, P6 section).
+ *   scales  fp16 bit patterns [n, k/32] row-major; scale b of row r covers
+ *           codes[r, 32b .. 32b+31] (model card, Provenance table).
+ *   packed  output, q4_packed_bytes(n, k) bytes, 16-byte aligned.
+ *   err_flag  optional (NULL allowed) device int32: set to 1 if any code is
+ *           outside [-8, 7]; such codes are stored as (c + 8) & 15. Never
+ *           cleared by the library.
+ * Errors: NULL pointer, n <= 0, k <= 0, k % 32 != 0, packed not 16-aligned. */
+int q4_pack(const int8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
+            void* packed, int32_t* err_flag, void* stream);
+
+/* q4_gemv: S=1 decode matvec y[r] = sum_k c[r,k] * d[r,k/32] * x[k]
+ * (fp32 accumulation; model card Provenance table, S=1 decode).
+ *   packed  from q4_pack with the same (n, k); 16-byte aligned.
+ *   x       bf16 [k], 16-byte aligned.
+ *   y       fp32 [n], 4-byte aligned; must not overlap packed or x.
+ * Errors: NULL pointer, n <= 0, k <= 0, k % 32 != 0, k > Q4DEC_MAX_K,
+ *         n >= 2^31, misalignment. */
+int q4_gemv(const void* packed, int64_t n, int64_t k, const uint16_t* x,
+            float* y, void* stream);
+
+/* q4_gemm_s64: chunked-prefill product Y[s, r] = sum_k X[s, k] * w[r, k] for
+ * s < n_tok <= 64 (model card: prefill entry point with a static query width
+ * of 64). MFMA kernel; codes enter the matrix cores as exact bf16 integers and
+ * each 32-wide block's fp16 scale is applied in fp32.
+ *   packed  from q4_pack with the same (n, k); 16-byte aligned.
+ *   x       bf16 [n_tok, k] row-major, 16-byte aligned.
+ *   y       fp32 [n_tok, n] row-major, 16-byte aligned.
+ * Errors: NULL pointer, n <= 0, k % 32 != 0, k > Q4DEC_MAX_K, n_tok not in
+ *         [1, 64], misalignment. */
+int q4_gemm_s64(const void* packed, int64_t n, int64_t k, const uint16_t* x,
+                int64_t n_tok, float* y, void* stream);
+
+/* Workspace bytes lmhead_softcap_argmax needs for a [vocab, k] head. */
+size_t lmhead_workspace_bytes(int64_t vocab, int64_t k);
+
+/* lmhead_softcap_argmax: z = W_h x, capped logits cap * tanh(z / cap), and
+ * the index and value of their maximum (E2B card: signature features and the
+ * fused head + two-level argmax). Lowest index wins among equal maxima. The
+ * cap is strictly increasing, so the argmax is taken on z (no per-row tanh)
+ * and only the winning value is capped. Logits that are NaN never win; if no
+ * logit compares, idx_out = -1 and val_out = NaN.
+ *   packed   from q4_pack with (n = vocab, k); 16-byte aligned.
+ *   x        bf16 [k], 16-byte aligned.
+ *   cap      30.0 for Gemma 4; cap <= 0 returns the raw maximum logit.
+ *   ws       device workspace of ws_bytes >= lmhead_workspace_bytes(vocab, k),
+ *            8-byte aligned; scratch for per-workgroup partials.
+ *   idx_out  device int32 [1]; val_out device fp32 [1].
+ * Errors: NULL pointer, vocab <= 0 or >= 2^31, k constraints as q4_gemv,
+ *         workspace too small, misalignment. */
+int lmhead_softcap_argmax(const void* packed, int64_t vocab, int64_t k,
+                          const uint16_t* x, float cap, void* ws,
+                          size_t ws_bytes, int32_t* idx_out, float* val_out,
+                          void* stream);
+
+/* ple_gather: Per-Layer-Embedding row gather
+ * out[t, j] = RN_fp32(table[ids[t], j] * row_scale[ids[t]] * mult)
+ * (model card, PLE gather-table sidecar section: int8 table [V, L*ld], fp32
+ * per-row scale, embed_scale_pl 16.0). The product is rounded once to fp32,
+ * so results are bit-identical to the exact product rounded to nearest even.
+ *   table      int8 [vocab, dim] row-major.
+ *   row_scale  fp32 [vocab].
+ *   ids        int32 [n_ids]; an id outside [0, vocab) yields a zero row and
+ *              sets *err_flag = 1 (when err_flag is not NULL).
+ *   mult       16.0 for the PLE table.
+ *   out        fp32 [n_ids, dim] row-major.
+ * Errors: NULL pointer (err_flag may be NULL), vocab <= 0, dim <= 0,
+ *         n_ids < 0 (n_ids == 0 is a no-op), vocab or dim >= 2^31. */
+int ple_gather(const int8_t* table, const float* row_scale, int64_t vocab,
+               int64_t dim, const int32_t* ids, int64_t n_ids, float mult,
+               float* out, int32_t* err_flag, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4DEC_H */

@@ -1,0 +1,220 @@
+"""Python binding of libq4dec (q4_0 decode hot path on MI355X / gfx950).
+
+Argument marshalling only: every function checks that its torch tensors have
+the dtype, device and contiguity the C ABI expects, passes raw device pointers
+and the current HIP stream to the library, and raises ``Q4Error`` with the
+library's error text on a non-zero status. All compute runs in the HIP
+kernels of libq4dec.so; there is no other code path. If the shared library has
+not been built the import of any call fails loudly.
+
+The C declarations and their meaning are in include/q4dec.h.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libq4dec.so")
+HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "q4dec.h")
+
+ABI_VERSION = 1
+OK = 0
+ERR_NULL = -1
+ERR_SHAPE = -2
+ERR_ALIGN = -3
+ERR_WORKSPACE = -4
+ERR_UNSUPPORTED = -5
+ERR_HIP = -6
+MAX_K = 16384
+
+_c_i64 = ctypes.c_int64
+_c_p = ctypes.c_void_p
+_SIGNATURES = {
+    "q4dec_abi_version": (ctypes.c_int32, []),
+    "q4dec_last_error": (ctypes.c_char_p, []),
+    "q4_packed_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
+    "q4_pack": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
+    "q4_gemv": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
+    "q4_gemm_s64": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p]),
+    "lmhead_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
+    "lmhead_softcap_argmax": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, ctypes.c_float, _c_p,
+                                             ctypes.c_size_t, _c_p, _c_p, _c_p]),
+    "ple_gather": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_i64, ctypes.c_float, _c_p,
+                                  _c_p, _c_p]),
+}
+
+_lib = None
+
+
+class Q4Error(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libq4dec error {code}: {msg}")
+        self.code = code
+
+
+def lib():
+    """Load libq4dec.so (once). Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"libq4dec.so not found at {LIB_PATH}; build it with "
+                "`python -c 'import __graft_entry__ as g; g.build()'`")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        if h.q4dec_abi_version() != ABI_VERSION:
+            raise RuntimeError("libq4dec.so ABI version mismatch; rebuild it")
+        _lib = h
+    return _lib
+
+
+def header_functions():
+    """Names of the functions include/q4dec.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_0-9]+)\s*\(", text)) - {"defined"})
+
+
+def _check(rc: int):
+    if rc != OK:
+        raise Q4Error(rc, lib().q4dec_last_error().decode())
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtypes, numel=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    return t.data_ptr()
+
+
+_U16 = (torch.int16, torch.uint16, torch.bfloat16, torch.float16)
+_I8 = (torch.int8,)
+_F32 = (torch.float32,)
+_I32 = (torch.int32,)
+_BYTES = (torch.uint8, torch.int8)
+
+
+def _check_packed(packed: torch.Tensor, n: int, k: int):
+    need = q4_packed_bytes(n, k)
+    if need and packed.numel() * packed.element_size() < need:
+        raise ValueError(f"packed buffer holds {packed.numel() * packed.element_size()} bytes, "
+                         f"[{n}, {k}] needs {need}")
+
+
+def q4dec_abi_version() -> int:
+    return int(lib().q4dec_abi_version())
+
+
+def q4dec_last_error() -> str:
+    return lib().q4dec_last_error().decode()
+
+
+def q4_packed_bytes(n: int, k: int) -> int:
+    return int(lib().q4_packed_bytes(n, k))
+
+
+def q4_pack(codes: torch.Tensor, scales: torch.Tensor, packed: torch.Tensor | None = None,
+            err_flag: torch.Tensor | None = None) -> torch.Tensor:
+    """int8 codes [n, k] in [-8, 7] and fp16 scale bits [n, k/32] -> packed bytes."""
+    n, k = codes.shape
+    pc = _dev(codes, "codes", _I8)
+    ps = _dev(scales, "scales", _U16, n * (k // 32) if k % 32 == 0 else None)
+    nbytes = q4_packed_bytes(n, k)
+    if packed is None:
+        packed = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=codes.device)
+    pp = _dev(packed, "packed", _BYTES)
+    if packed.numel() * packed.element_size() < nbytes:
+        raise ValueError("packed buffer too small")
+    pe = _dev(err_flag, "err_flag", _I32, 1) if err_flag is not None else None
+    _check(lib().q4_pack(pc, ps, n, k, pp, pe, _stream(codes)))
+    return packed
+
+
+def q4_gemv(packed: torch.Tensor, n: int, k: int, x: torch.Tensor,
+            y: torch.Tensor | None = None) -> torch.Tensor:
+    """y[n] fp32 = dequant(W) @ x for bf16 x[k]."""
+    pp = _dev(packed, "packed", _BYTES)
+    _check_packed(packed, n, k)
+    px = _dev(x, "x", _U16, k)
+    if y is None:
+        y = torch.empty(n, dtype=torch.float32, device=x.device)
+    py = _dev(y, "y", _F32, n)
+    _check(lib().q4_gemv(pp, n, k, px, py, _stream(x)))
+    return y
+
+
+def q4_gemm_s64(packed: torch.Tensor, n: int, k: int, x: torch.Tensor,
+                y: torch.Tensor | None = None) -> torch.Tensor:
+    """Y[s, n] fp32 = X @ dequant(W)^T for bf16 X[s, k], 1 <= s <= 64."""
+    s = x.shape[0] if x.dim() == 2 else 1
+    pp = _dev(packed, "packed", _BYTES)
+    _check_packed(packed, n, k)
+    px = _dev(x, "x", _U16, s * k)
+    if y is None:
+        y = torch.empty((s, n), dtype=torch.float32, device=x.device)
+    py = _dev(y, "y", _F32, s * n)
+    _check(lib().q4_gemm_s64(pp, n, k, px, s, py, _stream(x)))
+    return y
+
+
+def lmhead_workspace_bytes(vocab: int, k: int) -> int:
+    return int(lib().lmhead_workspace_bytes(vocab, k))
+
+
+def lmhead_softcap_argmax(packed: torch.Tensor, vocab: int, k: int, x: torch.Tensor,
+                          cap: float = 30.0, ws: torch.Tensor | None = None,
+                          idx_out: torch.Tensor | None = None,
+                          val_out: torch.Tensor | None = None):
+    """(idx int32 [1], val fp32 [1]) of the softcapped head logits' maximum."""
+    pp = _dev(packed, "packed", _BYTES)
+    _check_packed(packed, vocab, k)
+    px = _dev(x, "x", _U16, k)
+    need = lmhead_workspace_bytes(vocab, k)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    pw = _dev(ws, "ws", _BYTES)
+    if idx_out is None:
+        idx_out = torch.empty(1, dtype=torch.int32, device=x.device)
+    if val_out is None:
+        val_out = torch.empty(1, dtype=torch.float32, device=x.device)
+    pi = _dev(idx_out, "idx_out", _I32, 1)
+    pv = _dev(val_out, "val_out", _F32, 1)
+    _check(lib().lmhead_softcap_argmax(pp, vocab, k, px, float(cap), pw,
+                                       ws.numel() * ws.element_size(), pi, pv, _stream(x)))
+    return idx_out, val_out
+
+
+def ple_gather(table: torch.Tensor, row_scale: torch.Tensor, ids: torch.Tensor,
+               mult: float = 16.0, out: torch.Tensor | None = None,
+               err_flag: torch.Tensor | None = None) -> torch.Tensor:
+    """out[t, :] fp32 = table[ids[t]] * row_scale[ids[t]] * mult, rounded once."""
+    vocab, dim = table.shape
+    pt = _dev(table, "table", _I8)
+    psc = _dev(row_scale, "row_scale", _F32, vocab)
+    pi = _dev(ids, "ids", _I32)
+    n_ids = ids.numel()
+    if out is None:
+        out = torch.empty((n_ids, dim), dtype=torch.float32, device=table.device)
+    po = _dev(out, "out", _F32, n_ids * dim)
+    pe = _dev(err_flag, "err_flag", _I32, 1) if err_flag is not None else None
+    _check(lib().ple_gather(pt, psc, vocab, dim, pi, n_ids, float(mult), po, pe, _stream(table)))
+    return out

@@ -1,0 +1,148 @@
+// Internal helpers shared by the libq4dec translation units (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "q4dec.h"
+
+namespace q4dec {
+
+// ---------------------------------------------------------------- host side
+// Thread-local error text; returns `code` so call sites can `return fail(...)`.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+// Compute units of the current device (cached per device id).
+int device_cu_count();
+
+inline bool aligned(const void* p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Offsets of the two planes inside a packed [n, k] matrix.
+inline size_t nib_plane_bytes(int64_t n, int64_t k) { return align256(size_t(n) * size_t(k) / 2); }
+inline size_t scale_plane_bytes(int64_t n, int64_t k) { return align256(size_t(n) * size_t(k / 32) * 2); }
+
+inline int launch_status(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(Q4DEC_ERR_HIP, "%s: kernel launch failed: %s", what, hipGetErrorString(e));
+  return Q4DEC_OK;
+}
+
+// ------------------------------------------------------------- device side
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Packed layout of one 32-weight block (16 bytes, four dwords). Dword q holds
+// the codes of k = 8q .. 8q+7 as unsigned nibbles n = c + 8:
+//   byte0 = n[8q+0] | n[8q+2] << 4      byte1 = n[8q+4] | n[8q+6] << 4
+//   byte2 = n[8q+1] | n[8q+3] << 4      byte3 = n[8q+5] | n[8q+7] << 4
+// so masking a dword with 0x000F000F yields the pair (k=8q, 8q+1) in the low
+// nibble of each 16-bit half, 0x00F000F0 the pair (8q+2, 8q+3), and the same
+// two masks on dword >> 8 the pairs (8q+4, 8q+5) and (8q+6, 8q+7).
+__device__ __forceinline__ uint32_t pack_dword(const int8_t* c8) {
+  auto nb = [&](int i) -> uint32_t { return uint32_t(c8[i] + 8) & 15u; };
+  uint32_t b0 = nb(0) | (nb(2) << 4);
+  uint32_t b1 = nb(4) | (nb(6) << 4);
+  uint32_t b2 = nb(1) | (nb(3) << 4);
+  uint32_t b3 = nb(5) | (nb(7) << 4);
+  return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+}
+
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t orv) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(mask), "v"(orv));
+  return r;
+}
+
+// Exact fp16 code pairs of one dword. 0x6400 is fp16 1024 with unit spacing,
+// so OR-ing a nibble n into bits 0-3 gives 1024 + n and into bits 4-7 gives
+// 1024 + 16 n; subtracting 1032, or scaling by 1/16 and subtracting 72,
+// leaves c = n - 8 exactly.
+struct CodePairs { half2_t p[4]; };
+__device__ __forceinline__ CodePairs unpack_dword(uint32_t w, uint32_t m_lo, uint32_t m_hi, uint32_t magic) {
+  const half2_t off_lo = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const half2_t sc_hi = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const half2_t off_hi = {(_Float16)-72.0f, (_Float16)-72.0f};
+  uint32_t w8 = w >> 8;
+  CodePairs r;
+  r.p[0] = __builtin_bit_cast(half2_t, and_or(w, m_lo, magic)) + off_lo;
+  r.p[1] = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, and_or(w, m_hi, magic)), sc_hi, off_hi);
+  r.p[2] = __builtin_bit_cast(half2_t, and_or(w8, m_lo, magic)) + off_lo;
+  r.p[3] = __builtin_elementwise_fma(__builtin_bit_cast(half2_t, and_or(w8, m_hi, magic)), sc_hi, off_hi);
+  return r;
+}
+
+// sum_{j<32} c_j * x'_j for one block, with x' as 16 fp16 pairs (k order).
+__device__ __forceinline__ float block_dot(uint4 q, const uint32_t* xh, uint32_t m_lo, uint32_t m_hi, uint32_t magic) {
+  float acc = 0.0f;
+  const uint32_t ws[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    CodePairs cp = unpack_dword(ws[i], m_lo, m_hi, magic);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc = __builtin_amdgcn_fdot2(cp.p[j], __builtin_bit_cast(half2_t, xh[4 * i + j]), acc, false);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h16) {
+  return __builtin_bit_cast(float, h16 << 16);
+}
+
+// Convert the 32 bf16 activations of one block into 16 fp16 pairs scaled by
+// 2^-E, with E chosen from the block's largest exponent so the largest
+// magnitude lands in [2^14, 2^15): every bf16 value keeps its 8-bit
+// significand unless it is below max * 2^-31. Returns 2^E as fp32.
+__device__ __forceinline__ float convert_x_block(const uint16_t* xb, uint32_t* out16) {
+  const uint4* src = reinterpret_cast<const uint4*>(xb);
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint4 v = src[i];
+    w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+  }
+  uint32_t emax = 1;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    uint32_t lo = (w[i] >> 7) & 0xFFu, hi = (w[i] >> 23) & 0xFFu;
+    emax = max(emax, max(lo, hi));
+  }
+  const int e = int(emax) - 127 - 14;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float a = ldexpf(bf16_to_f32(w[i] & 0xFFFFu), -e);
+    float b = ldexpf(bf16_to_f32(w[i] >> 16), -e);
+    half2_t h = {(_Float16)a, (_Float16)b};
+    out16[i] = __builtin_bit_cast(uint32_t, h);
+  }
+  return ldexpf(1.0f, e);
+}
+
+// ---- cross-lane sums ------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// Sum over aligned groups of L lanes (L in 4..64); every lane of the group
+// receives the total.
+template <int L>
+__device__ __forceinline__ float group_sum(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  if constexpr (L >= 8) v += dpp_f<0x141>(v);   // row_half_mirror
+  if constexpr (L >= 16) v += dpp_f<0x140>(v);  // row_mirror
+  if constexpr (L >= 32) v += __shfl_xor(v, 16);
+  if constexpr (L >= 64) v += __shfl_xor(v, 32);
+  return v;
+}
+
+// (value desc, index asc) comparator for the argmax; NaN never wins.
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+}  // namespace q4dec

@@ -1,0 +1,132 @@
+"""CPU checks of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before touching the
+GPU (no compute call is made here)."""
+import ctypes
+import os
+
+import pytest
+
+import int4_weight_only_block_amd as q4
+
+pytestmark = pytest.mark.skipif(not os.path.exists(q4.LIB_PATH), reason="libq4dec.so not built")
+
+EXPECTED = {
+    "q4dec_abi_version", "q4dec_last_error", "q4_packed_bytes", "q4_pack", "q4_gemv",
+    "q4_gemm_s64", "lmhead_workspace_bytes", "lmhead_softcap_argmax", "ple_gather",
+}
+
+
+def test_header_declares_expected_functions():
+    assert set(q4.header_functions()) == EXPECTED
+
+
+def test_library_exports_every_header_symbol():
+    h = ctypes.CDLL(q4.LIB_PATH)
+    for name in q4.header_functions():
+        assert hasattr(h, name), name
+    assert q4.q4dec_abi_version() == q4.ABI_VERSION
+
+
+def test_packed_bytes():
+    assert q4.q4_packed_bytes(1536, 1536) == 1536 * 768 + 1536 * 48 * 2
+    assert q4.q4_packed_bytes(262144, 1536) == 226_492_416
+    assert q4.q4_packed_bytes(3, 32) == 256 + 256  # each plane padded to 256 B
+    assert q4.q4_packed_bytes(4, 33) == 0
+    assert q4.q4_packed_bytes(0, 32) == 0
+    assert q4.q4_packed_bytes(-1, 32) == 0
+    assert q4.lmhead_workspace_bytes(262144, 1536) >= 8
+
+
+FAKE = 0x10000  # 64 KiB-aligned non-NULL address; never dereferenced
+
+
+def _rc_and_msg(rc):
+    return rc, q4.q4dec_last_error()
+
+
+def test_gemv_validation():
+    L = q4.lib()
+    rc, msg = _rc_and_msg(L.q4_gemv(None, 16, 32, FAKE, FAKE, None))
+    assert rc == q4.ERR_NULL and "packed" in msg
+    rc, msg = _rc_and_msg(L.q4_gemv(FAKE, 16, 32, None, FAKE, None))
+    assert rc == q4.ERR_NULL and "x" in msg
+    rc, msg = _rc_and_msg(L.q4_gemv(FAKE, 16, 32, FAKE, None, None))
+    assert rc == q4.ERR_NULL and "y" in msg
+    rc, msg = _rc_and_msg(L.q4_gemv(FAKE, 0, 32, FAKE, FAKE, None))
+    assert rc == q4.ERR_SHAPE and "n" in msg
+    rc, msg = _rc_and_msg(L.q4_gemv(FAKE, 16, 48, FAKE, FAKE, None))
+    assert rc == q4.ERR_SHAPE and "k" in msg
+    rc, msg = _rc_and_msg(L.q4_gemv(FAKE, 16, q4.MAX_K + 32, FAKE, FAKE, None))
+    assert rc == q4.ERR_UNSUPPORTED
+    rc, msg = _rc_and_msg(L.q4_gemv(FAKE + 4, 16, 32, FAKE, FAKE, None))
+    assert rc == q4.ERR_ALIGN and "packed" in msg
+    rc, msg = _rc_and_msg(L.q4_gemv(FAKE, 16, 32, FAKE + 2, FAKE, None))
+    assert rc == q4.ERR_ALIGN and "x" in msg
+    rc, msg = _rc_and_msg(L.q4_gemv(FAKE, 16, 32, FAKE, FAKE + 2, None))
+    assert rc == q4.ERR_ALIGN and "y" in msg
+    rc, msg = _rc_and_msg(L.q4_gemv(FAKE, 1 << 31, 32, FAKE, FAKE, None))
+    assert rc == q4.ERR_SHAPE
+
+
+def test_pack_validation():
+    L = q4.lib()
+    assert L.q4_pack(None, FAKE, 4, 32, FAKE, None, None) == q4.ERR_NULL
+    assert L.q4_pack(FAKE, None, 4, 32, FAKE, None, None) == q4.ERR_NULL
+    assert L.q4_pack(FAKE, FAKE, 4, 32, None, None, None) == q4.ERR_NULL
+    assert L.q4_pack(FAKE, FAKE, 4, 31, FAKE, None, None) == q4.ERR_SHAPE
+    assert L.q4_pack(FAKE, FAKE, -4, 32, FAKE, None, None) == q4.ERR_SHAPE
+    assert L.q4_pack(FAKE, FAKE, 4, 32, FAKE + 8, None, None) == q4.ERR_ALIGN
+    assert "packed" in q4.q4dec_last_error()
+
+
+def test_lmhead_validation():
+    L = q4.lib()
+    need = q4.lmhead_workspace_bytes(1024, 64)
+    args = [FAKE, 1024, 64, FAKE, 30.0, FAKE, need, FAKE, FAKE, None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["packed", "vocab", "k", "x", "cap", "ws", "ws_bytes", "idx", "val", "stream"]
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return L.lmhead_softcap_argmax(*a)
+
+    assert call(ws=None) == q4.ERR_NULL and "ws" in q4.q4dec_last_error()
+    assert call(idx=None) == q4.ERR_NULL
+    assert call(val=None) == q4.ERR_NULL
+    assert call(ws_bytes=need - 1) == q4.ERR_WORKSPACE
+    assert call(vocab=0) == q4.ERR_SHAPE and "vocab" in q4.q4dec_last_error()
+    assert call(k=40) == q4.ERR_SHAPE
+    assert call(ws=FAKE + 4) == q4.ERR_ALIGN
+    assert call(idx=FAKE + 2) == q4.ERR_ALIGN
+
+
+def test_gemm_validation():
+    L = q4.lib()
+    assert L.q4_gemm_s64(FAKE, 64, 64, FAKE, 0, FAKE, None) == q4.ERR_SHAPE
+    assert L.q4_gemm_s64(FAKE, 64, 64, FAKE, 65, FAKE, None) == q4.ERR_SHAPE
+    assert L.q4_gemm_s64(None, 64, 64, FAKE, 64, FAKE, None) == q4.ERR_NULL
+    assert L.q4_gemm_s64(FAKE, 64, 48, FAKE, 64, FAKE, None) == q4.ERR_SHAPE
+
+
+def test_ple_validation():
+    L = q4.lib()
+    ok = [FAKE, FAKE, 100, 64, FAKE, 4, 16.0, FAKE, None, None]
+    assert L.ple_gather(None, *ok[1:]) == q4.ERR_NULL
+    a = list(ok); a[2] = 0
+    assert L.ple_gather(*a) == q4.ERR_SHAPE and "vocab" in q4.q4dec_last_error()
+    a = list(ok); a[3] = -1
+    assert L.ple_gather(*a) == q4.ERR_SHAPE and "dim" in q4.q4dec_last_error()
+    a = list(ok); a[5] = -1
+    assert L.ple_gather(*a) == q4.ERR_SHAPE
+    a = list(ok); a[5] = 0  # empty gather is a no-op and touches nothing
+    assert L.ple_gather(*a) == q4.OK
+    a = list(ok); a[7] = FAKE + 2
+    assert L.ple_gather(*a) == q4.ERR_ALIGN
+
+
+def test_binding_rejects_host_tensors():
+    import torch
+
+    with pytest.raises(ValueError):
+        q4.q4_gemv(torch.zeros(100, dtype=torch.uint8), 2, 32, torch.zeros(32, dtype=torch.int16))

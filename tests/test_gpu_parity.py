@@ -1,0 +1,290 @@
+"""GPU parity of the HIP path against the fp64 oracle, through the C ABI.
+
+Bars: bit-exact for packing (one-hot column sweep), integer-exact GEMV cases
+and the PLE gather; |y - y_ref| <= 1e-4 * sum|w x| + 1e-6 for fp32-accumulated
+GEMV outputs; exact argmax indices when the top-2 margin of the capped logits
+is >= 1e-3 (smaller margins are excluded and counted), capped value within the
+GEMV tolerance of the winning row.
+"""
+import struct
+
+import numpy as np
+import pytest
+import torch
+
+import int4_weight_only_block_amd as q4
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = torch.device("cuda:0")
+
+
+def d(a: np.ndarray) -> torch.Tensor:
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(DEV)
+
+
+def fp16_bits(v: float) -> int:
+    return struct.unpack("<H", struct.pack("<e", v))[0]
+
+
+def bf16_bits_of_ints(vals) -> np.ndarray:
+    out = np.array([struct.unpack("<I", struct.pack("<f", float(v)))[0] >> 16 for v in vals], dtype=np.uint16)
+    return out
+
+
+def pack(codes, sb):
+    return q4.q4_pack(d(codes), d(sb))
+
+
+def assert_within_tol(y_gpu, y_ref, a_ref, what=""):
+    y = np.asarray(y_gpu, dtype=np.float64)
+    err = np.abs(y - y_ref)
+    tol = oracle.gemv_tolerance(a_ref)
+    bad = np.nonzero(~(err <= tol))[0]
+    assert bad.size == 0, (f"{what}: {bad.size} outputs over tolerance, first {bad[:5]}, "
+                           f"err/tol {float(np.max(err / tol)):.3g}")
+    return float(np.max(err / tol))
+
+
+# K values covering every (lanes per row, blocks per lane) kernel variant,
+# including ragged block counts
+K_VARIANTS = [32, 64, 96, 160, 1536, 2048, 2560, 3072, 4096, 5120, 6144, 8192, 10240, 12288, 14336, 16384]
+
+
+@pytest.mark.parametrize("k", K_VARIANTS)
+def test_gemv_integer_exact(k):
+    """Power-of-two scales and integer activations: every partial sum is
+    exact in fp32 in any order, so the GPU must equal the oracle bit-exactly."""
+    rng = np.random.default_rng(100 + k)
+    n = 77 if k > 4096 else 301  # ragged row counts: not a multiple of any row-group size
+    codes = rng.integers(-8, 8, size=(n, k), dtype=np.int8)
+    p = rng.integers(6, 9, size=(n, k // 32))
+    sb = np.vectorize(lambda e: fp16_bits(2.0 ** -int(e)))(p).astype(np.uint16)
+    x = bf16_bits_of_ints(rng.integers(-8, 9, size=k))
+    y = q4.q4_gemv(pack(codes, sb), n, k, d(x)).cpu().numpy()
+    yr, _ = oracle.gemv(codes, sb, x)
+    assert np.array_equal(y.astype(np.float64), yr)
+
+
+@pytest.mark.parametrize("n,k", [(1536, 1536), (1, 1536), (3, 32), (1000, 2560), (513, 10240), (64, 16384)])
+def test_gemv_random_tolerance(n, k):
+    rng = synth.rng_for(0, n, k)
+    codes, sb = synth.q4_weights(rng, n, k)
+    x = synth.bf16_normal(rng, k)
+    y = q4.q4_gemv(pack(codes, sb), n, k, d(x)).cpu().numpy()
+    yr, a = oracle.gemv(codes, sb, x)
+    assert_within_tol(y, yr, a, f"gemv {n}x{k}")
+
+
+def test_pack_layout_onehot_full_sweep():
+    """x = e_k for every k of the 1536 x 1536 matrix returns column k exactly:
+    a complete pin of the packed layout, the nibble offset and scale indexing."""
+    n = k = 1536
+    rng = synth.rng_for(0)
+    codes, sb = synth.q4_weights(rng, n, k)
+    packed = pack(codes, sb)
+    eye = np.zeros((k, k), dtype=np.uint16)
+    eye[np.arange(k), np.arange(k)] = 0x3F80  # bf16 1.0
+    xs = d(eye)
+    out = torch.empty((k, n), dtype=torch.float32, device=DEV)
+    for kk in range(k):
+        q4.q4_gemv(packed, n, k, xs[kk], out[kk])
+    got = out.cpu().numpy().T.astype(np.float64)
+    assert np.array_equal(got, oracle.dequant(codes, sb))
+
+
+def test_gemv_degenerate_inputs():
+    rng = synth.rng_for(1)
+    n, k = 300, 2560
+    codes, sb = synth.q4_weights(rng, n, k)
+    x = synth.bf16_normal(rng, k)
+    # all-zero codes: exactly zero
+    y = q4.q4_gemv(pack(np.zeros_like(codes), sb), n, k, d(x)).cpu().numpy()
+    assert (y == 0).all()
+    # all-zero activations: exactly zero
+    packed = pack(codes, sb)
+    y = q4.q4_gemv(packed, n, k, d(np.zeros(k, np.uint16))).cpu().numpy()
+    assert (y == 0).all()
+    # extreme codes -8 / 7
+    for c in (-8, 7):
+        cc = np.full_like(codes, c)
+        y = q4.q4_gemv(pack(cc, sb), n, k, d(x)).cpu().numpy()
+        yr, a = oracle.gemv(cc, sb, x)
+        assert_within_tol(y, yr, a, f"codes {c}")
+    # wide dynamic range of activations inside one block and across blocks
+    xf = rng.standard_normal(k).astype(np.float32)
+    xf[::7] *= 1e20
+    xf[3::11] *= 1e-25
+    xf[64:96] *= 1e-30
+    xw = synth.f32_to_bf16_bits(xf)
+    y = q4.q4_gemv(packed, n, k, d(xw)).cpu().numpy()
+    yr, a = oracle.gemv(codes, sb, xw)
+    assert_within_tol(y, yr, a, "wide range")
+
+
+def test_pack_err_flag():
+    codes = np.zeros((4, 64), dtype=np.int8)
+    sb = np.full((4, 2), fp16_bits(1.0), dtype=np.uint16)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    q4.q4_pack(d(codes), d(sb), err_flag=flag)
+    assert int(flag.item()) == 0
+    codes[2, 5] = 9
+    q4.q4_pack(d(codes), d(sb), err_flag=flag)
+    assert int(flag.item()) == 1
+
+
+def test_ffn_pair():
+    """E2B FFN: fused gate+up GEMV [2*6144, 1536], host fp32 GELU-tanh * up
+    rounded to bf16, down GEMV [1536, 6144]. The oracle's bf16 product feeds
+    both sides so each GEMV is checked on its own."""
+    s = synth.SHAPES["ffn_e2b"]
+    rng = synth.rng_for(0, 2)
+    gu_codes, gu_sb = synth.q4_weights(rng, *s["gate_up"])
+    dn_codes, dn_sb = synth.q4_weights(rng, *s["down"])
+    x = synth.bf16_normal(rng, s["gate_up"][1])
+    gu = q4.q4_gemv(pack(gu_codes, gu_sb), *s["gate_up"], d(x)).cpu().numpy()
+    gur, gua = oracle.gemv(gu_codes, gu_sb, x)
+    assert_within_tol(gu, gur, gua, "gate_up")
+    inter = s["inter"]
+    a_bits = oracle.ffn_down_input_bits(gur[:inter].astype(np.float32), gur[inter:].astype(np.float32))
+    y = q4.q4_gemv(pack(dn_codes, dn_sb), *s["down"], d(a_bits)).cpu().numpy()
+    yr, ya = oracle.gemv(dn_codes, dn_sb, a_bits)
+    assert_within_tol(y, yr, ya, "down")
+
+
+@pytest.mark.parametrize("name", ["qkv", "o", "gate_up", "down"])
+def test_gemv_e4b_layer_shapes(name):
+    shapes = {"qkv": (3072, 2560), "o": (2560, 2048), "gate_up": (20480, 2560), "down": (2560, 10240)}
+    n, k = shapes[name]
+    rng = synth.rng_for(5, list(shapes).index(name))
+    codes, sb = synth.q4_weights(rng, n, k)
+    x = synth.bf16_normal(rng, k)
+    y = q4.q4_gemv(pack(codes, sb), n, k, d(x)).cpu().numpy()
+    yr, a = oracle.gemv(codes, sb, x)
+    assert_within_tol(y, yr, a, name)
+
+
+# ------------------------------------------------------------------- head --
+def _check_head_batch(codes, sb, xs, cap=30.0):
+    vocab, k = codes.shape
+    packed = pack(codes, sb)
+    ws = torch.empty(q4.lmhead_workspace_bytes(vocab, k), dtype=torch.uint8, device=DEV)
+    got = []
+    for x in xs:
+        i, v = q4.lmhead_softcap_argmax(packed, vocab, k, d(x), cap, ws)
+        got.append((int(i.item()), float(v.item())))
+    z, a = oracle.gemm(codes, sb, np.stack(xs))
+    excluded = 0
+    for s, (gi, gv) in enumerate(got):
+        c = oracle.softcap(z[s], cap)
+        ri = oracle.first_argmax(c)
+        m = oracle.top2_margin(c)
+        if m >= 1e-3:
+            assert gi == ri, (s, gi, ri, m)
+        else:
+            excluded += 1
+            assert c[ri] - c[gi] < 1e-3 + 1e-4 * a[s, gi] + 1e-6
+        assert abs(gv - c[ri]) <= 1e-4 * a[s, ri] + 1e-6, (s, gv, c[ri])
+    return excluded
+
+
+def test_lmhead_e2b_full_100_vectors():
+    s = synth.SHAPES["head_e2b"]
+    rng = synth.rng_for(0, 3)
+    codes, sb = synth.q4_weights(rng, s["vocab"], s["k"])
+    xs = [synth.bf16_normal(rng, s["k"]) for _ in range(s["n_vectors"])]
+    excluded = _check_head_batch(codes, sb, xs)
+    print(f"head: {excluded} of {len(xs)} vectors excluded (top-2 margin < 1e-3)")
+    assert excluded <= 5
+
+
+def test_lmhead_planted_ties_and_boundaries():
+    vocab, k = 262144, 1536
+    rng = synth.rng_for(7)
+    codes = rng.integers(-2, 3, size=(vocab, k), dtype=np.int8)
+    sb = np.full((vocab, k // 32), fp16_bits(2.0 ** -7), dtype=np.uint16)
+    xi = rng.integers(-3, 4, size=k)
+    x = bf16_bits_of_ints(xi)
+    planted = np.where(xi > 0, 7, np.where(xi < 0, -8, 0)).astype(np.int8)
+    packed_rows = {}
+    for rows, expect in [((5, 77777, 262143), 5), ((262143,), 262143), ((0, 262143), 0),
+                         ((1023, 1024, 4096), 1023)]:
+        cc = codes.copy()
+        for r in rows:
+            cc[r] = planted
+        packed = pack(cc, sb)
+        i, v = q4.lmhead_softcap_argmax(packed, vocab, k, d(x), 30.0)
+        assert int(i.item()) == expect, rows
+        zr = float(sum(int(planted[j]) * int(xi[j]) for j in range(k))) / 128.0
+        assert abs(float(v.item()) - float(oracle.softcap(zr))) <= 1e-6 + 1e-4 * abs(zr)
+        packed_rows[rows] = packed
+    # cap <= 0 returns the raw logit (exact for integer inputs)
+    i, v = q4.lmhead_softcap_argmax(packed_rows[(262143,)], vocab, k, d(x), 0.0)
+    assert int(i.item()) == 262143
+    assert float(v.item()) == float(sum(int(planted[j]) * int(xi[j]) for j in range(k))) / 128.0
+
+
+def test_lmhead_small_vocab_ragged():
+    for vocab, k in [(1, 64), (3, 32), (1000, 1536), (4099, 2560), (777, 10240)]:
+        rng = synth.rng_for(11, vocab, k)
+        codes, sb = synth.q4_weights(rng, vocab, k)
+        xs = [synth.bf16_normal(rng, k) for _ in range(3)]
+        _check_head_batch(codes, sb, xs)
+
+
+def test_lmhead_e4b_head_shape():
+    rng = synth.rng_for(0, 4)
+    codes, sb = synth.q4_weights(rng, 262144, 2560)
+    xs = [synth.bf16_normal(rng, 2560) for _ in range(4)]
+    _check_head_batch(codes, sb, xs)
+
+
+# -------------------------------------------------------------------- PLE --
+@pytest.mark.parametrize("dim", [8960, 10752])
+def test_ple_gather_full_tables(dim):
+    vocab = synth.VOCAB
+    g = torch.Generator(device=DEV)
+    g.manual_seed(1234 + dim)
+    table = torch.randint(-127, 128, (vocab, dim), dtype=torch.int8, device=DEV, generator=g)
+    scale = torch.empty(vocab, dtype=torch.float32, device=DEV).uniform_(1e-3, 1e-2, generator=g)
+    rng = synth.rng_for(0, dim)
+    for n_ids in (1, 64):
+        ids = synth.ple_ids(rng, vocab, n_ids)
+        if n_ids == 64:
+            ids[:4] = [0, vocab - 1, ids[10], ids[10]]  # boundaries and duplicates
+        idt = d(ids)
+        out = q4.ple_gather(table, scale, idt, 16.0).cpu().numpy()
+        rows = table[idt.long()].cpu().numpy()
+        rsc = scale[idt.long()].cpu().numpy()
+        ref, err = oracle.ple_gather(rows, rsc, np.arange(n_ids, dtype=np.int32), 16.0)
+        assert err == 0
+        assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+
+
+def test_ple_gather_general_multiplier_and_ragged_dim():
+    rng = synth.rng_for(3)
+    for dim in (8960, 100, 7, 4096 + 3):
+        table, scale, ids = synth.ple_inputs(rng, 5000, dim, 37)
+        for mult in (16.0, float(np.float32(np.sqrt(1536.0))), 0.3):
+            out = q4.ple_gather(d(table), d(scale), d(ids), mult).cpu().numpy()
+            ref, _ = oracle.ple_gather(table, scale, ids, mult)
+            assert np.array_equal(out.view(np.uint32), ref.view(np.uint32)), (dim, mult)
+
+
+def test_ple_gather_out_of_range_ids():
+    rng = synth.rng_for(4)
+    table, scale, _ = synth.ple_inputs(rng, 100, 256, 1)
+    ids = np.array([3, -1, 100, 99], dtype=np.int32)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = q4.ple_gather(d(table), d(scale), d(ids), 16.0, err_flag=flag).cpu().numpy()
+    ref, err = oracle.ple_gather(table, scale, ids, 16.0)
+    assert int(flag.item()) == 1 and err == 1
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+    flag.zero_()
+    q4.ple_gather(d(table), d(scale), d(np.array([0, 99], np.int32)), 16.0, err_flag=flag)
+    assert int(flag.item()) == 0
