@@ -1,0 +1,372 @@
+"""Benchmark: one E4B-shaped S=1 decode step of the q4_0 hot path on one GPU.
+
+A step is one pass of the whole hot path over one token:
+  PLE gather (one id, E4B table [262144, 10752] int8, x16.0)
+  -> 42 layers x {QKV [3072, 2560], O [2560, 2048], gate+up [20480, 2560],
+                  down [2560, 10240]} q4_0 GEMVs
+  -> LM head [262144, 2560] GEMV + softcap 30 + argmax.
+Each GEMV reads its own resident bf16 N(0,1) activation vector; the kernels
+run in dependency order on one stream, captured once in a HIP graph and
+replayed. Weight bytes per step: 2,545,090,560 (0.5625 B per weight).
+
+Prints ONE JSON line: value = decode-step weight bytes / step time (GB/s),
+plus the roofline of the kernel that takes the most time per step (per-launch
+durations from back-to-back HIP event pairs on the launch stream), the LM head
+roofline, the S=64 prefill step when the GEMM is available, and the fp64
+oracle timed on a bounded sample on the host cores.
+
+Only one GPU is used; --gpus N with N > 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "q4_0 GEMV/LM-head achieved HBM GB/s (% of peak); decode-step weight bytes/s"
+HBM_PEAK_GBS = 8000.0
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "hbm_counters.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "int4_weight_only_block_amd", "csrc", f)
+                  for f in ("q4_gemv.hip", "q4dec_internal.h")]
+
+
+def q4_bytes(n: int, k: int) -> int:
+    """Algorithmic bytes of one q4_0 GEMV launch: nibbles + fp16 scales +
+    bf16 activations + fp32 outputs."""
+    return n * k // 2 + n * (k // 32) * 2 + 2 * k + 4 * n
+
+
+def weight_bytes(n: int, k: int) -> int:
+    return n * k // 2 + n * (k // 32) * 2
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe", action="store_true", help="skip per-kernel event timing")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+class Workload:
+    """Resident inputs of one decode step (drawn on the GPU, seeded)."""
+
+    def __init__(self, dev, seed: int):
+        import torch
+
+        import int4_weight_only_block_amd as q4
+        import synth
+
+        self.q4 = q4
+        g = torch.Generator(device=dev)
+        g.manual_seed(seed)
+        self.mats = synth.stack_e4b_matrices()
+        self.packed, self.xs, self.ys = [], [], []
+        for _, n, k in self.mats:
+            codes, scales = synth.torch_q4_weights(g, n, k, dev)
+            self.packed.append(q4.q4_pack(codes, scales))
+            del codes, scales
+            self.xs.append(synth.torch_bf16_normal(g, k, dev))
+            self.ys.append(torch.empty(n, dtype=torch.float32, device=dev))
+        s = synth.SHAPES["ple_e4b"]
+        self.vocab = s["vocab"]
+        self.ple_dim = s["dim"]
+        self.table = torch.randint(-127, 128, (s["vocab"], s["dim"]), dtype=torch.int8, device=dev,
+                                   generator=g)
+        self.scale = torch.empty(s["vocab"], dtype=torch.float32, device=dev).uniform_(1e-3, 1e-2, generator=g)
+        self.ids = torch.randint(0, s["vocab"], (1,), dtype=torch.int32, device=dev, generator=g)
+        self.ple_out = torch.empty((1, s["dim"]), dtype=torch.float32, device=dev)
+        hn, hk = self.mats[-1][1], self.mats[-1][2]
+        self.head_nk = (hn, hk)
+        self.ws = torch.empty(q4.lmhead_workspace_bytes(hn, hk), dtype=torch.uint8, device=dev)
+        self.idx = torch.empty(1, dtype=torch.int32, device=dev)
+        self.val = torch.empty(1, dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+
+    # one kernel-enqueuing callable per launch, in step order
+    def launches(self):
+        q4 = self.q4
+        out = [("ple", lambda: q4.ple_gather(self.table, self.scale, self.ids, 16.0, out=self.ple_out))]
+        for i, (name, n, k) in enumerate(self.mats[:-1]):
+            out.append((name.split(".")[1], (lambda i=i, n=n, k=k: q4.q4_gemv(self.packed[i], n, k, self.xs[i],
+                                                                               self.ys[i]))))
+        hn, hk = self.head_nk
+        out.append(("head", lambda: q4.lmhead_softcap_argmax(self.packed[-1], hn, hk, self.xs[-1], 30.0, self.ws,
+                                                             self.idx, self.val)))
+        return out
+
+    def step(self):
+        for _, fn in self.launches():
+            fn()
+
+    def weight_bytes(self) -> int:
+        return sum(weight_bytes(n, k) for _, n, k in self.mats)
+
+
+def sleep_blocker(torch, ms: float):
+    """Enqueue a GPU spin of about `ms` milliseconds so the launches queued
+    behind it run back to back."""
+    if not hasattr(torch.cuda, "_sleep"):
+        a = torch.empty((4096, 4096), dtype=torch.float32, device="cuda")
+        for _ in range(max(1, int(ms / 2))):
+            a = a @ a * 0.0
+        return
+    cycles = int(getattr(sleep_blocker, "cycles_per_ms", 1e5) * ms)
+    torch.cuda._sleep(cycles)
+
+
+def calibrate_sleep(torch):
+    if not hasattr(torch.cuda, "_sleep"):
+        return
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    torch.cuda._sleep(1_000_000)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = max(e0.elapsed_time(e1), 1e-3)
+    sleep_blocker.cycles_per_ms = 1_000_000 / ms
+
+
+def probe_kernels(torch, wl: Workload, reps: int = 5):
+    """Per-launch durations (ms) by launch kind, from HIP event pairs around
+    each launch on the launch stream while the stream is backed up."""
+    launches = wl.launches()
+    calibrate_sleep(torch)
+    per_kind: dict[str, list[float]] = {}
+    for _ in range(reps):
+        pairs = []
+        torch.cuda.synchronize()
+        sleep_blocker(torch, 40.0)
+        for kind, fn in launches:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            pairs.append((kind, e0, e1))
+        torch.cuda.synchronize()
+        for kind, e0, e1 in pairs:
+            per_kind.setdefault(kind, []).append(e0.elapsed_time(e1))
+    return per_kind
+
+
+def cpu_baseline(seconds: float):
+    """fp64 oracle on a bounded sample of the decode step: whole matrices of
+    layer 0 (QKV, O, gate+up, down) and then row slices of the head until the
+    time budget is spent. Returns weight-GB/s on the host cores."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    import synth
+
+    rng = synth.rng_for(0, 99)
+    sample = [("qkv", 3072, 2560), ("o", 2560, 2048), ("gate_up", 20480, 2560), ("down", 2560, 10240)]
+    mats = []
+    for name, n, k in sample:
+        codes, sb = synth.q4_weights(rng, n, k)
+        mats.append((name, codes, sb, synth.bf16_normal(rng, k)))
+    head_rows = 16384
+    hc, hs = synth.q4_weights(rng, head_rows, 2560)
+    hx = synth.bf16_normal(rng, 2560)
+    done_bytes = 0
+    parts = []
+    t0 = time.perf_counter()
+    for name, codes, sb, x in mats:
+        oracle.gemv(codes, sb, x)
+        done_bytes += weight_bytes(*codes.shape)
+        parts.append(name)
+    n_head = 0
+    while time.perf_counter() - t0 < seconds:
+        out = oracle.lmhead(hc, hs, hx)
+        assert out["idx"] >= 0
+        done_bytes += weight_bytes(head_rows, 2560)
+        n_head += head_rows
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {
+        "value": round(done_bytes / dt / 1e9, 3),
+        "unit": "GB/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle: E4B layer-0 {'/'.join(parts)} GEMVs plus {n_head} head rows "
+                   f"[{head_rows}-row slices of 262144x2560 with softcap+argmax]; "
+                   f"{done_bytes / 1e9:.3f} GB of q4_0 weights in {dt:.1f} s"),
+        "host_cpus": os.cpu_count(),
+    }
+
+
+def load_traffic(kernel: str, launches_per_step: dict):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    summaries, scaled by the copy-kernel calibration; None when absent or
+    when the kernel source changed since the counters were taken."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    with open(COUNTERS_FILE) as f:
+        c = json.load(f)
+    if c.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    k = c.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return k.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the hot path is built and measured on one GPU's share; see DESIGN.md for sharding)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "copies": 3}))
+        return
+
+    wl = Workload(dev, args.seed)
+    wl.step()  # eager pass: lazy init, device property cache
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        wl.step()
+    for _ in range(max(args.warmup, 0)):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    wbytes = wl.weight_bytes()
+    value = wbytes / (ms_step * 1e-3) / 1e9
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16*f16->f32",
+        "data": "synthetic (seeded on-device draws: codes U[-8,7], fp16 scales U[1e-3,2e-2], bf16 N(0,1))",
+        "config": {
+            "workload": "e4b_decode_step_s1",
+            "layers": 42, "hidden": 2560, "intermediate": 10240, "q_heads": 8, "kv_heads": 2,
+            "head_dim": 256, "vocab": 262144, "ple_dim": 10752, "softcap": 30.0,
+            "weight_bytes_per_step": wbytes, "launches_per_step": 1 + 168 + 2,
+            "graph": "hip graph, one stream",
+        },
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "timed_wall_s": round(wall, 3),
+    }
+
+    if not args.no_probe:
+        per_kind = probe_kernels(torch, wl)
+        shapes = {name.split(".")[-1] if "." in name else name: (n, k) for name, n, k in wl.mats}
+        groups = {
+            # kernel instantiation -> launch kinds it serves
+            "q4_rows_kernel<16,5,gemv> (K=2560: qkv, gate_up)": ["qkv", "gate_up"],
+            "q4_rows_kernel<16,4,gemv> (K=2048: o)": ["o"],
+            "q4_rows_kernel<64,5,gemv> (K=10240: down)": ["down"],
+            "q4_rows_kernel<16,5,head> + reduce (K=2560 head)": ["head"],
+            "ple_gather_kernel": ["ple"],
+        }
+        kernels = {}
+        for gname, kinds in groups.items():
+            tot_ms, tot_bytes, count = 0.0, 0, 0
+            for kind in kinds:
+                durs = per_kind.get(kind, [])
+                if not durs:
+                    continue
+                mean = sum(durs) / len(durs)
+                per_step = sum(1 for kk, _ in wl.launches() if kk == kind)
+                if kind == "ple":
+                    b = 4 + 4 + wl.ple_dim * (1 + 4)
+                else:
+                    n, k = shapes[kind] if kind != "head" else wl.head_nk
+                    b = q4_bytes(n, k) + (8 if kind == "head" else 0)
+                tot_ms += mean * per_step
+                tot_bytes += b * per_step
+                count += per_step
+            if count:
+                avg_ms = tot_ms / count
+                kernels[gname] = {
+                    "launches_per_step": count,
+                    "avg_launch_us": round(avg_ms * 1e3, 3),
+                    "ms_per_step": round(tot_ms, 4),
+                    "bytes_per_launch": tot_bytes // count,
+                    "achieved_GBs": round(tot_bytes / count / (avg_ms * 1e-3) / 1e9, 1),
+                }
+        result["kernels"] = kernels
+        dominant = max((g for g in kernels if not g.startswith("ple")), key=lambda g: kernels[g]["ms_per_step"])
+        kd = kernels[dominant]
+        result["roofline"] = {
+            "kernel": dominant,
+            "bound": "hbm",
+            "achieved": kd["achieved_GBs"],
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(kd["achieved_GBs"] / HBM_PEAK_GBS, 4),
+            "traffic": load_traffic(dominant, kd),
+            "avg_launch_us": kd["avg_launch_us"],
+            "bytes_per_launch": kd["bytes_per_launch"],
+        }
+        hk = "q4_rows_kernel<16,5,head> + reduce (K=2560 head)"
+        if hk in kernels:
+            kh = kernels[hk]
+            result["roofline_lmhead"] = {
+                "bound": "hbm", "achieved": kh["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(kh["achieved_GBs"] / HBM_PEAK_GBS, 4), "traffic": load_traffic(hk, kh),
+                "avg_launch_us": kh["avg_launch_us"], "bytes_per_launch": kh["bytes_per_launch"],
+            }
+        result["kernel_time_sum_ms"] = round(sum(v["ms_per_step"] for v in kernels.values()), 4)
+        result["launch_gap_ms_per_step"] = round(ms_step - result["kernel_time_sum_ms"], 4)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
