@@ -121,55 +121,54 @@ class Workload:
         for _, fn in self.launches():
             fn()
 
+    def head_copies_launches(self):
+        """Head launches over the resident head and two more copies of it
+        (1.1 GB in rotation), for timing the head kernel on its own."""
+        import torch
+
+        if not hasattr(self, "_head_copies"):
+            self._head_copies = [self.packed[-1]] + [self.packed[-1].clone() for _ in range(2)]
+            torch.cuda.synchronize()
+        q4, (hn, hk) = self.q4, self.head_nk
+        return [lambda p=p: q4.lmhead_softcap_argmax(p, hn, hk, self.xs[-1], 30.0, self.ws, self.idx, self.val)
+                for p in self._head_copies]
+
     def weight_bytes(self) -> int:
         return sum(weight_bytes(n, k) for _, n, k in self.mats)
 
 
-def sleep_blocker(torch, ms: float):
-    """Enqueue a GPU spin of about `ms` milliseconds so the launches queued
-    behind it run back to back."""
-    if not hasattr(torch.cuda, "_sleep"):
-        a = torch.empty((4096, 4096), dtype=torch.float32, device="cuda")
-        for _ in range(max(1, int(ms / 2))):
-            a = a @ a * 0.0
-        return
-    cycles = int(getattr(sleep_blocker, "cycles_per_ms", 1e5) * ms)
-    torch.cuda._sleep(cycles)
-
-
-def calibrate_sleep(torch):
-    if not hasattr(torch.cuda, "_sleep"):
-        return
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    torch.cuda._sleep(1_000_000)
-    e1.record()
-    torch.cuda.synchronize()
-    ms = max(e0.elapsed_time(e1), 1e-3)
-    sleep_blocker.cycles_per_ms = 1_000_000 / ms
-
-
-def probe_kernels(torch, wl: Workload, reps: int = 5):
-    """Per-launch durations (ms) by launch kind, from HIP event pairs around
-    each launch on the launch stream while the stream is backed up."""
+def probe_kernels(torch, wl: Workload, reps: int = 20):
+    """Average per-launch duration (ms) of each launch kind: the launches of
+    one kind (42 distinct matrices per GEMV kind; three distinct copies of the
+    head so consecutive launches cannot hit the infinity cache) are captured
+    in their own HIP graph and replayed between HIP events on the launch
+    stream."""
     launches = wl.launches()
-    calibrate_sleep(torch)
-    per_kind: dict[str, list[float]] = {}
-    for _ in range(reps):
-        pairs = []
+    kinds = []
+    for kind, _ in launches:
+        if kind not in kinds:
+            kinds.append(kind)
+    out = {}
+    for kind in kinds:
+        fns = [fn for kk, fn in launches if kk == kind]
+        if kind == "head":
+            fns = wl.head_copies_launches()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for fn in fns:
+                fn()
+        graph.replay()
+        graph.replay()
         torch.cuda.synchronize()
-        sleep_blocker(torch, 40.0)
-        for kind, fn in launches:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            pairs.append((kind, e0, e1))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
         torch.cuda.synchronize()
-        for kind, e0, e1 in pairs:
-            per_kind.setdefault(kind, []).append(e0.elapsed_time(e1))
-    return per_kind
+        out[kind] = e0.elapsed_time(e1) / (reps * len(fns))
+        del graph
+    return out
 
 
 def cpu_baseline(seconds: float):
@@ -315,10 +314,9 @@ def main():
         for gname, kinds in groups.items():
             tot_ms, tot_bytes, count = 0.0, 0, 0
             for kind in kinds:
-                durs = per_kind.get(kind, [])
-                if not durs:
+                if kind not in per_kind:
                     continue
-                mean = sum(durs) / len(durs)
+                mean = per_kind[kind]
                 per_step = sum(1 for kk, _ in wl.launches() if kk == kind)
                 if kind == "ple":
                     b = 4 + 4 + wl.ple_dim * (1 + 4)

@@ -17,6 +17,10 @@
 #include <math.h>
 #include <limits.h>
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 #include "q4dec_internal.h"
 
 namespace q4dec {
@@ -24,7 +28,60 @@ namespace q4dec {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
-template <int LPR, int BPL, bool HEAD>
+// Per-lane state of the weight stream: this lane's blocks of the row group
+// in flight, its activation registers and the running output state.
+template <int LPR, int BPL, bool FULL>
+struct Lane {
+  uint4 q[BPL];
+  uint32_t s[BPL];
+  uint32_t xr[BPL][16];
+  float fr[BPL];
+
+  __device__ __forceinline__ void load(const uint8_t* __restrict__ nib, const uint16_t* __restrict__ scl, int row,
+                                       int t, int B, size_t row_bytes) {
+    const u32x4* np = reinterpret_cast<const u32x4*>(nib + size_t(row) * row_bytes);
+    const uint16_t* sp = scl + size_t(row) * size_t(B);
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) {
+      const int b = j * LPR + t;
+      if (FULL || b < B) {
+        const u32x4 v = __builtin_nontemporal_load(np + b);
+        q[j] = make_uint4(v.x, v.y, v.z, v.w);
+        s[j] = __builtin_nontemporal_load(sp + b);
+      }
+    }
+  }
+
+  // Dot product of the row group held in q/s; with REFILL, block j's
+  // registers are reloaded from `row_next` right after their last use, so a
+  // row group of loads stays in flight with no second buffer.
+  template <bool REFILL>
+  __device__ __forceinline__ float dot(const uint8_t* __restrict__ nib, const uint16_t* __restrict__ scl,
+                                       int row_next, int t, int B, size_t row_bytes, uint32_t m_lo, uint32_t m_hi,
+                                       uint32_t magic) {
+    const u32x4* np = reinterpret_cast<const u32x4*>(nib + size_t(row_next) * row_bytes);
+    const uint16_t* sp = scl + size_t(row_next) * size_t(B);
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) {
+      const int b = j * LPR + t;
+      if (FULL || b < B) {
+        const float p = block_dot(q[j], xr[j], m_lo, m_hi, magic);
+        const float d = float(__builtin_bit_cast(_Float16, uint16_t(s[j])));
+        acc = fmaf(d * p, fr[j], acc);
+        if constexpr (REFILL) {
+          __builtin_amdgcn_sched_barrier(0);
+          const u32x4 v = __builtin_nontemporal_load(np + b);
+          q[j] = make_uint4(v.x, v.y, v.z, v.w);
+          s[j] = __builtin_nontemporal_load(sp + b);
+        }
+      }
+    }
+    return acc;
+  }
+};
+
+template <int LPR, int BPL, bool HEAD, bool FULL>
 __global__ __launch_bounds__(kThreads) void q4_rows_kernel(const uint8_t* __restrict__ nib,
                                                            const uint16_t* __restrict__ scl,
                                                            const uint16_t* __restrict__ x, int n, int k, int ipw,
@@ -34,33 +91,44 @@ __global__ __launch_bounds__(kThreads) void q4_rows_kernel(const uint8_t* __rest
   __shared__ uint32_t xs[MAXB * 16];
   __shared__ float xf[MAXB];
   const int B = k >> 5;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t = lane % LPR;
+  const int r = lane / LPR;
+  const int RG = (n + RPW - 1) / RPW;
+  const int rg_base = blockIdx.x * kWaves * ipw + wave;
+  const size_t row_bytes = size_t(k) >> 1;
+  // row groups this wave walks: rg_base, rg_base + kWaves, ... (uniform)
+  const int iters = rg_base < RG ? min(ipw, (RG - rg_base + kWaves - 1) / kWaves) : 0;
+  auto row_of = [&](int i) {
+    const int row = (rg_base + i * kWaves) * RPW + r;
+    return row < n ? row : n - 1;
+  };
+
+  Lane<LPR, BPL, FULL> L;
+  // The first row group's weights do not depend on x: put them in flight
+  // before the activations are staged.
+  if (iters > 0) L.load(nib, scl, row_of(0), t, B, row_bytes);
 
   // Stage the activations once per workgroup as block-scaled fp16 pairs.
   for (int b = threadIdx.x; b < B; b += kThreads) xf[b] = convert_x_block(x + 32 * b, xs + 16 * b);
   __syncthreads();
 
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int t = lane % LPR;
-  const int r = lane / LPR;
-
-  uint32_t xr[BPL][16];
-  float fr[BPL];
 #pragma unroll
   for (int j = 0; j < BPL; ++j) {
     const int b = j * LPR + t;
-    if (b < B) {
+    if (FULL || b < B) {
       const uint4* s4 = reinterpret_cast<const uint4*>(xs + 16 * b);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint4 v = s4[i];
-        xr[j][4 * i + 0] = v.x; xr[j][4 * i + 1] = v.y; xr[j][4 * i + 2] = v.z; xr[j][4 * i + 3] = v.w;
+        L.xr[j][4 * i + 0] = v.x; L.xr[j][4 * i + 1] = v.y; L.xr[j][4 * i + 2] = v.z; L.xr[j][4 * i + 3] = v.w;
       }
-      fr[j] = xf[b];
+      L.fr[j] = xf[b];
     } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) xr[j][i] = 0u;
-      fr[j] = 0.0f;
+      for (int i = 0; i < 16; ++i) L.xr[j][i] = 0u;
+      L.fr[j] = 0.0f;
     }
   }
 
@@ -69,53 +137,27 @@ __global__ __launch_bounds__(kThreads) void q4_rows_kernel(const uint8_t* __rest
   asm volatile("v_mov_b32 %0, 0x00F000F0" : "=v"(m_hi));
   asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 
-  const int RG = (n + RPW - 1) / RPW;
-  const int rg_base = blockIdx.x * kWaves * ipw + wave;
-  const size_t row_bytes = size_t(k) >> 1;
   float best = -INFINITY;
   int bidx = INT_MAX;
-
-  for (int i = 0; i < ipw; ++i) {
-    const int rg = rg_base + i * kWaves;
-    if (rg >= RG) break;
-    const int row = rg * RPW + r;
-    const bool rv = row < n;
-    const int rowc = rv ? row : n - 1;
-    const u32x4* np = reinterpret_cast<const u32x4*>(nib + size_t(rowc) * row_bytes);
-    const uint16_t* sp = scl + size_t(rowc) * size_t(B);
-    uint4 q[BPL];
-    uint32_t s[BPL];
-#pragma unroll
-    for (int j = 0; j < BPL; ++j) {
-      const int b = j * LPR + t;
-      if (b < B) {
-        const u32x4 v = __builtin_nontemporal_load(np + b);
-        q[j] = make_uint4(v.x, v.y, v.z, v.w);
-        s[j] = __builtin_nontemporal_load(sp + b);
-      } else {
-        q[j] = make_uint4(0u, 0u, 0u, 0u);
-        s[j] = 0u;
-      }
-    }
-    float acc = 0.0f;
-#pragma unroll
-    for (int j = 0; j < BPL; ++j) {
-      const int b = j * LPR + t;
-      if (b < B) {
-        const float p = block_dot(q[j], xr[j], m_lo, m_hi, magic);
-        const float d = float(__builtin_bit_cast(_Float16, uint16_t(s[j])));
-        acc = fmaf(d * p, fr[j], acc);
-      }
-    }
+  auto emit = [&](int i, float acc) {
     acc = group_sum<LPR>(acc);
+    const int row = (rg_base + i * kWaves) * RPW + r;
     if constexpr (!HEAD) {
-      if (t == 0 && rv) y[row] = acc;
+      if (t == 0 && row < n) y[row] = acc;
     } else {
-      if (rv && better(acc, row, best, bidx)) {
+      if (row < n && better(acc, row, best, bidx)) {
         best = acc;
         bidx = row;
       }
     }
+  };
+  for (int i = 0; i + 1 < iters; ++i) {
+    const float acc = L.template dot<true>(nib, scl, row_of(i + 1), t, B, row_bytes, m_lo, m_hi, magic);
+    emit(i, acc);
+  }
+  if (iters > 0) {
+    const float acc = L.template dot<false>(nib, scl, 0, t, B, row_bytes, m_lo, m_hi, magic);
+    emit(iters - 1, acc);
   }
 
   if constexpr (HEAD) {
@@ -196,8 +238,43 @@ __global__ __launch_bounds__(256) void lmhead_reduce_kernel(const uint2* __restr
 // ---------------------------------------------------------------- dispatch
 struct Plan {
   int lpr, bpl, rpw, rg, ipw, grid;
+  bool full;
+  const void* fn;
 };
 
+template <int L, int BP, bool HEAD, bool FULL>
+static const void* kernel_ptr() {
+  return reinterpret_cast<const void*>(&q4_rows_kernel<L, BP, HEAD, FULL>);
+}
+
+template <bool HEAD, bool FULL>
+static const void* pick_kernel(int lpr, int bpl) {
+#define Q4_CASE(L, BP) \
+  if (lpr == L && bpl == BP) return kernel_ptr<L, BP, HEAD, FULL>();
+  Q4_CASE(16, 1) Q4_CASE(16, 2) Q4_CASE(16, 3) Q4_CASE(16, 4) Q4_CASE(16, 5)
+  Q4_CASE(32, 3) Q4_CASE(32, 4) Q4_CASE(32, 5)
+  Q4_CASE(64, 3) Q4_CASE(64, 4) Q4_CASE(64, 5) Q4_CASE(64, 6) Q4_CASE(64, 7) Q4_CASE(64, 8)
+#undef Q4_CASE
+  return nullptr;
+}
+
+// Resident workgroups per CU of a kernel (cached per kernel and device).
+static int blocks_per_cu(const void* fn) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  std::lock_guard<std::mutex> lock(mu);
+  auto key = std::make_pair(fn, dev);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kThreads, 0) != hipSuccess || nb <= 0) nb = 2;
+  cache[key] = nb;
+  return nb;
+}
+
+template <bool HEAD>
 static Plan make_plan(int64_t n, int64_t k) {
   const int B = int(k / 32);
   Plan p{};
@@ -209,29 +286,27 @@ static Plan make_plan(int64_t n, int64_t k) {
     p.lpr = 64;
   }
   p.bpl = (B + p.lpr - 1) / p.lpr;
+  p.full = (B == p.lpr * p.bpl);
+  p.fn = p.full ? pick_kernel<HEAD, true>(p.lpr, p.bpl) : pick_kernel<HEAD, false>(p.lpr, p.bpl);
   p.rpw = 64 / p.lpr;
   p.rg = int((n + p.rpw - 1) / p.rpw);
-  const int waves_max = device_cu_count() * 16;
+  if (!p.fn) return p;
+  // one resident round: every workgroup is live at once
+  const int waves_max = device_cu_count() * blocks_per_cu(p.fn) * kWaves;
   p.ipw = (p.rg + waves_max - 1) / waves_max;
   const int waves = (p.rg + p.ipw - 1) / p.ipw;
   p.grid = (waves + kWaves - 1) / kWaves;
   return p;
 }
 
-template <bool HEAD>
 static int launch_rows(const Plan& p, const uint8_t* nib, const uint16_t* scl, const uint16_t* x, int n, int k,
                        float* y, uint2* partials, hipStream_t st) {
-#define Q4_CASE(L, BP)                                                                                     \
-  if (p.lpr == L && p.bpl == BP) {                                                                         \
-    hipLaunchKernelGGL((q4_rows_kernel<L, BP, HEAD>), dim3(p.grid), dim3(kThreads), 0, st, nib, scl, x, n, \
-                       k, p.ipw, y, partials);                                                             \
-    return Q4DEC_OK;                                                                                       \
-  }
-  Q4_CASE(16, 1) Q4_CASE(16, 2) Q4_CASE(16, 3) Q4_CASE(16, 4) Q4_CASE(16, 5)
-  Q4_CASE(32, 3) Q4_CASE(32, 4) Q4_CASE(32, 5)
-  Q4_CASE(64, 3) Q4_CASE(64, 4) Q4_CASE(64, 5) Q4_CASE(64, 6) Q4_CASE(64, 7) Q4_CASE(64, 8)
-#undef Q4_CASE
-  return fail(Q4DEC_ERR_UNSUPPORTED, "no kernel for k=%d (lpr=%d, bpl=%d)", k, p.lpr, p.bpl);
+  if (!p.fn) return fail(Q4DEC_ERR_UNSUPPORTED, "no kernel for k=%d (lpr=%d, bpl=%d)", k, p.lpr, p.bpl);
+  int ipw = p.ipw;
+  void* args[] = {&nib, &scl, &x, &n, &k, &ipw, &y, &partials};
+  hipError_t e = hipLaunchKernel(p.fn, dim3(p.grid), dim3(kThreads), args, 0, st);
+  if (e != hipSuccess) return fail(Q4DEC_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return Q4DEC_OK;
 }
 
 static int check_common(const char* fn, const void* packed, int64_t n, const char* nname, int64_t k,
@@ -256,10 +331,10 @@ extern "C" int q4_gemv(const void* packed, int64_t n, int64_t k, const uint16_t*
   if (rc) return rc;
   if (!y) return fail(Q4DEC_ERR_NULL, "q4_gemv: y is NULL");
   if (!aligned(y, 4)) return fail(Q4DEC_ERR_ALIGN, "q4_gemv: y must be 4-byte aligned");
-  const Plan p = make_plan(n, k);
+  const Plan p = make_plan<false>(n, k);
   const uint8_t* nib = static_cast<const uint8_t*>(packed);
   const uint16_t* scl = reinterpret_cast<const uint16_t*>(nib + nib_plane_bytes(n, k));
-  rc = launch_rows<false>(p, nib, scl, x, int(n), int(k), y, nullptr, static_cast<hipStream_t>(stream));
+  rc = launch_rows(p, nib, scl, x, int(n), int(k), y, nullptr, static_cast<hipStream_t>(stream));
   if (rc) return rc;
   return launch_status("q4_gemv");
 }
@@ -284,13 +359,13 @@ extern "C" int lmhead_softcap_argmax(const void* packed, int64_t vocab, int64_t 
   const size_t need = lmhead_workspace_bytes(vocab, k);
   if (ws_bytes < need)
     return fail(Q4DEC_ERR_WORKSPACE, "lmhead_softcap_argmax: ws_bytes %zu < required %zu", ws_bytes, need);
-  const Plan p = make_plan(vocab, k);
+  const Plan p = make_plan<true>(vocab, k);
   if (p.grid > kMaxPartials) return fail(Q4DEC_ERR_UNSUPPORTED, "lmhead_softcap_argmax: too many workgroups");
   const uint8_t* nib = static_cast<const uint8_t*>(packed);
   const uint16_t* scl = reinterpret_cast<const uint16_t*>(nib + nib_plane_bytes(vocab, k));
   uint2* partials = static_cast<uint2*>(ws);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  rc = launch_rows<true>(p, nib, scl, x, int(vocab), int(k), nullptr, partials, st);
+  rc = launch_rows(p, nib, scl, x, int(vocab), int(k), nullptr, partials, st);
   if (rc) return rc;
   hipLaunchKernelGGL(lmhead_reduce_kernel, dim3(1), dim3(256), 0, st, partials, p.grid, cap, idx_out, val_out);
   return launch_status("lmhead_softcap_argmax");
