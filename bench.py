@@ -65,6 +65,7 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true", help="skip per-kernel event timing")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the S=64 prefill step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -135,6 +136,37 @@ class Workload:
 
     def weight_bytes(self) -> int:
         return sum(weight_bytes(n, k) for _, n, k in self.mats)
+
+    # ------------------------------------------------------ S=64 prefill step
+    def prefill_setup(self, gen):
+        """64-token activations per GEMM (bf16 N(0,1)), fp32 outputs and one
+        shared workspace (the GEMMs run one after another on one stream)."""
+        import synth
+        import torch
+
+        dev = self.xs[0].device
+        self.pxs, self.pys = [], []
+        ws_need = 0
+        for _, n, k in self.mats[:-1]:
+            self.pxs.append(synth.torch_bf16_normal(gen, (64, k), dev))
+            self.pys.append(torch.empty((64, n), dtype=torch.float32, device=dev))
+            ws_need = max(ws_need, self.q4.q4_gemm_workspace_bytes(n, k))
+        self.pws = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+        self.p_head_x = synth.torch_bf16_normal(gen, (64, self.head_nk[1]), dev)
+        torch.cuda.synchronize()
+
+    def prefill_step(self):
+        """PLE gather for 64 ids, 42 x 4 S=64 GEMMs, head on the chunk's last
+        row (the only row a decoder samples from)."""
+        q4 = self.q4
+        q4.ple_gather(self.table, self.scale, self.p_ids, 16.0, out=self.p_ple_out)
+        for i, (_, n, k) in enumerate(self.mats[:-1]):
+            q4.q4_gemm_s64(self.packed[i], n, k, self.pxs[i], self.pys[i], self.pws)
+        hn, hk = self.head_nk
+        q4.lmhead_softcap_argmax(self.packed[-1], hn, hk, self.p_head_x[63], 30.0, self.ws, self.idx, self.val)
+
+    def prefill_flops(self) -> int:
+        return sum(2 * 64 * n * k for _, n, k in self.mats[:-1]) + 2 * self.head_nk[0] * self.head_nk[1]
 
 
 def probe_kernels(torch, wl: Workload, reps: int = 20):
@@ -359,6 +391,41 @@ def main():
             }
         result["kernel_time_sum_ms"] = round(sum(v["ms_per_step"] for v in kernels.values()), 4)
         result["launch_gap_ms_per_step"] = round(ms_step - result["kernel_time_sum_ms"], 4)
+
+    if not args.no_prefill:
+        g2 = torch.Generator(device=dev)
+        g2.manual_seed(args.seed + 1)
+        wl.prefill_setup(g2)
+        wl.p_ids = torch.randint(0, wl.vocab, (64,), dtype=torch.int32, device=dev, generator=g2)
+        wl.p_ple_out = torch.empty((64, wl.ple_dim), dtype=torch.float32, device=dev)
+        wl.prefill_step()
+        torch.cuda.synchronize()
+        pgraph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(pgraph):
+            wl.prefill_step()
+        for _ in range(3):
+            pgraph.replay()
+        torch.cuda.synchronize()
+        reps = max(5, args.steps // 10)
+        e0.record()
+        for _ in range(reps):
+            pgraph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        pms = e0.elapsed_time(e1) / reps
+        flops = wl.prefill_flops()
+        result["prefill_s64"] = {
+            "workload": "e4b_prefill_step_s64",
+            "ms_per_step": round(pms, 4),
+            "tokens_per_s": round(64 / (pms * 1e-3), 1),
+            "weight_GBs": round(wbytes / (pms * 1e-3) / 1e9, 1),
+            "TFLOPs": round(flops / (pms * 1e-3) / 1e12, 1),
+            "flops_per_step": flops,
+            "steps": reps,
+            "roofline": {"bound": "hbm", "floor_ms_at_8TBs": round(wbytes / 8e12 * 1e3, 4),
+                         "mfma_fp16_floor_ms": round(flops / 2.5e15 * 1e3, 4)},
+        }
+        del pgraph
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

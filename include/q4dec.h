@@ -89,17 +89,26 @@ int q4_pack(const int8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
 int q4_gemv(const void* packed, int64_t n, int64_t k, const uint16_t* x,
             float* y, void* stream);
 
+/* Workspace bytes q4_gemm_s64 needs for an [n, k] weight matrix
+ * (0 for invalid shapes). */
+size_t q4_gemm_workspace_bytes(int64_t n, int64_t k);
+
 /* q4_gemm_s64: chunked-prefill product Y[s, r] = sum_k X[s, k] * w[r, k] for
- * s < n_tok <= 64 (model card: prefill entry point with a static query width
- * of 64). MFMA kernel; codes enter the matrix cores as exact bf16 integers and
- * each 32-wide block's fp16 scale is applied in fp32.
+ * s < n_tok <= 64 (model card, Provenance table: the prefill entry point has a
+ * static query width of 64; the weights are read once per 64 tokens). MFMA
+ * kernel: codes enter the matrix cores as exact fp16 integers, activations as
+ * fp16 scaled by a per-token power of two, and each 32-wide block's fp16 scale
+ * is applied in fp32. Deterministic (fixed summation order).
  *   packed  from q4_pack with the same (n, k); 16-byte aligned.
- *   x       bf16 [n_tok, k] row-major, 16-byte aligned.
- *   y       fp32 [n_tok, n] row-major, 16-byte aligned.
+ *   x       bf16 [n_tok, k] row-major, 2-byte aligned.
+ *   y       fp32 [n_tok, n] row-major, 4-byte aligned.
+ *   ws      device workspace of ws_bytes >= q4_gemm_workspace_bytes(n, k),
+ *           256-byte aligned (converted activations and split-K partials).
  * Errors: NULL pointer, n <= 0, k % 32 != 0, k > Q4DEC_MAX_K, n_tok not in
- *         [1, 64], misalignment. */
+ *         [1, 64], workspace too small, misalignment. */
 int q4_gemm_s64(const void* packed, int64_t n, int64_t k, const uint16_t* x,
-                int64_t n_tok, float* y, void* stream);
+                int64_t n_tok, float* y, void* ws, size_t ws_bytes,
+                void* stream);
 
 /* Workspace bytes lmhead_softcap_argmax needs for a [vocab, k] head. */
 size_t lmhead_workspace_bytes(int64_t vocab, int64_t k);

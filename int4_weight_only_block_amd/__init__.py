@@ -39,7 +39,8 @@ _SIGNATURES = {
     "q4_packed_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
     "q4_pack": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "q4_gemv": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
-    "q4_gemm_s64": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p]),
+    "q4_gemm_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
+    "q4_gemm_s64": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p, ctypes.c_size_t, _c_p]),
     "lmhead_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
     "lmhead_softcap_argmax": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, ctypes.c_float, _c_p,
                                              ctypes.c_size_t, _c_p, _c_p, _c_p]),
@@ -162,8 +163,12 @@ def q4_gemv(packed: torch.Tensor, n: int, k: int, x: torch.Tensor,
     return y
 
 
+def q4_gemm_workspace_bytes(n: int, k: int) -> int:
+    return int(lib().q4_gemm_workspace_bytes(n, k))
+
+
 def q4_gemm_s64(packed: torch.Tensor, n: int, k: int, x: torch.Tensor,
-                y: torch.Tensor | None = None) -> torch.Tensor:
+                y: torch.Tensor | None = None, ws: torch.Tensor | None = None) -> torch.Tensor:
     """Y[s, n] fp32 = X @ dequant(W)^T for bf16 X[s, k], 1 <= s <= 64."""
     s = x.shape[0] if x.dim() == 2 else 1
     pp = _dev(packed, "packed", _BYTES)
@@ -172,7 +177,11 @@ def q4_gemm_s64(packed: torch.Tensor, n: int, k: int, x: torch.Tensor,
     if y is None:
         y = torch.empty((s, n), dtype=torch.float32, device=x.device)
     py = _dev(y, "y", _F32, s * n)
-    _check(lib().q4_gemm_s64(pp, n, k, px, s, py, _stream(x)))
+    need = q4_gemm_workspace_bytes(n, k)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    pw = _dev(ws, "ws", _BYTES)
+    _check(lib().q4_gemm_s64(pp, n, k, px, s, py, pw, ws.numel() * ws.element_size(), _stream(x)))
     return y
 
 

@@ -12,7 +12,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(q4.LIB_PATH), reason="libq4de
 
 EXPECTED = {
     "q4dec_abi_version", "q4dec_last_error", "q4_packed_bytes", "q4_pack", "q4_gemv",
-    "q4_gemm_s64", "lmhead_workspace_bytes", "lmhead_softcap_argmax", "ple_gather",
+    "q4_gemm_s64", "q4_gemm_workspace_bytes", "lmhead_workspace_bytes", "lmhead_softcap_argmax", "ple_gather",
 }
 
 
@@ -103,10 +103,24 @@ def test_lmhead_validation():
 
 def test_gemm_validation():
     L = q4.lib()
-    assert L.q4_gemm_s64(FAKE, 64, 64, FAKE, 0, FAKE, None) == q4.ERR_SHAPE
-    assert L.q4_gemm_s64(FAKE, 64, 64, FAKE, 65, FAKE, None) == q4.ERR_SHAPE
-    assert L.q4_gemm_s64(None, 64, 64, FAKE, 64, FAKE, None) == q4.ERR_NULL
-    assert L.q4_gemm_s64(FAKE, 64, 48, FAKE, 64, FAKE, None) == q4.ERR_SHAPE
+    need = q4.q4_gemm_workspace_bytes(64, 64)
+    assert need > 0 and q4.q4_gemm_workspace_bytes(64, 40) == 0
+    ok = [FAKE, 64, 64, FAKE, 64, FAKE, FAKE, need, None]
+
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return L.q4_gemm_s64(*a)
+
+    assert call(4, 0) == q4.ERR_SHAPE and "n_tok" in q4.q4dec_last_error()
+    assert call(4, 65) == q4.ERR_SHAPE
+    assert call(0, None) == q4.ERR_NULL
+    assert call(6, None) == q4.ERR_NULL and "ws" in q4.q4dec_last_error()
+    assert call(2, 48) == q4.ERR_SHAPE
+    assert call(2, q4.MAX_K + 32) == q4.ERR_UNSUPPORTED
+    assert call(7, need - 1) == q4.ERR_WORKSPACE
+    assert call(6, FAKE + 16) == q4.ERR_ALIGN
+    assert call(0, FAKE + 8) == q4.ERR_ALIGN
 
 
 def test_ple_validation():

@@ -288,3 +288,48 @@ def test_ple_gather_out_of_range_ids():
     flag.zero_()
     q4.ple_gather(d(table), d(scale), d(np.array([0, 99], np.int32)), 16.0, err_flag=flag)
     assert int(flag.item()) == 0
+
+
+# ----------------------------------------------------------- S=64 GEMM --
+@pytest.mark.parametrize("n,k,n_tok", [(1536, 1536, 64), (64, 32, 64), (100, 96, 1), (300, 2560, 37),
+                                       (3072, 2560, 64), (2560, 10240, 64), (77, 16384, 5)])
+def test_gemm_s64_tolerance(n, k, n_tok):
+    rng = synth.rng_for(20, n, k, n_tok)
+    codes, sb = synth.q4_weights(rng, n, k)
+    xs = synth.bf16_normal(rng, (n_tok, k))
+    y = q4.q4_gemm_s64(pack(codes, sb), n, k, d(xs)).cpu().numpy()
+    yr, a = oracle.gemm(codes, sb, xs)
+    assert_within_tol(y.ravel(), yr.ravel(), a.ravel(), f"gemm {n}x{k} s={n_tok}")
+
+
+@pytest.mark.parametrize("n,k", [(300, 1536), (64, 4096), (1000, 2048)])
+def test_gemm_s64_integer_exact(n, k):
+    """Integer activations and power-of-two scales: exact in fp32 in any order."""
+    rng = np.random.default_rng(300 + k)
+    codes = rng.integers(-8, 8, size=(n, k), dtype=np.int8)
+    p = rng.integers(6, 9, size=(n, k // 32))
+    sb = np.vectorize(lambda e: fp16_bits(2.0 ** -int(e)))(p).astype(np.uint16)
+    xi = rng.integers(-8, 9, size=(64, k))
+    xs = bf16_bits_of_ints(xi.ravel()).reshape(64, k)
+    y = q4.q4_gemm_s64(pack(codes, sb), n, k, d(xs)).cpu().numpy()
+    yr, _ = oracle.gemm(codes, sb, xs)
+    assert np.array_equal(y.astype(np.float64), yr)
+
+
+def test_gemm_rows_match_gemv_and_are_deterministic():
+    n, k = 2560, 2048
+    rng = synth.rng_for(21)
+    codes, sb = synth.q4_weights(rng, n, k)
+    xs = synth.bf16_normal(rng, (64, k))
+    packed = pack(codes, sb)
+    xd = d(xs)
+    y1 = q4.q4_gemm_s64(packed, n, k, xd).cpu().numpy()
+    y2 = q4.q4_gemm_s64(packed, n, k, xd).cpu().numpy()
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    _, a = oracle.gemm(codes, sb, xs)
+    for s in (0, 31, 63):
+        yv = q4.q4_gemv(packed, n, k, xd[s]).cpu().numpy()
+        assert (np.abs(y1[s].astype(np.float64) - yv) <= 2 * oracle.gemv_tolerance(a[s])).all()
+    # a chunk shorter than 64 returns the same rows as the full chunk
+    y5 = q4.q4_gemm_s64(packed, n, k, xd[:5].contiguous()).cpu().numpy()
+    assert (np.abs(y5.astype(np.float64) - y1[:5]) <= 2 * oracle.gemv_tolerance(a[:5])).all()
