@@ -62,8 +62,9 @@ int32_t q4dec_abi_version(void);
 const char* q4dec_last_error(void);
 
 /* Bytes of device memory a packed [n, k] q4_0 matrix occupies:
- * a nibble plane of n*k/2 bytes and an fp16 scale plane of n*(k/32)*2 bytes,
- * each padded to 256 bytes. Returns 0 if n <= 0, k <= 0 or k % 32 != 0. */
+ * a nibble plane of n*k/2 bytes, an fp16 scale plane of n*(k/32)*2 bytes and
+ * a per-row byte plane of n bytes (largest scale exponent of each row), each
+ * padded to 256 bytes. Returns 0 if n <= 0, k <= 0 or k % 32 != 0. */
 size_t q4_packed_bytes(int64_t n, int64_t k);
 
 /* q4_pack: q4_0 codes and scales -> packed layout (load time, not per token).

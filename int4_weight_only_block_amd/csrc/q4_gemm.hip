@@ -3,19 +3,24 @@
 // point has a static query width of 64 and reads the weights once per 64
 // tokens).
 //
-// Numerics. A bf16 or fp16 copy of c * d would round the 15-bit product, so
-// the weights enter the MFMA as exact fp16 integer codes (the nibble trick of
-// the GEMV) and each 32-wide block's fp16 scale is applied in fp32 after the
-// block's v_mfma_f32_16x16x32_f16: acc += T_b * d[r, b]. Activations are
-// converted once per call into fp16 scaled by a per-token power of two (the
-// largest magnitude of the token lands in [2^14, 2^15)), which is undone on
-// the output. Products are exact; only fp32 sums round.
+// Numerics. A single fp16 or bf16 copy of c * d would round the 15-bit
+// product, so each fp16 block scale d is split into d_hi (its top 7
+// significant bits) and d_lo = d - d_hi (at most 4 bits). Both c * d_hi and
+// c * d_lo are exact in fp16, and the two v_mfma_f32_16x16x32_f16 products
+// accumulate straight into fp32, so the sum is exact up to fp32 accumulation
+// and no per-block fold runs on the VALU. Activations are converted once per
+// call into fp16 scaled by a per-token power of two (the largest magnitude of
+// the token lands in [2^14, 2^15)); a row whose largest scale would let
+// c * d_hi overflow fp16 is scaled down by a power of two for the slice. Both
+// factors are undone on the output.
 //
-// Work split. A workgroup (4 waves) owns 64 output rows (16 per wave) for all
-// 64 token slots and one K slice; the activation chunk of 4 blocks is staged
-// in LDS and shared by the 4 waves. Small-N matrices split K over several
-// workgroups; their partial sums go to the workspace and a second kernel adds
-// them in a fixed order, so results are deterministic.
+// Work split. A workgroup (4 waves) owns 128 output rows (32 per wave, two
+// MFMA column tiles) for all 64 token slots and one K slice. Activations move
+// through LDS in chunks of 8 blocks (32 KB, double-buffered) shared by the 4
+// waves; the next chunk's weights and activations are loaded into registers
+// while the current chunk runs on the matrix cores. Small-N matrices split K
+// over several workgroups; their partial sums go to the workspace and a second
+// kernel adds them in a fixed order, so results are deterministic.
 #include <math.h>
 
 #include <algorithm>
@@ -27,9 +32,10 @@ namespace q4dec {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kTok = 64;    // token slots
-constexpr int kTileN = 64;  // weight rows per workgroup
-constexpr int kChunk = 4;   // 32-wide blocks per LDS chunk
+constexpr int kTok = 64;     // token slots
+constexpr int kSub = 2;      // 16-row MFMA column tiles per wave
+constexpr int kTileN = 128;  // weight rows per workgroup (4 waves x kSub x 16)
+constexpr int kChunk = 8;    // 32-wide blocks per LDS chunk
 
 struct GemmPlan {
   int slices;        // K slices
@@ -43,7 +49,7 @@ static GemmPlan gemm_plan(int64_t n, int64_t k) {
   const int64_t tiles = (n + kTileN - 1) / kTileN;
   // enough workgroups to cover the chip, slices of at least 8 blocks
   int s = 1;
-  while (tiles * s < 512 && B / (2 * s) >= 8) s *= 2;
+  while (tiles * s < 256 && B / (2 * s) >= 8) s *= 2;
   p.slices = s;
   p.bps = (B + s - 1) / s;
   p.slices = (B + p.bps - 1) / p.bps;
@@ -55,26 +61,54 @@ static GemmPlan gemm_plan(int64_t n, int64_t k) {
 }
 
 // One workgroup per token slot: find the token's largest exponent, convert
-// its row to scaled fp16, store 2^E. Slots >= n_tok are zero-filled.
+// its row to scaled fp16, store 2^E. Slots >= n_tok are zero-filled. Rows are
+// handled 8 values (16 bytes) at a time when 16-byte aligned.
 __global__ __launch_bounds__(256) void gemm_x_prep_kernel(const uint16_t* __restrict__ x, int k, int n_tok,
                                                           _Float16* __restrict__ xh, float* __restrict__ xf) {
   const int s = blockIdx.x;
   _Float16* dst = xh + size_t(s) * size_t(k);
+  const int k8 = k >> 3;  // k % 32 == 0
   if (s >= n_tok) {
-    for (int i = threadIdx.x; i < k; i += 256) dst[i] = (_Float16)0.0f;
+    for (int i = threadIdx.x; i < k8; i += 256) reinterpret_cast<uint4*>(dst)[i] = make_uint4(0u, 0u, 0u, 0u);
     if (threadIdx.x == 0) xf[s] = 0.0f;
     return;
   }
   const uint16_t* src = x + size_t(s) * size_t(k);
+  const bool vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0;
   uint32_t emax = 1;
-  for (int i = threadIdx.x; i < k; i += 256) emax = max(emax, (uint32_t(src[i]) >> 7) & 0xFFu);
+  if (vec) {
+    const uint4* s4 = reinterpret_cast<const uint4*>(src);
+    for (int i = threadIdx.x; i < k8; i += 256) {
+      const uint4 v = s4[i];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) emax = max(emax, max((w[j] >> 7) & 0xFFu, (w[j] >> 23) & 0xFFu));
+    }
+  } else {
+    for (int i = threadIdx.x; i < k; i += 256) emax = max(emax, (uint32_t(src[i]) >> 7) & 0xFFu);
+  }
   for (int off = 32; off >= 1; off >>= 1) emax = max(emax, uint32_t(__shfl_xor(int(emax), off)));
   __shared__ uint32_t wm[4];
   if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = emax;
   __syncthreads();
   emax = max(max(wm[0], wm[1]), max(wm[2], wm[3]));
   const int e = int(emax) - 127 - 14;
-  for (int i = threadIdx.x; i < k; i += 256) dst[i] = (_Float16)ldexpf(bf16_to_f32(src[i]), -e);
+  if (vec) {
+    const uint4* s4 = reinterpret_cast<const uint4*>(src);
+    for (int i = threadIdx.x; i < k8; i += 256) {
+      const uint4 v = s4[i];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        half2_t h = {(_Float16)ldexpf(bf16_to_f32(w[j] & 0xFFFFu), -e), (_Float16)ldexpf(bf16_to_f32(w[j] >> 16), -e)};
+        o[j] = __builtin_bit_cast(uint32_t, h);
+      }
+      reinterpret_cast<uint4*>(dst)[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  } else {
+    for (int i = threadIdx.x; i < k; i += 256) dst[i] = (_Float16)ldexpf(bf16_to_f32(src[i]), -e);
+  }
   if (threadIdx.x == 0) xf[s] = ldexpf(1.0f, e);
 }
 
@@ -86,90 +120,179 @@ __device__ __forceinline__ half8_t codes_f16x8(uint32_t w, uint32_t m_lo, uint32
   return r;
 }
 
+// Registers of one chunk (kChunk = 8 blocks = 2 groups of 4). Lane (col, q)
+// holds block 4g + q of its rows: the k-slots of lane group q inside one MFMA
+// then come from block 4g + q, and the A operand follows the same mapping.
+// Mixing blocks inside one MFMA is exact because the scale is already inside
+// the fp16 B operand (c * d_hi, c * d_lo).
+struct ChunkRegs {
+  uint4 w[kSub][2];      // full 16-byte block (32 codes) per column tile and group
+  uint32_t sd[kSub][2];  // its fp16 scale bits
+  uint4 xr[(kChunk * kTok * 4) / 256];
+};
+
+// LDS slot of activation quarter qq of a token: swizzled so the 16 lanes of a
+// ds_read_b128 (16 tokens, same quarter) hit 16 distinct bank groups.
+__device__ __forceinline__ int xslot(int tok, int qq) { return qq ^ ((tok >> 2) & 3); }
+
+__device__ __forceinline__ void load_chunk(ChunkRegs& R, const uint4* const (&wrow)[kSub],
+                                           const uint16_t* const (&srow)[kSub], const _Float16* __restrict__ xh,
+                                           int k, int q, int b0, int b_end) {
+#pragma unroll
+  for (int u = 0; u < kSub; ++u)
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int bb = b0 + 4 * g + q;
+      const int bc = bb < b_end ? bb : b0;  // ragged tail: any valid block, zeroed by its scale
+      R.w[u][g] = wrow[u][bc];
+      R.sd[u][g] = bb < b_end ? uint32_t(srow[u][bc]) : 0u;
+    }
+#pragma unroll
+  for (int i = 0; i < (kChunk * kTok * 4) / 256; ++i) {
+    const int idx = threadIdx.x + 256 * i;
+    const int c = idx / (kTok * 4);
+    const int rem = idx % (kTok * 4);
+    const int sx = rem >> 2, qq = rem & 3;
+    const int bb = b0 + c;
+    R.xr[i] = bb < b_end ? *reinterpret_cast<const uint4*>(xh + size_t(sx) * size_t(k) + size_t(bb) * 32 + qq * 8)
+                         : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+// exact split of one fp16 scale (already shifted into range): hi keeps the
+// top 7 significant bits, lo = d - hi
+__device__ __forceinline__ void split_scale(uint32_t dbits, half2_t& hi, half2_t& lo) {
+  const _Float16 d = __builtin_bit_cast(_Float16, uint16_t(dbits));
+  const _Float16 h = __builtin_bit_cast(_Float16, uint16_t(dbits & 0xFFF0u));
+  const _Float16 l = d - h;
+  hi = half2_t{h, h};
+  lo = half2_t{l, l};
+}
+
 template <bool PARTIAL>
 __global__ __launch_bounds__(256) void q4_gemm_kernel(const uint8_t* __restrict__ nib, const uint16_t* __restrict__ scl,
-                                                      const _Float16* __restrict__ xh, const float* __restrict__ xf,
-                                                      int n, int k, int n_tok, int bps, float* __restrict__ out) {
-  __shared__ uint4 xs[kChunk][kTok][4];  // [block][token][k quarter], 16 KB
+                                                      const uint8_t* __restrict__ rexp, const _Float16* __restrict__ xh,
+                                                      const float* __restrict__ xf, int n, int k, int n_tok, int bps,
+                                                      float* __restrict__ out) {
+  __shared__ uint4 xs[kChunk][kTok][4];  // [block][token][k quarter, swizzled], 32 KB
   const int B = k >> 5;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int q = lane >> 4;        // k group of this lane in a block: k = 8q .. 8q+7
-  const int col = lane & 15;      // output row within the wave's 16
-  const int r_lane = blockIdx.x * kTileN + wave * 16 + col;
-  const bool r_ok = r_lane < n;
-  const int r_c = r_ok ? r_lane : n - 1;
+  const int q = lane >> 4;    // lane group: block 4g + q of a chunk
+  const int col = lane & 15;  // row within a 16-row MFMA column tile
   const int b_begin = blockIdx.y * bps;
   const int b_end = min(B, b_begin + bps);
-  const uint8_t* wrow = nib + size_t(r_c) * size_t(k >> 1);
-  const uint16_t* srow = scl + size_t(r_c) * size_t(B);
+
+  const uint4* wrow[kSub];
+  const uint16_t* srow[kSub];
+  int rows[kSub];
+  int shift[kSub];  // power-of-two range shift of the row's scales
+#pragma unroll
+  for (int u = 0; u < kSub; ++u) {
+    rows[u] = blockIdx.x * kTileN + (wave * kSub + u) * 16 + col;
+    const int rc = rows[u] < n ? rows[u] : n - 1;
+    wrow[u] = reinterpret_cast<const uint4*>(nib + size_t(rc) * size_t(k >> 1));
+    srow[u] = scl + size_t(rc) * size_t(B);
+    // largest fp16 exponent field of the row's scales (computed by q4_pack);
+    // keep every scale below 2^11 so |c * d_hi| < 2^14 stays finite in fp16
+    shift[u] = max(0, int(rexp[rc]) - 15 - 10);
+  }
 
   uint32_t m_lo, m_hi, magic;
   asm volatile("v_mov_b32 %0, 0x000F000F" : "=v"(m_lo));
   asm volatile("v_mov_b32 %0, 0x00F000F0" : "=v"(m_hi));
   asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 
-  float4_t acc[4];
+  float4_t acc[kSub][4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) acc[m] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int u = 0; u < kSub; ++u)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[u][m] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  ChunkRegs cur;
+  if (b_begin < b_end) load_chunk(cur, wrow, srow, xh, k, q, b_begin, b_end);
 
   for (int b0 = b_begin; b0 < b_end; b0 += kChunk) {
-    const int nb = min(kChunk, b_end - b0);
-    // weights of this chunk: dword q of each block of row r_c
-    uint32_t wq[kChunk];
-    uint32_t sd[kChunk];
-#pragma unroll
-    for (int c = 0; c < kChunk; ++c) {
-      if (c < nb) {
-        wq[c] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(wrow + size_t(b0 + c) * 16) + q);
-        sd[c] = __builtin_nontemporal_load(srow + b0 + c);
-      } else {
-        wq[c] = 0u;
-        sd[c] = 0u;
-      }
-    }
-    // stage the activation chunk: kChunk blocks x 64 tokens x 64 bytes
+    __syncthreads();  // previous chunk fully consumed
 #pragma unroll
     for (int i = 0; i < (kChunk * kTok * 4) / 256; ++i) {
       const int idx = threadIdx.x + 256 * i;
       const int c = idx / (kTok * 4);
       const int rem = idx % (kTok * 4);
-      const int s = rem >> 2, qq = rem & 3;
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (c < nb) v = *reinterpret_cast<const uint4*>(xh + size_t(s) * size_t(k) + size_t(b0 + c) * 32 + qq * 8);
-      xs[c][s][qq] = v;
+      const int sx = rem >> 2;
+      xs[c][sx][xslot(sx, rem & 3)] = cur.xr[i];
     }
-    __syncthreads();
+    uint4 w[kSub][2];
+    uint32_t sd[kSub][2];
 #pragma unroll
-    for (int c = 0; c < kChunk; ++c) {
-      if (c < nb) {
-        const half8_t bw = codes_f16x8(wq[c], m_lo, m_hi, magic);
-        const float d = float(__builtin_bit_cast(_Float16, uint16_t(sd[c])));
+    for (int u = 0; u < kSub; ++u)
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        w[u][g] = cur.w[u][g];
+        sd[u][g] = cur.sd[u][g];
+      }
+    __syncthreads();
+    // next chunk in flight while this one runs on the matrix cores
+    if (b0 + kChunk < b_end) load_chunk(cur, wrow, srow, xh, k, q, b0 + kChunk, b_end);
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      if (b0 + 4 * g >= b_end) break;
+      half2_t dh[kSub], dl[kSub];
+#pragma unroll
+      for (int u = 0; u < kSub; ++u) {
+        uint32_t dbits = sd[u][g];
+        if (shift[u] > 0) {  // rare: rows with scales >= 2^11
+          const float df = ldexpf(float(__builtin_bit_cast(_Float16, uint16_t(dbits))), -shift[u]);
+          dbits = __builtin_bit_cast(uint16_t, (_Float16)df);
+        }
+        split_scale(dbits, dh[u], dl[u]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        half8_t a[4];
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const uint4 av = xs[c][16 * m + col][q];
-          const half8_t a = __builtin_bit_cast(half8_t, av);
-          const float4_t t =
-              __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bw, float4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+          const int tok = 16 * m + col;
+          a[m] = __builtin_bit_cast(half8_t, xs[4 * g + q][tok][xslot(tok, j)]);
+        }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[m][i] = fmaf(t[i], d, acc[m][i]);
+        for (int u = 0; u < kSub; ++u) {
+          const uint32_t wd = j == 0 ? w[u][g].x : j == 1 ? w[u][g].y : j == 2 ? w[u][g].z : w[u][g].w;
+          const CodePairs cp = unpack_dword(wd, m_lo, m_hi, magic);
+          half8_t bh, bl;
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const half2_t ph = cp.p[jj] * dh[u];
+            const half2_t pl = cp.p[jj] * dl[u];
+            bh[2 * jj] = ph[0]; bh[2 * jj + 1] = ph[1];
+            bl[2 * jj] = pl[0]; bl[2 * jj + 1] = pl[1];
+          }
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            acc[u][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[m], bh, acc[u][m], 0, 0, 0);
+            acc[u][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[m], bl, acc[u][m], 0, 0, 0);
+          }
         }
       }
     }
-    __syncthreads();
   }
 
-  // lane holds tokens s = 16m + 4q + i of output row r_lane
-  if (!r_ok) return;
+  // lane holds tokens s = 16m + 4q + i of output rows rows[u]
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int u = 0; u < kSub; ++u) {
+    if (rows[u] >= n) continue;
+    const float rf = ldexpf(1.0f, shift[u]);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int s = 16 * m + 4 * q + i;
-      if (PARTIAL) {
-        out[(size_t(blockIdx.y) * kTok + s) * size_t(n) + r_lane] = acc[m][i] * xf[s];
-      } else if (s < n_tok) {
-        out[size_t(s) * size_t(n) + r_lane] = acc[m][i] * xf[s];
+    for (int m = 0; m < 4; ++m) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = 16 * m + 4 * q + i;
+        const float v = acc[u][m][i] * (xf[s] * rf);
+        if (PARTIAL) {
+          out[(size_t(blockIdx.y) * kTok + s) * size_t(n) + rows[u]] = v;
+        } else if (s < n_tok) {
+          out[size_t(s) * size_t(n) + rows[u]] = v;
+        }
       }
     }
   }
@@ -223,14 +346,15 @@ extern "C" int q4_gemm_s64(const void* packed, int64_t n, int64_t k, const uint1
   float* part = reinterpret_cast<float*>(w8 + p.part_off);
   const uint8_t* nib = static_cast<const uint8_t*>(packed);
   const uint16_t* scl = reinterpret_cast<const uint16_t*>(nib + nib_plane_bytes(n, k));
+  const uint8_t* rexp = nib + nib_plane_bytes(n, k) + scale_plane_bytes(n, k);
   hipLaunchKernelGGL(gemm_x_prep_kernel, dim3(kTok), dim3(256), 0, st, x, int(k), int(n_tok), xh, xf);
   const dim3 grid(unsigned((n + kTileN - 1) / kTileN), unsigned(p.slices));
   if (p.slices == 1) {
-    hipLaunchKernelGGL(q4_gemm_kernel<false>, grid, dim3(256), 0, st, nib, scl, xh, xf, int(n), int(k), int(n_tok),
-                       p.bps, y);
+    hipLaunchKernelGGL(q4_gemm_kernel<false>, grid, dim3(256), 0, st, nib, scl, rexp, xh, xf, int(n), int(k),
+                       int(n_tok), p.bps, y);
   } else {
-    hipLaunchKernelGGL(q4_gemm_kernel<true>, grid, dim3(256), 0, st, nib, scl, xh, xf, int(n), int(k), int(n_tok),
-                       p.bps, part);
+    hipLaunchKernelGGL(q4_gemm_kernel<true>, grid, dim3(256), 0, st, nib, scl, rexp, xh, xf, int(n), int(k),
+                       int(n_tok), p.bps, part);
     const size_t total = size_t(n_tok) * size_t(n);
     const unsigned rgrid = unsigned(std::min<size_t>((total + 255) / 256, 4096));
     hipLaunchKernelGGL(gemm_reduce_kernel, dim3(rgrid), dim3(256), 0, st, part, p.slices, int(n), int(n_tok), y);

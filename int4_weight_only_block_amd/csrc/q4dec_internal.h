@@ -21,9 +21,11 @@ inline bool aligned(const void* p, size_t a) {
 }
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Offsets of the two planes inside a packed [n, k] matrix.
+// Planes of a packed [n, k] matrix, in order: nibbles, fp16 scales, and one
+// byte per row holding the largest fp16 exponent field among the row's scales.
 inline size_t nib_plane_bytes(int64_t n, int64_t k) { return align256(size_t(n) * size_t(k) / 2); }
 inline size_t scale_plane_bytes(int64_t n, int64_t k) { return align256(size_t(n) * size_t(k / 32) * 2); }
+inline size_t rexp_plane_bytes(int64_t n) { return align256(size_t(n)); }
 
 inline int launch_status(const char* what) {
   hipError_t e = hipGetLastError();

@@ -333,3 +333,20 @@ def test_gemm_rows_match_gemv_and_are_deterministic():
     # a chunk shorter than 64 returns the same rows as the full chunk
     y5 = q4.q4_gemm_s64(packed, n, k, xd[:5].contiguous()).cpu().numpy()
     assert (np.abs(y5.astype(np.float64) - y1[:5]) <= 2 * oracle.gemv_tolerance(a[:5])).all()
+
+
+def test_gemm_s64_scale_range():
+    """Scales across the fp16 range: large scales take the per-row range
+    shift, tiny and subnormal scales exercise the exact hi/lo split."""
+    n, k = 256, 1024
+    rng = synth.rng_for(22)
+    codes, _ = synth.q4_weights(rng, n, k)
+    e = rng.uniform(-24, 15.9, size=(n, k // 32))
+    sb = np.float16(2.0 ** e).view(np.uint16).copy()
+    sb[:8] = np.float16(3.0e4).view(np.uint16)      # rows of only large scales
+    sb[8:16, ::2] = np.float16(2.0 ** -20).view(np.uint16)  # subnormal scales
+    xs = synth.bf16_normal(rng, (64, k))
+    y = q4.q4_gemm_s64(pack(codes, sb), n, k, d(xs)).cpu().numpy()
+    yr, a = oracle.gemm(codes, sb, xs)
+    assert np.isfinite(y[:, :8]).all()
+    assert_within_tol(y.ravel(), yr.ravel(), a.ravel(), "gemm scale range")
