@@ -1,13 +1,14 @@
 // S=1 q4_0 dequant-GEMV and the LM head with softcap + argmax.
 //
 // Weight stream: each lane owns a fixed set of 32-wide k-blocks of its row
-// group (block b = j * LPR + t for j < BPL, t = lane % LPR), keeps the matching
-// activations in registers for the whole kernel, and walks down the rows. One
+// group (block b = j * LPR + t for j < BPL, t = lane % LPR), reads the matching
+// activations from LDS (broadcast across the row groups of a wave), and walks
+// down the rows. One
 // 16-byte non-temporal load per lane per block; LPR lanes of a row read
 // LPR * 16 contiguous bytes, so every load instruction is fully coalesced in
 // the row-major nibble plane. Codes are unpacked to exact fp16 integers in
 // registers and reduced with v_dot2c_f32_f16 against activations converted
-// once per workgroup into block-scaled fp16 (LDS), then each block partial is
+// once per workgroup into block-scaled fp16 in LDS, then each block partial is
 // scaled by its fp16 weight scale and the block's power of two in fp32. The
 // LPR partials of a row are summed with DPP.
 //
@@ -28,14 +29,12 @@ namespace q4dec {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
-// Per-lane state of the weight stream: this lane's blocks of the row group
-// in flight, its activation registers and the running output state.
+// Per-lane state of the weight stream: this lane's blocks of the current row
+// group in flight and the power-of-two factors of its activation blocks.
 template <int LPR, int BPL, bool FULL>
 struct Lane {
   uint4 q[BPL];
   uint32_t s[BPL];
-  uint32_t xr[BPL][16];
-  float fr[BPL];
 
   __device__ __forceinline__ void load(const uint8_t* __restrict__ nib, const uint16_t* __restrict__ scl, int row,
                                        int t, int B, size_t row_bytes) {
@@ -52,13 +51,13 @@ struct Lane {
     }
   }
 
-  // Dot product of the row group held in q/s; with REFILL, block j's
-  // registers are reloaded from `row_next` right after their last use, so a
-  // row group of loads stays in flight with no second buffer.
+  // Dot product of the row group held in q/s against the activations in LDS;
+  // with REFILL, block j's registers are reloaded from `row_next` right after
+  // their last use, so a row group of loads stays in flight per wave.
   template <bool REFILL>
   __device__ __forceinline__ float dot(const uint8_t* __restrict__ nib, const uint16_t* __restrict__ scl,
-                                       int row_next, int t, int B, size_t row_bytes, uint32_t m_lo, uint32_t m_hi,
-                                       uint32_t magic) {
+                                       const uint32_t* __restrict__ xs, const float* fr, int row_next, int t,
+                                       int B, size_t row_bytes, uint32_t m_lo, uint32_t m_hi, uint32_t magic) {
     const u32x4* np = reinterpret_cast<const u32x4*>(nib + size_t(row_next) * row_bytes);
     const uint16_t* sp = scl + size_t(row_next) * size_t(B);
     float acc = 0.0f;
@@ -66,7 +65,14 @@ struct Lane {
     for (int j = 0; j < BPL; ++j) {
       const int b = j * LPR + t;
       if (FULL || b < B) {
-        const float p = block_dot(q[j], xr[j], m_lo, m_hi, magic);
+        uint32_t xh[16];
+        const uint4* s4 = reinterpret_cast<const uint4*>(xs + 16 * b);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 v = s4[i ^ (b & 3)];  // quarter i sits in slot i ^ (b & 3)
+          xh[4 * i + 0] = v.x; xh[4 * i + 1] = v.y; xh[4 * i + 2] = v.z; xh[4 * i + 3] = v.w;
+        }
+        const float p = block_dot(q[j], xh, m_lo, m_hi, magic);
         const float d = float(__builtin_bit_cast(_Float16, uint16_t(s[j])));
         acc = fmaf(d * p, fr[j], acc);
         if constexpr (REFILL) {
@@ -88,6 +94,9 @@ __global__ __launch_bounds__(kThreads) void q4_rows_kernel(const uint8_t* __rest
                                                            float* __restrict__ y, uint2* __restrict__ partials) {
   constexpr int RPW = 64 / LPR;  // rows per wave per iteration
   constexpr int MAXB = LPR * BPL;
+  // activations as block-scaled fp16 pairs: block b at xs[16 b], its four
+  // 16-byte quarters swizzled (quarter i in slot i ^ (b & 3)) so the 16
+  // distinct blocks of one ds_read_b128 hit distinct banks
   __shared__ uint32_t xs[MAXB * 16];
   __shared__ float xf[MAXB];
   const int B = k >> 5;
@@ -111,25 +120,20 @@ __global__ __launch_bounds__(kThreads) void q4_rows_kernel(const uint8_t* __rest
   if (iters > 0) L.load(nib, scl, row_of(0), t, B, row_bytes);
 
   // Stage the activations once per workgroup as block-scaled fp16 pairs.
-  for (int b = threadIdx.x; b < B; b += kThreads) xf[b] = convert_x_block(x + 32 * b, xs + 16 * b);
+  for (int b = threadIdx.x; b < B; b += kThreads) {
+    uint32_t tmp[16];
+    xf[b] = convert_x_block(x + 32 * b, tmp);
+    uint4* d4 = reinterpret_cast<uint4*>(xs + 16 * b);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d4[i ^ (b & 3)] = make_uint4(tmp[4 * i], tmp[4 * i + 1], tmp[4 * i + 2], tmp[4 * i + 3]);
+  }
   __syncthreads();
 
+  float fr[BPL];
 #pragma unroll
   for (int j = 0; j < BPL; ++j) {
     const int b = j * LPR + t;
-    if (FULL || b < B) {
-      const uint4* s4 = reinterpret_cast<const uint4*>(xs + 16 * b);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint4 v = s4[i];
-        L.xr[j][4 * i + 0] = v.x; L.xr[j][4 * i + 1] = v.y; L.xr[j][4 * i + 2] = v.z; L.xr[j][4 * i + 3] = v.w;
-      }
-      L.fr[j] = xf[b];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) L.xr[j][i] = 0u;
-      L.fr[j] = 0.0f;
-    }
+    fr[j] = (FULL || b < B) ? xf[b] : 0.0f;
   }
 
   uint32_t m_lo, m_hi, magic;
@@ -152,11 +156,11 @@ __global__ __launch_bounds__(kThreads) void q4_rows_kernel(const uint8_t* __rest
     }
   };
   for (int i = 0; i + 1 < iters; ++i) {
-    const float acc = L.template dot<true>(nib, scl, row_of(i + 1), t, B, row_bytes, m_lo, m_hi, magic);
+    const float acc = L.template dot<true>(nib, scl, xs, fr, row_of(i + 1), t, B, row_bytes, m_lo, m_hi, magic);
     emit(i, acc);
   }
   if (iters > 0) {
-    const float acc = L.template dot<false>(nib, scl, 0, t, B, row_bytes, m_lo, m_hi, magic);
+    const float acc = L.template dot<false>(nib, scl, xs, fr, 0, t, B, row_bytes, m_lo, m_hi, magic);
     emit(iters - 1, acc);
   }
 
