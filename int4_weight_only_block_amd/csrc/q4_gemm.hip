@@ -9,17 +9,18 @@
 // c * d_lo are exact in fp16, and the two v_mfma_f32_16x16x32_f16 products
 // accumulate straight into fp32, so the sum is exact up to fp32 accumulation
 // and no per-block fold runs on the VALU. Activations are converted once per
-// call into fp16 scaled by a per-token power of two (the largest magnitude of
-// the token lands in [2^14, 2^15)); a row whose largest scale would let
-// c * d_hi overflow fp16 is scaled down by a power of two for the slice. Both
-// factors are undone on the output.
+// call into fp16 scaled by a per-token power of two (the token's largest
+// magnitude lands in [2^14, 2^15)) by a small prep kernel, so the conversion
+// is not repeated by every workgroup; a row whose largest scale would let
+// c * d_hi overflow fp16 is scaled down by a power of two. Both factors are
+// undone on the output.
 //
 // Work split. A workgroup (4 waves) owns 128 output rows (32 per wave, two
 // MFMA column tiles) for all 64 token slots and one K slice. Activations move
-// through LDS in chunks of 8 blocks (32 KB, double-buffered) shared by the 4
-// waves; the next chunk's weights and activations are loaded into registers
-// while the current chunk runs on the matrix cores. Small-N matrices split K
-// over several workgroups; their partial sums go to the workspace and a second
+// through LDS in chunks of 8 blocks shared by the 4 waves; the weights and
+// activations of the next two chunks are in flight in registers while the
+// current chunk runs on the matrix cores. Small-N matrices split K over
+// several workgroups; their partial sums go to the workspace and a second
 // kernel adds them in a fixed order, so results are deterministic.
 #include <math.h>
 
@@ -38,9 +39,9 @@ constexpr int kTileN = 128;  // weight rows per workgroup (4 waves x kSub x 16)
 constexpr int kChunk = 8;    // 32-wide blocks per LDS chunk
 
 struct GemmPlan {
-  int slices;        // K slices
-  int bps;           // blocks per slice
-  size_t xh_off, xf_off, part_off, total;
+  int slices;  // K slices
+  int bps;     // blocks per slice
+  size_t xh_off, xf_off, part_off, total;  // workspace: fp16 activations, token factors, partials
 };
 
 static GemmPlan gemm_plan(int64_t n, int64_t k) {
@@ -62,30 +63,25 @@ static GemmPlan gemm_plan(int64_t n, int64_t k) {
 
 // One workgroup per token slot: find the token's largest exponent, convert
 // its row to scaled fp16, store 2^E. Slots >= n_tok are zero-filled. Rows are
-// handled 8 values (16 bytes) at a time when 16-byte aligned.
+// read and written 8 values (16 bytes) at a time (x is 16-byte aligned and
+// k % 32 == 0).
 __global__ __launch_bounds__(256) void gemm_x_prep_kernel(const uint16_t* __restrict__ x, int k, int n_tok,
                                                           _Float16* __restrict__ xh, float* __restrict__ xf) {
   const int s = blockIdx.x;
-  _Float16* dst = xh + size_t(s) * size_t(k);
-  const int k8 = k >> 3;  // k % 32 == 0
+  uint4* dst = reinterpret_cast<uint4*>(xh + size_t(s) * size_t(k));
+  const int k8 = k >> 3;
   if (s >= n_tok) {
-    for (int i = threadIdx.x; i < k8; i += 256) reinterpret_cast<uint4*>(dst)[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int i = threadIdx.x; i < k8; i += 256) dst[i] = make_uint4(0u, 0u, 0u, 0u);
     if (threadIdx.x == 0) xf[s] = 0.0f;
     return;
   }
-  const uint16_t* src = x + size_t(s) * size_t(k);
-  const bool vec = (reinterpret_cast<uintptr_t>(src) & 15) == 0;
+  const uint4* s4 = reinterpret_cast<const uint4*>(x + size_t(s) * size_t(k));
   uint32_t emax = 1;
-  if (vec) {
-    const uint4* s4 = reinterpret_cast<const uint4*>(src);
-    for (int i = threadIdx.x; i < k8; i += 256) {
-      const uint4 v = s4[i];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  for (int i = threadIdx.x; i < k8; i += 256) {
+    const uint4 v = s4[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) emax = max(emax, max((w[j] >> 7) & 0xFFu, (w[j] >> 23) & 0xFFu));
-    }
-  } else {
-    for (int i = threadIdx.x; i < k; i += 256) emax = max(emax, (uint32_t(src[i]) >> 7) & 0xFFu);
+    for (int j = 0; j < 4; ++j) emax = max(emax, max((w[j] >> 7) & 0xFFu, (w[j] >> 23) & 0xFFu));
   }
   for (int off = 32; off >= 1; off >>= 1) emax = max(emax, uint32_t(__shfl_xor(int(emax), off)));
   __shared__ uint32_t wm[4];
@@ -93,21 +89,17 @@ __global__ __launch_bounds__(256) void gemm_x_prep_kernel(const uint16_t* __rest
   __syncthreads();
   emax = max(max(wm[0], wm[1]), max(wm[2], wm[3]));
   const int e = int(emax) - 127 - 14;
-  if (vec) {
-    const uint4* s4 = reinterpret_cast<const uint4*>(src);
-    for (int i = threadIdx.x; i < k8; i += 256) {
-      const uint4 v = s4[i];
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-      uint32_t o[4];
+  for (int i = threadIdx.x; i < k8; i += 256) {
+    const uint4 v = s4[i];
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        half2_t h = {(_Float16)ldexpf(bf16_to_f32(w[j] & 0xFFFFu), -e), (_Float16)ldexpf(bf16_to_f32(w[j] >> 16), -e)};
-        o[j] = __builtin_bit_cast(uint32_t, h);
-      }
-      reinterpret_cast<uint4*>(dst)[i] = make_uint4(o[0], o[1], o[2], o[3]);
+    for (int j = 0; j < 4; ++j) {
+      const half2_t h = {(_Float16)ldexpf(bf16_to_f32(w[j] & 0xFFFFu), -e),
+                         (_Float16)ldexpf(bf16_to_f32(w[j] >> 16), -e)};
+      o[j] = __builtin_bit_cast(uint32_t, h);
     }
-  } else {
-    for (int i = threadIdx.x; i < k; i += 256) dst[i] = (_Float16)ldexpf(bf16_to_f32(src[i]), -e);
+    dst[i] = make_uint4(o[0], o[1], o[2], o[3]);
   }
   if (threadIdx.x == 0) xf[s] = ldexpf(1.0f, e);
 }
@@ -128,13 +120,14 @@ __device__ __forceinline__ half8_t codes_f16x8(uint32_t w, uint32_t m_lo, uint32
 struct ChunkRegs {
   uint4 w[kSub][2];      // full 16-byte block (32 codes) per column tile and group
   uint32_t sd[kSub][2];  // its fp16 scale bits
-  uint4 xr[(kChunk * kTok * 4) / 256];
+  uint4 xr[(kChunk * kTok * 4) / 256];  // scaled fp16 activations
 };
 
 // LDS slot of activation quarter qq of a token: swizzled so the 16 lanes of a
 // ds_read_b128 (16 tokens, same quarter) hit 16 distinct bank groups.
 __device__ __forceinline__ int xslot(int tok, int qq) { return qq ^ ((tok >> 2) & 3); }
 
+// Thread tid stages token tid / 4, quarter tid % 4 of each block of a chunk.
 __device__ __forceinline__ void load_chunk(ChunkRegs& R, const uint4* const (&wrow)[kSub],
                                            const uint16_t* const (&srow)[kSub], const _Float16* __restrict__ xh,
                                            int k, int q, int b0, int b_end) {
@@ -147,16 +140,20 @@ __device__ __forceinline__ void load_chunk(ChunkRegs& R, const uint4* const (&wr
       R.w[u][g] = wrow[u][bc];
       R.sd[u][g] = bb < b_end ? uint32_t(srow[u][bc]) : 0u;
     }
+  const int sx = threadIdx.x >> 2, qq = threadIdx.x & 3;
 #pragma unroll
-  for (int i = 0; i < (kChunk * kTok * 4) / 256; ++i) {
-    const int idx = threadIdx.x + 256 * i;
-    const int c = idx / (kTok * 4);
-    const int rem = idx % (kTok * 4);
-    const int sx = rem >> 2, qq = rem & 3;
+  for (int c = 0; c < kChunk; ++c) {
     const int bb = b0 + c;
-    R.xr[i] = bb < b_end ? *reinterpret_cast<const uint4*>(xh + size_t(sx) * size_t(k) + size_t(bb) * 32 + qq * 8)
+    R.xr[c] = bb < b_end ? *reinterpret_cast<const uint4*>(xh + size_t(sx) * size_t(k) + size_t(bb) * 32 + qq * 8)
                          : make_uint4(0u, 0u, 0u, 0u);
   }
+}
+
+// Writes the staged chunk to LDS (thread tid: token tid / 4, quarter tid % 4).
+__device__ __forceinline__ void store_chunk(const ChunkRegs& R, uint4 (*xs)[kTok][4]) {
+  const int sx = threadIdx.x >> 2, qq = threadIdx.x & 3;
+#pragma unroll
+  for (int c = 0; c < kChunk; ++c) xs[c][sx][xslot(sx, qq)] = R.xr[c];
 }
 
 // exact split of one fp16 scale (already shifted into range): hi keeps the
@@ -167,6 +164,55 @@ __device__ __forceinline__ void split_scale(uint32_t dbits, half2_t& hi, half2_t
   const _Float16 l = d - h;
   hi = half2_t{h, h};
   lo = half2_t{l, l};
+}
+
+// One chunk on the matrix cores: 2 groups x 4 k-slices x kSub column tiles x
+// 4 token tiles x (hi, lo), accumulated into t.
+__device__ __forceinline__ void mma_chunk(float4_t (&t)[kSub][4], const uint4 (&w)[kSub][2],
+                                          const uint32_t (&sd)[kSub][2], const int (&shift)[kSub],
+                                          const uint4 (*xs)[kTok][4], int q, int col, int ngroups,
+                                          uint32_t m_lo, uint32_t m_hi, uint32_t magic) {
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {
+    if (g >= ngroups) break;
+    half2_t dh[kSub], dl[kSub];
+#pragma unroll
+    for (int u = 0; u < kSub; ++u) {
+      uint32_t dbits = sd[u][g];
+      if (shift[u] > 0) {  // rare: rows with scales >= 2^11
+        const float df = ldexpf(float(__builtin_bit_cast(_Float16, uint16_t(dbits))), -shift[u]);
+        dbits = __builtin_bit_cast(uint16_t, (_Float16)df);
+      }
+      split_scale(dbits, dh[u], dl[u]);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      half8_t a[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int tok = 16 * m + col;
+        a[m] = __builtin_bit_cast(half8_t, xs[4 * g + q][tok][xslot(tok, j)]);
+      }
+#pragma unroll
+      for (int u = 0; u < kSub; ++u) {
+        const uint32_t wd = j == 0 ? w[u][g].x : j == 1 ? w[u][g].y : j == 2 ? w[u][g].z : w[u][g].w;
+        const CodePairs cp = unpack_dword(wd, m_lo, m_hi, magic);
+        half8_t bh, bl;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const half2_t ph = cp.p[jj] * dh[u];
+          const half2_t pl = cp.p[jj] * dl[u];
+          bh[2 * jj] = ph[0]; bh[2 * jj + 1] = ph[1];
+          bl[2 * jj] = pl[0]; bl[2 * jj + 1] = pl[1];
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          t[u][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[m], bh, t[u][m], 0, 0, 0);
+          t[u][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[m], bl, t[u][m], 0, 0, 0);
+        }
+      }
+    }
+  }
 }
 
 template <bool PARTIAL>
@@ -209,72 +255,32 @@ __global__ __launch_bounds__(256) void q4_gemm_kernel(const uint8_t* __restrict_
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[u][m] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  ChunkRegs cur;
-  if (b_begin < b_end) load_chunk(cur, wrow, srow, xh, k, q, b_begin, b_end);
+  // two chunks in flight: A holds chunks 0, 2, 4, ..., B holds 1, 3, 5, ...
+  ChunkRegs ra, rb;
+  if (b_begin < b_end) load_chunk(ra, wrow, srow, xh, k, q, b_begin, b_end);
+  if (b_begin + kChunk < b_end) load_chunk(rb, wrow, srow, xh, k, q, b_begin + kChunk, b_end);
 
-  for (int b0 = b_begin; b0 < b_end; b0 += kChunk) {
+  auto run = [&](ChunkRegs& R, int b0) {
     __syncthreads();  // previous chunk fully consumed
-#pragma unroll
-    for (int i = 0; i < (kChunk * kTok * 4) / 256; ++i) {
-      const int idx = threadIdx.x + 256 * i;
-      const int c = idx / (kTok * 4);
-      const int rem = idx % (kTok * 4);
-      const int sx = rem >> 2;
-      xs[c][sx][xslot(sx, rem & 3)] = cur.xr[i];
-    }
+    store_chunk(R, xs);
     uint4 w[kSub][2];
     uint32_t sd[kSub][2];
 #pragma unroll
     for (int u = 0; u < kSub; ++u)
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
-        w[u][g] = cur.w[u][g];
-        sd[u][g] = cur.sd[u][g];
+        w[u][g] = R.w[u][g];
+        sd[u][g] = R.sd[u][g];
       }
     __syncthreads();
-    // next chunk in flight while this one runs on the matrix cores
-    if (b0 + kChunk < b_end) load_chunk(cur, wrow, srow, xh, k, q, b0 + kChunk, b_end);
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      if (b0 + 4 * g >= b_end) break;
-      half2_t dh[kSub], dl[kSub];
-#pragma unroll
-      for (int u = 0; u < kSub; ++u) {
-        uint32_t dbits = sd[u][g];
-        if (shift[u] > 0) {  // rare: rows with scales >= 2^11
-          const float df = ldexpf(float(__builtin_bit_cast(_Float16, uint16_t(dbits))), -shift[u]);
-          dbits = __builtin_bit_cast(uint16_t, (_Float16)df);
-        }
-        split_scale(dbits, dh[u], dl[u]);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        half8_t a[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int tok = 16 * m + col;
-          a[m] = __builtin_bit_cast(half8_t, xs[4 * g + q][tok][xslot(tok, j)]);
-        }
-#pragma unroll
-        for (int u = 0; u < kSub; ++u) {
-          const uint32_t wd = j == 0 ? w[u][g].x : j == 1 ? w[u][g].y : j == 2 ? w[u][g].z : w[u][g].w;
-          const CodePairs cp = unpack_dword(wd, m_lo, m_hi, magic);
-          half8_t bh, bl;
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            const half2_t ph = cp.p[jj] * dh[u];
-            const half2_t pl = cp.p[jj] * dl[u];
-            bh[2 * jj] = ph[0]; bh[2 * jj + 1] = ph[1];
-            bl[2 * jj] = pl[0]; bl[2 * jj + 1] = pl[1];
-          }
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            acc[u][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[m], bh, acc[u][m], 0, 0, 0);
-            acc[u][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[m], bl, acc[u][m], 0, 0, 0);
-          }
-        }
-      }
-    }
+    // refill this register set with the chunk after next
+    if (b0 + 2 * kChunk < b_end) load_chunk(R, wrow, srow, xh, k, q, b0 + 2 * kChunk, b_end);
+    const int ngroups = (min(kChunk, b_end - b0) + 3) / 4;
+    mma_chunk(acc, w, sd, shift, xs, q, col, ngroups, m_lo, m_hi, magic);
+  };
+  for (int b0 = b_begin; b0 < b_end; b0 += 2 * kChunk) {
+    run(ra, b0);
+    if (b0 + kChunk < b_end) run(rb, b0 + kChunk);
   }
 
   // lane holds tokens s = 16m + 4q + i of output rows rows[u]
@@ -323,7 +329,6 @@ extern "C" int q4_gemm_s64(const void* packed, int64_t n, int64_t k, const uint1
   if (!packed) return fail(Q4DEC_ERR_NULL, "q4_gemm_s64: packed is NULL");
   if (!x) return fail(Q4DEC_ERR_NULL, "q4_gemm_s64: x is NULL");
   if (!y) return fail(Q4DEC_ERR_NULL, "q4_gemm_s64: y is NULL");
-  if (!ws) return fail(Q4DEC_ERR_NULL, "q4_gemm_s64: ws is NULL");
   if (n <= 0 || n >= (int64_t(1) << 31))
     return fail(Q4DEC_ERR_SHAPE, "q4_gemm_s64: n must be in [1, 2^31) (got %lld)", (long long)n);
   if (k <= 0 || k % 32)
@@ -333,8 +338,9 @@ extern "C" int q4_gemm_s64(const void* packed, int64_t n, int64_t k, const uint1
   if (n_tok < 1 || n_tok > 64)
     return fail(Q4DEC_ERR_SHAPE, "q4_gemm_s64: n_tok must be in [1, 64] (got %lld)", (long long)n_tok);
   if (!aligned(packed, 16)) return fail(Q4DEC_ERR_ALIGN, "q4_gemm_s64: packed must be 16-byte aligned");
-  if (!aligned(x, 2)) return fail(Q4DEC_ERR_ALIGN, "q4_gemm_s64: x must be 2-byte aligned");
+  if (!aligned(x, 16)) return fail(Q4DEC_ERR_ALIGN, "q4_gemm_s64: x must be 16-byte aligned");
   if (!aligned(y, 4)) return fail(Q4DEC_ERR_ALIGN, "q4_gemm_s64: y must be 4-byte aligned");
+  if (!ws) return fail(Q4DEC_ERR_NULL, "q4_gemm_s64: ws is NULL");
   if (!aligned(ws, 256)) return fail(Q4DEC_ERR_ALIGN, "q4_gemm_s64: ws must be 256-byte aligned");
   const GemmPlan p = gemm_plan(n, k);
   if (ws_bytes < p.total)
