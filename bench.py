@@ -101,7 +101,7 @@ class Workload:
         self.ple_out = torch.empty((1, s["dim"]), dtype=torch.float32, device=dev)
         hn, hk = self.mats[-1][1], self.mats[-1][2]
         self.head_nk = (hn, hk)
-        self.ws = torch.empty(q4.lmhead_workspace_bytes(hn, hk), dtype=torch.uint8, device=dev)
+        self.ws = torch.zeros(q4.lmhead_workspace_bytes(hn, hk), dtype=torch.uint8, device=dev)
         self.idx = torch.empty(1, dtype=torch.int32, device=dev)
         self.val = torch.empty(1, dtype=torch.float32, device=dev)
         torch.cuda.synchronize()
@@ -338,10 +338,10 @@ def main():
         shapes = {name.split(".")[-1] if "." in name else name: (n, k) for name, n, k in wl.mats}
         groups = {
             # kernel instantiation -> launch kinds it serves
-            "q4_rows_kernel<16,5,gemv> (K=2560: qkv, gate_up)": ["qkv", "gate_up"],
-            "q4_rows_kernel<16,4,gemv> (K=2048: o)": ["o"],
-            "q4_rows_kernel<64,5,gemv> (K=10240: down)": ["down"],
-            "q4_rows_kernel<16,5,head> + reduce (K=2560 head)": ["head"],
+            "q4_rows_kernel gemv (K=2560: qkv, gate_up)": ["qkv", "gate_up"],
+            "q4_rows_kernel gemv (K=2048: o)": ["o"],
+            "q4_rows_kernel gemv (K=10240: down)": ["down"],
+            "q4_rows_kernel head + reduce (K=2560)": ["head"],
             "ple_gather_kernel": ["ple"],
         }
         kernels = {}
@@ -384,7 +384,7 @@ def main():
             "avg_launch_us": kd["avg_launch_us"],
             "bytes_per_launch": kd["bytes_per_launch"],
         }
-        hk = "q4_rows_kernel<16,5,head> + reduce (K=2560 head)"
+        hk = "q4_rows_kernel head + reduce (K=2560)"
         if hk in kernels:
             kh = kernels[hk]
             result["roofline_lmhead"] = {

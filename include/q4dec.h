@@ -119,12 +119,16 @@ size_t lmhead_workspace_bytes(int64_t vocab, int64_t k);
  * fused head + two-level argmax). Lowest index wins among equal maxima. The
  * cap is strictly increasing, so the argmax is taken on z (no per-row tanh)
  * and only the winning value is capped. Logits that are NaN never win; if no
- * logit compares, idx_out = -1 and val_out = NaN.
+ * logit compares, idx_out = -1 and val_out = NaN. Two launches on `stream`:
+ * every workgroup of the first leaves its best (value, row) in ws, a
+ * one-workgroup second launch reduces them.
  *   packed   from q4_pack with (n = vocab, k); 16-byte aligned.
  *   x        bf16 [k], 16-byte aligned.
  *   cap      30.0 for Gemma 4; cap <= 0 returns the raw maximum logit.
  *   ws       device workspace of ws_bytes >= lmhead_workspace_bytes(vocab, k),
- *            8-byte aligned; scratch for per-workgroup partials.
+ *            8-byte aligned, owned by the caller; scratch for per-workgroup
+ *            partials, no initial contents needed. Calls that share one ws
+ *            must not overlap (use one stream or separate buffers).
  *   idx_out  device int32 [1]; val_out device fp32 [1].
  * Errors: NULL pointer, vocab <= 0 or >= 2^31, k constraints as q4_gemv,
  *         workspace too small, misalignment. */

@@ -6,7 +6,9 @@
 // down the rows. One
 // 16-byte non-temporal load per lane per block; LPR lanes of a row read
 // LPR * 16 contiguous bytes, so every load instruction is fully coalesced in
-// the row-major nibble plane. Codes are unpacked to exact fp16 integers in
+// the row-major nibble plane. The 2-byte scale loads of one instruction cover
+// only part of a cache line, so they go through the cache (a streaming load
+// would let the line be dropped and fetched again for the next block). Codes are unpacked to exact fp16 integers in
 // registers and reduced with v_dot2c_f32_f16 against activations converted
 // once per workgroup into block-scaled fp16 in LDS, then each block partial is
 // scaled by its fp16 weight scale and the block's power of two in fp32. The
@@ -46,7 +48,7 @@ struct Lane {
       if (FULL || b < B) {
         const u32x4 v = __builtin_nontemporal_load(np + b);
         q[j] = make_uint4(v.x, v.y, v.z, v.w);
-        s[j] = __builtin_nontemporal_load(sp + b);
+        s[j] = sp[b];
       }
     }
   }
@@ -79,13 +81,29 @@ struct Lane {
           __builtin_amdgcn_sched_barrier(0);
           const u32x4 v = __builtin_nontemporal_load(np + b);
           q[j] = make_uint4(v.x, v.y, v.z, v.w);
-          s[j] = __builtin_nontemporal_load(sp + b);
+          s[j] = sp[b];
         }
       }
     }
     return acc;
   }
 };
+
+// Upper bound on head workgroups (one (value, row) partial each).
+constexpr int kMaxPartials = 8192;
+
+// Best (value, row) of the wave into every lane.
+__device__ __forceinline__ void wave_best(float& best, int& bidx) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(best, off);
+    const int oi = __shfl_xor(bidx, off);
+    if (better(ov, oi, best, bidx)) {
+      best = ov;
+      bidx = oi;
+    }
+  }
+}
 
 template <int LPR, int BPL, bool HEAD, bool FULL>
 __global__ __launch_bounds__(kThreads) void q4_rows_kernel(const uint8_t* __restrict__ nib,
@@ -165,15 +183,8 @@ __global__ __launch_bounds__(kThreads) void q4_rows_kernel(const uint8_t* __rest
   }
 
   if constexpr (HEAD) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(best, off);
-      const int oi = __shfl_xor(bidx, off);
-      if (better(ov, oi, best, bidx)) {
-        best = ov;
-        bidx = oi;
-      }
-    }
+    // pass 1: this workgroup's best (value, row) into its partial slot
+    wave_best(best, bidx);
     __shared__ float sv[kWaves];
     __shared__ int si[kWaves];
     if (lane == 0) {
@@ -192,31 +203,37 @@ __global__ __launch_bounds__(kThreads) void q4_rows_kernel(const uint8_t* __rest
   }
 }
 
-__global__ __launch_bounds__(256) void lmhead_reduce_kernel(const uint2* __restrict__ partials, int g, float cap,
-                                                            int32_t* __restrict__ idx_out,
-                                                            float* __restrict__ val_out) {
+// Pass 2: one workgroup reduces the pass-1 partials. Each thread issues all
+// of its (at most kPartialsPerThread) loads before comparing, so the pass
+// costs one load latency. The comparator is a total order on (value, row),
+// so the result is independent of the reduction order.
+constexpr int kReduceThreads = 1024;
+constexpr int kPartialsPerThread = kMaxPartials / kReduceThreads;
+
+__global__ __launch_bounds__(kReduceThreads) void lmhead_reduce_kernel(const uint2* __restrict__ partials, int g,
+                                                                       float cap, int32_t* __restrict__ idx_out,
+                                                                       float* __restrict__ val_out) {
+  uint2 p[kPartialsPerThread];
+#pragma unroll
+  for (int j = 0; j < kPartialsPerThread; ++j) {
+    const int i = threadIdx.x + j * kReduceThreads;
+    p[j] = i < g ? partials[i] : make_uint2(__builtin_bit_cast(uint32_t, -INFINITY), uint32_t(INT_MAX));
+  }
   float best = -INFINITY;
   int bidx = INT_MAX;
-  for (int i = threadIdx.x; i < g; i += 256) {
-    const uint2 p = partials[i];
-    const float v = __builtin_bit_cast(float, p.x);
-    const int ix = int(p.y);
+#pragma unroll
+  for (int j = 0; j < kPartialsPerThread; ++j) {
+    const float v = __builtin_bit_cast(float, p[j].x);
+    const int ix = int(p[j].y);
     if (better(v, ix, best, bidx)) {
       best = v;
       bidx = ix;
     }
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(best, off);
-    const int oi = __shfl_xor(bidx, off);
-    if (better(ov, oi, best, bidx)) {
-      best = ov;
-      bidx = oi;
-    }
-  }
-  __shared__ float sv[4];
-  __shared__ int si[4];
+  wave_best(best, bidx);
+  constexpr int kW = kReduceThreads / 64;
+  __shared__ float sv[kW];
+  __shared__ int si[kW];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (lane == 0) {
     sv[wave] = best;
@@ -224,7 +241,7 @@ __global__ __launch_bounds__(256) void lmhead_reduce_kernel(const uint2* __restr
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int w = 1; w < 4; ++w)
+    for (int w = 1; w < kW; ++w)
       if (better(sv[w], si[w], best, bidx)) {
         best = sv[w];
         bidx = si[w];
@@ -234,6 +251,7 @@ __global__ __launch_bounds__(256) void lmhead_reduce_kernel(const uint2* __restr
       *val_out = __builtin_nanf("");
     } else {
       *idx_out = bidx;
+      // the cap is increasing: capping the winner alone gives the capped maximum
       *val_out = cap > 0.0f ? cap * tanhf(best / cap) : best;
     }
   }
@@ -256,8 +274,8 @@ static const void* pick_kernel(int lpr, int bpl) {
 #define Q4_CASE(L, BP) \
   if (lpr == L && bpl == BP) return kernel_ptr<L, BP, HEAD, FULL>();
   Q4_CASE(16, 1) Q4_CASE(16, 2) Q4_CASE(16, 3) Q4_CASE(16, 4) Q4_CASE(16, 5)
-  Q4_CASE(32, 3) Q4_CASE(32, 4) Q4_CASE(32, 5)
-  Q4_CASE(64, 3) Q4_CASE(64, 4) Q4_CASE(64, 5) Q4_CASE(64, 6) Q4_CASE(64, 7) Q4_CASE(64, 8)
+  Q4_CASE(32, 2) Q4_CASE(32, 3) Q4_CASE(32, 4) Q4_CASE(32, 5) Q4_CASE(32, 6)
+  Q4_CASE(64, 1) Q4_CASE(64, 2) Q4_CASE(64, 3) Q4_CASE(64, 4) Q4_CASE(64, 5) Q4_CASE(64, 6) Q4_CASE(64, 7) Q4_CASE(64, 8)
 #undef Q4_CASE
   return nullptr;
 }
@@ -279,27 +297,56 @@ static int blocks_per_cu(const void* fn) {
 }
 
 template <bool HEAD>
-static Plan make_plan(int64_t n, int64_t k) {
-  const int B = int(k / 32);
+static Plan plan_for(int64_t n, int B, int lpr) {
   Plan p{};
-  if ((B + 15) / 16 <= 5) {
-    p.lpr = 16;
-  } else if ((B + 31) / 32 <= 5) {
-    p.lpr = 32;
-  } else {
-    p.lpr = 64;
-  }
-  p.bpl = (B + p.lpr - 1) / p.lpr;
-  p.full = (B == p.lpr * p.bpl);
-  p.fn = p.full ? pick_kernel<HEAD, true>(p.lpr, p.bpl) : pick_kernel<HEAD, false>(p.lpr, p.bpl);
-  p.rpw = 64 / p.lpr;
+  p.lpr = lpr;
+  p.bpl = (B + lpr - 1) / lpr;
+  p.full = (B == lpr * p.bpl);
+  p.fn = p.full ? pick_kernel<HEAD, true>(lpr, p.bpl) : pick_kernel<HEAD, false>(lpr, p.bpl);
+  p.rpw = 64 / lpr;
   p.rg = int((n + p.rpw - 1) / p.rpw);
   if (!p.fn) return p;
   // one resident round: every workgroup is live at once
-  const int waves_max = device_cu_count() * blocks_per_cu(p.fn) * kWaves;
+  const int cus = device_cu_count();
+  const int waves_max = cus * blocks_per_cu(p.fn) * kWaves;
   p.ipw = (p.rg + waves_max - 1) / waves_max;
+  // With one row per wave, converting x into LDS costs a workgroup about as
+  // much as its rows; let each wave walk up to three rows while the grid
+  // still covers most of the CUs.
+  if (p.rpw == 1 && p.ipw < 3) {
+    for (int want = 3; want > p.ipw; --want) {
+      const int64_t grid = ((p.rg + want - 1) / want + kWaves - 1) / kWaves;
+      if (grid * 5 >= int64_t(cus) * 4) {
+        p.ipw = want;
+        break;
+      }
+    }
+  }
   const int waves = (p.rg + p.ipw - 1) / p.ipw;
   p.grid = (waves + kWaves - 1) / kWaves;
+  return p;
+}
+
+template <bool HEAD>
+static Plan make_plan(int64_t n, int64_t k) {
+  const int B = int(k / 32);
+  int lpr = 64;
+  if ((B + 15) / 16 <= 5) {
+    lpr = 16;
+  } else if ((B + 31) / 32 <= 6) {
+    lpr = 32;
+  }
+  Plan p = plan_for<HEAD>(n, B, lpr);
+  // A matrix that fits one resident round at this split takes the widest
+  // split that still fills every lane: shorter block chains per wave and more
+  // waves to cover the load latency.
+  if (p.fn && p.ipw == 1) {
+    for (int wide = 64; wide > lpr; wide /= 2) {
+      if (B % wide || B / wide < 1) continue;
+      const Plan q = plan_for<HEAD>(n, B, wide);
+      if (q.fn && q.ipw == 1) return q;
+    }
+  }
   return p;
 }
 
@@ -325,7 +372,6 @@ static int check_common(const char* fn, const void* packed, int64_t n, const cha
   return Q4DEC_OK;
 }
 
-static constexpr int kMaxPartials = 8192;
 
 }  // namespace q4dec
 
@@ -371,6 +417,7 @@ extern "C" int lmhead_softcap_argmax(const void* packed, int64_t vocab, int64_t 
   hipStream_t st = static_cast<hipStream_t>(stream);
   rc = launch_rows(p, nib, scl, x, int(vocab), int(k), nullptr, partials, st);
   if (rc) return rc;
-  hipLaunchKernelGGL(lmhead_reduce_kernel, dim3(1), dim3(256), 0, st, partials, p.grid, cap, idx_out, val_out);
+  hipLaunchKernelGGL(lmhead_reduce_kernel, dim3(1), dim3(kReduceThreads), 0, st, partials, p.grid, cap, idx_out,
+                     val_out);
   return launch_status("lmhead_softcap_argmax");
 }

@@ -173,7 +173,7 @@ def test_gemv_e4b_layer_shapes(name):
 def _check_head_batch(codes, sb, xs, cap=30.0):
     vocab, k = codes.shape
     packed = pack(codes, sb)
-    ws = torch.empty(q4.lmhead_workspace_bytes(vocab, k), dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(q4.lmhead_workspace_bytes(vocab, k), dtype=torch.uint8, device=DEV)
     got = []
     for x in xs:
         i, v = q4.lmhead_softcap_argmax(packed, vocab, k, d(x), cap, ws)
@@ -242,6 +242,57 @@ def test_lmhead_e4b_head_shape():
     codes, sb = synth.q4_weights(rng, 262144, 2560)
     xs = [synth.bf16_normal(rng, 2560) for _ in range(4)]
     _check_head_batch(codes, sb, xs)
+
+
+def test_lmhead_shared_workspace_and_graph_replays():
+    """One workspace serves calls of different sizes back to back and the
+    replays of a captured call; every call writes a fresh result (outputs are
+    preset to a sentinel before each call)."""
+    ws = torch.zeros(q4.lmhead_workspace_bytes(262144, 2560), dtype=torch.uint8, device=DEV)
+    idx = torch.empty(1, dtype=torch.int32, device=DEV)
+    val = torch.empty(1, dtype=torch.float32, device=DEV)
+    cases = []
+    for vocab, k in [(262144, 1536), (4099, 2560), (1, 64), (70000, 2560)]:
+        rng = synth.rng_for(12, vocab, k)
+        codes, sb = synth.q4_weights(rng, vocab, k)
+        cases.append((vocab, k, codes, sb, pack(codes, sb)))
+    for vocab, k, codes, sb, packed in cases + cases[::-1]:
+        rng = synth.rng_for(13, vocab, k)
+        x = synth.bf16_normal(rng, k)
+        idx.fill_(-7)
+        val.fill_(float("nan"))
+        q4.lmhead_softcap_argmax(packed, vocab, k, d(x), 30.0, ws, idx, val)
+        z, a = oracle.gemm(codes, sb, x[None, :])
+        c = oracle.softcap(z[0])
+        ri = oracle.first_argmax(c)
+        gi = int(idx.item())
+        assert gi != -7, (vocab, k)
+        if oracle.top2_margin(c) >= 1e-3:
+            assert gi == ri, (vocab, k, gi, ri)
+        assert abs(float(val.item()) - c[ri]) <= 1e-4 * a[0, ri] + 1e-6
+
+    vocab, k, codes, sb, packed = cases[3]
+    xbuf = torch.zeros(k, dtype=torch.int16, device=DEV)
+    q4.lmhead_softcap_argmax(packed, vocab, k, xbuf, 30.0, ws, idx, val)  # warm-up outside capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        q4.lmhead_softcap_argmax(packed, vocab, k, xbuf, 30.0, ws, idx, val)
+    for rep in range(4):
+        x = synth.bf16_normal(synth.rng_for(14, rep), k)
+        xbuf.copy_(d(x))
+        idx.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        z, a = oracle.gemm(codes, sb, x[None, :])
+        c = oracle.softcap(z[0])
+        ri = oracle.first_argmax(c)
+        gi = int(idx.item())
+        assert gi != -7, rep
+        if oracle.top2_margin(c) >= 1e-3:
+            assert gi == ri, (rep, gi, ri)
+        assert abs(float(val.item()) - c[ri]) <= 1e-4 * a[0, ri] + 1e-6
 
 
 # -------------------------------------------------------------------- PLE --
