@@ -203,31 +203,34 @@ __global__ __launch_bounds__(kThreads) void q4_rows_kernel(const uint8_t* __rest
   }
 }
 
-// Pass 2: one workgroup reduces the pass-1 partials. Each thread issues all
-// of its (at most kPartialsPerThread) loads before comparing, so the pass
-// costs one load latency. The comparator is a total order on (value, row),
-// so the result is independent of the reduction order.
-constexpr int kReduceThreads = 1024;
-constexpr int kPartialsPerThread = kMaxPartials / kReduceThreads;
+// Pass 2: one workgroup reduces the pass-1 partials. Each thread issues 16
+// loads before comparing, so up to 4096 partials cost one load latency (a
+// 256-thread workgroup starts and synchronises faster than a 1024-thread
+// one). The comparator is a total order on (value, row), so the result is
+// independent of the reduction order.
+constexpr int kReduceThreads = 256;
+constexpr int kReduceBatch = 16;
 
 __global__ __launch_bounds__(kReduceThreads) void lmhead_reduce_kernel(const uint2* __restrict__ partials, int g,
                                                                        float cap, int32_t* __restrict__ idx_out,
                                                                        float* __restrict__ val_out) {
-  uint2 p[kPartialsPerThread];
-#pragma unroll
-  for (int j = 0; j < kPartialsPerThread; ++j) {
-    const int i = threadIdx.x + j * kReduceThreads;
-    p[j] = i < g ? partials[i] : make_uint2(__builtin_bit_cast(uint32_t, -INFINITY), uint32_t(INT_MAX));
-  }
   float best = -INFINITY;
   int bidx = INT_MAX;
+  for (int base = 0; base < g; base += kReduceThreads * kReduceBatch) {
+    uint2 p[kReduceBatch];
 #pragma unroll
-  for (int j = 0; j < kPartialsPerThread; ++j) {
-    const float v = __builtin_bit_cast(float, p[j].x);
-    const int ix = int(p[j].y);
-    if (better(v, ix, best, bidx)) {
-      best = v;
-      bidx = ix;
+    for (int j = 0; j < kReduceBatch; ++j) {
+      const int i = base + threadIdx.x + j * kReduceThreads;
+      p[j] = i < g ? partials[i] : make_uint2(__builtin_bit_cast(uint32_t, -INFINITY), uint32_t(INT_MAX));
+    }
+#pragma unroll
+    for (int j = 0; j < kReduceBatch; ++j) {
+      const float v = __builtin_bit_cast(float, p[j].x);
+      const int ix = int(p[j].y);
+      if (better(v, ix, best, bidx)) {
+        best = v;
+        bidx = ix;
+      }
     }
   }
   wave_best(best, bidx);
