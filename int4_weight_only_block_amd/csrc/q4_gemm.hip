@@ -131,6 +131,12 @@ __device__ __forceinline__ int xslot(int tok, int qq) { return qq ^ ((tok >> 2) 
 __device__ __forceinline__ void load_chunk(ChunkRegs& R, const uint4* const (&wrow)[kSub],
                                            const uint16_t* const (&srow)[kSub], const _Float16* __restrict__ xh,
                                            int k, int q, int b0, int b_end) {
+  // Every load is issued unconditionally and nothing is computed from the
+  // loaded values here, so the number of loads in flight is the same on
+  // every path and the wait before a chunk's first use only covers that
+  // chunk, not the chunk loaded after it. A block past the slice's end reads
+  // a valid block instead; its weight scale is zeroed when the chunk is used,
+  // which zeroes its products with the (finite) activations as well.
 #pragma unroll
   for (int u = 0; u < kSub; ++u)
 #pragma unroll
@@ -138,14 +144,14 @@ __device__ __forceinline__ void load_chunk(ChunkRegs& R, const uint4* const (&wr
       const int bb = b0 + 4 * g + q;
       const int bc = bb < b_end ? bb : b0;  // ragged tail: any valid block, zeroed by its scale
       R.w[u][g] = wrow[u][bc];
-      R.sd[u][g] = bb < b_end ? uint32_t(srow[u][bc]) : 0u;
+      R.sd[u][g] = srow[u][bc];  // zeroed at use when bb >= b_end
     }
   const int sx = threadIdx.x >> 2, qq = threadIdx.x & 3;
 #pragma unroll
   for (int c = 0; c < kChunk; ++c) {
     const int bb = b0 + c;
-    R.xr[c] = bb < b_end ? *reinterpret_cast<const uint4*>(xh + size_t(sx) * size_t(k) + size_t(bb) * 32 + qq * 8)
-                         : make_uint4(0u, 0u, 0u, 0u);
+    const int bc = bb < b_end ? bb : b0;
+    R.xr[c] = *reinterpret_cast<const uint4*>(xh + size_t(sx) * size_t(k) + size_t(bc) * 32 + qq * 8);
   }
 }
 
@@ -256,9 +262,11 @@ __global__ __launch_bounds__(256) void q4_gemm_kernel(const uint8_t* __restrict_
     for (int m = 0; m < 4; ++m) acc[u][m] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   // two chunks in flight: A holds chunks 0, 2, 4, ..., B holds 1, 3, 5, ...
+  // (every slice holds at least one block; a chunk past the slice's end is
+  // replaced by its first chunk, which is loaded but never used)
   ChunkRegs ra, rb;
-  if (b_begin < b_end) load_chunk(ra, wrow, srow, xh, k, q, b_begin, b_end);
-  if (b_begin + kChunk < b_end) load_chunk(rb, wrow, srow, xh, k, q, b_begin + kChunk, b_end);
+  load_chunk(ra, wrow, srow, xh, k, q, b_begin, b_end);
+  load_chunk(rb, wrow, srow, xh, k, q, b_begin + kChunk < b_end ? b_begin + kChunk : b_begin, b_end);
 
   auto run = [&](ChunkRegs& R, int b0) {
     __syncthreads();  // previous chunk fully consumed
@@ -270,18 +278,28 @@ __global__ __launch_bounds__(256) void q4_gemm_kernel(const uint8_t* __restrict_
 #pragma unroll
       for (int g = 0; g < 2; ++g) {
         w[u][g] = R.w[u][g];
-        sd[u][g] = R.sd[u][g];
+        sd[u][g] = b0 + 4 * g + q < b_end ? R.sd[u][g] : 0u;
+        // opaque copy: w gets registers of its own, so the refill below
+        // lands in R's registers in place (otherwise the compiler reuses R's
+        // registers for w and moves the refilled values back at the end of
+        // the loop, waiting on their loads)
+        asm volatile("" : "+v"(w[u][g].x), "+v"(w[u][g].y), "+v"(w[u][g].z), "+v"(w[u][g].w));
       }
     __syncthreads();
-    // refill this register set with the chunk after next
-    if (b0 + 2 * kChunk < b_end) load_chunk(R, wrow, srow, xh, k, q, b0 + 2 * kChunk, b_end);
+    // refill this register set with the chunk after next (or, past the end,
+    // with the current chunk again: cache hits, never used)
+    load_chunk(R, wrow, srow, xh, k, q, b0 + 2 * kChunk < b_end ? b0 + 2 * kChunk : b0, b_end);
     const int ngroups = (min(kChunk, b_end - b0) + 3) / 4;
     mma_chunk(acc, w, sd, shift, xs, q, col, ngroups, m_lo, m_hi, magic);
   };
-  for (int b0 = b_begin; b0 < b_end; b0 += 2 * kChunk) {
+  // pairs of chunks with no conditional inside, so both register sets stay
+  // in place across iterations (no copies that would wait on their loads)
+  int b0 = b_begin;
+  for (; b0 + kChunk < b_end; b0 += 2 * kChunk) {
     run(ra, b0);
-    if (b0 + kChunk < b_end) run(rb, b0 + kChunk);
+    run(rb, b0 + kChunk);
   }
+  if (b0 < b_end) run(ra, b0);
 
   // lane holds tokens s = 16m + 4q + i of output rows rows[u]
 #pragma unroll
