@@ -90,21 +90,26 @@ int q4_pack(const int8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
 int q4_gemv(const void* packed, int64_t n, int64_t k, const uint16_t* x,
             float* y, void* stream);
 
-/* Workspace bytes q4_gemm_s64 needs for an [n, k] weight matrix
- * (0 for invalid shapes). */
+/* Workspace bytes q4_gemm_s64 needs for an [n, k] weight matrix (0 for
+ * invalid shapes). */
 size_t q4_gemm_workspace_bytes(int64_t n, int64_t k);
 
 /* q4_gemm_s64: chunked-prefill product Y[s, r] = sum_k X[s, k] * w[r, k] for
  * s < n_tok <= 64 (model card, Provenance table: the prefill entry point has a
  * static query width of 64; the weights are read once per 64 tokens). MFMA
- * kernel: codes enter the matrix cores as exact fp16 integers, activations as
- * fp16 scaled by a per-token power of two, and each 32-wide block's fp16 scale
- * is applied in fp32. Deterministic (fixed summation order).
+ * kernel: each fp16 block scale d is split exactly into d_hi (top 7
+ * significant bits) and d_lo = d - d_hi, so c * d_hi and c * d_lo are exact
+ * fp16 values; activations enter as fp16 scaled by a per-token power of two;
+ * two MFMAs per product accumulate in fp32. Deterministic (fixed summation
+ * order). Launches on `stream`: an activation conversion, the MFMA kernel
+ * and, when K is split over several workgroups, an in-order slice sum.
  *   packed  from q4_pack with the same (n, k); 16-byte aligned.
- *   x       bf16 [n_tok, k] row-major, 2-byte aligned.
+ *   x       bf16 [n_tok, k] row-major, 16-byte aligned.
  *   y       fp32 [n_tok, n] row-major, 4-byte aligned.
  *   ws      device workspace of ws_bytes >= q4_gemm_workspace_bytes(n, k),
- *           256-byte aligned (converted activations and split-K partials).
+ *           256-byte aligned, caller-owned (converted activations and split-K
+ *           partial sums; no initial contents needed). Calls that share one
+ *           ws must not overlap.
  * Errors: NULL pointer, n <= 0, k % 32 != 0, k > Q4DEC_MAX_K, n_tok not in
  *         [1, 64], workspace too small, misalignment. */
 int q4_gemm_s64(const void* packed, int64_t n, int64_t k, const uint16_t* x,
