@@ -10,7 +10,11 @@ from .q4_oracle import (  # noqa: F401
     f16_bits_to_f64,
     ffn_down_input_bits,
     first_argmax,
+    GELU_SLOPE_MAX,
+    gelu_mul,
+    gelu_mul_tolerance,
     gelu_tanh_f32,
+    gelu_tanh_f64,
     gemm,
     gemv,
     gemv_tolerance,

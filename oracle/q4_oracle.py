@@ -214,6 +214,51 @@ def ffn_down_input_bits(g, u):
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
+def gelu_tanh_f64(g):
+    """tanh-form GELU in fp64: 0.5 * g * (1 + tanh(sqrt(2/pi) * (g + 0.044715 g^3)))."""
+    g = np.asarray(g, dtype=np.float64)
+    return 0.5 * g * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (g + 0.044715 * g ** 3)))
+
+
+# Bound on |d gelu_tanh / dg| over the reals (the maximum, about 1.129, sits
+# near g = 1.5; the minimum, about -0.17, near g = -1.5); checked on a grid
+# in the pins.
+GELU_SLOPE_MAX = 1.2
+
+
+def gelu_mul(codes, scale_bits, x_bits):
+    """Fused gate/up with the GELU epilogue ([MIX] fused gate/up kernels:
+    one pass over the concatenated [gate; up] rows, fp32 tanh GELU in the
+    epilogue). With h = n / 2: g = W[:h] x, u = W[h:] x (exact, fp64) and
+    a = gelu_tanh(g) * u in fp64. Returns (a, g, u, A_g, A_u), where A_* are
+    the magnitude sums of the two GEMVs."""
+    codes = np.asarray(codes)
+    n = codes.shape[0]
+    if n % 2:
+        raise ValueError("gelu_mul needs an even number of rows ([gate; up])")
+    y, a_mag = gemv(codes, scale_bits, x_bits)
+    h = n // 2
+    g, u = y[:h], y[h:]
+    return gelu_tanh_f64(g) * u, g, u, a_mag[:h], a_mag[h:]
+
+
+def gelu_mul_tolerance(g, u, a_g, a_u):
+    """Per-output bound for a bf16 result of gelu_mul computed from fp32
+    GEMV sums. Each sum is within t = 1e-4 * A + 1e-6 of the exact value
+    (the GEMV bar); the GELU's slope is at most GELU_SLOPE_MAX; fp32
+    evaluation of the GELU adds at most 1e-6 * (|g| + 1); the fp32 product
+    and the final rounding to bf16 add at most 2^-8 relative (half a bf16
+    ulp) plus 2^-23. Returns the bound on |a_gpu - a_exact|."""
+    g = np.asarray(g, np.float64)
+    u = np.asarray(u, np.float64)
+    tg = gemv_tolerance(a_g)
+    tu = gemv_tolerance(a_u)
+    gel = np.abs(gelu_tanh_f64(g))
+    e = np.abs(u) * (GELU_SLOPE_MAX * tg + 1e-6 * (np.abs(g) + 1.0)) + (gel + GELU_SLOPE_MAX * tg) * tu
+    a = gel * np.abs(u)
+    return (2.0 ** -8 + 2.0 ** -23) * (a + e) + e + 1e-30
+
+
 # ------------------------------------------------------------- tolerances --
 def gemv_tolerance(a):
     """Per-output tolerance for fp32-accumulated GEMV results:

@@ -376,3 +376,88 @@ def test_decoders_exact():
     got = oracle.bf16_bits_to_f64(xb)
     for i in range(0, 1000, 37):
         assert got[i] == float(bf16_exact(xb[i]))
+
+
+# ------------------------------------------------ fused gate/up + GELU --
+def _decimal_gelu(g: float) -> decimal.Decimal:
+    """tanh-form GELU at 40 digits: tanh from exp (decimal module), the
+    constant sqrt(2/pi) from decimal's sqrt and a 40-digit pi."""
+    with decimal.localcontext() as ctx:
+        ctx.prec = 40
+        pi = decimal.Decimal("3.141592653589793238462643383279502884197")
+        gd = decimal.Decimal(g)
+        z = (decimal.Decimal(2) / pi).sqrt() * (gd + decimal.Decimal("0.044715") * gd ** 3)
+        e2 = (2 * z).exp()
+        return decimal.Decimal("0.5") * gd * (1 + (e2 - 1) / (e2 + 1))
+
+
+def test_gelu_f64_against_decimal():
+    for g in (-7.5, -3.0, -1.5, -0.25, 1e-3, 0.5, 1.0, 1.5, 2.75, 6.0):
+        ref = _decimal_gelu(g)
+        got = oracle.gelu_tanh_f64(np.array([g]))[0]
+        # 1 + tanh cancels for negative g: the fp64 form is accurate to a few
+        # ulps of |g| in absolute terms, not relative to a tiny result
+        bound = abs(ref) * decimal.Decimal("1e-14") + decimal.Decimal(4 * 2.0 ** -52 * abs(g))
+        assert abs(decimal.Decimal(got) - ref) <= bound, g
+    # 0.5 * g * (1 + tanh(...)): an odd tanh gives gelu(g) - gelu(-g) = g
+    g = np.linspace(-30, 30, 6001)
+    np.testing.assert_allclose(oracle.gelu_tanh_f64(g) - oracle.gelu_tanh_f64(-g), g, rtol=0, atol=1e-12)
+
+
+def test_gelu_slope_bound():
+    # central differences of the decimal GELU on a grid over [-12, 12]; the
+    # oracle's slope bound must cover them and not be loose by more than 10%
+    h = decimal.Decimal("1e-12")
+    slopes = []
+    for g in np.linspace(-12, 12, 241):
+        gd = float(g)
+        with decimal.localcontext() as ctx:
+            ctx.prec = 40
+            d = (_decimal_gelu(gd + 1e-6) - _decimal_gelu(gd - 1e-6)) / decimal.Decimal(2e-6)
+        slopes.append(float(d))
+    assert max(abs(s) for s in slopes) <= oracle.GELU_SLOPE_MAX
+    assert max(slopes) > oracle.GELU_SLOPE_MAX / 1.1
+    assert min(slopes) < -0.1  # the tanh form dips below zero near g = -1.5
+    del h
+
+
+def test_gelu_mul_pairs_gate_and_up_rows():
+    # 2h rows: g from rows 0..h-1, u from rows h..2h-1, each checked against a
+    # Fraction brute-force dot product; a = gelu(g) * u at fp64 accuracy
+    rng = np.random.default_rng(21)
+    h, k = 3, 64
+    codes, sb = synth.q4_weights(rng, 2 * h, k)
+    x = synth.bf16_normal(rng, k)
+    a, g, u, ag, au = oracle.gelu_mul(codes, sb, x)
+    ye, ae = exact_gemv(codes, sb, x)
+    for j in range(h):
+        assert abs(Fraction(g[j]) - ye[j]) <= Fraction(1, 10 ** 12) * ae[j]
+        assert abs(Fraction(u[j]) - ye[h + j]) <= Fraction(1, 10 ** 12) * ae[h + j]
+        assert abs(Fraction(ag[j]) - ae[j]) <= Fraction(1, 10 ** 12) * ae[j]
+        ref = _decimal_gelu(float(ye[j])) * decimal.Decimal(float(ye[h + j]))
+        assert abs(decimal.Decimal(a[j]) - ref) <= abs(ref) * decimal.Decimal("1e-12") + decimal.Decimal("1e-200")
+    with pytest.raises(ValueError):
+        oracle.gelu_mul(codes[:5], sb[:5], x)
+
+
+def test_gelu_mul_tolerance_covers_rounding_and_catches_swaps():
+    rng = np.random.default_rng(22)
+    h, k = 400, 1536
+    codes, sb = synth.q4_weights(rng, 2 * h, k)
+    x = synth.bf16_normal(rng, k)
+    a, g, u, ag, au = oracle.gelu_mul(codes, sb, x)
+    tol = oracle.gelu_mul_tolerance(g, u, ag, au)
+    # the bf16 rounding of the exact value (half an ulp) is inside the bound
+    import torch
+    rb = torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    assert np.all(np.abs(rb - a) <= tol)
+    # a gate/up swap or a dropped GELU falls outside it for most outputs (the
+    # GELU is close to the identity for large positive g, so not for all)
+    swapped = oracle.gelu_tanh_f64(u) * g
+    no_gelu = g * u
+    assert np.mean(np.abs(swapped - a) > tol) > 0.85
+    assert np.mean(np.abs(no_gelu - a) > tol) > 0.7
+    # the bound is a few percent of the values it guards: it inherits the
+    # GEMV bar 1e-4 * sum|w x|, which is loose next to |sum w x| itself
+    big = np.abs(a) > 1e-3
+    assert np.median(tol[big] / np.abs(a[big])) < 5e-2
