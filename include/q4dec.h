@@ -53,6 +53,9 @@ extern "C" {
 
 /* Largest K (input dimension) the GEMV, head and GEMM kernels accept. */
 #define Q4DEC_MAX_K 16384
+/* Largest k q4_gemv_gelu_mul handles (the gate/up pairing needs at least two
+ * rows per wave step, i.e. at most 32 lanes per row and 6 blocks per lane). */
+#define Q4DEC_GELU_MAX_K 6144
 
 /* Library ABI version (Q4DEC_ABI_VERSION of the built library). */
 int32_t q4dec_abi_version(void);
@@ -89,6 +92,22 @@ int q4_pack(const int8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
  *         n >= 2^31, misalignment. */
 int q4_gemv(const void* packed, int64_t n, int64_t k, const uint16_t* x,
             float* y, void* stream);
+
+/* q4_gemv_gelu_mul: fused gate/up matvec with the GELU-tanh * up epilogue
+ * (mixed-bit page, fused gate/up kernels: one launch over the concatenated
+ * [gate; up] rows, fp32 tanh-form GELU in the epilogue). With h = n / 2,
+ *   g_j = row j of W . x,  u_j = row h + j of W . x  (fp32 accumulation),
+ *   a[j] = RN_bf16(gelu(g_j) * u_j),  gelu(g) = 0.5 g (1 + tanh(sqrt(2/pi)
+ *          (g + 0.044715 g^3))) evaluated in fp32,  for j < h.
+ * The result is the down projection's bf16 input; no fp32 g or u leaves the
+ * kernel. Same weight bytes as q4_gemv on the [n, k] matrix.
+ *   packed  from q4_pack of the [gate; up] codes/scales, n rows, n even.
+ *   x       bf16 [k], 16-byte aligned.
+ *   a       bf16 bit patterns [n / 2], 2-byte aligned, caller-owned.
+ * Errors: NULL pointer, n odd or <= 0, k <= 0, k % 32 != 0,
+ *         k > Q4DEC_GELU_MAX_K (unsupported), misalignment. */
+int q4_gemv_gelu_mul(const void* packed, int64_t n, int64_t k,
+                     const uint16_t* x, uint16_t* a, void* stream);
 
 /* Workspace bytes q4_gemm_s64 needs for an [n, k] weight matrix (0 for
  * invalid shapes). */

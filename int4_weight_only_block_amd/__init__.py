@@ -30,6 +30,7 @@ ERR_WORKSPACE = -4
 ERR_UNSUPPORTED = -5
 ERR_HIP = -6
 MAX_K = 16384
+GELU_MAX_K = 6144
 
 _c_i64 = ctypes.c_int64
 _c_p = ctypes.c_void_p
@@ -39,6 +40,7 @@ _SIGNATURES = {
     "q4_packed_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
     "q4_pack": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "q4_gemv": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
+    "q4_gemv_gelu_mul": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "q4_gemm_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
     "q4_gemm_s64": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p, ctypes.c_size_t, _c_p]),
     "lmhead_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
@@ -161,6 +163,20 @@ def q4_gemv(packed: torch.Tensor, n: int, k: int, x: torch.Tensor,
     py = _dev(y, "y", _F32, n)
     _check(lib().q4_gemv(pp, n, k, px, py, _stream(x)))
     return y
+
+
+def q4_gemv_gelu_mul(packed: torch.Tensor, n: int, k: int, x: torch.Tensor,
+                     a: torch.Tensor | None = None) -> torch.Tensor:
+    """a[j] = bf16(gelu_tanh(g_j) * u_j) for the [gate; up] matrix of n rows
+    (g = rows 0 .. n/2-1, u = rows n/2 .. n-1); returns bf16 bits (int16)."""
+    pp = _dev(packed, "packed", _BYTES)
+    _check_packed(packed, n, k)
+    px = _dev(x, "x", _U16, k)
+    if a is None:
+        a = torch.empty(max(n // 2, 1), dtype=torch.int16, device=x.device)
+    pa = _dev(a, "a", _U16, max(n // 2, 1))
+    _check(lib().q4_gemv_gelu_mul(pp, n, k, px, pa, _stream(x)))
+    return a
 
 
 def q4_gemm_workspace_bytes(n: int, k: int) -> int:

@@ -105,12 +105,37 @@ __device__ __forceinline__ void wave_best(float& best, int& bidx) {
   }
 }
 
-template <int LPR, int BPL, bool HEAD, bool FULL>
+// What a row kernel does with its row sums.
+enum RowMode : int {
+  kGemv = 0,  // y[row] = sum (fp32)
+  kHead = 1,  // per-workgroup (max, lowest row) partial
+  kGelu = 2,  // fused [gate; up] rows: a[j] = bf16(gelu_tanh(gate_j) * up_j)
+};
+
+// tanh-form GELU in fp32: 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))).
+__device__ __forceinline__ float gelu_tanh(float g) {
+  const float k0 = 0.7978845608028654f, k1 = 0.044715f;
+  return 0.5f * g * (1.0f + tanhf(k0 * (g + k1 * g * g * g)));
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x40u);
+  return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <int LPR, int BPL, int MODE, bool FULL>
 __global__ __launch_bounds__(kThreads) void q4_rows_kernel(const uint8_t* __restrict__ nib,
                                                            const uint16_t* __restrict__ scl,
                                                            const uint16_t* __restrict__ x, int n, int k, int ipw,
-                                                           float* __restrict__ y, uint2* __restrict__ partials) {
+                                                           void* __restrict__ out, uint2* __restrict__ partials) {
   constexpr int RPW = 64 / LPR;  // rows per wave per iteration
+  // GELU mode: lane groups r < RPW/2 take gate rows, the others the up rows
+  // of the same outputs (n/2 apart), so each output's pair ends up 32 lanes
+  // apart after the row reduction
+  static_assert(MODE != kGelu || RPW >= 2, "the gate/up pairing needs two rows per wave step");
+  constexpr int UPW = MODE == kGelu ? RPW / 2 : RPW;  // outputs per wave step
   constexpr int MAXB = LPR * BPL;
   // activations as block-scaled fp16 pairs: block b at xs[16 b], its four
   // 16-byte quarters swizzled (quarter i in slot i ^ (b & 3)) so the 16
@@ -122,14 +147,20 @@ __global__ __launch_bounds__(kThreads) void q4_rows_kernel(const uint8_t* __rest
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t = lane % LPR;
   const int r = lane / LPR;
-  const int RG = (n + RPW - 1) / RPW;
+  const int units = MODE == kGelu ? n / 2 : n;  // outputs (row pairs in GELU mode)
+  const int RG = (units + UPW - 1) / UPW;
   const int rg_base = blockIdx.x * kWaves * ipw + wave;
   const size_t row_bytes = size_t(k) >> 1;
   // row groups this wave walks: rg_base, rg_base + kWaves, ... (uniform)
   const int iters = rg_base < RG ? min(ipw, (RG - rg_base + kWaves - 1) / kWaves) : 0;
   auto row_of = [&](int i) {
-    const int row = (rg_base + i * kWaves) * RPW + r;
-    return row < n ? row : n - 1;
+    if constexpr (MODE == kGelu) {
+      const int v = (rg_base + i * kWaves) * UPW + (r % UPW);
+      return (v < units ? v : units - 1) + (r / UPW) * units;
+    } else {
+      const int row = (rg_base + i * kWaves) * RPW + r;
+      return row < n ? row : n - 1;
+    }
   };
 
   Lane<LPR, BPL, FULL> L;
@@ -163,14 +194,20 @@ __global__ __launch_bounds__(kThreads) void q4_rows_kernel(const uint8_t* __rest
   int bidx = INT_MAX;
   auto emit = [&](int i, float acc) {
     acc = group_sum<LPR>(acc);
-    const int row = (rg_base + i * kWaves) * RPW + r;
-    if constexpr (!HEAD) {
-      if (t == 0 && row < n) y[row] = acc;
-    } else {
+    if constexpr (MODE == kGemv) {
+      const int row = (rg_base + i * kWaves) * RPW + r;
+      if (t == 0 && row < n) static_cast<float*>(out)[row] = acc;
+    } else if constexpr (MODE == kHead) {
+      const int row = (rg_base + i * kWaves) * RPW + r;
       if (row < n && better(acc, row, best, bidx)) {
         best = acc;
         bidx = row;
       }
+    } else {
+      const float up = __shfl_xor(acc, 32);  // the up row's sum
+      const int v = (rg_base + i * kWaves) * UPW + r;
+      if (t == 0 && r < UPW && v < units)
+        static_cast<uint16_t*>(out)[v] = f32_to_bf16_rne(gelu_tanh(acc) * up);
     }
   };
   for (int i = 0; i + 1 < iters; ++i) {
@@ -182,7 +219,7 @@ __global__ __launch_bounds__(kThreads) void q4_rows_kernel(const uint8_t* __rest
     emit(iters - 1, acc);
   }
 
-  if constexpr (HEAD) {
+  if constexpr (MODE == kHead) {
     // pass 1: this workgroup's best (value, row) into its partial slot
     wave_best(best, bidx);
     __shared__ float sv[kWaves];
@@ -267,15 +304,19 @@ struct Plan {
   const void* fn;
 };
 
-template <int L, int BP, bool HEAD, bool FULL>
+template <int L, int BP, int MODE, bool FULL>
 static const void* kernel_ptr() {
-  return reinterpret_cast<const void*>(&q4_rows_kernel<L, BP, HEAD, FULL>);
+  if constexpr (MODE == kGelu && L == 64) {
+    return nullptr;  // one row per wave step: no gate/up pairing
+  } else {
+    return reinterpret_cast<const void*>(&q4_rows_kernel<L, BP, MODE, FULL>);
+  }
 }
 
-template <bool HEAD, bool FULL>
+template <int MODE, bool FULL>
 static const void* pick_kernel(int lpr, int bpl) {
 #define Q4_CASE(L, BP) \
-  if (lpr == L && bpl == BP) return kernel_ptr<L, BP, HEAD, FULL>();
+  if (lpr == L && bpl == BP) return kernel_ptr<L, BP, MODE, FULL>();
   Q4_CASE(16, 1) Q4_CASE(16, 2) Q4_CASE(16, 3) Q4_CASE(16, 4) Q4_CASE(16, 5)
   Q4_CASE(32, 2) Q4_CASE(32, 3) Q4_CASE(32, 4) Q4_CASE(32, 5) Q4_CASE(32, 6)
   Q4_CASE(64, 1) Q4_CASE(64, 2) Q4_CASE(64, 3) Q4_CASE(64, 4) Q4_CASE(64, 5) Q4_CASE(64, 6) Q4_CASE(64, 7) Q4_CASE(64, 8)
@@ -299,16 +340,20 @@ static int blocks_per_cu(const void* fn) {
   return nb;
 }
 
-template <bool HEAD>
+template <int MODE>
 static Plan plan_for(int64_t n, int B, int lpr) {
   Plan p{};
   p.lpr = lpr;
   p.bpl = (B + lpr - 1) / lpr;
   p.full = (B == lpr * p.bpl);
-  p.fn = p.full ? pick_kernel<HEAD, true>(lpr, p.bpl) : pick_kernel<HEAD, false>(lpr, p.bpl);
+  p.fn = p.full ? pick_kernel<MODE, true>(lpr, p.bpl) : pick_kernel<MODE, false>(lpr, p.bpl);
   p.rpw = 64 / lpr;
-  p.rg = int((n + p.rpw - 1) / p.rpw);
   if (!p.fn) return p;
+  // outputs per wave step: rows, or gate/up row pairs in GELU mode (a GELU
+  // kernel exists only for rpw >= 2)
+  const int64_t units = MODE == kGelu ? n / 2 : n;
+  const int upw = MODE == kGelu ? p.rpw / 2 : p.rpw;
+  p.rg = int((units + upw - 1) / upw);
   // one resident round: every workgroup is live at once
   const int cus = device_cu_count();
   const int waves_max = cus * blocks_per_cu(p.fn) * kWaves;
@@ -330,7 +375,7 @@ static Plan plan_for(int64_t n, int B, int lpr) {
   return p;
 }
 
-template <bool HEAD>
+template <int MODE>
 static Plan make_plan(int64_t n, int64_t k) {
   const int B = int(k / 32);
   int lpr = 64;
@@ -339,14 +384,14 @@ static Plan make_plan(int64_t n, int64_t k) {
   } else if ((B + 31) / 32 <= 6) {
     lpr = 32;
   }
-  Plan p = plan_for<HEAD>(n, B, lpr);
+  Plan p = plan_for<MODE>(n, B, lpr);
   // A matrix that fits one resident round at this split takes the widest
   // split that still fills every lane: shorter block chains per wave and more
   // waves to cover the load latency.
   if (p.fn && p.ipw == 1) {
     for (int wide = 64; wide > lpr; wide /= 2) {
       if (B % wide || B / wide < 1) continue;
-      const Plan q = plan_for<HEAD>(n, B, wide);
+      const Plan q = plan_for<MODE>(n, B, wide);
       if (q.fn && q.ipw == 1) return q;
     }
   }
@@ -354,10 +399,10 @@ static Plan make_plan(int64_t n, int64_t k) {
 }
 
 static int launch_rows(const Plan& p, const uint8_t* nib, const uint16_t* scl, const uint16_t* x, int n, int k,
-                       float* y, uint2* partials, hipStream_t st) {
+                       void* out, uint2* partials, hipStream_t st) {
   if (!p.fn) return fail(Q4DEC_ERR_UNSUPPORTED, "no kernel for k=%d (lpr=%d, bpl=%d)", k, p.lpr, p.bpl);
   int ipw = p.ipw;
-  void* args[] = {&nib, &scl, &x, &n, &k, &ipw, &y, &partials};
+  void* args[] = {&nib, &scl, &x, &n, &k, &ipw, &out, &partials};
   hipError_t e = hipLaunchKernel(p.fn, dim3(p.grid), dim3(kThreads), args, 0, st);
   if (e != hipSuccess) return fail(Q4DEC_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return Q4DEC_OK;
@@ -384,7 +429,7 @@ extern "C" int q4_gemv(const void* packed, int64_t n, int64_t k, const uint16_t*
   if (rc) return rc;
   if (!y) return fail(Q4DEC_ERR_NULL, "q4_gemv: y is NULL");
   if (!aligned(y, 4)) return fail(Q4DEC_ERR_ALIGN, "q4_gemv: y must be 4-byte aligned");
-  const Plan p = make_plan<false>(n, k);
+  const Plan p = make_plan<kGemv>(n, k);
   const uint8_t* nib = static_cast<const uint8_t*>(packed);
   const uint16_t* scl = reinterpret_cast<const uint16_t*>(nib + nib_plane_bytes(n, k));
   rc = launch_rows(p, nib, scl, x, int(n), int(k), y, nullptr, static_cast<hipStream_t>(stream));
@@ -412,7 +457,7 @@ extern "C" int lmhead_softcap_argmax(const void* packed, int64_t vocab, int64_t 
   const size_t need = lmhead_workspace_bytes(vocab, k);
   if (ws_bytes < need)
     return fail(Q4DEC_ERR_WORKSPACE, "lmhead_softcap_argmax: ws_bytes %zu < required %zu", ws_bytes, need);
-  const Plan p = make_plan<true>(vocab, k);
+  const Plan p = make_plan<kHead>(vocab, k);
   if (p.grid > kMaxPartials) return fail(Q4DEC_ERR_UNSUPPORTED, "lmhead_softcap_argmax: too many workgroups");
   const uint8_t* nib = static_cast<const uint8_t*>(packed);
   const uint16_t* scl = reinterpret_cast<const uint16_t*>(nib + nib_plane_bytes(vocab, k));
@@ -423,4 +468,23 @@ extern "C" int lmhead_softcap_argmax(const void* packed, int64_t vocab, int64_t 
   hipLaunchKernelGGL(lmhead_reduce_kernel, dim3(1), dim3(kReduceThreads), 0, st, partials, p.grid, cap, idx_out,
                      val_out);
   return launch_status("lmhead_softcap_argmax");
+}
+
+extern "C" int q4_gemv_gelu_mul(const void* packed, int64_t n, int64_t k, const uint16_t* x, uint16_t* a,
+                                void* stream) {
+  using namespace q4dec;
+  int rc = check_common("q4_gemv_gelu_mul", packed, n, "n", k, x);
+  if (rc) return rc;
+  if (n % 2) return fail(Q4DEC_ERR_SHAPE, "q4_gemv_gelu_mul: n must be even ([gate; up] rows), got %lld", (long long)n);
+  if (!a) return fail(Q4DEC_ERR_NULL, "q4_gemv_gelu_mul: a is NULL");
+  if (!aligned(a, 2)) return fail(Q4DEC_ERR_ALIGN, "q4_gemv_gelu_mul: a must be 2-byte aligned");
+  const Plan p = make_plan<kGelu>(n, k);
+  if (!p.fn)
+    return fail(Q4DEC_ERR_UNSUPPORTED, "q4_gemv_gelu_mul: k must be <= %d (got %lld)", Q4DEC_GELU_MAX_K,
+                (long long)k);
+  const uint8_t* nib = static_cast<const uint8_t*>(packed);
+  const uint16_t* scl = reinterpret_cast<const uint16_t*>(nib + nib_plane_bytes(n, k));
+  rc = launch_rows(p, nib, scl, x, int(n), int(k), a, nullptr, static_cast<hipStream_t>(stream));
+  if (rc) return rc;
+  return launch_status("q4_gemv_gelu_mul");
 }

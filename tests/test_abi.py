@@ -11,7 +11,7 @@ import int4_weight_only_block_amd as q4
 pytestmark = pytest.mark.skipif(not os.path.exists(q4.LIB_PATH), reason="libq4dec.so not built")
 
 EXPECTED = {
-    "q4dec_abi_version", "q4dec_last_error", "q4_packed_bytes", "q4_pack", "q4_gemv",
+    "q4dec_abi_version", "q4dec_last_error", "q4_packed_bytes", "q4_pack", "q4_gemv", "q4_gemv_gelu_mul",
     "q4_gemm_s64", "q4_gemm_workspace_bytes", "lmhead_workspace_bytes", "lmhead_softcap_argmax", "ple_gather",
 }
 
@@ -66,6 +66,24 @@ def test_gemv_validation():
     assert rc == q4.ERR_ALIGN and "y" in msg
     rc, msg = _rc_and_msg(L.q4_gemv(FAKE, 1 << 31, 32, FAKE, FAKE, None))
     assert rc == q4.ERR_SHAPE
+
+
+def test_gemv_gelu_mul_validation():
+    L = q4.lib()
+    rc, msg = _rc_and_msg(L.q4_gemv_gelu_mul(None, 16, 32, FAKE, FAKE, None))
+    assert rc == q4.ERR_NULL and "packed" in msg
+    rc, msg = _rc_and_msg(L.q4_gemv_gelu_mul(FAKE, 16, 32, FAKE, None, None))
+    assert rc == q4.ERR_NULL and "a" in msg
+    rc, msg = _rc_and_msg(L.q4_gemv_gelu_mul(FAKE, 15, 32, FAKE, FAKE, None))
+    assert rc == q4.ERR_SHAPE and "even" in msg
+    rc, msg = _rc_and_msg(L.q4_gemv_gelu_mul(FAKE, 16, 40, FAKE, FAKE, None))
+    assert rc == q4.ERR_SHAPE and "k" in msg
+    rc, msg = _rc_and_msg(L.q4_gemv_gelu_mul(FAKE, 16, q4.GELU_MAX_K + 32, FAKE, FAKE, None))
+    assert rc == q4.ERR_UNSUPPORTED and "k" in msg
+    rc, msg = _rc_and_msg(L.q4_gemv_gelu_mul(FAKE, 16, 32, FAKE, FAKE + 1, None))
+    assert rc == q4.ERR_ALIGN and "a" in msg
+    rc, msg = _rc_and_msg(L.q4_gemv_gelu_mul(FAKE, 16, 32, FAKE + 8, FAKE, None))
+    assert rc == q4.ERR_ALIGN and "x" in msg
 
 
 def test_pack_validation():

@@ -157,6 +157,68 @@ def test_ffn_pair():
     assert_within_tol(y, yr, ya, "down")
 
 
+# ------------------------------------------------ fused gate/up + GELU --
+def _gelu_mul_gpu(codes, sb, x):
+    n, k = codes.shape
+    bits = q4.q4_gemv_gelu_mul(pack(codes, sb), n, k, d(x)).cpu().numpy().view(np.uint16)
+    return bits
+
+
+# E2B and E4B FFN shapes, ragged pair counts, and every lane split the fused
+# kernel has (16 lanes x 1..5 blocks, 32 lanes x 2..6 blocks, ragged blocks)
+@pytest.mark.parametrize("h,k", [(6144, 1536), (10240, 2560), (37, 96), (300, 4096), (129, 6144),
+                                 (1, 32), (1000, 2048), (77, 5120), (513, 160)])
+def test_gelu_mul_tolerance(h, k):
+    rng = synth.rng_for(31, h, k)
+    codes, sb = synth.q4_weights(rng, 2 * h, k)
+    x = synth.bf16_normal(rng, k)
+    got = oracle.bf16_bits_to_f64(_gelu_mul_gpu(codes, sb, x))
+    a, g, u, ag, au = oracle.gelu_mul(codes, sb, x)
+    tol = oracle.gelu_mul_tolerance(g, u, ag, au)
+    bad = np.nonzero(~(np.abs(got - a) <= tol))[0]
+    assert bad.size == 0, (f"{bad.size} of {h} over the bound, first {bad[:5]}, "
+                           f"got {got[bad[:3]]} want {a[bad[:3]]} tol {tol[bad[:3]]}")
+
+
+def test_gelu_mul_integer_inputs_match_host_epilogue():
+    """Power-of-two scales and x in {-1, 0, 1}: g and u are exact in fp32 on
+    both sides, so the GPU result may differ from the host fp32 GELU-tanh
+    product rounded to bf16 only through the two tanh implementations: at
+    most one bf16 ulp, and rarely."""
+    h, k = 6144, 1536
+    rng = synth.rng_for(32)
+    codes = rng.integers(-8, 8, size=(2 * h, k), dtype=np.int8)
+    sb = np.full((2 * h, k // 32), fp16_bits(2.0 ** -8), dtype=np.uint16)
+    xi = rng.integers(-1, 2, size=k)
+    x = bf16_bits_of_ints(xi)
+    got = _gelu_mul_gpu(codes, sb, x)
+    _, g, u, _, _ = oracle.gelu_mul(codes, sb, x)
+    assert np.all(g.astype(np.float32) == g) and np.all(u.astype(np.float32) == u)
+    want = oracle.ffn_down_input_bits(g.astype(np.float32), u.astype(np.float32))
+    diff = np.abs(got.astype(np.int32) - want.astype(np.int32))
+    same_sign = (got >> 15) == (want >> 15)
+    assert np.all(same_sign | (diff == 0) | (np.abs(oracle.bf16_bits_to_f64(want)) < 1e-30))
+    assert diff.max() <= 1, diff.max()
+    assert np.mean(diff == 0) > 0.99
+
+
+def test_ffn_chain_fused():
+    """E2B FFN as one fused launch plus the down GEMV on its bf16 output; the
+    down GEMV is checked against the oracle fed the GPU's own a."""
+    s = synth.SHAPES["ffn_e2b"]
+    rng = synth.rng_for(0, 2)
+    gu_codes, gu_sb = synth.q4_weights(rng, *s["gate_up"])
+    dn_codes, dn_sb = synth.q4_weights(rng, *s["down"])
+    x = synth.bf16_normal(rng, s["gate_up"][1])
+    a_gpu = q4.q4_gemv_gelu_mul(pack(gu_codes, gu_sb), *s["gate_up"], d(x))
+    a_bits = a_gpu.cpu().numpy().view(np.uint16)
+    a, g, u, ag, au = oracle.gelu_mul(gu_codes, gu_sb, x)
+    assert np.all(np.abs(oracle.bf16_bits_to_f64(a_bits) - a) <= oracle.gelu_mul_tolerance(g, u, ag, au))
+    y = q4.q4_gemv(pack(dn_codes, dn_sb), *s["down"], a_gpu).cpu().numpy()
+    yr, ya = oracle.gemv(dn_codes, dn_sb, a_bits)
+    assert_within_tol(y, yr, ya, "down after fused gate/up")
+
+
 @pytest.mark.parametrize("name", ["qkv", "o", "gate_up", "down"])
 def test_gemv_e4b_layer_shapes(name):
     shapes = {"qkv": (3072, 2560), "o": (2560, 2048), "gate_up": (20480, 2560), "down": (2560, 10240)}
