@@ -21,6 +21,9 @@ from .q4_oracle import (  # noqa: F401
     lmhead,
     nibbles_from_codes,
     ple_gather,
+    q4_quantize,
+    QUANT_ABSMAX7,
+    QUANT_Q4_0,
     softcap,
     top2_margin,
 )

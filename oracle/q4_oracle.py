@@ -85,6 +85,59 @@ def dequant(codes, scale_bits) -> np.ndarray:
     return codes.astype(np.float64) * np.repeat(d, 32, axis=1)
 
 
+# --------------------------------------------------------------- quantiser --
+QUANT_Q4_0 = 0     # q4_0 grid: d = m / -8, m the block's largest-magnitude value
+QUANT_ABSMAX7 = 1  # symmetric: d = max|x| / 7, codes in [-7, 7]
+
+
+def q4_quantize(x_bits, rule: int = QUANT_Q4_0):
+    """bf16 weights [n, k] -> q4_0 codes (int8 [n, k]) and fp16 scale bits
+    (uint16 [n, k/32]), plus a per-block flag for blocks the format cannot
+    hold (a NaN input, or a scale beyond the fp16 range).
+
+    [E2B] "QAT weights": q4_0 is per-block-32 absmax symmetric int4 (the ggml
+    q4_0 grid); the plain absmax variant (--lin-sym) is the literal grid.
+    [CARD] Provenance: the int4 rounding happens at export. The pages give no
+    formula, so this is the plain reading, every step in fp32:
+      m   = the block value of largest magnitude (lowest index on ties),
+      d   = m / -8 (rule QUANT_Q4_0; exact) or max|x| / 7 (QUANT_ABSMAX7,
+            correctly rounded), stored as fp16 (round to nearest even),
+      c_j = clamp(rint(x_j / d16), lo, 7), the quotient a correctly rounded
+            fp32 division, rint to nearest even, lo = -8 (q4_0) or -7;
+            c_j = 0 when d16 is zero or not finite; a zero scale is +0.
+    With the q4_0 rule the largest-magnitude value gets the code -8 exactly
+    unless its fp16 scale rounds away from m / -8.
+    """
+    x = (np.ascontiguousarray(x_bits).view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+    n, k = x.shape
+    if k % 32:
+        raise ValueError("K must be a multiple of 32")
+    xb = x.reshape(n, k // 32, 32)
+    ax = np.abs(xb)
+    nan_blk = np.isnan(xb).any(axis=2)
+    ax = np.where(np.isnan(ax), np.float32(-1.0), ax)
+    jmax = np.argmax(ax, axis=2)  # first index of the largest magnitude
+    m = np.take_along_axis(xb, jmax[..., None], axis=2)[..., 0]
+    if rule == QUANT_Q4_0:
+        d = m / np.float32(-8.0)
+        lo = -8
+    elif rule == QUANT_ABSMAX7:
+        d = np.abs(m) / np.float32(7.0)
+        lo = -7
+    else:
+        raise ValueError("unknown rule")
+    with np.errstate(over="ignore"):
+        d16 = d.astype(np.float16)
+    d16 = np.where(d16 == 0, np.float16(0.0), d16)  # a zero block stores +0, not -0
+    d32 = d16.astype(np.float32)
+    usable = np.isfinite(d32) & (d32 != 0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.rint(xb / np.where(usable, d32, np.float32(1.0))[..., None])
+    q = np.where(usable[..., None] & ~np.isnan(q), np.clip(q, lo, 7), 0).astype(np.int8)
+    flags = nan_blk | ~np.isfinite(d32)
+    return q.reshape(n, k), d16.view(np.uint16), flags
+
+
 # -------------------------------------------------------------------- GEMV --
 def gemv(codes, scale_bits, x_bits):
     """y[n] = sum_k w[n, k] * x[k] in fp64, plus A[n] = sum_k |w[n, k] x[k]|.

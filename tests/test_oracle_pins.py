@@ -461,3 +461,99 @@ def test_gelu_mul_tolerance_covers_rounding_and_catches_swaps():
     # GEMV bar 1e-4 * sum|w x|, which is loose next to |sum w x| itself
     big = np.abs(a) > 1e-3
     assert np.median(tol[big] / np.abs(a[big])) < 5e-2
+
+
+# -------------------------------------------------------------- quantiser --
+def _rne_int(fr: Fraction) -> int:
+    """Round a rational to the nearest integer, ties to even."""
+    f = fr.numerator // fr.denominator
+    rem = fr - f
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and f % 2 == 1):
+        f += 1
+    return f
+
+
+def _f16_rne(fr: Fraction) -> int:
+    """fp16 bits of a rational, round half to even (struct's 'e' packing of
+    the correctly rounded double, valid here because the doubles involved
+    are exact: m / -8 or a single fp32 quotient)."""
+    return struct.unpack("<H", struct.pack("<e", float(fr)))[0]
+
+
+def _quantize_block_exact(xbits, rule):
+    xs = [bf16_exact(b) for b in xbits]
+    mags = [abs(v) for v in xs]
+    j = mags.index(max(mags))  # first index of the largest magnitude
+    if rule == oracle.QUANT_Q4_0:
+        d = xs[j] / -8
+        lo = -8
+    else:
+        d = Fraction(float(np.float32(float(mags[j])) / np.float32(7.0)))  # fp32 quotient, correctly rounded
+        lo = -7
+    dbits = _f16_rne(d)
+    d16 = f16_exact(dbits)
+    codes = [0] * 32 if d16 == 0 else [max(lo, min(7, _rne_int(v / d16))) for v in xs]
+    return codes, dbits
+
+
+@pytest.mark.parametrize("rule", [0, 1])
+def test_quantize_bruteforce_fraction(rule):
+    # exact rational quotients and ties-to-even against the oracle's fp32
+    # division + rint; 8 x 96 random blocks plus blocks with planted ties
+    rng = np.random.default_rng(40 + rule)
+    x = synth.bf16_normal(rng, 8 * 96).reshape(8, 96)
+    # planted: a block of exact half-way quotients (x = (i + 1/2) * d) and a
+    # block whose largest magnitude appears twice with opposite signs
+    half = [struct.unpack("<I", struct.pack("<f", (i - 7.5) * 0.25))[0] >> 16 for i in range(16)]
+    x[0, :32] = np.array(half + half, dtype=np.uint16)
+    x[1, 32:64] = 0
+    x[1, 40] = struct.unpack("<I", struct.pack("<f", 3.0))[0] >> 16
+    x[1, 50] = struct.unpack("<I", struct.pack("<f", -3.0))[0] >> 16
+    codes, sbits, flags = oracle.q4_quantize(x, rule)
+    assert not flags.any()
+    for r in range(8):
+        for b in range(3):
+            ec, ed = _quantize_block_exact(x[r, 32 * b:32 * b + 32], rule)
+            assert int(sbits[r, b]) == ed, (r, b)
+            assert codes[r, 32 * b:32 * b + 32].tolist() == ec, (r, b)
+    if rule == oracle.QUANT_Q4_0:
+        # first of +3 / -3 wins: d = -3/8, +3 -> -8, -3 -> +8 clamped to 7
+        assert codes[1, 40] == -8 and codes[1, 50] == 7
+
+
+def test_quantize_invariants():
+    rng = np.random.default_rng(44)
+    x = synth.bf16_normal(rng, 64 * 256).reshape(64, 256)
+    xf = oracle.bf16_bits_to_f64(x).reshape(64, 8, 32)
+    c, s, f = oracle.q4_quantize(x, oracle.QUANT_Q4_0)
+    d = oracle.f16_bits_to_f64(s)
+    cb = c.reshape(64, 8, 32).astype(np.float64)
+    jmax = np.argmax(np.abs(xf), axis=2)
+    # the largest magnitude lands on -8 exactly (m / -8 is exact in fp16 here)
+    assert np.all(np.take_along_axis(cb, jmax[..., None], axis=2) == -8)
+    assert np.all(d == np.take_along_axis(xf, jmax[..., None], axis=2)[..., 0] / -8)
+    # reconstruction error at most half a scale step, except where the q4_0
+    # grid's missing +8 clamps a value of the other sign (quotient in
+    # (7.5, 8]): there at most one step
+    err = np.abs(cb * d[..., None] - xf)
+    clamped = xf / d[..., None] > 7.5
+    dd = np.broadcast_to(np.abs(d)[..., None], err.shape)
+    assert np.all(err[~clamped] <= dd[~clamped] / 2)
+    assert np.all(err[clamped] <= dd[clamped]) and np.all(cb[clamped] == 7)
+    # the symmetric rule is odd: negating x negates the codes, keeps the scale
+    c7, s7, _ = oracle.q4_quantize(x, oracle.QUANT_ABSMAX7)
+    c7n, s7n, _ = oracle.q4_quantize(x ^ np.uint16(0x8000), oracle.QUANT_ABSMAX7)
+    assert np.array_equal(c7n, -c7) and np.array_equal(s7n, s7)
+    assert c7.min() >= -7 and c7.max() <= 7
+
+
+def test_quantize_special_blocks():
+    x = np.zeros((1, 128), dtype=np.uint16)  # block 0: all zero
+    x[0, 32] = 0x7FC0                         # block 1: NaN
+    x[0, 64] = 0x7F00                         # block 2: 2^127 -> scale overflows fp16
+    x[0, 96:128] = 0x3F80                     # block 3: all 1.0
+    c, s, f = oracle.q4_quantize(x)
+    assert f.tolist() == [[False, True, True, False]]
+    assert s[0, 0] == 0 and not c[0, :32].any()
+    assert not c[0, 64:96].any()
+    assert oracle.f16_bits_to_f64(s[0, 3:4])[0] == -0.125 and np.all(c[0, 96:] == -8)
