@@ -70,6 +70,32 @@ const char* q4dec_last_error(void);
  * padded to 256 bytes. Returns 0 if n <= 0, k <= 0 or k % 32 != 0. */
 size_t q4_packed_bytes(int64_t n, int64_t k);
 
+/* Scale rules of q4_quantize. */
+#define Q4DEC_QUANT_Q4_0 0    /* d = m / -8, m the largest-magnitude value; codes in [-8, 7] */
+#define Q4DEC_QUANT_ABSMAX7 1 /* d = max|x| / 7; codes in [-7, 7] */
+
+/* q4_quantize: bf16 weights -> q4_0 codes and fp16 block scales, the export
+ * step in front of q4_pack (E2B card, QAT weights section: q4_0 is
+ * per-block-32 absmax symmetric int4 on the ggml q4_0 grid; the plain absmax
+ * variant is the literal grid; model card, Provenance: int4 rounding happens
+ * at export). The pages give no formula; per 32-wide block, in fp32:
+ *   m   = the value of largest magnitude (lowest index on ties, NaN never),
+ *   d   = m / -8 (Q4DEC_QUANT_Q4_0) or max|x| / 7 (Q4DEC_QUANT_ABSMAX7, a
+ *         correctly rounded division), stored as fp16 by round to nearest
+ *         even (a zero scale is +0),
+ *   c_j = clamp(rint(x_j / d16), -8 or -7, 7) with a correctly rounded fp32
+ *         quotient and ties to even; c_j = 0 when d16 is 0 or not finite.
+ *   x        bf16 [n, k] row-major, 16-byte aligned.
+ *   codes    int8 [n, k] row-major output, 16-byte aligned (q4_pack input).
+ *   scales   fp16 bit patterns [n, k/32] output, 2-byte aligned.
+ *   err_flag optional (NULL allowed) device int32: set to 1 if a block holds
+ *            a NaN or its scale overflows fp16; never cleared.
+ * Errors: NULL pointer, n <= 0, k <= 0, k % 32 != 0, unknown rule,
+ *         misalignment. */
+int q4_quantize(const uint16_t* x, int64_t n, int64_t k, int32_t rule,
+                int8_t* codes, uint16_t* scales, int32_t* err_flag,
+                void* stream);
+
 /* q4_pack: q4_0 codes and scales -> packed layout (load time, not per token).
  *   codes   int8 [n, k] row-major, values in [-8, 7]; stored nibble = c + 8
  *           (mixed-bit page, P6 section).

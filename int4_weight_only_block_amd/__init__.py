@@ -31,6 +31,8 @@ ERR_UNSUPPORTED = -5
 ERR_HIP = -6
 MAX_K = 16384
 GELU_MAX_K = 6144
+QUANT_Q4_0 = 0
+QUANT_ABSMAX7 = 1
 
 _c_i64 = ctypes.c_int64
 _c_p = ctypes.c_void_p
@@ -39,6 +41,7 @@ _SIGNATURES = {
     "q4dec_last_error": (ctypes.c_char_p, []),
     "q4_packed_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
     "q4_pack": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
+    "q4_quantize": (ctypes.c_int, [_c_p, _c_i64, _c_i64, ctypes.c_int32, _c_p, _c_p, _c_p, _c_p]),
     "q4_gemv": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "q4_gemv_gelu_mul": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "q4_gemm_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
@@ -150,6 +153,24 @@ def q4_pack(codes: torch.Tensor, scales: torch.Tensor, packed: torch.Tensor | No
     pe = _dev(err_flag, "err_flag", _I32, 1) if err_flag is not None else None
     _check(lib().q4_pack(pc, ps, n, k, pp, pe, _stream(codes)))
     return packed
+
+
+def q4_quantize(x: torch.Tensor, rule: int = QUANT_Q4_0, codes: torch.Tensor | None = None,
+                scales: torch.Tensor | None = None, err_flag: torch.Tensor | None = None):
+    """bf16 [n, k] -> (int8 codes [n, k], fp16 scale bits int16 [n, k/32])."""
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D [n, k]")
+    n, k = x.shape
+    px = _dev(x, "x", _U16)
+    if codes is None:
+        codes = torch.empty((n, k), dtype=torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty((n, max(k // 32, 1)), dtype=torch.int16, device=x.device)
+    pc = _dev(codes, "codes", _I8, n * k)
+    ps = _dev(scales, "scales", _U16, n * max(k // 32, 1))
+    pe = _dev(err_flag, "err_flag", _I32, 1) if err_flag is not None else None
+    _check(lib().q4_quantize(px, n, k, int(rule), pc, ps, pe, _stream(x)))
+    return codes, scales
 
 
 def q4_gemv(packed: torch.Tensor, n: int, k: int, x: torch.Tensor,

@@ -11,7 +11,7 @@ import int4_weight_only_block_amd as q4
 pytestmark = pytest.mark.skipif(not os.path.exists(q4.LIB_PATH), reason="libq4dec.so not built")
 
 EXPECTED = {
-    "q4dec_abi_version", "q4dec_last_error", "q4_packed_bytes", "q4_pack", "q4_gemv", "q4_gemv_gelu_mul",
+    "q4dec_abi_version", "q4dec_last_error", "q4_packed_bytes", "q4_pack", "q4_quantize", "q4_gemv", "q4_gemv_gelu_mul",
     "q4_gemm_s64", "q4_gemm_workspace_bytes", "lmhead_workspace_bytes", "lmhead_softcap_argmax", "ple_gather",
 }
 
@@ -84,6 +84,29 @@ def test_gemv_gelu_mul_validation():
     assert rc == q4.ERR_ALIGN and "a" in msg
     rc, msg = _rc_and_msg(L.q4_gemv_gelu_mul(FAKE, 16, 32, FAKE + 8, FAKE, None))
     assert rc == q4.ERR_ALIGN and "x" in msg
+
+
+def test_quantize_validation():
+    L = q4.lib()
+    ok = [FAKE, 16, 64, 0, FAKE, FAKE, None, None]
+
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return _rc_and_msg(L.q4_quantize(*a))
+
+    assert call(0, None)[0] == q4.ERR_NULL
+    rc, msg = call(4, None)
+    assert rc == q4.ERR_NULL and "codes" in msg
+    rc, msg = call(5, None)
+    assert rc == q4.ERR_NULL and "scales" in msg
+    assert call(1, 0)[0] == q4.ERR_SHAPE
+    assert call(2, 48)[0] == q4.ERR_SHAPE
+    rc, msg = call(3, 2)
+    assert rc == q4.ERR_SHAPE and "rule" in msg
+    assert call(0, FAKE + 2)[0] == q4.ERR_ALIGN
+    assert call(4, FAKE + 8)[0] == q4.ERR_ALIGN
+    assert call(5, FAKE + 1)[0] == q4.ERR_ALIGN
 
 
 def test_pack_validation():

@@ -157,6 +157,73 @@ def test_ffn_pair():
     assert_within_tol(y, yr, ya, "down")
 
 
+# -------------------------------------------------------------- quantiser --
+def _quantize_gpu(x, rule):
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    c, sc = q4.q4_quantize(d(x), rule, err_flag=err)
+    return c.cpu().numpy(), sc.cpu().numpy().view(np.uint16), int(err.item())
+
+
+@pytest.mark.parametrize("rule", [q4.QUANT_Q4_0, q4.QUANT_ABSMAX7])
+@pytest.mark.parametrize("n,k", [(12288, 1536), (3, 32), (777, 96), (64, 16384)])
+def test_quantize_bit_exact(rule, n, k):
+    rng = synth.rng_for(50, n, k, rule)
+    x = synth.bf16_normal(rng, n * k).reshape(n, k)
+    c, sc, err = _quantize_gpu(x, rule)
+    rc, rs, rf = oracle.q4_quantize(x, rule)
+    assert np.array_equal(sc, rs)
+    assert np.array_equal(c, rc)
+    assert err == int(rf.any()) == 0
+
+
+@pytest.mark.parametrize("rule", [q4.QUANT_Q4_0, q4.QUANT_ABSMAX7])
+def test_quantize_special_blocks(rule):
+    def b(v):
+        return struct.unpack("<I", struct.pack("<f", v))[0] >> 16
+    x = np.zeros((4, 256), dtype=np.uint16)
+    x[0, 32:64] = [b((i - 15.5) * 0.25) for i in range(32)]         # half-way quotients
+    x[0, 64:96] = 0x8000                                              # -0 block
+    x[0, 100], x[0, 110] = b(3.0), b(-3.0)                            # equal magnitudes, both signs
+    x[0, 128:160] = b(2.0 ** -130)                        # bf16 denormals
+    x[1, :32] = np.arange(32, dtype=np.uint16) | 0x0100               # tiny normals
+    x[2, :] = synth.bf16_normal(synth.rng_for(51), 256)
+    x[2, 40] = b(1e5)                                                 # one outlier in a block
+    x[3, 0:32] = b(1.0)
+    x[3, 33] = 0x7FC0                                                 # NaN in block 1
+    x[3, 64] = 0x7F70                                                 # scale overflows fp16
+    c, sc, err = _quantize_gpu(x, rule)
+    rc, rs, rf = oracle.q4_quantize(x, rule)
+    assert np.array_equal(sc, rs)
+    assert np.array_equal(c, rc)
+    assert err == 1 and rf[3, 1] and rf[3, 2] and not rf[:3].any()
+
+
+@pytest.mark.parametrize("rule", [q4.QUANT_Q4_0, q4.QUANT_ABSMAX7])
+def test_quantize_pack_gemv_gemm_head_chain(rule):
+    """Quantise on the GPU, pack, then GEMV, S=64 GEMM and the head on the
+    result: q4_0 scales come out negative for blocks whose largest value is
+    positive, which the synthetic scale distribution never produces."""
+    n, k = 3000, 1536
+    rng = synth.rng_for(52, rule)
+    w = synth.bf16_normal(rng, n * k).reshape(n, k)
+    c, sc, _ = _quantize_gpu(w, rule)
+    if rule == q4.QUANT_Q4_0:
+        assert (oracle.f16_bits_to_f64(sc) < 0).mean() > 0.3
+    packed = pack(c, sc)
+    x = synth.bf16_normal(rng, k)
+    y = q4.q4_gemv(packed, n, k, d(x)).cpu().numpy()
+    yr, a = oracle.gemv(c, sc, x)
+    assert_within_tol(y, yr, a, "gemv on quantised weights")
+    xs = synth.bf16_normal(rng, 64 * k).reshape(64, k)
+    ws = torch.empty(q4.q4_gemm_workspace_bytes(n, k), dtype=torch.uint8, device=DEV)
+    out = torch.empty((64, n), dtype=torch.float32, device=DEV)
+    q4.q4_gemm_s64(packed, n, k, d(xs), out, ws)
+    yg, ag = oracle.gemm(c, sc, xs)
+    assert_within_tol(out.cpu().numpy().ravel(), yg.ravel(), ag.ravel(), "gemm on quantised weights")
+    excluded = _check_head_batch(c, sc, [x, xs[0], xs[1]])
+    assert excluded <= 1
+
+
 # ------------------------------------------------ fused gate/up + GELU --
 def _gelu_mul_gpu(codes, sb, x):
     n, k = codes.shape
