@@ -218,6 +218,76 @@ def probe_kernels(torch, wl: Workload, reps: int = 20):
     return out
 
 
+def probe_verify_m4(torch, wl: Workload, seed: int, reps: int = 10):
+    """The 168 layer GEMVs of the step with m = 4 activation vectors each
+    (q4_gemv_multi: a 4-token verify reads every weight once), one HIP
+    graph; reported as ms per pass and weight bytes/s. Not part of the
+    decode step."""
+    import int4_weight_only_block_amd as q4
+    import synth
+
+    g = torch.Generator(device=wl.xs[0].device)
+    g.manual_seed(seed + 3)
+    mats = wl.mats[:-1]
+    xs4 = [synth.torch_bf16_normal(g, (4, k), wl.xs[0].device) for _, n, k in mats]
+    ys4 = [torch.empty((4, n), dtype=torch.float32, device=wl.xs[0].device) for _, n, k in mats]
+
+    def run():
+        for i, (_, n, k) in enumerate(mats):
+            q4.q4_gemv_multi(wl.packed[i], n, k, xs4[i], ys4[i])
+
+    run()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    wb = sum(weight_bytes(n, k) for _, n, k in mats)
+    return {"m": 4, "launches": len(mats), "ms_per_pass": round(ms, 4), "weight_bytes": wb,
+            "weight_GBs": round(wb / (ms * 1e-3) / 1e9, 1), "frac_of_hbm_peak": round(wb / (ms * 1e-3) / 8e12, 4)}
+
+
+def probe_quantize(torch, dev, seed: int, reps: int = 20):
+    """q4_quantize on an E4B gate+up sized bf16 matrix [20480, 2560] (the
+    export step, not part of a decode step): bf16 read + int8 codes + fp16
+    scales written, four distinct matrices in rotation."""
+    import int4_weight_only_block_amd as q4
+    import synth
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed + 2)
+    n, k = 20480, 2560
+    xs = [synth.torch_bf16_normal(g, (n, k), dev) for _ in range(4)]
+    codes = torch.empty((n, k), dtype=torch.int8, device=dev)
+    scales = torch.empty((n, k // 32), dtype=torch.int16, device=dev)
+    q4.q4_quantize(xs[0], q4.QUANT_Q4_0, codes, scales)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for x in xs:
+            q4.q4_quantize(x, q4.QUANT_Q4_0, codes, scales)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * len(xs))
+    b = n * k * 2 + n * k + n * (k // 32) * 2
+    return {"shape": [n, k], "rule": "q4_0", "avg_launch_us": round(us, 3), "bytes_per_launch": b,
+            "achieved_GBs": round(b / us / 1e3, 1), "frac_of_hbm_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(seconds: float):
     """fp64 oracle on a bounded sample of the decode step: whole matrices of
     layer 0 (QKV, O, gate+up, down) and then row slices of the head until the
@@ -452,6 +522,10 @@ def main():
                          "mfma_fp16_floor_ms": round(flops / 2.5e15 * 1e3, 4)},
         }
         del pgraph
+
+    if not args.no_probe:
+        result["verify_m4_layers"] = probe_verify_m4(torch, wl, args.seed)
+        result["quantize_e4b_gate_up"] = probe_quantize(torch, dev, args.seed)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

@@ -119,6 +119,20 @@ int q4_pack(const int8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
 int q4_gemv(const void* packed, int64_t n, int64_t k, const uint16_t* x,
             float* y, void* stream);
 
+/* q4_gemv_multi: the S=1 matvec for m <= 8 activation vectors at once,
+ * y[v, r] = sum_k c[r,k] * d[r,k/32] * x[v, k] (fp32 accumulation), with the
+ * weights read once for all m (E2B card: a speculative verify of 4 rows reads
+ * the weights once; mixed-bit page: the FFN and head dominate such a step).
+ * Same numerics per vector as q4_gemv; m = 1 is q4_gemv.
+ *   packed  from q4_pack with the same (n, k); 16-byte aligned.
+ *   x       bf16 [m, k] row-major, 16-byte aligned.
+ *   y       fp32 [m, n] row-major, 4-byte aligned, caller-owned.
+ * Errors: NULL pointer, n or k as q4_gemv, m not in [1, 8], misalignment;
+ *         unsupported when the m staged vectors (m * k * 2.125 bytes) do not
+ *         fit in one workgroup's LDS. */
+int q4_gemv_multi(const void* packed, int64_t n, int64_t k, const uint16_t* x,
+                  int64_t m, float* y, void* stream);
+
 /* q4_gemv_gelu_mul: fused gate/up matvec with the GELU-tanh * up epilogue
  * (mixed-bit page, fused gate/up kernels: one launch over the concatenated
  * [gate; up] rows, fp32 tanh-form GELU in the epilogue). With h = n / 2,

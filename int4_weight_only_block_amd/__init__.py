@@ -44,6 +44,7 @@ _SIGNATURES = {
     "q4_quantize": (ctypes.c_int, [_c_p, _c_i64, _c_i64, ctypes.c_int32, _c_p, _c_p, _c_p, _c_p]),
     "q4_gemv": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "q4_gemv_gelu_mul": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
+    "q4_gemv_multi": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p]),
     "q4_gemm_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
     "q4_gemm_s64": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p, ctypes.c_size_t, _c_p]),
     "lmhead_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
@@ -183,6 +184,21 @@ def q4_gemv(packed: torch.Tensor, n: int, k: int, x: torch.Tensor,
         y = torch.empty(n, dtype=torch.float32, device=x.device)
     py = _dev(y, "y", _F32, n)
     _check(lib().q4_gemv(pp, n, k, px, py, _stream(x)))
+    return y
+
+
+def q4_gemv_multi(packed: torch.Tensor, n: int, k: int, x: torch.Tensor,
+                  y: torch.Tensor | None = None) -> torch.Tensor:
+    """y fp32 [m, n] = W x[v] for the m <= 8 bf16 rows of x [m, k], the
+    weights read once."""
+    m = x.shape[0] if x.dim() == 2 else 1
+    pp = _dev(packed, "packed", _BYTES)
+    _check_packed(packed, n, k)
+    px = _dev(x, "x", _U16, m * k)
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    py = _dev(y, "y", _F32, m * n)
+    _check(lib().q4_gemv_multi(pp, n, k, px, m, py, _stream(x)))
     return y
 
 

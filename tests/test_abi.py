@@ -11,7 +11,7 @@ import int4_weight_only_block_amd as q4
 pytestmark = pytest.mark.skipif(not os.path.exists(q4.LIB_PATH), reason="libq4dec.so not built")
 
 EXPECTED = {
-    "q4dec_abi_version", "q4dec_last_error", "q4_packed_bytes", "q4_pack", "q4_quantize", "q4_gemv", "q4_gemv_gelu_mul",
+    "q4dec_abi_version", "q4dec_last_error", "q4_packed_bytes", "q4_pack", "q4_quantize", "q4_gemv", "q4_gemv_gelu_mul", "q4_gemv_multi",
     "q4_gemm_s64", "q4_gemm_workspace_bytes", "lmhead_workspace_bytes", "lmhead_softcap_argmax", "ple_gather",
 }
 
@@ -107,6 +107,22 @@ def test_quantize_validation():
     assert call(0, FAKE + 2)[0] == q4.ERR_ALIGN
     assert call(4, FAKE + 8)[0] == q4.ERR_ALIGN
     assert call(5, FAKE + 1)[0] == q4.ERR_ALIGN
+
+
+def test_gemv_multi_validation():
+    L = q4.lib()
+    rc, msg = _rc_and_msg(L.q4_gemv_multi(FAKE, 16, 32, FAKE, 0, FAKE, None))
+    assert rc == q4.ERR_SHAPE and "m" in msg
+    rc, msg = _rc_and_msg(L.q4_gemv_multi(FAKE, 16, 32, FAKE, 9, FAKE, None))
+    assert rc == q4.ERR_SHAPE
+    rc, msg = _rc_and_msg(L.q4_gemv_multi(FAKE, 16, 32, FAKE, 4, None, None))
+    assert rc == q4.ERR_NULL and "y" in msg
+    rc, msg = _rc_and_msg(L.q4_gemv_multi(FAKE, 16, 32, FAKE, 4, FAKE + 2, None))
+    assert rc == q4.ERR_ALIGN and "y" in msg
+    rc, msg = _rc_and_msg(L.q4_gemv_multi(FAKE, 16, 48, FAKE, 4, FAKE, None))
+    assert rc == q4.ERR_SHAPE and "k" in msg
+    rc, msg = _rc_and_msg(L.q4_gemv_multi(None, 16, 32, FAKE, 4, FAKE, None))
+    assert rc == q4.ERR_NULL and "packed" in msg
 
 
 def test_pack_validation():

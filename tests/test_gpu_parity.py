@@ -157,6 +157,46 @@ def test_ffn_pair():
     assert_within_tol(y, yr, ya, "down")
 
 
+# ------------------------------------------------- multi-vector GEMV --
+@pytest.mark.parametrize("m,n,k", [(2, 1536, 1536), (3, 777, 96), (4, 3072, 2560), (4, 2560, 10240),
+                                   (8, 2560, 2048), (5, 5, 32), (4, 20480, 2560), (7, 1000, 6144),
+                                   (2, 300, 16384)])
+def test_gemv_multi_tolerance(m, n, k):
+    rng = synth.rng_for(60, m, n, k)
+    codes, sb = synth.q4_weights(rng, n, k)
+    xs = synth.bf16_normal(rng, m * k).reshape(m, k)
+    y = q4.q4_gemv_multi(pack(codes, sb), n, k, d(xs)).cpu().numpy()
+    yr, a = oracle.gemm(codes, sb, xs)
+    assert_within_tol(y.ravel(), yr.ravel(), a.ravel(), f"multi m={m}")
+
+
+@pytest.mark.parametrize("k", [64, 1536, 2560, 10240])
+def test_gemv_multi_integer_exact(k):
+    n, m = 515, 4
+    rng = synth.rng_for(61, k)
+    codes = rng.integers(-8, 8, size=(n, k), dtype=np.int8)
+    sb = np.full((n, k // 32), fp16_bits(2.0 ** -6), dtype=np.uint16)
+    xi = rng.integers(-4, 5, size=(m, k))
+    xs = np.stack([bf16_bits_of_ints(r) for r in xi])
+    y = q4.q4_gemv_multi(pack(codes, sb), n, k, d(xs)).cpu().numpy()
+    want = (codes.astype(np.int64) @ xi.T.astype(np.int64)).T / 64.0
+    assert np.array_equal(y.astype(np.float64), want)
+
+
+def test_gemv_multi_lds_limit_and_m1():
+    n, k = 64, 16384
+    rng = synth.rng_for(62)
+    codes, sb = synth.q4_weights(rng, n, k)
+    packed = pack(codes, sb)
+    xs = synth.bf16_normal(rng, 8 * k).reshape(8, k)
+    with pytest.raises(q4.Q4Error) as e:
+        q4.q4_gemv_multi(packed, n, k, d(xs))
+    assert e.value.code == q4.ERR_UNSUPPORTED
+    y1 = q4.q4_gemv_multi(packed, n, k, d(xs[:1])).cpu().numpy()
+    y0 = q4.q4_gemv(packed, n, k, d(xs[0])).cpu().numpy()
+    assert np.array_equal(y1[0], y0)
+
+
 # -------------------------------------------------------------- quantiser --
 def _quantize_gpu(x, rule):
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
