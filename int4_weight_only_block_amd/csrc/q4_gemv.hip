@@ -101,6 +101,12 @@ struct Lane {
                                             uint32_t m_hi, uint32_t magic) {
     const u32x4* np = reinterpret_cast<const u32x4*>(nib + size_t(row_next) * row_bytes);
     const uint16_t* sp = scl + size_t(row_next) * size_t(B);
+    // The LDS addresses of every (vector, block, quarter) are the same for
+    // every row group; left free, the compiler computes all of them once
+    // before the row loop and holds them in VGPRs (some 200 at 8 vectors),
+    // which costs most of the occupancy. Making the strides opaque here
+    // keeps each address next to its read.
+    asm volatile("" : "+s"(xstride), "+s"(fstride));
 #pragma unroll
     for (int v = 0; v < NV; ++v) acc[v] = 0.0f;
 #pragma unroll
