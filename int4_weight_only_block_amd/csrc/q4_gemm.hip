@@ -48,11 +48,13 @@ static GemmPlan gemm_plan(int64_t n, int64_t k) {
   GemmPlan p{};
   const int B = int(k / 32);
   const int64_t tiles = (n + kTileN - 1) / kTileN;
-  // enough workgroups to cover the chip, slices of at least 8 blocks
-  int s = 1;
-  while (tiles * s < 256 && B / (2 * s) >= 8) s *= 2;
-  p.slices = s;
-  p.bps = (B + s - 1) / s;
+  // About one workgroup per CU: split K when the row tiles alone leave CUs
+  // idle, in slices of whole chunks (a partial last chunk runs its MFMAs on
+  // zeroed scales). Matrices with >= 128 tiles are not split, so they need
+  // no second launch.
+  const int64_t s_target = std::max<int64_t>(1, 256 / tiles);
+  const int per = int((B + s_target - 1) / s_target);
+  p.bps = ((per + kChunk - 1) / kChunk) * kChunk;
   p.slices = (B + p.bps - 1) / p.bps;
   p.xh_off = 0;
   p.xf_off = align256(size_t(kTok) * size_t(k) * 2);
