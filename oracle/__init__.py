@@ -22,6 +22,9 @@ from .q4_oracle import (  # noqa: F401
     nibbles_from_codes,
     ple_gather,
     q4_quantize,
+    rowq_gemv,
+    rowq_pack,
+    rowq_unpack,
     QUANT_ABSMAX7,
     QUANT_Q4_0,
     softcap,

@@ -85,6 +85,50 @@ def dequant(codes, scale_bits) -> np.ndarray:
     return codes.astype(np.float64) * np.repeat(d, 32, axis=1)
 
 
+# ---------------------------------------------- per-row INT4 / INT2 GEMV --
+def rowq_unpack(w_bytes, n: int, k: int, bits: int) -> np.ndarray:
+    """Dense-packed per-row symmetric codes -> int8 [n, k] ([MIX] decode
+    recipe: per-channel symmetric linear, all zero points 0, bytes = elements *
+    bits / 8; packing convention: INT2 holds 4 codes per byte with the first
+    code in bits [1:0], two's complement in [-2, 1]; INT4 is the same with
+    nibbles, low nibble first, in [-8, 7])."""
+    if bits not in (2, 4):
+        raise ValueError("bits must be 2 or 4")
+    per = 8 // bits
+    b = np.ascontiguousarray(w_bytes).view(np.uint8).reshape(n, k // per)
+    shifts = np.arange(per, dtype=np.uint8) * bits
+    u = (b[..., None] >> shifts) & ((1 << bits) - 1)         # [n, k/per, per], first code lowest
+    c = u.astype(np.int16) - ((u >> (bits - 1)) << bits)     # two's complement
+    return c.reshape(n, k).astype(np.int8)
+
+
+def rowq_pack(codes, bits: int) -> np.ndarray:
+    """int8 codes [n, k] in range -> the dense bytes rowq_unpack reads."""
+    c = np.asarray(codes).astype(np.int16)
+    lo, hi = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
+    if ((c < lo) | (c > hi)).any():
+        raise ValueError("codes out of range")
+    per = 8 // bits
+    n, k = c.shape
+    u = (c & ((1 << bits) - 1)).astype(np.uint8).reshape(n, k // per, per)
+    out = np.zeros((n, k // per), dtype=np.uint8)
+    for i in range(per):
+        out |= (u[..., i] << (i * bits)).astype(np.uint8)
+    return out
+
+
+def rowq_gemv(w_bytes, row_scale, bits: int, x_bits):
+    """y[r] = scale[r] * sum_k c[r, k] x[k] in fp64 ([MIX] receiving-end
+    design: per-row scale, the raw integer-weighted sum is scaled once per
+    row), plus A[r] = |scale[r]| * sum_k |c[r, k] x[k]| for the GEMV bar."""
+    x = bf16_bits_to_f64(x_bits)
+    k = x.size
+    sc = np.asarray(row_scale, dtype=np.float32).astype(np.float64)
+    n = sc.size
+    c = rowq_unpack(w_bytes, n, k, bits).astype(np.float64)
+    return sc * (c @ x), np.abs(sc) * (np.abs(c) @ np.abs(x))
+
+
 # --------------------------------------------------------------- quantiser --
 QUANT_Q4_0 = 0     # q4_0 grid: d = m / -8, m the block's largest-magnitude value
 QUANT_ABSMAX7 = 1  # symmetric: d = max|x| / 7, codes in [-7, 7]

@@ -557,3 +557,40 @@ def test_quantize_special_blocks():
     assert s[0, 0] == 0 and not c[0, :32].any()
     assert not c[0, 64:96].any()
     assert oracle.f16_bits_to_f64(s[0, 3:4])[0] == -0.125 and np.all(c[0, 96:] == -8)
+
+
+# ------------------------------------------------ per-row INT4 / INT2 --
+def test_rowq_unpack_bytes_follow_the_stated_convention():
+    # INT2: 4 codes per byte, first code in bits [1:0], two's complement
+    # 0xE4 = 0b11_10_01_00 -> 0, 1, -2, -1 ; 0x1B = 0b00_01_10_11 -> -1, -2, 1, 0
+    b = np.array([[0xE4, 0x1B]], dtype=np.uint8)
+    assert oracle.rowq_unpack(b, 1, 8, 2).tolist() == [[0, 1, -2, -1, -1, -2, 1, 0]]
+    # INT4: low nibble first, two's complement: 0x8F -> -1, -8 ; 0x70 -> 0, 7
+    b = np.array([[0x8F, 0x70]], dtype=np.uint8)
+    assert oracle.rowq_unpack(b, 1, 4, 4).tolist() == [[-1, -8, 0, 7]]
+    rng = np.random.default_rng(70)
+    for bits in (2, 4):
+        c = rng.integers(-(1 << (bits - 1)), 1 << (bits - 1), size=(3, 64)).astype(np.int8)
+        assert np.array_equal(oracle.rowq_unpack(oracle.rowq_pack(c, bits), 3, 64, bits), c)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_rowq_gemv_bruteforce_fraction(bits):
+    rng = np.random.default_rng(71 + bits)
+    n, k = 5, 128
+    w = rng.integers(0, 256, size=(n, k * bits // 8), dtype=np.uint8)
+    sc = rng.uniform(1e-3, 1e-2, size=n).astype(np.float32)
+    x = synth.bf16_normal(rng, k)
+    y, a = oracle.rowq_gemv(w, sc, bits, x)
+    # independent decode: walk the bytes bit by bit
+    for r in range(n):
+        codes = []
+        for byte in w[r].tolist():
+            for i in range(8 // bits):
+                u = (byte >> (i * bits)) & ((1 << bits) - 1)
+                codes.append(u - (1 << bits) if u >= (1 << (bits - 1)) else u)
+        xs = [bf16_exact(v) for v in x]
+        ye = Fraction(float(sc[r])) * sum(Fraction(c) * v for c, v in zip(codes, xs))
+        ae = abs(Fraction(float(sc[r]))) * sum(abs(Fraction(c) * v) for c, v in zip(codes, xs))
+        assert abs(Fraction(y[r]) - ye) <= Fraction(1, 10 ** 12) * ae
+        assert abs(Fraction(a[r]) - ae) <= Fraction(1, 10 ** 12) * ae
