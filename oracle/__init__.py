@@ -22,6 +22,7 @@ from .q4_oracle import (  # noqa: F401
     nibbles_from_codes,
     ple_gather,
     q4_quantize,
+    rowq_gelu_mul,
     rowq_gemv,
     rowq_pack,
     rowq_unpack,

@@ -339,6 +339,21 @@ def gelu_mul(codes, scale_bits, x_bits):
     return gelu_tanh_f64(g) * u, g, u, a_mag[:h], a_mag[h:]
 
 
+def rowq_gelu_mul(w_bytes, row_scale, bits: int, x_bits):
+    """gelu_mul on the per-row INT4 / INT2 formats ([MIX] fused gate/up
+    kernels for the int2 / int4 symmetric layouts): the n rows are [gate; up],
+    g = rowq_gemv of rows 0 .. h-1, u = rowq_gemv of rows h .. n-1 (each with
+    its own row scale), a = gelu_tanh(g) * u in fp64. Returns (a, g, u, A_g,
+    A_u) like gelu_mul."""
+    y, a_mag = rowq_gemv(w_bytes, row_scale, bits, x_bits)
+    n = y.size
+    if n % 2:
+        raise ValueError("rowq_gelu_mul needs an even number of rows ([gate; up])")
+    h = n // 2
+    g, u = y[:h], y[h:]
+    return gelu_tanh_f64(g) * u, g, u, a_mag[:h], a_mag[h:]
+
+
 def gelu_mul_tolerance(g, u, a_g, a_u):
     """Per-output bound for a bf16 result of gelu_mul computed from fp32
     GEMV sums. Each sum is within t = 1e-4 * A + 1e-6 of the exact value

@@ -594,3 +594,19 @@ def test_rowq_gemv_bruteforce_fraction(bits):
         ae = abs(Fraction(float(sc[r]))) * sum(abs(Fraction(c) * v) for c, v in zip(codes, xs))
         assert abs(Fraction(y[r]) - ye) <= Fraction(1, 10 ** 12) * ae
         assert abs(Fraction(a[r]) - ae) <= Fraction(1, 10 ** 12) * ae
+
+
+def test_rowq_gelu_mul_pairs_gate_row_j_with_up_row_h_plus_j():
+    # INT4, k = 32, rows [gate0, gate1, up0, up1] with constant codes 1, 0, 2, 3,
+    # x = 1 and unit scales: g = (32, 0), u = (64, 96); gelu(32) = 32 to
+    # double precision and gelu(0) = 0, so a = (2048, 0). Pairing row j with
+    # row j + 1 instead (interleaved gate/up) would give a = (0, gelu(64) * 96).
+    w = np.array([[0x11] * 16, [0x00] * 16, [0x22] * 16, [0x33] * 16], dtype=np.uint8)
+    sc = np.ones(4, dtype=np.float32)
+    x = np.full(32, 0x3F80, dtype=np.uint16)  # bf16 1.0
+    a, g, u, ag, au = oracle.rowq_gelu_mul(w, sc, 4, x)
+    assert g.tolist() == [32.0, 0.0] and u.tolist() == [64.0, 96.0]
+    assert a.tolist() == [2048.0, 0.0]
+    assert ag.tolist() == [32.0, 0.0] and au.tolist() == [64.0, 96.0]
+    with pytest.raises(ValueError):
+        oracle.rowq_gelu_mul(w[:3], sc[:3], 4, x)
