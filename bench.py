@@ -288,6 +288,49 @@ def probe_quantize(torch, dev, seed: int, reps: int = 20):
             "achieved_GBs": round(b / us / 1e3, 1), "frac_of_hbm_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
 
 
+def probe_rowq(torch, dev, seed: int, reps: int = 20):
+    """Per-row symmetric INT2 GEMVs on the mobile mixed-bit kernel-probe
+    workload: six INT2 FFNs (gate and up [12288, 1536], down [1536, 12288])
+    and the INT2 262,144-row head [262144, 1536], 185 MB of codes per run,
+    one HIP graph. Not part of the q4_0 decode step. Bytes counted: packed
+    codes + fp32 row scales + bf16 x + fp32 y."""
+    import int4_weight_only_block_amd as q4
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed + 4)
+    ffn = [(12288, 1536), (12288, 1536), (1536, 12288)]
+    mats = ffn * 6 + [(262144, 1536)]
+    # six distinct FFN weight sets and one head, as on the page's probe
+    ws = [torch.randint(0, 256, (n, k // 4), dtype=torch.uint8, device=dev, generator=g) for n, k in mats]
+    scs = [torch.empty(n, dtype=torch.float32, device=dev).uniform_(1e-3, 1e-2, generator=g) for n, _ in mats]
+    xs = [(torch.randn(k, device=dev, generator=g)).to(torch.bfloat16) for _, k in mats]
+    ys = [torch.empty(n, dtype=torch.float32, device=dev) for n, _ in mats]
+
+    def run():
+        for (n, k), w, sc, x, y in zip(mats, ws, scs, xs, ys):
+            q4.rowq_gemv(w, sc, n, k, 2, x, y)
+
+    run()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    code_bytes = sum(n * k // 4 for n, k in mats)
+    b = sum(n * k // 4 + 4 * n + 2 * k + 4 * n for n, k in mats)
+    return {"workload": "int2_kprobe_6ffn_plus_head", "launches": len(mats), "ms_per_run": round(ms, 4),
+            "code_bytes": code_bytes, "bytes_per_run": b, "achieved_GBs": round(b / (ms * 1e-3) / 1e9, 1),
+            "frac_of_hbm_peak": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+
 def cpu_baseline(seconds: float):
     """fp64 oracle on a bounded sample of the decode step: whole matrices of
     layer 0 (QKV, O, gate+up, down) and then row slices of the head until the
@@ -526,6 +569,7 @@ def main():
     if not args.no_probe:
         result["verify_m4_layers"] = probe_verify_m4(torch, wl, args.seed)
         result["quantize_e4b_gate_up"] = probe_quantize(torch, dev, args.seed)
+        result["rowq_int2_kprobe"] = probe_rowq(torch, dev, args.seed)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)

@@ -133,6 +133,23 @@ int q4_gemv(const void* packed, int64_t n, int64_t k, const uint16_t* x,
 int q4_gemv_multi(const void* packed, int64_t n, int64_t k, const uint16_t* x,
                   int64_t m, float* y, void* stream);
 
+/* rowq_gemv: per-row symmetric INT4 / INT2 matvec on the dense packing of the
+ * mixed-bit recipe (mixed-bit page: decode recipe, per-channel symmetric
+ * linear weights with all zero points 0; packing convention: INT2 holds 4
+ * codes per byte, first code in bits [1:0], two's complement in [-2, 1];
+ * INT4 likewise with nibbles, low nibble first, in [-8, 7]; receiving-end
+ * design: the integer-weighted sum is scaled once per row):
+ *   y[r] = row_scale[r] * sum_k c[r, k] * x[k]   (fp32 accumulation).
+ * The raw packed bytes are the kernel's layout (no repacking).
+ *   w          [n, k * bits / 8] bytes row-major, 16-byte aligned.
+ *   row_scale  fp32 [n], 4-byte aligned.
+ *   bits       2 or 4; k a multiple of 64 (INT2) or 32 (INT4).
+ *   x          bf16 [k], 16-byte aligned.   y  fp32 [n], 4-byte aligned.
+ * Errors: NULL pointer, bits not 2 or 4, n <= 0 or >= 2^31, k not a
+ *         multiple of the 16-byte code chunk, k > Q4DEC_MAX_K, misalignment. */
+int rowq_gemv(const void* w, const float* row_scale, int64_t n, int64_t k,
+              int32_t bits, const uint16_t* x, float* y, void* stream);
+
 /* q4_gemv_gelu_mul: fused gate/up matvec with the GELU-tanh * up epilogue
  * (mixed-bit page, fused gate/up kernels: one launch over the concatenated
  * [gate; up] rows, fp32 tanh-form GELU in the epilogue). With h = n / 2,

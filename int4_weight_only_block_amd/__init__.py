@@ -45,6 +45,7 @@ _SIGNATURES = {
     "q4_gemv": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "q4_gemv_gelu_mul": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "q4_gemv_multi": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p]),
+    "rowq_gemv": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, ctypes.c_int32, _c_p, _c_p, _c_p]),
     "q4_gemm_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
     "q4_gemm_s64": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p, ctypes.c_size_t, _c_p]),
     "lmhead_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
@@ -199,6 +200,20 @@ def q4_gemv_multi(packed: torch.Tensor, n: int, k: int, x: torch.Tensor,
         y = torch.empty((m, n), dtype=torch.float32, device=x.device)
     py = _dev(y, "y", _F32, m * n)
     _check(lib().q4_gemv_multi(pp, n, k, px, m, py, _stream(x)))
+    return y
+
+
+def rowq_gemv(w: torch.Tensor, row_scale: torch.Tensor, n: int, k: int, bits: int, x: torch.Tensor,
+              y: torch.Tensor | None = None) -> torch.Tensor:
+    """y fp32 [n] = row_scale * (codes @ x) for dense-packed per-row INT2 /
+    INT4 codes w [n, k * bits / 8] (uint8)."""
+    pw = _dev(w, "w", _BYTES, n * k * bits // 8)
+    ps = _dev(row_scale, "row_scale", _F32, n)
+    px = _dev(x, "x", _U16, k)
+    if y is None:
+        y = torch.empty(n, dtype=torch.float32, device=x.device)
+    py = _dev(y, "y", _F32, n)
+    _check(lib().rowq_gemv(pw, ps, n, k, int(bits), px, py, _stream(x)))
     return y
 
 

@@ -1,0 +1,362 @@
+// rowq_gemv: per-row symmetric INT4 / INT2 matvec on the dense packing of the
+// mixed-bit recipe ("Gemma-4 E2B mobile mixed-bit QAT weights" knowledge page:
+// decode recipe with per-channel symmetric linear weights, all zero points 0,
+// bytes = elements * bits / 8; packing convention: INT2 holds 4 codes per byte
+// with the first code in bits [1:0], two's complement, INT4 likewise with
+// nibbles, low nibble first; receiving-end design: the integer-weighted sum is
+// scaled by the row's scale once).
+//
+// The weight stream follows q4_gemv: lane t of a row group owns 16-byte chunks
+// t, t + LPR, ... of its row (64 INT2 or 32 INT4 codes each) and walks down
+// the rows with one row group of loads in flight. Because a lane meets the
+// same chunks on every row, its share of x lives in registers: the workgroup
+// converts x once into LDS, each lane copies its blocks out, and the row loop
+// touches no LDS.
+//
+// Codes are not converted to fp16 on their own. Each field is moved into
+// mantissa bits of an fp16 whose exponent is that of 1024 (OR with 0x6400), so
+// the half holds 1024 + 2^s * u exactly, u = code + 2 (INT2) or code + 8
+// (INT4) after an XOR of the packed word. The matching activation is stored
+// pre-multiplied by 2^-s, so the dot product yields code * x plus
+// (1024 * 2^-s + offset) * x, a term that depends on x alone: each block's sum
+// of those terms is computed once at staging and starts the block's fp32
+// accumulator with the opposite sign. Shifts s of 4 to 8 keep that term within
+// a small multiple of the codes' own contribution.
+#include <math.h>
+
+#include <map>
+#include <mutex>
+#include <tuple>
+
+#include "q4dec_internal.h"
+
+namespace q4dec {
+namespace {
+
+constexpr int kRWaves = 4;
+constexpr int kRThreads = 64 * kRWaves;
+
+// field isolation in plain C: the compiler forms v_and_or_b32 / v_bitop3_b32
+// itself and so knows the hazards between it and the dot product
+__device__ __forceinline__ uint32_t field(uint32_t a, uint32_t mask, uint32_t magic) { return (a & mask) | magic; }
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
+}
+
+// One dword of codes against its activation pairs. Pair f of dword d of a
+// 32-code block holds block elements elem(d, f) and elem(d, f) + kSecond,
+// matching the low-half and high-half field that one AND-OR isolates.
+template <int BITS>
+struct Fields;
+
+template <>
+struct Fields<2> {
+  static constexpr int kPairs = 8;   // pairs per dword
+  static constexpr int kDwords = 2;  // dwords per block
+  static constexpr int kSecond = 8;
+  static constexpr int kOffset = 2;  // u = code + 2
+  __device__ static constexpr int elem(int d, int f) { return 16 * d + f; }
+  // field f sits at bits 6-7 (f even) or 8-9 (f odd) of each half
+  __device__ static constexpr int shift(int f) { return (f & 1) ? 8 : 6; }
+  __device__ __forceinline__ static float dot(uint32_t w, const uint32_t* xp, float p, uint32_t magic) {
+    w ^= 0xAAAAAAAAu;
+    const uint32_t s[4] = {w << 6, w << 2, w >> 2, w >> 6};  // fields (0,1) (2,3) (4,5) (6,7)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      p = dot2(field(s[g], 0x00C000C0u, magic), xp[2 * g], p);
+      p = dot2(field(s[g], 0x03000300u, magic), xp[2 * g + 1], p);
+    }
+    return p;
+  }
+};
+
+template <>
+struct Fields<4> {
+  static constexpr int kPairs = 4;
+  static constexpr int kDwords = 4;
+  static constexpr int kSecond = 4;
+  static constexpr int kOffset = 8;  // u = code + 8
+  __device__ static constexpr int elem(int d, int f) { return 8 * d + f; }
+  // every nibble is moved to bits 4-7 of each half
+  __device__ static constexpr int shift(int) { return 4; }
+  __device__ __forceinline__ static float dot(uint32_t w, const uint32_t* xp, float p, uint32_t magic) {
+    w ^= 0x88888888u;
+    const uint32_t s[4] = {w << 4, w, w >> 4, w >> 8};  // nibbles 0 1 2 3
+#pragma unroll
+    for (int f = 0; f < 4; ++f) p = dot2(field(s[f], 0x00F000F0u, magic), xp[f], p);
+    return p;
+  }
+};
+
+// Stage block b of x: its 16 activation pairs, element e scaled by 2^-(E + s)
+// where 2^E brings the block's largest bf16 exponent to 2^14 (as in q4_gemv)
+// and s is the shift of the field the element meets; quarter i of the 64
+// bytes goes to slot i ^ (sw & 3). cx receives (-C, 2^E), C being the block's
+// sum of (1024 + offset * 2^s) * x'. Both factors are exact fp16 values, so
+// the dot-product instruction forms each product exactly and C carries only
+// the fp32 rounding of its sums.
+template <int BITS>
+__device__ __forceinline__ void stage_block(const uint16_t* __restrict__ xb, uint32_t* __restrict__ dst, int sw,
+                                            float2* __restrict__ cx) {
+  using F = Fields<BITS>;
+  uint32_t raw[16];
+  const uint4* src = reinterpret_cast<const uint4*>(xb);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = src[i];
+    raw[4 * i] = v.x; raw[4 * i + 1] = v.y; raw[4 * i + 2] = v.z; raw[4 * i + 3] = v.w;
+  }
+  auto elem = [&](int e) -> float {
+    const uint32_t v = raw[e >> 1];
+    return __builtin_bit_cast(float, (e & 1) ? (v & 0xFFFF0000u) : (v << 16));
+  };
+  uint32_t emax = 1;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) emax = max(emax, max((raw[i] >> 7) & 0xFFu, (raw[i] >> 23) & 0xFFu));
+  const int e = int(emax) - 127 - 14;
+  uint32_t out[16];
+  float c = 0.0f;
+#pragma unroll
+  for (int d = 0; d < F::kDwords; ++d) {
+#pragma unroll
+    for (int f = 0; f < F::kPairs; ++f) {
+      const int e0 = F::elem(d, f), s = F::shift(f);
+      const half2_t h = {(_Float16)ldexpf(elem(e0), -e - s), (_Float16)ldexpf(elem(e0 + F::kSecond), -e - s)};
+      const _Float16 bias = (_Float16)(1024 + (F::kOffset << s));  // 1152 or 1536, exact
+      const half2_t bb = {bias, bias};
+      c = __builtin_amdgcn_fdot2(h, bb, c, false);
+      out[d * F::kPairs + f] = __builtin_bit_cast(uint32_t, h);
+    }
+  }
+  uint4* d4 = reinterpret_cast<uint4*>(dst);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) d4[i ^ (sw & 3)] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+  *cx = make_float2(-c, ldexpf(1.0f, e));
+}
+
+// DEPTH row groups of loads in flight per wave (1 or 2).
+template <int BITS, int LPR, int CPL, int DEPTH, bool FULL>
+__global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __restrict__ w,
+                                                              const float* __restrict__ row_scale,
+                                                              const uint16_t* __restrict__ x, int n, int k, int ipw,
+                                                              float* __restrict__ y) {
+  using F = Fields<BITS>;
+  constexpr int RPW = 64 / LPR;
+  constexpr int BPC = BITS == 2 ? 2 : 1;  // activation blocks per 16-byte chunk
+  constexpr int NB = CPL * BPC;           // blocks held by one lane
+  constexpr int MAXB = LPR * NB;
+  __shared__ uint32_t xs[MAXB * 16];
+  __shared__ float2 xc[MAXB];
+  const int U = (k * BITS) >> 7;  // 16-byte chunks per row
+  const int B = k >> 5;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int t = lane % LPR;
+  const int r = lane / LPR;
+  const int RG = (n + RPW - 1) / RPW;
+  const int rg_base = blockIdx.x * kRWaves * ipw + wave;
+  const size_t row_bytes = size_t(U) * 16;
+  const int iters = rg_base < RG ? min(ipw, (RG - rg_base + kRWaves - 1) / kRWaves) : 0;
+  auto row_of = [&](int i) {
+    const int row = (rg_base + i * kRWaves) * RPW + r;
+    return row < n ? row : n - 1;
+  };
+
+  uint4 qa[CPL], qb[CPL];
+  auto load = [&](uint4(&q)[CPL], int row) {
+    const u32x4* p = reinterpret_cast<const u32x4*>(w + size_t(row) * row_bytes);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = j * LPR + t;
+      if (FULL || c < U) {
+        const u32x4 v = __builtin_nontemporal_load(p + c);
+        q[j] = make_uint4(v.x, v.y, v.z, v.w);
+      }
+    }
+  };
+  if (iters > 0) load(qa, row_of(0));
+  if (DEPTH == 2 && iters > 1) load(qb, row_of(1));
+
+  for (int b = threadIdx.x; b < B; b += kRThreads) stage_block<BITS>(x + 32 * b, xs + 16 * b, b / BPC, xc + b);
+  // LDS writes done and visible; the weight loads above stay in flight
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+  uint32_t xp[NB][16];
+  float cneg[NB], xf[NB];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    const int c = j * LPR + t;
+    if (FULL || c < U) {
+#pragma unroll
+      for (int bb = 0; bb < BPC; ++bb) {
+        const int b = c * BPC + bb, l = j * BPC + bb;
+        const uint4* s4 = reinterpret_cast<const uint4*>(xs + 16 * b);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint4 v = s4[i ^ (c & 3)];
+          xp[l][4 * i] = v.x; xp[l][4 * i + 1] = v.y; xp[l][4 * i + 2] = v.z; xp[l][4 * i + 3] = v.w;
+        }
+        const float2 cc = xc[b];
+        cneg[l] = cc.x;
+        xf[l] = cc.y;
+      }
+    }
+  }
+
+  uint32_t magic;
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+
+  auto dot = [&](uint4(&q)[CPL], bool refill, int row_next) -> float {
+    const u32x4* pn = reinterpret_cast<const u32x4*>(w + size_t(row_next) * row_bytes);
+    float acc = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = j * LPR + t;
+      if (FULL || c < U) {
+        const uint32_t wd[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
+#pragma unroll
+        for (int bb = 0; bb < BPC; ++bb) {
+          const int l = j * BPC + bb;
+          float p = cneg[l];
+#pragma unroll
+          for (int d = 0; d < F::kDwords; ++d) p = F::dot(wd[bb * F::kDwords + d], &xp[l][d * F::kPairs], p, magic);
+          acc = fmaf(p, xf[l], acc);
+        }
+        // keep one chunk's work together so its temporaries die before the
+        // next chunk's begin
+        asm volatile("" : "+v"(acc));
+        __builtin_amdgcn_sched_barrier(0);
+        if (refill) {
+          const u32x4 v = __builtin_nontemporal_load(pn + c);
+          q[j] = make_uint4(v.x, v.y, v.z, v.w);
+        }
+      }
+    }
+    return acc;
+  };
+  auto emit = [&](int i, float acc) {
+    acc = group_sum<LPR>(acc);
+    const int row = (rg_base + i * kRWaves) * RPW + r;
+    if (t == 0 && row < n) y[row] = acc * row_scale[row];
+  };
+  if constexpr (DEPTH == 1) {
+    for (int i = 0; i + 1 < iters; ++i) emit(i, dot(qa, true, row_of(i + 1)));
+    if (iters > 0) emit(iters - 1, dot(qa, false, 0));
+  } else {
+    // qa holds row group i, qb row group i + 1; each refills two ahead
+    int i = 0;
+    for (; i + 3 < iters; i += 2) {
+      emit(i, dot(qa, true, row_of(i + 2)));
+      emit(i + 1, dot(qb, true, row_of(i + 3)));
+    }
+    if (i + 2 < iters) {  // three left
+      emit(i, dot(qa, true, row_of(i + 2)));
+      emit(i + 1, dot(qb, false, 0));
+      emit(i + 2, dot(qa, false, 0));
+    } else {
+      if (i < iters) emit(i, dot(qa, false, 0));
+      if (i + 1 < iters) emit(i + 1, dot(qb, false, 0));
+    }
+  }
+}
+
+struct RPlan {
+  int lpr, cpl, rpw, rg, ipw, grid;
+  const void* fn;
+};
+
+// (lanes per row, chunks per lane) pairs the plan below can ask for
+template <int BITS, bool FULL>
+const void* pick_rowq(int lpr, int cpl) {
+#define RQ_CASE(L, C) \
+  if (lpr == L && cpl == C) return reinterpret_cast<const void*>(&rowq_rows_kernel<BITS, L, C, 1, FULL>);
+  if constexpr (BITS == 2) {
+    RQ_CASE(8, 1) RQ_CASE(8, 2) RQ_CASE(8, 3)
+    RQ_CASE(16, 2) RQ_CASE(16, 3)
+    RQ_CASE(32, 2) RQ_CASE(32, 3)
+    RQ_CASE(64, 2) RQ_CASE(64, 3) RQ_CASE(64, 4)
+  } else {
+    RQ_CASE(8, 1) RQ_CASE(8, 2) RQ_CASE(8, 3) RQ_CASE(8, 4) RQ_CASE(8, 5) RQ_CASE(8, 6)
+    RQ_CASE(16, 4) RQ_CASE(16, 5) RQ_CASE(16, 6)
+    RQ_CASE(32, 4) RQ_CASE(32, 5) RQ_CASE(32, 6)
+    RQ_CASE(64, 4) RQ_CASE(64, 5) RQ_CASE(64, 6) RQ_CASE(64, 7) RQ_CASE(64, 8)
+  }
+#undef RQ_CASE
+  return nullptr;
+}
+
+int rowq_blocks_per_cu(const void* fn) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  std::lock_guard<std::mutex> lock(mu);
+  auto key = std::make_pair(fn, dev);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kRThreads, 0) != hipSuccess || nb <= 0) nb = 1;
+  cache[key] = nb;
+  return nb;
+}
+
+template <int BITS>
+RPlan rowq_plan(int64_t n, int64_t k) {
+  constexpr int BPC = BITS == 2 ? 2 : 1;
+  const int U = int((k * BITS) >> 7);
+  RPlan p{};
+  // smallest split of at least 8 lanes (128 contiguous bytes per row and
+  // instruction) whose lanes hold at most 6 activation blocks (108 VGPRs);
+  // rows too wide for that take 64 lanes and up to 8 blocks
+  p.lpr = 64;
+  for (int l = 8; l <= 64; l *= 2)
+    if ((U + l - 1) / l * BPC <= 6) {
+      p.lpr = l;
+      break;
+    }
+  p.cpl = (U + p.lpr - 1) / p.lpr;
+  const bool full = U == p.lpr * p.cpl;
+  p.fn = full ? pick_rowq<BITS, true>(p.lpr, p.cpl) : pick_rowq<BITS, false>(p.lpr, p.cpl);
+  p.rpw = 64 / p.lpr;
+  if (!p.fn) return p;
+  p.rg = int((n + p.rpw - 1) / p.rpw);
+  const int waves_max = device_cu_count() * rowq_blocks_per_cu(p.fn) * kRWaves;
+  p.ipw = (p.rg + waves_max - 1) / waves_max;
+  const int waves = (p.rg + p.ipw - 1) / p.ipw;
+  p.grid = (waves + kRWaves - 1) / kRWaves;
+  return p;
+}
+
+}  // namespace
+}  // namespace q4dec
+
+extern "C" int rowq_gemv(const void* w, const float* row_scale, int64_t n, int64_t k, int32_t bits,
+                         const uint16_t* x, float* y, void* stream) {
+  using namespace q4dec;
+  if (!w) return fail(Q4DEC_ERR_NULL, "rowq_gemv: w is NULL");
+  if (!row_scale) return fail(Q4DEC_ERR_NULL, "rowq_gemv: row_scale is NULL");
+  if (!x) return fail(Q4DEC_ERR_NULL, "rowq_gemv: x is NULL");
+  if (!y) return fail(Q4DEC_ERR_NULL, "rowq_gemv: y is NULL");
+  if (bits != 2 && bits != 4) return fail(Q4DEC_ERR_SHAPE, "rowq_gemv: bits must be 2 or 4 (got %d)", int(bits));
+  if (n <= 0 || n >= (int64_t(1) << 31))
+    return fail(Q4DEC_ERR_SHAPE, "rowq_gemv: n must be in [1, 2^31) (got %lld)", (long long)n);
+  const int64_t kq = bits == 2 ? 64 : 32;  // one 16-byte chunk of codes
+  if (k <= 0 || k % kq)
+    return fail(Q4DEC_ERR_SHAPE, "rowq_gemv: k must be a positive multiple of %lld for %d-bit codes (got %lld)",
+                (long long)kq, int(bits), (long long)k);
+  if (k > Q4DEC_MAX_K) return fail(Q4DEC_ERR_UNSUPPORTED, "rowq_gemv: k must be <= %d (got %lld)", Q4DEC_MAX_K,
+                                   (long long)k);
+  if (!aligned(w, 16)) return fail(Q4DEC_ERR_ALIGN, "rowq_gemv: w must be 16-byte aligned");
+  if (!aligned(x, 16)) return fail(Q4DEC_ERR_ALIGN, "rowq_gemv: x must be 16-byte aligned");
+  if (!aligned(row_scale, 4) || !aligned(y, 4))
+    return fail(Q4DEC_ERR_ALIGN, "rowq_gemv: row_scale and y must be 4-byte aligned");
+  const RPlan p = bits == 2 ? rowq_plan<2>(n, k) : rowq_plan<4>(n, k);
+  if (!p.fn) return fail(Q4DEC_ERR_UNSUPPORTED, "rowq_gemv: no kernel for k=%lld", (long long)k);
+  const uint8_t* wp = static_cast<const uint8_t*>(w);
+  int ni = int(n), ki = int(k), ipw = p.ipw;
+  void* args[] = {&wp, &row_scale, &x, &ni, &ki, &ipw, &y};
+  hipError_t e = hipLaunchKernel(p.fn, dim3(p.grid), dim3(kRThreads), args, 0, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(Q4DEC_ERR_HIP, "rowq_gemv: kernel launch failed: %s", hipGetErrorString(e));
+  return launch_status("rowq_gemv");
+}

@@ -11,7 +11,7 @@ import int4_weight_only_block_amd as q4
 pytestmark = pytest.mark.skipif(not os.path.exists(q4.LIB_PATH), reason="libq4dec.so not built")
 
 EXPECTED = {
-    "q4dec_abi_version", "q4dec_last_error", "q4_packed_bytes", "q4_pack", "q4_quantize", "q4_gemv", "q4_gemv_gelu_mul", "q4_gemv_multi",
+    "q4dec_abi_version", "q4dec_last_error", "q4_packed_bytes", "q4_pack", "q4_quantize", "q4_gemv", "q4_gemv_gelu_mul", "q4_gemv_multi", "rowq_gemv",
     "q4_gemm_s64", "q4_gemm_workspace_bytes", "lmhead_workspace_bytes", "lmhead_softcap_argmax", "ple_gather",
 }
 
@@ -123,6 +123,32 @@ def test_gemv_multi_validation():
     assert rc == q4.ERR_SHAPE and "k" in msg
     rc, msg = _rc_and_msg(L.q4_gemv_multi(None, 16, 32, FAKE, 4, FAKE, None))
     assert rc == q4.ERR_NULL and "packed" in msg
+
+
+def test_rowq_gemv_validation():
+    L = q4.lib()
+    ok = [FAKE, FAKE, 16, 128, 2, FAKE, FAKE, None]
+
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return _rc_and_msg(L.rowq_gemv(*a))
+
+    for i, name in [(0, "w"), (1, "row_scale"), (5, "x"), (6, "y")]:
+        rc, msg = call(i, None)
+        assert rc == q4.ERR_NULL and name in msg
+    rc, msg = call(4, 3)
+    assert rc == q4.ERR_SHAPE and "bits" in msg
+    rc, msg = call(3, 96)
+    assert rc == q4.ERR_SHAPE and "64" in msg  # INT2 codes come in 64-wide 16-byte chunks
+    a = list(ok); a[3] = 48; a[4] = 4
+    rc, msg = _rc_and_msg(L.rowq_gemv(*a))
+    assert rc == q4.ERR_SHAPE and "32" in msg  # INT4 in 32-wide ones
+    assert call(2, 0)[0] == q4.ERR_SHAPE
+    assert call(3, q4.MAX_K + 64)[0] == q4.ERR_UNSUPPORTED
+    assert call(0, FAKE + 8)[0] == q4.ERR_ALIGN
+    assert call(5, FAKE + 2)[0] == q4.ERR_ALIGN
+    assert call(6, FAKE + 2)[0] == q4.ERR_ALIGN
 
 
 def test_pack_validation():

@@ -197,6 +197,39 @@ def test_gemv_multi_lds_limit_and_m1():
     assert np.array_equal(y1[0], y0)
 
 
+# ---------------------------------------------- per-row INT4 / INT2 GEMV --
+def _rowq_inputs(rng, n, k, bits):
+    w = rng.integers(0, 256, size=(n, k * bits // 8), dtype=np.uint8)  # uniform codes
+    sc = rng.uniform(1e-3, 1e-2, size=n).astype(np.float32)
+    x = synth.bf16_normal(rng, k)
+    return w, sc, x
+
+
+# the mixed-bit E2B decode shapes (INT2 FFN L15-34 and the INT2 head, INT4 FFN
+# L0-14 and attention q/o), ragged row counts, and every lane split
+@pytest.mark.parametrize("bits,n,k", [(2, 12288, 1536), (2, 1536, 12288), (2, 262144, 1536), (4, 6144, 1536),
+                                      (4, 1536, 6144), (4, 2048, 1536), (4, 1536, 2048), (2, 77, 64), (4, 301, 32),
+                                      (2, 515, 4096), (4, 1000, 16384), (2, 33, 16384), (4, 129, 960)])
+def test_rowq_gemv_tolerance(bits, n, k):
+    rng = synth.rng_for(80, bits, n, k)
+    w, sc, x = _rowq_inputs(rng, n, k, bits)
+    y = q4.rowq_gemv(d(w), d(sc), n, k, bits, d(x)).cpu().numpy()
+    yr, a = oracle.rowq_gemv(w, sc, bits, x)
+    assert_within_tol(y, yr, a, f"rowq int{bits}")
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_rowq_gemv_integer_exact(bits):
+    n, k = 700, 3072
+    rng = synth.rng_for(81, bits)
+    w = rng.integers(0, 256, size=(n, k * bits // 8), dtype=np.uint8)
+    sc = np.full(n, 2.0 ** -5, dtype=np.float32)
+    xi = rng.integers(-4, 5, size=k)
+    y = q4.rowq_gemv(d(w), d(sc), n, k, bits, d(bf16_bits_of_ints(xi))).cpu().numpy()
+    codes = oracle.rowq_unpack(w, n, k, bits).astype(np.int64)
+    assert np.array_equal(y.astype(np.float64), (codes @ xi) / 32.0)
+
+
 # -------------------------------------------------------------- quantiser --
 def _quantize_gpu(x, rule):
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
@@ -484,6 +517,24 @@ def test_ple_gather_full_tables(dim):
         ref, err = oracle.ple_gather(rows, rsc, np.arange(n_ids, dtype=np.int32), 16.0)
         assert err == 0
         assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+
+
+def test_token_embedding_gather_full_table():
+    """The E2B token embedding: int8 [262144, 1536] with a per-row scale,
+    gathered rows multiplied by sqrt(1536) (the model card's 39.191837)."""
+    vocab, dim = synth.VOCAB, 1536
+    g = torch.Generator(device=DEV)
+    g.manual_seed(4321)
+    table = torch.randint(-127, 128, (vocab, dim), dtype=torch.int8, device=DEV, generator=g)
+    scale = torch.empty(vocab, dtype=torch.float32, device=DEV).uniform_(1e-3, 1e-2, generator=g)
+    ids = synth.ple_ids(synth.rng_for(5), vocab, 64)
+    ids[:3] = [0, vocab - 1, ids[7]]
+    idt = d(ids)
+    out = q4.ple_gather(table, scale, idt, 39.191837).cpu().numpy()
+    ref, err = oracle.ple_gather(table[idt.long()].cpu().numpy(), scale[idt.long()].cpu().numpy(),
+                                 np.arange(64, dtype=np.int32), 39.191837)
+    assert err == 0
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
 
 
 def test_ple_gather_general_multiplier_and_ragged_dim():
