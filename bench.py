@@ -292,42 +292,67 @@ def probe_rowq(torch, dev, seed: int, reps: int = 20):
     """Per-row symmetric INT2 GEMVs on the mobile mixed-bit kernel-probe
     workload: six INT2 FFNs (gate and up [12288, 1536], down [1536, 12288])
     and the INT2 262,144-row head [262144, 1536], 185 MB of codes per run,
-    one HIP graph. Not part of the q4_0 decode step. Bytes counted: packed
-    codes + fp32 row scales + bf16 x + fp32 y."""
+    one HIP graph. Each FFN runs as the fused gate/up GELU launch plus the
+    down GEMV (13 launches); the unfused run (gate, up and down as separate
+    GEMVs, 19 launches) is timed too. Not part of the q4_0 decode step. Bytes
+    counted: packed codes + fp32 row scales + bf16 x + the outputs."""
     import int4_weight_only_block_amd as q4
 
     g = torch.Generator(device=dev)
     g.manual_seed(seed + 4)
-    ffn = [(12288, 1536), (12288, 1536), (1536, 12288)]
-    mats = ffn * 6 + [(262144, 1536)]
-    # six distinct FFN weight sets and one head, as on the page's probe
-    ws = [torch.randint(0, 256, (n, k // 4), dtype=torch.uint8, device=dev, generator=g) for n, k in mats]
-    scs = [torch.empty(n, dtype=torch.float32, device=dev).uniform_(1e-3, 1e-2, generator=g) for n, _ in mats]
-    xs = [(torch.randn(k, device=dev, generator=g)).to(torch.bfloat16) for _, k in mats]
-    ys = [torch.empty(n, dtype=torch.float32, device=dev) for n, _ in mats]
+    H, D, V = 12288, 1536, 262144
 
-    def run():
-        for (n, k), w, sc, x, y in zip(mats, ws, scs, xs, ys):
-            q4.rowq_gemv(w, sc, n, k, 2, x, y)
+    def codes(n, k):
+        return torch.randint(0, 256, (n, k // 4), dtype=torch.uint8, device=dev, generator=g)
 
-    run()
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        run()
-    graph.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
+    def scales(n):
+        return torch.empty(n, dtype=torch.float32, device=dev).uniform_(1e-3, 1e-2, generator=g)
+
+    ffn = [(codes(2 * H, D), scales(2 * H), codes(D, H), scales(D)) for _ in range(6)]
+    head, head_sc = codes(V, D), scales(V)
+    x = torch.randn(D, device=dev, generator=g).to(torch.bfloat16)
+    a = torch.empty(H, dtype=torch.int16, device=dev)
+    gu = torch.empty(2 * H, dtype=torch.float32, device=dev)
+    y = torch.empty(D, dtype=torch.float32, device=dev)
+    logits = torch.empty(V, dtype=torch.float32, device=dev)
+
+    def run_fused():
+        for w_gu, s_gu, w_dn, s_dn in ffn:
+            q4.rowq_gemv_gelu_mul(w_gu, s_gu, 2 * H, D, 2, x, a)
+            q4.rowq_gemv(w_dn, s_dn, D, H, 2, a, y)
+        q4.rowq_gemv(head, head_sc, V, D, 2, x, logits)
+
+    def run_unfused():
+        for w_gu, s_gu, w_dn, s_dn in ffn:
+            q4.rowq_gemv(w_gu[:H], s_gu[:H], H, D, 2, x, gu[:H])
+            q4.rowq_gemv(w_gu[H:], s_gu[H:], H, D, 2, x, gu[H:])
+            q4.rowq_gemv(w_dn, s_dn, D, H, 2, a, y)
+        q4.rowq_gemv(head, head_sc, V, D, 2, x, logits)
+
+    def time_graph(fn):
+        fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
         graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    code_bytes = sum(n * k // 4 for n, k in mats)
-    b = sum(n * k // 4 + 4 * n + 2 * k + 4 * n for n, k in mats)
-    return {"workload": "int2_kprobe_6ffn_plus_head", "launches": len(mats), "ms_per_run": round(ms, 4),
-            "code_bytes": code_bytes, "bytes_per_run": b, "achieved_GBs": round(b / (ms * 1e-3) / 1e9, 1),
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms = time_graph(run_fused)
+    ms_unfused = time_graph(run_unfused)
+    code_bytes = 6 * (2 * H * D + D * H) // 4 + V * D // 4
+    b = (code_bytes + 4 * (6 * (2 * H + D) + V) + 2 * (6 * (D + H) + D)
+         + 6 * (2 * H + 4 * D) + 4 * V)
+    return {"workload": "int2_kprobe_6ffn_plus_head", "launches": 13, "ms_per_run": round(ms, 4),
+            "ms_per_run_unfused_19_launches": round(ms_unfused, 4), "code_bytes": code_bytes,
+            "bytes_per_run": b, "achieved_GBs": round(b / (ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 

@@ -150,6 +150,19 @@ int q4_gemv_multi(const void* packed, int64_t n, int64_t k, const uint16_t* x,
 int rowq_gemv(const void* w, const float* row_scale, int64_t n, int64_t k,
               int32_t bits, const uint16_t* x, float* y, void* stream);
 
+/* rowq_gemv_gelu_mul: rowq_gemv over the concatenated [gate; up] rows with
+ * the fused GELU-tanh * up epilogue (mixed-bit page: the int2 / int4
+ * symmetric gate+up kernels run gate, up, GELU and the product in one
+ * dispatch). With h = n / 2 and the rowq_gemv sums,
+ *   g_j = y[j],  u_j = y[h + j]  (each row with its own scale),
+ *   a[j] = RN_bf16(gelu(g_j) * u_j), gelu as in q4_gemv_gelu_mul, j < h.
+ *   w, row_scale, bits, x  as rowq_gemv, n rows ([gate; up]), n even.
+ *   a          bf16 bit patterns [n / 2], 2-byte aligned, caller-owned.
+ * Errors: those of rowq_gemv, n odd, k > Q4DEC_GELU_MAX_K (unsupported). */
+int rowq_gemv_gelu_mul(const void* w, const float* row_scale, int64_t n,
+                       int64_t k, int32_t bits, const uint16_t* x,
+                       uint16_t* a, void* stream);
+
 /* q4_gemv_gelu_mul: fused gate/up matvec with the GELU-tanh * up epilogue
  * (mixed-bit page, fused gate/up kernels: one launch over the concatenated
  * [gate; up] rows, fp32 tanh-form GELU in the epilogue). With h = n / 2,

@@ -46,6 +46,7 @@ _SIGNATURES = {
     "q4_gemv_gelu_mul": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "q4_gemv_multi": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p]),
     "rowq_gemv": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, ctypes.c_int32, _c_p, _c_p, _c_p]),
+    "rowq_gemv_gelu_mul": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, ctypes.c_int32, _c_p, _c_p, _c_p]),
     "q4_gemm_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
     "q4_gemm_s64": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p, ctypes.c_size_t, _c_p]),
     "lmhead_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
@@ -215,6 +216,21 @@ def rowq_gemv(w: torch.Tensor, row_scale: torch.Tensor, n: int, k: int, bits: in
     py = _dev(y, "y", _F32, n)
     _check(lib().rowq_gemv(pw, ps, n, k, int(bits), px, py, _stream(x)))
     return y
+
+
+def rowq_gemv_gelu_mul(w: torch.Tensor, row_scale: torch.Tensor, n: int, k: int, bits: int, x: torch.Tensor,
+                       a: torch.Tensor | None = None) -> torch.Tensor:
+    """a[j] = bf16(gelu_tanh(g_j) * u_j) for per-row INT2 / INT4 [gate; up]
+    rows (g = rows 0 .. n/2-1, u = rows n/2 .. n-1, each scaled by its own
+    row scale); returns bf16 bits (int16)."""
+    pw = _dev(w, "w", _BYTES, n * k * bits // 8)
+    ps = _dev(row_scale, "row_scale", _F32, n)
+    px = _dev(x, "x", _U16, k)
+    if a is None:
+        a = torch.empty(max(n // 2, 1), dtype=torch.int16, device=x.device)
+    pa = _dev(a, "a", _U16, max(n // 2, 1))
+    _check(lib().rowq_gemv_gelu_mul(pw, ps, n, k, int(bits), px, pa, _stream(x)))
+    return a
 
 
 def q4_gemv_gelu_mul(packed: torch.Tensor, n: int, k: int, x: torch.Tensor,

@@ -13,15 +13,15 @@
 // converts x once into LDS, each lane copies its blocks out, and the row loop
 // touches no LDS.
 //
-// Codes are not converted to fp16 on their own. Each field is moved into
-// mantissa bits of an fp16 whose exponent is that of 1024 (OR with 0x6400), so
-// the half holds 1024 + 2^s * u exactly, u = code + 2 (INT2) or code + 8
-// (INT4) after an XOR of the packed word. The matching activation is stored
+// Codes are not converted to fp16 on their own. Each field is read at bit
+// offset s of an fp16 whose exponent is that of 1024 (OR with 0x6400), so the
+// half holds 1024 + 2^s * u exactly, u = code + 2 (INT2) or code + 8 (INT4)
+// after an XOR of the packed word. The matching activation is stored
 // pre-multiplied by 2^-s, so the dot product yields code * x plus
 // (1024 * 2^-s + offset) * x, a term that depends on x alone: each block's sum
 // of those terms is computed once at staging and starts the block's fp32
-// accumulator with the opposite sign. Shifts s of 4 to 8 keep that term within
-// a small multiple of the codes' own contribution.
+// accumulator with the opposite sign. Offsets s of 4 to 8 keep that term
+// within about 66 times the codes' own contribution (six of fp32's 24 bits).
 #include <math.h>
 
 #include <map>
@@ -57,16 +57,21 @@ struct Fields<2> {
   static constexpr int kSecond = 8;
   static constexpr int kOffset = 2;  // u = code + 2
   __device__ static constexpr int elem(int d, int f) { return 16 * d + f; }
-  // field f sits at bits 6-7 (f even) or 8-9 (f odd) of each half
-  __device__ static constexpr int shift(int f) { return (f & 1) ? 8 : 6; }
+  // bit offset (within each half) at which field f is read: fields 0-2 from
+  // w << 4, fields 3-4 from w, fields 5-7 from w >> 6, so every field lands
+  // at bits 4-9 and two shifts serve all eight
+  __device__ static constexpr int shift(int f) { return f == 0 || f == 5 ? 4 : (f == 1 || f == 3 || f == 6) ? 6 : 8; }
   __device__ __forceinline__ static float dot(uint32_t w, const uint32_t* xp, float p, uint32_t magic) {
     w ^= 0xAAAAAAAAu;
-    const uint32_t s[4] = {w << 6, w << 2, w >> 2, w >> 6};  // fields (0,1) (2,3) (4,5) (6,7)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      p = dot2(field(s[g], 0x00C000C0u, magic), xp[2 * g], p);
-      p = dot2(field(s[g], 0x03000300u, magic), xp[2 * g + 1], p);
-    }
+    const uint32_t a = w << 4, c = w >> 6;
+    p = dot2(field(a, 0x00300030u, magic), xp[0], p);
+    p = dot2(field(a, 0x00C000C0u, magic), xp[1], p);
+    p = dot2(field(a, 0x03000300u, magic), xp[2], p);
+    p = dot2(field(w, 0x00C000C0u, magic), xp[3], p);
+    p = dot2(field(w, 0x03000300u, magic), xp[4], p);
+    p = dot2(field(c, 0x00300030u, magic), xp[5], p);
+    p = dot2(field(c, 0x00C000C0u, magic), xp[6], p);
+    p = dot2(field(c, 0x03000300u, magic), xp[7], p);
     return p;
   }
 };
@@ -135,14 +140,34 @@ __device__ __forceinline__ void stage_block(const uint16_t* __restrict__ xb, uin
   *cx = make_float2(-c, ldexpf(1.0f, e));
 }
 
-// DEPTH row groups of loads in flight per wave (1 or 2).
-template <int BITS, int LPR, int CPL, int DEPTH, bool FULL>
+enum RowqMode { kRowqGemv = 0, kRowqGelu = 1 };
+
+// fused [gate; up] epilogue: tanh-form GELU in fp32 and the bf16 rounding of
+// the product (same definitions as the q4_0 fused kernel)
+__device__ __forceinline__ float rq_gelu_tanh(float g) {
+  const float k0 = 0.7978845608028654f, k1 = 0.044715f;
+  return 0.5f * g * (1.0f + tanhf(k0 * (g + k1 * g * g * g)));
+}
+__device__ __forceinline__ uint16_t rq_bf16_rne(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x40u);
+  return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// DEPTH row groups of loads in flight per wave (1 or 2). MODE kRowqGemv
+// writes y[row] (fp32); kRowqGelu reads the n rows as [gate; up] and writes
+// bf16(gelu(g_j) * u_j) for j < n / 2: lane groups r < RPW / 2 take gate
+// rows, the others the up rows of the same outputs, so each pair of sums is
+// 32 lanes apart after the row reduction.
+template <int BITS, int LPR, int CPL, int DEPTH, int MODE, bool FULL>
 __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __restrict__ w,
                                                               const float* __restrict__ row_scale,
                                                               const uint16_t* __restrict__ x, int n, int k, int ipw,
-                                                              float* __restrict__ y) {
+                                                              void* __restrict__ out) {
   using F = Fields<BITS>;
   constexpr int RPW = 64 / LPR;
+  static_assert(MODE != kRowqGelu || RPW >= 2, "the gate/up pairing needs two rows per wave step");
+  constexpr int UPW = MODE == kRowqGelu ? RPW / 2 : RPW;  // outputs per wave step
   constexpr int BPC = BITS == 2 ? 2 : 1;  // activation blocks per 16-byte chunk
   constexpr int NB = CPL * BPC;           // blocks held by one lane
   constexpr int MAXB = LPR * NB;
@@ -154,13 +179,19 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int t = lane % LPR;
   const int r = lane / LPR;
-  const int RG = (n + RPW - 1) / RPW;
+  const int units = MODE == kRowqGelu ? n / 2 : n;
+  const int RG = (units + UPW - 1) / UPW;
   const int rg_base = blockIdx.x * kRWaves * ipw + wave;
   const size_t row_bytes = size_t(U) * 16;
   const int iters = rg_base < RG ? min(ipw, (RG - rg_base + kRWaves - 1) / kRWaves) : 0;
   auto row_of = [&](int i) {
-    const int row = (rg_base + i * kRWaves) * RPW + r;
-    return row < n ? row : n - 1;
+    if constexpr (MODE == kRowqGelu) {
+      const int v = (rg_base + i * kRWaves) * UPW + (r % UPW);
+      return (v < units ? v : units - 1) + (r / UPW) * units;
+    } else {
+      const int row = (rg_base + i * kRWaves) * RPW + r;
+      return row < n ? row : n - 1;
+    }
   };
 
   uint4 qa[CPL], qb[CPL];
@@ -237,8 +268,15 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
   };
   auto emit = [&](int i, float acc) {
     acc = group_sum<LPR>(acc);
-    const int row = (rg_base + i * kRWaves) * RPW + r;
-    if (t == 0 && row < n) y[row] = acc * row_scale[row];
+    if constexpr (MODE == kRowqGelu) {
+      const float v = acc * row_scale[row_of(i)];
+      const float up = __shfl_xor(v, 32);  // the up row's scaled sum
+      const int j = (rg_base + i * kRWaves) * UPW + r;
+      if (t == 0 && r < UPW && j < units) static_cast<uint16_t*>(out)[j] = rq_bf16_rne(rq_gelu_tanh(v) * up);
+    } else {
+      const int row = (rg_base + i * kRWaves) * RPW + r;
+      if (t == 0 && row < n) static_cast<float*>(out)[row] = acc * row_scale[row];
+    }
   };
   if constexpr (DEPTH == 1) {
     for (int i = 0; i + 1 < iters; ++i) emit(i, dot(qa, true, row_of(i + 1)));
@@ -266,11 +304,17 @@ struct RPlan {
   const void* fn;
 };
 
-// (lanes per row, chunks per lane) pairs the plan below can ask for
-template <int BITS, bool FULL>
+// (lanes per row, chunks per lane) pairs the plan below can ask for; the
+// GELU mode needs two rows per wave step, so at most 32 lanes per row
+template <int BITS, int MODE, bool FULL>
 const void* pick_rowq(int lpr, int cpl) {
-#define RQ_CASE(L, C) \
-  if (lpr == L && cpl == C) return reinterpret_cast<const void*>(&rowq_rows_kernel<BITS, L, C, 1, FULL>);
+#define RQ_CASE(L, C)                                                                                  \
+  if (lpr == L && cpl == C) {                                                                          \
+    if constexpr (MODE == kRowqGemv || L <= 32)                                                        \
+      return reinterpret_cast<const void*>(&rowq_rows_kernel<BITS, L, C, 1, MODE, FULL>);              \
+    else                                                                                               \
+      return nullptr;                                                                                  \
+  }
   if constexpr (BITS == 2) {
     RQ_CASE(8, 1) RQ_CASE(8, 2) RQ_CASE(8, 3)
     RQ_CASE(16, 2) RQ_CASE(16, 3)
@@ -301,7 +345,7 @@ int rowq_blocks_per_cu(const void* fn) {
   return nb;
 }
 
-template <int BITS>
+template <int BITS, int MODE>
 RPlan rowq_plan(int64_t n, int64_t k) {
   constexpr int BPC = BITS == 2 ? 2 : 1;
   const int U = int((k * BITS) >> 7);
@@ -317,15 +361,52 @@ RPlan rowq_plan(int64_t n, int64_t k) {
     }
   p.cpl = (U + p.lpr - 1) / p.lpr;
   const bool full = U == p.lpr * p.cpl;
-  p.fn = full ? pick_rowq<BITS, true>(p.lpr, p.cpl) : pick_rowq<BITS, false>(p.lpr, p.cpl);
+  p.fn = full ? pick_rowq<BITS, MODE, true>(p.lpr, p.cpl) : pick_rowq<BITS, MODE, false>(p.lpr, p.cpl);
   p.rpw = 64 / p.lpr;
   if (!p.fn) return p;
-  p.rg = int((n + p.rpw - 1) / p.rpw);
+  const int64_t units = MODE == kRowqGelu ? n / 2 : n;
+  const int upw = MODE == kRowqGelu ? p.rpw / 2 : p.rpw;
+  p.rg = int((units + upw - 1) / upw);
   const int waves_max = device_cu_count() * rowq_blocks_per_cu(p.fn) * kRWaves;
   p.ipw = (p.rg + waves_max - 1) / waves_max;
   const int waves = (p.rg + p.ipw - 1) / p.ipw;
   p.grid = (waves + kRWaves - 1) / kRWaves;
   return p;
+}
+
+// argument checks shared by both entry points; returns 0 or an error code
+int rowq_check(const char* name, const void* w, const float* row_scale, int64_t n, int64_t k, int32_t bits,
+               const uint16_t* x, const void* out, const char* out_name, int64_t max_k) {
+  if (!w) return fail(Q4DEC_ERR_NULL, "%s: w is NULL", name);
+  if (!row_scale) return fail(Q4DEC_ERR_NULL, "%s: row_scale is NULL", name);
+  if (!x) return fail(Q4DEC_ERR_NULL, "%s: x is NULL", name);
+  if (!out) return fail(Q4DEC_ERR_NULL, "%s: %s is NULL", name, out_name);
+  if (bits != 2 && bits != 4) return fail(Q4DEC_ERR_SHAPE, "%s: bits must be 2 or 4 (got %d)", name, int(bits));
+  if (n <= 0 || n >= (int64_t(1) << 31))
+    return fail(Q4DEC_ERR_SHAPE, "%s: n must be in [1, 2^31) (got %lld)", name, (long long)n);
+  const int64_t kq = bits == 2 ? 64 : 32;  // one 16-byte chunk of codes
+  if (k <= 0 || k % kq)
+    return fail(Q4DEC_ERR_SHAPE, "%s: k must be a positive multiple of %lld for %d-bit codes (got %lld)", name,
+                (long long)kq, int(bits), (long long)k);
+  if (k > max_k)
+    return fail(Q4DEC_ERR_UNSUPPORTED, "%s: k must be <= %lld (got %lld)", name, (long long)max_k, (long long)k);
+  if (!aligned(w, 16)) return fail(Q4DEC_ERR_ALIGN, "%s: w must be 16-byte aligned", name);
+  if (!aligned(x, 16)) return fail(Q4DEC_ERR_ALIGN, "%s: x must be 16-byte aligned", name);
+  if (!aligned(row_scale, 4)) return fail(Q4DEC_ERR_ALIGN, "%s: row_scale must be 4-byte aligned", name);
+  return 0;
+}
+
+template <int MODE>
+int rowq_launch(const char* name, const void* w, const float* row_scale, int64_t n, int64_t k, int32_t bits,
+                const uint16_t* x, void* out, void* stream) {
+  const RPlan p = bits == 2 ? rowq_plan<2, MODE>(n, k) : rowq_plan<4, MODE>(n, k);
+  if (!p.fn) return fail(Q4DEC_ERR_UNSUPPORTED, "%s: no kernel for k=%lld", name, (long long)k);
+  const uint8_t* wp = static_cast<const uint8_t*>(w);
+  int ni = int(n), ki = int(k), ipw = p.ipw;
+  void* args[] = {&wp, &row_scale, &x, &ni, &ki, &ipw, &out};
+  hipError_t e = hipLaunchKernel(p.fn, dim3(p.grid), dim3(kRThreads), args, 0, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(Q4DEC_ERR_HIP, "%s: kernel launch failed: %s", name, hipGetErrorString(e));
+  return launch_status(name);
 }
 
 }  // namespace
@@ -334,29 +415,17 @@ RPlan rowq_plan(int64_t n, int64_t k) {
 extern "C" int rowq_gemv(const void* w, const float* row_scale, int64_t n, int64_t k, int32_t bits,
                          const uint16_t* x, float* y, void* stream) {
   using namespace q4dec;
-  if (!w) return fail(Q4DEC_ERR_NULL, "rowq_gemv: w is NULL");
-  if (!row_scale) return fail(Q4DEC_ERR_NULL, "rowq_gemv: row_scale is NULL");
-  if (!x) return fail(Q4DEC_ERR_NULL, "rowq_gemv: x is NULL");
-  if (!y) return fail(Q4DEC_ERR_NULL, "rowq_gemv: y is NULL");
-  if (bits != 2 && bits != 4) return fail(Q4DEC_ERR_SHAPE, "rowq_gemv: bits must be 2 or 4 (got %d)", int(bits));
-  if (n <= 0 || n >= (int64_t(1) << 31))
-    return fail(Q4DEC_ERR_SHAPE, "rowq_gemv: n must be in [1, 2^31) (got %lld)", (long long)n);
-  const int64_t kq = bits == 2 ? 64 : 32;  // one 16-byte chunk of codes
-  if (k <= 0 || k % kq)
-    return fail(Q4DEC_ERR_SHAPE, "rowq_gemv: k must be a positive multiple of %lld for %d-bit codes (got %lld)",
-                (long long)kq, int(bits), (long long)k);
-  if (k > Q4DEC_MAX_K) return fail(Q4DEC_ERR_UNSUPPORTED, "rowq_gemv: k must be <= %d (got %lld)", Q4DEC_MAX_K,
-                                   (long long)k);
-  if (!aligned(w, 16)) return fail(Q4DEC_ERR_ALIGN, "rowq_gemv: w must be 16-byte aligned");
-  if (!aligned(x, 16)) return fail(Q4DEC_ERR_ALIGN, "rowq_gemv: x must be 16-byte aligned");
-  if (!aligned(row_scale, 4) || !aligned(y, 4))
-    return fail(Q4DEC_ERR_ALIGN, "rowq_gemv: row_scale and y must be 4-byte aligned");
-  const RPlan p = bits == 2 ? rowq_plan<2>(n, k) : rowq_plan<4>(n, k);
-  if (!p.fn) return fail(Q4DEC_ERR_UNSUPPORTED, "rowq_gemv: no kernel for k=%lld", (long long)k);
-  const uint8_t* wp = static_cast<const uint8_t*>(w);
-  int ni = int(n), ki = int(k), ipw = p.ipw;
-  void* args[] = {&wp, &row_scale, &x, &ni, &ki, &ipw, &y};
-  hipError_t e = hipLaunchKernel(p.fn, dim3(p.grid), dim3(kRThreads), args, 0, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(Q4DEC_ERR_HIP, "rowq_gemv: kernel launch failed: %s", hipGetErrorString(e));
-  return launch_status("rowq_gemv");
+  if (int rc = rowq_check("rowq_gemv", w, row_scale, n, k, bits, x, y, "y", Q4DEC_MAX_K)) return rc;
+  if (!aligned(y, 4)) return fail(Q4DEC_ERR_ALIGN, "rowq_gemv: y must be 4-byte aligned");
+  return rowq_launch<kRowqGemv>("rowq_gemv", w, row_scale, n, k, bits, x, y, stream);
+}
+
+extern "C" int rowq_gemv_gelu_mul(const void* w, const float* row_scale, int64_t n, int64_t k, int32_t bits,
+                                  const uint16_t* x, uint16_t* a, void* stream) {
+  using namespace q4dec;
+  if (int rc = rowq_check("rowq_gemv_gelu_mul", w, row_scale, n, k, bits, x, a, "a", Q4DEC_GELU_MAX_K)) return rc;
+  if (n % 2) return fail(Q4DEC_ERR_SHAPE, "rowq_gemv_gelu_mul: n must be even ([gate; up] rows, got %lld)",
+                         (long long)n);
+  if (!aligned(a, 2)) return fail(Q4DEC_ERR_ALIGN, "rowq_gemv_gelu_mul: a must be 2-byte aligned");
+  return rowq_launch<kRowqGelu>("rowq_gemv_gelu_mul", w, row_scale, n, k, bits, x, a, stream);
 }

@@ -11,7 +11,7 @@ import int4_weight_only_block_amd as q4
 pytestmark = pytest.mark.skipif(not os.path.exists(q4.LIB_PATH), reason="libq4dec.so not built")
 
 EXPECTED = {
-    "q4dec_abi_version", "q4dec_last_error", "q4_packed_bytes", "q4_pack", "q4_quantize", "q4_gemv", "q4_gemv_gelu_mul", "q4_gemv_multi", "rowq_gemv",
+    "q4dec_abi_version", "q4dec_last_error", "q4_packed_bytes", "q4_pack", "q4_quantize", "q4_gemv", "q4_gemv_gelu_mul", "q4_gemv_multi", "rowq_gemv", "rowq_gemv_gelu_mul",
     "q4_gemm_s64", "q4_gemm_workspace_bytes", "lmhead_workspace_bytes", "lmhead_softcap_argmax", "ple_gather",
 }
 
@@ -149,6 +149,28 @@ def test_rowq_gemv_validation():
     assert call(0, FAKE + 8)[0] == q4.ERR_ALIGN
     assert call(5, FAKE + 2)[0] == q4.ERR_ALIGN
     assert call(6, FAKE + 2)[0] == q4.ERR_ALIGN
+
+
+def test_rowq_gemv_gelu_mul_validation():
+    L = q4.lib()
+    ok = [FAKE, FAKE, 16, 128, 2, FAKE, FAKE, None]
+
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return _rc_and_msg(L.rowq_gemv_gelu_mul(*a))
+
+    for i, name in [(0, "w"), (1, "row_scale"), (5, "x"), (6, "a")]:
+        rc, msg = call(i, None)
+        assert rc == q4.ERR_NULL and name in msg
+    rc, msg = call(2, 15)
+    assert rc == q4.ERR_SHAPE and "even" in msg
+    rc, msg = call(3, q4.GELU_MAX_K + 64)
+    assert rc == q4.ERR_UNSUPPORTED and str(q4.GELU_MAX_K) in msg
+    assert call(4, 8)[0] == q4.ERR_SHAPE
+    assert call(3, 96)[0] == q4.ERR_SHAPE
+    assert call(6, FAKE + 1)[0] == q4.ERR_ALIGN
+    assert call(1, FAKE + 2)[0] == q4.ERR_ALIGN
 
 
 def test_pack_validation():

@@ -230,6 +230,63 @@ def test_rowq_gemv_integer_exact(bits):
     assert np.array_equal(y.astype(np.float64), (codes @ xi) / 32.0)
 
 
+# fused [gate; up] GELU on the per-row formats: the E2B INT2 and INT4 FFN
+# halves, ragged output counts, and the widest supported k
+@pytest.mark.parametrize("bits,h,k", [(2, 12288, 1536), (4, 6144, 1536), (2, 77, 64), (4, 301, 32),
+                                      (2, 515, 6144), (4, 1000, 6144), (2, 33, 4096), (4, 129, 960)])
+def test_rowq_gelu_mul_tolerance(bits, h, k):
+    rng = synth.rng_for(82, bits, h, k)
+    w, sc, x = _rowq_inputs(rng, 2 * h, k, bits)
+    bits_out = q4.rowq_gemv_gelu_mul(d(w), d(sc), 2 * h, k, bits, d(x)).cpu().numpy().view(np.uint16)
+    got = oracle.bf16_bits_to_f64(bits_out)
+    a, g, u, ag, au = oracle.rowq_gelu_mul(w, sc, bits, x)
+    tol = oracle.gelu_mul_tolerance(g, u, ag, au)
+    bad = np.nonzero(~(np.abs(got - a) <= tol))[0]
+    assert bad.size == 0, (f"{bad.size} of {h} over the bound, first {bad[:5]}, "
+                           f"got {got[bad[:3]]} want {a[bad[:3]]} tol {tol[bad[:3]]}")
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_rowq_gelu_mul_integer_inputs_match_host_epilogue(bits):
+    """Power-of-two row scales and x in {-1, 0, 1}: g and u are exact in fp32
+    on both sides, so the result may differ from the host fp32 GELU-tanh
+    product rounded to bf16 only through the two tanh implementations. The
+    scale 2^-8 keeps |g| below about 3: far down the negative tail (g near
+    -10) fp32's 1 + tanh cancels to a few bits and two correct fp32 GELUs
+    part by many ulps, which the tolerance test above covers instead."""
+    h, k = 4096, 1536
+    rng = synth.rng_for(83, bits)
+    w = rng.integers(0, 256, size=(2 * h, k * bits // 8), dtype=np.uint8)
+    sc = np.full(2 * h, 2.0 ** -8, dtype=np.float32)
+    x = bf16_bits_of_ints(rng.integers(-1, 2, size=k))
+    got = q4.rowq_gemv_gelu_mul(d(w), d(sc), 2 * h, k, bits, d(x)).cpu().numpy().view(np.uint16)
+    _, g, u, _, _ = oracle.rowq_gelu_mul(w, sc, bits, x)
+    assert np.all(g.astype(np.float32) == g) and np.all(u.astype(np.float32) == u)
+    want = oracle.ffn_down_input_bits(g.astype(np.float32), u.astype(np.float32))
+    diff = np.abs(got.astype(np.int32) - want.astype(np.int32))
+    same_sign = (got >> 15) == (want >> 15)
+    assert np.all(same_sign | (diff == 0) | (np.abs(oracle.bf16_bits_to_f64(want)) < 1e-30))
+    assert diff.max() <= 1, diff.max()
+    assert np.mean(diff == 0) > 0.99
+
+
+def test_rowq_int2_ffn_chain():
+    """One E2B INT2 FFN layer (gate and up [12288, 1536], down [1536, 12288])
+    as the fused launch plus the down GEMV on its bf16 output; the down GEMV
+    is checked against the oracle fed the GPU's own a."""
+    rng = synth.rng_for(84)
+    w_gu, sc_gu, x = _rowq_inputs(rng, 2 * 12288, 1536, 2)
+    w_dn = rng.integers(0, 256, size=(1536, 12288 // 4), dtype=np.uint8)
+    sc_dn = rng.uniform(1e-3, 1e-2, size=1536).astype(np.float32)
+    a_gpu = q4.rowq_gemv_gelu_mul(d(w_gu), d(sc_gu), 2 * 12288, 1536, 2, d(x))
+    y = q4.rowq_gemv(d(w_dn), d(sc_dn), 1536, 12288, 2, a_gpu).cpu().numpy()
+    a_bits = a_gpu.cpu().numpy().view(np.uint16)
+    a, g, u, ag, au = oracle.rowq_gelu_mul(w_gu, sc_gu, 2, x)
+    assert np.all(np.abs(oracle.bf16_bits_to_f64(a_bits) - a) <= oracle.gelu_mul_tolerance(g, u, ag, au))
+    yr, am = oracle.rowq_gemv(w_dn, sc_dn, 2, a_bits)
+    assert_within_tol(y, yr, am, "rowq int2 down")
+
+
 # -------------------------------------------------------------- quantiser --
 def _quantize_gpu(x, rule):
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
