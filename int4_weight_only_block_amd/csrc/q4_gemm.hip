@@ -66,7 +66,9 @@ static GemmPlan gemm_plan(int64_t n, int64_t k) {
 // One workgroup per token slot: find the token's largest exponent, convert
 // its row to scaled fp16, store 2^E. Slots >= n_tok are zero-filled. Rows are
 // read and written 8 values (16 bytes) at a time (x is 16-byte aligned and
-// k % 32 == 0).
+// k % 32 == 0); a thread keeps its at most kPrepVec vectors in registers
+// between the exponent scan and the conversion, so the row is read once.
+constexpr int kPrepVec = Q4DEC_MAX_K / 8 / 256;
 __global__ __launch_bounds__(256) void gemm_x_prep_kernel(const uint16_t* __restrict__ x, int k, int n_tok,
                                                           _Float16* __restrict__ xh, float* __restrict__ xf) {
   const int s = blockIdx.x;
@@ -78,10 +80,16 @@ __global__ __launch_bounds__(256) void gemm_x_prep_kernel(const uint16_t* __rest
     return;
   }
   const uint4* s4 = reinterpret_cast<const uint4*>(x + size_t(s) * size_t(k));
+  uint4 v[kPrepVec];
+#pragma unroll
+  for (int r = 0; r < kPrepVec; ++r) {
+    const int i = threadIdx.x + 256 * r;
+    v[r] = i < k8 ? s4[i] : make_uint4(0u, 0u, 0u, 0u);
+  }
   uint32_t emax = 1;
-  for (int i = threadIdx.x; i < k8; i += 256) {
-    const uint4 v = s4[i];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int r = 0; r < kPrepVec; ++r) {
+    const uint32_t w[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
 #pragma unroll
     for (int j = 0; j < 4; ++j) emax = max(emax, max((w[j] >> 7) & 0xFFu, (w[j] >> 23) & 0xFFu));
   }
@@ -91,9 +99,11 @@ __global__ __launch_bounds__(256) void gemm_x_prep_kernel(const uint16_t* __rest
   __syncthreads();
   emax = max(max(wm[0], wm[1]), max(wm[2], wm[3]));
   const int e = int(emax) - 127 - 14;
-  for (int i = threadIdx.x; i < k8; i += 256) {
-    const uint4 v = s4[i];
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int r = 0; r < kPrepVec; ++r) {
+    const int i = threadIdx.x + 256 * r;
+    if (i >= k8) break;
+    const uint32_t w[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
     uint32_t o[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -174,51 +184,61 @@ __device__ __forceinline__ void split_scale(uint32_t dbits, half2_t& hi, half2_t
   lo = half2_t{l, l};
 }
 
+// Activation tiles of step (g, j): the 4 token tiles' A operands.
+__device__ __forceinline__ void load_a(half8_t (&a)[4], const uint4 (*xs)[kTok][4], int g, int j, int q, int col) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int tok = 16 * m + col;
+    a[m] = __builtin_bit_cast(half8_t, xs[4 * g + q][tok][xslot(tok, j)]);
+  }
+}
+
 // One chunk on the matrix cores: 2 groups x 4 k-slices x kSub column tiles x
-// 4 token tiles x (hi, lo), accumulated into t.
+// 4 token tiles x (hi, lo), accumulated into t. The A operands of the next
+// step are read from LDS before this step's products are issued, so the LDS
+// latency runs under the matrix-core work.
 __device__ __forceinline__ void mma_chunk(float4_t (&t)[kSub][4], const uint4 (&w)[kSub][2],
                                           const uint32_t (&sd)[kSub][2], const int (&shift)[kSub],
                                           const uint4 (*xs)[kTok][4], int q, int col, int ngroups,
                                           uint32_t m_lo, uint32_t m_hi, uint32_t magic) {
+  half8_t a0[4], a1[4];
+  load_a(a0, xs, 0, 0, q, col);
+  half2_t dh[kSub], dl[kSub];
 #pragma unroll
-  for (int g = 0; g < 2; ++g) {
+  for (int st = 0; st < 8; ++st) {
+    const int g = st >> 2, j = st & 3;
     if (g >= ngroups) break;
-    half2_t dh[kSub], dl[kSub];
-#pragma unroll
-    for (int u = 0; u < kSub; ++u) {
-      uint32_t dbits = sd[u][g];
-      if (shift[u] > 0) {  // rare: rows with scales >= 2^11
-        const float df = ldexpf(float(__builtin_bit_cast(_Float16, uint16_t(dbits))), -shift[u]);
-        dbits = __builtin_bit_cast(uint16_t, (_Float16)df);
-      }
-      split_scale(dbits, dh[u], dl[u]);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      half8_t a[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int tok = 16 * m + col;
-        a[m] = __builtin_bit_cast(half8_t, xs[4 * g + q][tok][xslot(tok, j)]);
-      }
+    half8_t(&cur)[4] = (st & 1) ? a1 : a0;
+    half8_t(&nxt)[4] = (st & 1) ? a0 : a1;
+    // the tiles past the last used group are valid LDS, read and ignored
+    if (st + 1 < 8) load_a(nxt, xs, (st + 1) >> 2, (st + 1) & 3, q, col);
+    if (j == 0) {
 #pragma unroll
       for (int u = 0; u < kSub; ++u) {
-        const uint32_t wd = j == 0 ? w[u][g].x : j == 1 ? w[u][g].y : j == 2 ? w[u][g].z : w[u][g].w;
-        const CodePairs cp = unpack_dword(wd, m_lo, m_hi, magic);
-        half8_t bh, bl;
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const half2_t ph = cp.p[jj] * dh[u];
-          const half2_t pl = cp.p[jj] * dl[u];
-          bh[2 * jj] = ph[0]; bh[2 * jj + 1] = ph[1];
-          bl[2 * jj] = pl[0]; bl[2 * jj + 1] = pl[1];
+        uint32_t dbits = sd[u][g];
+        if (shift[u] > 0) {  // rare: rows with scales >= 2^11
+          const float df = ldexpf(float(__builtin_bit_cast(_Float16, uint16_t(dbits))), -shift[u]);
+          dbits = __builtin_bit_cast(uint16_t, (_Float16)df);
         }
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          t[u][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[m], bh, t[u][m], 0, 0, 0);
-          t[u][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[m], bl, t[u][m], 0, 0, 0);
-        }
+        split_scale(dbits, dh[u], dl[u]);
       }
+    }
+#pragma unroll
+    for (int u = 0; u < kSub; ++u) {
+      const uint32_t wd = j == 0 ? w[u][g].x : j == 1 ? w[u][g].y : j == 2 ? w[u][g].z : w[u][g].w;
+      const CodePairs cp = unpack_dword(wd, m_lo, m_hi, magic);
+      half8_t bh, bl;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const half2_t ph = cp.p[jj] * dh[u];
+        const half2_t pl = cp.p[jj] * dl[u];
+        bh[2 * jj] = ph[0]; bh[2 * jj + 1] = ph[1];
+        bl[2 * jj] = pl[0]; bl[2 * jj + 1] = pl[1];
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) t[u][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[m], bh, t[u][m], 0, 0, 0);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) t[u][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[m], bl, t[u][m], 0, 0, 0);
     }
   }
 }
@@ -256,6 +276,14 @@ __global__ __launch_bounds__(256) void q4_gemm_kernel(const uint8_t* __restrict_
   asm volatile("v_mov_b32 %0, 0x000F000F" : "=v"(m_lo));
   asm volatile("v_mov_b32 %0, 0x00F000F0" : "=v"(m_hi));
   asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+
+  // the lane's 16 token factors, loaded now so they arrive under the main
+  // loop instead of one dependent load per output at the end
+  float tf[16];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tf[4 * m + i] = xf[16 * m + 4 * q + i];
 
   float4_t acc[kSub][4];
 #pragma unroll
@@ -313,7 +341,7 @@ __global__ __launch_bounds__(256) void q4_gemm_kernel(const uint8_t* __restrict_
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int s = 16 * m + 4 * q + i;
-        const float v = acc[u][m][i] * (xf[s] * rf);
+        const float v = acc[u][m][i] * (tf[4 * m + i] * rf);
         if (PARTIAL) {
           out[(size_t(blockIdx.y) * kTok + s) * size_t(n) + rows[u]] = v;
         } else if (s < n_tok) {
@@ -330,8 +358,19 @@ __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restric
   const size_t total = size_t(n_tok) * size_t(n);
   const size_t stride = size_t(kTok) * size_t(n);
   for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < total; i += size_t(gridDim.x) * 256) {
+    // slices added left to right; the loads of four slices are issued
+    // before their adds so they are in flight together
     float v = part[i];
-    for (int sl = 1; sl < slices; ++sl) v += part[size_t(sl) * stride + i];
+    int sl = 1;
+    for (; sl + 4 <= slices; sl += 4) {
+      const float a = part[size_t(sl) * stride + i], b = part[size_t(sl + 1) * stride + i];
+      const float c = part[size_t(sl + 2) * stride + i], d = part[size_t(sl + 3) * stride + i];
+      v += a;
+      v += b;
+      v += c;
+      v += d;
+    }
+    for (; sl < slices; ++sl) v += part[size_t(sl) * stride + i];
     y[i] = v;
   }
 }
