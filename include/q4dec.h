@@ -123,13 +123,17 @@ int q4_gemv(const void* packed, int64_t n, int64_t k, const uint16_t* x,
  * y[v, r] = sum_k c[r,k] * d[r,k/32] * x[v, k] (fp32 accumulation), with the
  * weights read once for all m (E2B card: a speculative verify of 4 rows reads
  * the weights once; mixed-bit page: the FFN and head dominate such a step).
- * Same numerics per vector as q4_gemv; m = 1 is q4_gemv.
+ * m = 1 is q4_gemv. For m >= 2 the products run on the matrix cores: each
+ * vector is converted once to fp16 scaled by one power of two (its largest
+ * value lands in [2^14, 2^15)), codes times activations accumulate in fp32
+ * per block, and each block sum is scaled by d; results are within the
+ * q4_gemv bar of the exact sums.
  *   packed  from q4_pack with the same (n, k); 16-byte aligned.
  *   x       bf16 [m, k] row-major, 16-byte aligned.
  *   y       fp32 [m, n] row-major, 4-byte aligned, caller-owned.
  * Errors: NULL pointer, n or k as q4_gemv, m not in [1, 8], misalignment;
- *         unsupported when the m staged vectors (m * k * 2.125 bytes) do not
- *         fit in one workgroup's LDS. */
+ *         unsupported when the staged vectors (4 * ceil(m / 4) rows of
+ *         (k + 8) fp16 values) do not fit in one workgroup's LDS. */
 int q4_gemv_multi(const void* packed, int64_t n, int64_t k, const uint16_t* x,
                   int64_t m, float* y, void* stream);
 

@@ -88,62 +88,6 @@ struct Lane {
     }
     return acc;
   }
-
-  // Dot products of the row group against m <= kMaxVecs activation vectors
-  // in LDS (vector v at xs + v * xstride, its block factors at
-  // xf + v * fstride): the codes of a block are unpacked once and reused for
-  // every vector. REFILL as in dot().
-  template <bool REFILL, int NV>
-  __device__ __forceinline__ void dot_multi(const uint8_t* __restrict__ nib, const uint16_t* __restrict__ scl,
-                                            const uint32_t* __restrict__ xs, int xstride,
-                                            const float* __restrict__ xf, int fstride, int m, float (&acc)[NV],
-                                            int row_next, int t, int B, size_t row_bytes, uint32_t m_lo,
-                                            uint32_t m_hi, uint32_t magic) {
-    const u32x4* np = reinterpret_cast<const u32x4*>(nib + size_t(row_next) * row_bytes);
-    const uint16_t* sp = scl + size_t(row_next) * size_t(B);
-    // The LDS addresses of every (vector, block, quarter) are the same for
-    // every row group; left free, the compiler computes all of them once
-    // before the row loop and holds them in VGPRs (some 200 at 8 vectors),
-    // which costs most of the occupancy. Making the strides opaque here
-    // keeps each address next to its read.
-    asm volatile("" : "+s"(xstride), "+s"(fstride));
-#pragma unroll
-    for (int v = 0; v < NV; ++v) acc[v] = 0.0f;
-#pragma unroll
-    for (int j = 0; j < BPL; ++j) {
-      const int b = j * LPR + t;
-      if (FULL || b < B) {
-        CodePairs cp[4];
-        cp[0] = unpack_dword(q[j].x, m_lo, m_hi, magic);
-        cp[1] = unpack_dword(q[j].y, m_lo, m_hi, magic);
-        cp[2] = unpack_dword(q[j].z, m_lo, m_hi, magic);
-        cp[3] = unpack_dword(q[j].w, m_lo, m_hi, magic);
-        const float d = float(__builtin_bit_cast(_Float16, uint16_t(s[j])));
-#pragma unroll
-        for (int v = 0; v < NV; ++v) {
-          if (v < m) {  // wave-uniform
-            const uint4* s4 = reinterpret_cast<const uint4*>(xs + v * xstride + 16 * b);
-            float p = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const uint4 xv = s4[i ^ (b & 3)];
-              const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-#pragma unroll
-              for (int jj = 0; jj < 4; ++jj)
-                p = __builtin_amdgcn_fdot2(cp[i].p[jj], __builtin_bit_cast(half2_t, xw[jj]), p, false);
-            }
-            acc[v] = fmaf(d * p, xf[v * fstride + b], acc[v]);
-          }
-        }
-        if constexpr (REFILL) {
-          __builtin_amdgcn_sched_barrier(0);
-          const u32x4 nv = __builtin_nontemporal_load(np + b);
-          q[j] = make_uint4(nv.x, nv.y, nv.z, nv.w);
-          s[j] = sp[b];
-        }
-      }
-    }
-  }
 };
 
 // Most activation vectors one multi-vector GEMV launch takes.
@@ -357,74 +301,6 @@ __global__ __launch_bounds__(kReduceThreads) void lmhead_reduce_kernel(const uin
   }
 }
 
-// Multi-vector GEMV: y[v, r] = W[r, :] . x[v, :] for v < m <= kMaxVecs, the
-// weights streamed once for all m vectors (the same lane mapping and refill
-// as q4_rows_kernel; activations staged per workgroup into dynamic LDS, m
-// vectors of B blocks).
-template <int LPR, int BPL, bool FULL>
-__global__ __launch_bounds__(kThreads) void q4_rows_multi_kernel(const uint8_t* __restrict__ nib,
-                                                                 const uint16_t* __restrict__ scl,
-                                                                 const uint16_t* __restrict__ x, int n, int k, int m,
-                                                                 int ipw, float* __restrict__ y) {
-  constexpr int RPW = 64 / LPR;
-  extern __shared__ uint32_t dyn_lds[];
-  const int B = k >> 5;
-  uint32_t* xs = dyn_lds;                                  // [m][B * 16], quarters swizzled
-  float* xf = reinterpret_cast<float*>(dyn_lds + m * B * 16);  // [m][B]
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int t = lane % LPR;
-  const int r = lane / LPR;
-  const int RG = (n + RPW - 1) / RPW;
-  const int rg_base = blockIdx.x * kWaves * ipw + wave;
-  const size_t row_bytes = size_t(k) >> 1;
-  const int iters = rg_base < RG ? min(ipw, (RG - rg_base + kWaves - 1) / kWaves) : 0;
-  auto row_of = [&](int i) {
-    const int row = (rg_base + i * kWaves) * RPW + r;
-    return row < n ? row : n - 1;
-  };
-
-  Lane<LPR, BPL, FULL> L;
-  if (iters > 0) L.load(nib, scl, row_of(0), t, B, row_bytes);
-
-  for (int idx = threadIdx.x; idx < m * B; idx += kThreads) {
-    const int v = idx / B, b = idx - v * B;
-    uint32_t tmp[16];
-    xf[v * B + b] = convert_x_block(x + size_t(v) * size_t(k) + 32 * b, tmp);
-    uint4* d4 = reinterpret_cast<uint4*>(xs + v * B * 16 + 16 * b);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) d4[i ^ (b & 3)] = make_uint4(tmp[4 * i], tmp[4 * i + 1], tmp[4 * i + 2], tmp[4 * i + 3]);
-  }
-  __syncthreads();
-
-  uint32_t m_lo, m_hi, magic;
-  asm volatile("v_mov_b32 %0, 0x000F000F" : "=v"(m_lo));
-  asm volatile("v_mov_b32 %0, 0x00F000F0" : "=v"(m_hi));
-  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
-
-  float acc[kMaxVecs];
-  auto emit = [&](int i) {
-    const int row = (rg_base + i * kWaves) * RPW + r;
-#pragma unroll
-    for (int v = 0; v < kMaxVecs; ++v) {
-      if (v < m) {
-        const float sum = group_sum<LPR>(acc[v]);
-        if (t == 0 && row < n) y[size_t(v) * size_t(n) + row] = sum;
-      }
-    }
-  };
-  for (int i = 0; i + 1 < iters; ++i) {
-    L.template dot_multi<true, kMaxVecs>(nib, scl, xs, B * 16, xf, B, m, acc, row_of(i + 1), t, B, row_bytes, m_lo,
-                                         m_hi, magic);
-    emit(i);
-  }
-  if (iters > 0) {
-    L.template dot_multi<false, kMaxVecs>(nib, scl, xs, B * 16, xf, B, m, acc, 0, t, B, row_bytes, m_lo, m_hi,
-                                          magic);
-    emit(iters - 1);
-  }
-}
-
 // ---------------------------------------------------------------- dispatch
 struct Plan {
   int lpr, bpl, rpw, rg, ipw, grid;
@@ -448,17 +324,6 @@ static const void* pick_kernel(int lpr, int bpl) {
   Q4_CASE(16, 1) Q4_CASE(16, 2) Q4_CASE(16, 3) Q4_CASE(16, 4) Q4_CASE(16, 5)
   Q4_CASE(32, 2) Q4_CASE(32, 3) Q4_CASE(32, 4) Q4_CASE(32, 5) Q4_CASE(32, 6)
   Q4_CASE(64, 1) Q4_CASE(64, 2) Q4_CASE(64, 3) Q4_CASE(64, 4) Q4_CASE(64, 5) Q4_CASE(64, 6) Q4_CASE(64, 7) Q4_CASE(64, 8)
-#undef Q4_CASE
-  return nullptr;
-}
-
-template <bool FULL>
-static const void* pick_multi_kernel(int lpr, int bpl) {
-#define Q4_CASE(L, BP) \
-  if (lpr == L && bpl == BP) return reinterpret_cast<const void*>(&q4_rows_multi_kernel<L, BP, FULL>);
-  Q4_CASE(16, 1) Q4_CASE(16, 2) Q4_CASE(16, 3) Q4_CASE(16, 4) Q4_CASE(16, 5)
-  Q4_CASE(32, 3) Q4_CASE(32, 4) Q4_CASE(32, 5) Q4_CASE(32, 6)
-  Q4_CASE(64, 3) Q4_CASE(64, 4) Q4_CASE(64, 5) Q4_CASE(64, 6) Q4_CASE(64, 7) Q4_CASE(64, 8)
 #undef Q4_CASE
   return nullptr;
 }
@@ -638,45 +503,6 @@ extern "C" int q4_gemv_gelu_mul(const void* packed, int64_t n, int64_t k, const 
 
 namespace q4dec {
 
-// LDS of a multi-vector launch: m vectors of B blocks as fp16 pairs plus
-// their block factors.
-static size_t multi_lds_bytes(int m, int B) { return size_t(m) * size_t(B) * (64 + 4); }
-
-static Plan make_multi_plan(int64_t n, int64_t k, int m) {
-  const int B = int(k / 32);
-  int lpr = 64;
-  if ((B + 15) / 16 <= 5) {
-    lpr = 16;
-  } else if ((B + 31) / 32 <= 6) {
-    lpr = 32;
-  }
-  Plan p{};
-  p.lpr = lpr;
-  p.bpl = (B + lpr - 1) / lpr;
-  p.full = (B == lpr * p.bpl);
-  p.fn = p.full ? pick_multi_kernel<true>(lpr, p.bpl) : pick_multi_kernel<false>(lpr, p.bpl);
-  p.rpw = 64 / lpr;
-  if (!p.fn) return p;
-  p.rg = int((n + p.rpw - 1) / p.rpw);
-  const int cus = device_cu_count();
-  const int waves_max = cus * blocks_per_cu(p.fn, multi_lds_bytes(m, B)) * kWaves;
-  p.ipw = (p.rg + waves_max - 1) / waves_max;
-  // the per-workgroup staging is m times that of q4_gemv: as there, one-row
-  // waves walk up to three rows while the grid covers most of the CUs
-  if (p.rpw == 1 && p.ipw < 3) {
-    for (int want = 3; want > p.ipw; --want) {
-      const int64_t grid = ((p.rg + want - 1) / want + kWaves - 1) / kWaves;
-      if (grid * 5 >= int64_t(cus) * 4) {
-        p.ipw = want;
-        break;
-      }
-    }
-  }
-  const int waves = (p.rg + p.ipw - 1) / p.ipw;
-  p.grid = (waves + kWaves - 1) / kWaves;
-  return p;
-}
-
 }  // namespace q4dec
 
 extern "C" int q4_gemv_multi(const void* packed, int64_t n, int64_t k, const uint16_t* x, int64_t m, float* y,
@@ -689,17 +515,11 @@ extern "C" int q4_gemv_multi(const void* packed, int64_t n, int64_t k, const uin
   if (!y) return fail(Q4DEC_ERR_NULL, "q4_gemv_multi: y is NULL");
   if (!aligned(y, 4)) return fail(Q4DEC_ERR_ALIGN, "q4_gemv_multi: y must be 4-byte aligned");
   if (m == 1) return q4_gemv(packed, n, k, x, y, stream);
-  const size_t lds = multi_lds_bytes(int(m), int(k / 32));
+  const size_t lds = multi_mfma_lds_bytes(int(m), k);
   if (lds > max_lds_per_block())
     return fail(Q4DEC_ERR_UNSUPPORTED, "q4_gemv_multi: m * k too large (%zu bytes of LDS, device allows %zu)", lds,
                 max_lds_per_block());
-  const Plan p = make_multi_plan(n, k, int(m));
-  if (!p.fn) return fail(Q4DEC_ERR_UNSUPPORTED, "q4_gemv_multi: no kernel for k=%lld", (long long)k);
   const uint8_t* nib = static_cast<const uint8_t*>(packed);
   const uint16_t* scl = reinterpret_cast<const uint16_t*>(nib + nib_plane_bytes(n, k));
-  int ni = int(n), ki = int(k), mi = int(m), ipw = p.ipw;
-  void* args[] = {&nib, &scl, &x, &ni, &ki, &mi, &ipw, &y};
-  hipError_t e = hipLaunchKernel(p.fn, dim3(p.grid), dim3(kThreads), args, lds, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) return fail(Q4DEC_ERR_HIP, "q4_gemv_multi: kernel launch failed: %s", hipGetErrorString(e));
-  return launch_status("q4_gemv_multi");
+  return multi_mfma_launch(nib, scl, n, k, x, int(m), y, static_cast<hipStream_t>(stream));
 }

@@ -27,6 +27,12 @@ inline size_t nib_plane_bytes(int64_t n, int64_t k) { return align256(size_t(n) 
 inline size_t scale_plane_bytes(int64_t n, int64_t k) { return align256(size_t(n) * size_t(k / 32) * 2); }
 inline size_t rexp_plane_bytes(int64_t n) { return align256(size_t(n)); }
 
+// Multi-vector GEMV on the matrix cores (q4_multi.hip), for 2 <= m <= 8:
+// dynamic LDS it needs, and the launch (arguments already validated).
+size_t multi_mfma_lds_bytes(int m, int64_t k);
+int multi_mfma_launch(const uint8_t* nib, const uint16_t* scl, int64_t n, int64_t k, const uint16_t* x, int m,
+                      float* y, hipStream_t stream);
+
 inline int launch_status(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(Q4DEC_ERR_HIP, "%s: kernel launch failed: %s", what, hipGetErrorString(e));
