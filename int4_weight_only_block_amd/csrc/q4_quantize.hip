@@ -3,8 +3,8 @@
 // weights section: q4_0 is per-block-32 absmax symmetric int4 on the ggml
 // q4_0 grid; "visible-cx/gemma-4-E2B-CoreAI", Provenance: the int4 rounding
 // happens at export). One thread quantises one 32-wide block; every step is
-// fp32 with correctly rounded division, so each code is the same integer a
-// host evaluating the same steps gets.
+// fp32 and each code is rint of the correctly rounded quotient, the same
+// integer a host evaluating the same steps gets.
 #include "q4dec_internal.h"
 
 namespace q4dec {
@@ -47,13 +47,27 @@ __global__ __launch_bounds__(256) void q4_quantize_kernel(const uint16_t* __rest
   const float d32 = float(__builtin_bit_cast(_Float16, dbits));
   const bool usable = d32 == d32 && fabsf(d32) <= 65504.0f && d32 != 0.0f;
   const float lo = rule == 0 ? -8.0f : -7.0f;
+  // The code is rint of the correctly rounded quotient. |x / d16| <= 8.004
+  // on both grids, so t = x * RN(1 / d16) lies within 1.5e-6 of RN(x / d16)
+  // (two roundings of 2^-24 relative each) and has the same rint unless its
+  // fraction is within 4e-6 of one half; only then is the division done.
+  const float rcp = usable ? __fdiv_rn(1.0f, d32) : 0.0f;
   uint32_t packed[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     uint32_t word = 0;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      float q = usable ? rintf(__fdiv_rn(v[4 * i + b], d32)) : 0.0f;
+      const float xv = v[4 * i + b];
+      float t = xv * rcp;
+      const bool near_half = fabsf(t - floorf(t) - 0.5f) < 4e-6f;
+      // wave-uniform test, so the division runs only in the rare waves
+      // that need it (a per-lane branch is turned into computing both)
+      if (__builtin_amdgcn_ballot_w64(near_half) != 0) {
+        asm volatile("" ::: "memory");  // keeps the division inside the branch
+        if (near_half) t = __fdiv_rn(xv, d32);
+      }
+      float q = usable ? rintf(t) : 0.0f;
       q = q != q ? 0.0f : fminf(fmaxf(q, lo), 7.0f);
       word |= (uint32_t(int32_t(q)) & 0xFFu) << (8 * b);
     }
