@@ -321,6 +321,15 @@ def test_quantize_special_blocks(rule):
     x[3, 0:32] = b(1.0)
     x[3, 33] = 0x7FC0                                                 # NaN in block 1
     x[3, 64] = 0x7F70                                                 # scale overflows fp16
+    # exact ties x / d16 = j + 1/2 with d16 = 31/64, whose reciprocal is not
+    # exact (x * RN(1/d) lands a few ulps off the half): block 2 of row 1 has
+    # q4_0's scale (largest magnitude -3.875), block 3 the absmax/7 one
+    # (largest 217/64)
+    halves = [s * (2 * j + 1) * 31 / 128 for j in range(4) for s in (1, -1)]
+    x[1, 64] = b(-3.875)
+    x[1, 65:73] = [b(v) for v in halves]
+    x[1, 96] = b(217 / 64)
+    x[1, 97:105] = [b(v) for v in halves]
     c, sc, err = _quantize_gpu(x, rule)
     rc, rs, rf = oracle.q4_quantize(x, rule)
     assert np.array_equal(sc, rs)
