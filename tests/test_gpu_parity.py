@@ -629,7 +629,10 @@ def test_ple_gather_out_of_range_ids():
 
 # ----------------------------------------------------------- S=64 GEMM --
 @pytest.mark.parametrize("n,k,n_tok", [(1536, 1536, 64), (64, 32, 64), (100, 96, 1), (300, 2560, 37),
-                                       (3072, 2560, 64), (2560, 10240, 64), (77, 16384, 5)])
+                                       (3072, 2560, 64), (2560, 10240, 64), (77, 16384, 5),
+                                       # >= 128 row tiles: one K slice, no reduce (E4B gate+up; a
+                                       # ragged last tile)
+                                       (20480, 2560, 64), (16400, 512, 17)])
 def test_gemm_s64_tolerance(n, k, n_tok):
     rng = synth.rng_for(20, n, k, n_tok)
     codes, sb = synth.q4_weights(rng, n, k)
