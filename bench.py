@@ -219,40 +219,57 @@ def probe_kernels(torch, wl: Workload, reps: int = 20):
 
 
 def probe_verify_m4(torch, wl: Workload, seed: int, reps: int = 10):
-    """The 168 layer GEMVs of the step with m = 4 activation vectors each
-    (q4_gemv_multi: a 4-token verify reads every weight once), one HIP
-    graph; reported as ms per pass and weight bytes/s. Not part of the
-    decode step."""
+    """A 4-token verify pass: the 168 layer GEMVs with m = 4 activation
+    vectors each (q4_gemv_multi: every weight read once for the 4 tokens)
+    and the head for the same 4 vectors with softcap and per-vector argmax
+    (lmhead_softcap_argmax_multi), one HIP graph; reported as ms per pass,
+    the head alone in us, and weight bytes/s. Not part of the decode step."""
     import int4_weight_only_block_amd as q4
     import synth
 
-    g = torch.Generator(device=wl.xs[0].device)
+    dev = wl.xs[0].device
+    g = torch.Generator(device=dev)
     g.manual_seed(seed + 3)
     mats = wl.mats[:-1]
-    xs4 = [synth.torch_bf16_normal(g, (4, k), wl.xs[0].device) for _, n, k in mats]
-    ys4 = [torch.empty((4, n), dtype=torch.float32, device=wl.xs[0].device) for _, n, k in mats]
+    _, vocab, kh = wl.mats[-1]
+    xs4 = [synth.torch_bf16_normal(g, (4, k), dev) for _, n, k in mats]
+    ys4 = [torch.empty((4, n), dtype=torch.float32, device=dev) for _, n, k in mats]
+    xh4 = synth.torch_bf16_normal(g, (4, kh), dev)
+    ws = torch.empty(q4.lmhead_multi_workspace_bytes(vocab, kh, 4), dtype=torch.uint8, device=dev)
+    idx = torch.empty(4, dtype=torch.int32, device=dev)
+    val = torch.empty(4, dtype=torch.float32, device=dev)
+
+    def head():
+        q4.lmhead_softcap_argmax_multi(wl.packed[-1], vocab, kh, xh4, 30.0, ws, idx, val)
 
     def run():
         for i, (_, n, k) in enumerate(mats):
             q4.q4_gemv_multi(wl.packed[i], n, k, xs4[i], ys4[i])
+        head()
 
-    run()
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        run()
-    graph.replay()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(reps):
+    def time_graph(fn, r):
+        fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
         graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    wb = sum(weight_bytes(n, k) for _, n, k in mats)
-    return {"m": 4, "launches": len(mats), "ms_per_pass": round(ms, 4), "weight_bytes": wb,
-            "weight_GBs": round(wb / (ms * 1e-3) / 1e9, 1), "frac_of_hbm_peak": round(wb / (ms * 1e-3) / 8e12, 4)}
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(r):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / r
+
+    ms = time_graph(run, reps)
+    head_us = time_graph(head, 10 * reps) * 1e3
+    wb = sum(weight_bytes(n, k) for _, n, k in mats) + weight_bytes(vocab, kh)
+    hb = weight_bytes(vocab, kh)
+    return {"m": 4, "launches": len(mats) + 2, "ms_per_pass": round(ms, 4), "weight_bytes": wb,
+            "weight_GBs": round(wb / (ms * 1e-3) / 1e9, 1), "frac_of_hbm_peak": round(wb / (ms * 1e-3) / 8e12, 4),
+            "head_4_vectors_us": round(head_us, 2), "head_weight_GBs": round(hb / head_us / 1e3, 1)}
 
 
 def probe_quantize(torch, dev, seed: int, reps: int = 20):
@@ -592,7 +609,7 @@ def main():
         del pgraph
 
     if not args.no_probe:
-        result["verify_m4_layers"] = probe_verify_m4(torch, wl, args.seed)
+        result["verify_m4"] = probe_verify_m4(torch, wl, args.seed)
         result["quantize_e4b_gate_up"] = probe_quantize(torch, dev, args.seed)
         result["rowq_int2_kprobe"] = probe_rowq(torch, dev, args.seed)
 

@@ -235,6 +235,31 @@ int lmhead_softcap_argmax(const void* packed, int64_t vocab, int64_t k,
                           size_t ws_bytes, int32_t* idx_out, float* val_out,
                           void* stream);
 
+/* Workspace bytes lmhead_softcap_argmax_multi needs (m <= 8 vectors). */
+size_t lmhead_multi_workspace_bytes(int64_t vocab, int64_t k, int64_t m);
+
+/* lmhead_softcap_argmax_multi: lmhead_softcap_argmax for m <= 8 activation
+ * vectors with the head read once (E2B card: the speculative verify of 4
+ * draft rows reads the head once and argmaxes each row). For each v < m:
+ * idx_out[v], val_out[v] as lmhead_softcap_argmax on x[v]; the logits are
+ * those of q4_gemv_multi (matrix cores, one power-of-two fp16 factor per
+ * vector). Two launches on `stream`: the first leaves every workgroup's best
+ * (value, row) per vector in ws, the second (one workgroup per vector)
+ * reduces them and caps the winner.
+ *   packed   from q4_pack with (n = vocab, k); 16-byte aligned.
+ *   x        bf16 [m, k] row-major, 16-byte aligned.
+ *   ws       device workspace, ws_bytes >= lmhead_multi_workspace_bytes,
+ *            8-byte aligned, caller-owned, no initial contents needed; calls
+ *            sharing one ws must not overlap.
+ *   idx_out  device int32 [m]; val_out device fp32 [m].
+ * Errors: as lmhead_softcap_argmax, m not in [1, 8], and unsupported when
+ *         the staged vectors (4 * ceil(m / 4) rows of (k + 8) fp16 values)
+ *         do not fit in one workgroup's LDS. */
+int lmhead_softcap_argmax_multi(const void* packed, int64_t vocab, int64_t k,
+                                const uint16_t* x, int64_t m, float cap,
+                                void* ws, size_t ws_bytes, int32_t* idx_out,
+                                float* val_out, void* stream);
+
 /* ple_gather: Per-Layer-Embedding row gather
  * out[t, j] = RN_fp32(table[ids[t], j] * row_scale[ids[t]] * mult)
  * (model card, PLE gather-table sidecar section: int8 table [V, L*ld], fp32

@@ -50,6 +50,9 @@ _SIGNATURES = {
     "q4_gemm_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
     "q4_gemm_s64": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p, ctypes.c_size_t, _c_p]),
     "lmhead_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
+    "lmhead_multi_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, _c_i64]),
+    "lmhead_softcap_argmax_multi": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, ctypes.c_float, _c_p,
+                                                   ctypes.c_size_t, _c_p, _c_p, _c_p]),
     "lmhead_softcap_argmax": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, ctypes.c_float, _c_p,
                                              ctypes.c_size_t, _c_p, _c_p, _c_p]),
     "ple_gather": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_i64, ctypes.c_float, _c_p,
@@ -293,6 +296,35 @@ def lmhead_softcap_argmax(packed: torch.Tensor, vocab: int, k: int, x: torch.Ten
     pv = _dev(val_out, "val_out", _F32, 1)
     _check(lib().lmhead_softcap_argmax(pp, vocab, k, px, float(cap), pw,
                                        ws.numel() * ws.element_size(), pi, pv, _stream(x)))
+    return idx_out, val_out
+
+
+def lmhead_multi_workspace_bytes(vocab: int, k: int, m: int) -> int:
+    return int(lib().lmhead_multi_workspace_bytes(vocab, k, m))
+
+
+def lmhead_softcap_argmax_multi(packed: torch.Tensor, vocab: int, k: int, x: torch.Tensor,
+                                cap: float = 30.0, ws: torch.Tensor | None = None,
+                                idx_out: torch.Tensor | None = None,
+                                val_out: torch.Tensor | None = None):
+    """(idx int32 [m], val fp32 [m]): the softcapped head maximum for each of
+    the m <= 8 bf16 vectors x [m, k], with the head read once."""
+    m = x.shape[0] if x.dim() == 2 else 1
+    pp = _dev(packed, "packed", _BYTES)
+    _check_packed(packed, vocab, k)
+    px = _dev(x, "x", _U16, m * k)
+    need = lmhead_multi_workspace_bytes(vocab, k, m)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    pw = _dev(ws, "ws", _BYTES)
+    if idx_out is None:
+        idx_out = torch.empty(m, dtype=torch.int32, device=x.device)
+    if val_out is None:
+        val_out = torch.empty(m, dtype=torch.float32, device=x.device)
+    pi = _dev(idx_out, "idx_out", _I32, m)
+    pv = _dev(val_out, "val_out", _F32, m)
+    _check(lib().lmhead_softcap_argmax_multi(pp, vocab, k, px, m, float(cap), pw,
+                                             ws.numel() * ws.element_size(), pi, pv, _stream(x)))
     return idx_out, val_out
 
 

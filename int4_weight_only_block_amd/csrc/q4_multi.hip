@@ -19,6 +19,7 @@
 // matching 4 activations straight from LDS, where each vector is stored as
 // fp16 in k order, scaled by one power of two per vector (its largest bf16
 // exponent lands at 2^14, as the prefill GEMM's per-token factor).
+#include <limits.h>
 #include <math.h>
 
 #include <map>
@@ -38,15 +39,41 @@ constexpr int kMWaves = 4;
 constexpr int kMThreads = 64 * kMWaves;
 constexpr int kMaxBpl = 6;  // blocks per lane per row segment
 
+constexpr int kMultiVecs = 8;         // most vectors of one launch
+constexpr int kMultiPartials = 8192;  // most workgroups of one head launch
+
 // halves per activation row in LDS: k plus 8 (16 bytes), so the 4 vectors a
 // 4-lane group reads sit in different bank quads
 __device__ __host__ inline int x_stride(int k) { return k + 8; }
 
-template <int BPL, int NG, bool FULL>
+// What the kernel does with its row sums.
+enum MultiMode : int {
+  kMultiGemv = 0,  // y[v, row] (fp32)
+  kMultiHead = 1,  // per workgroup and vector: the largest sum and its lowest row
+};
+
+// Best (value, row) of the wave into every lane (the single-vector head's
+// comparator: larger value, then lower row; NaN never wins).
+__device__ __forceinline__ void multi_wave_best(float& best, int& bidx) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(best, off);
+    const int oi = __shfl_xor(bidx, off);
+    if (better(ov, oi, best, bidx)) {
+      best = ov;
+      bidx = oi;
+    }
+  }
+}
+
+// partials (head mode): entry blockIdx.x * kMultiVecs + v holds the
+// workgroup's best (value bits, row) for vector v.
+template <int BPL, int NG, int MODE, bool FULL>
 __global__ __launch_bounds__(kMThreads) void q4_multi_kernel(const uint8_t* __restrict__ nib,
                                                              const uint16_t* __restrict__ scl,
                                                              const uint16_t* __restrict__ x, int n, int k, int m,
-                                                             int nseg, int ipw, float* __restrict__ y) {
+                                                             int nseg, int ipw, float* __restrict__ y,
+                                                             uint2* __restrict__ partials) {
   extern __shared__ uint32_t dyn_lds[];
   const int B = k >> 5;
   const int xsn = x_stride(k);
@@ -125,6 +152,8 @@ __global__ __launch_bounds__(kMThreads) void q4_multi_kernel(const uint8_t* __re
       }
       o = make_uint4(h[0], h[1], h[2], h[3]);
       if (i == 0) ef[v] = ldexpf(1.0f, e);
+    } else if (i == 0) {
+      ef[v] = 0.0f;
     }
     *slot = o;
   }
@@ -137,10 +166,16 @@ __global__ __launch_bounds__(kMThreads) void q4_multi_kernel(const uint8_t* __re
   asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 
   float acc[NG][4];
+  float best[NG][4];  // head mode: best (sum, row) per vector over this lane's rows
+  int bidx[NG][4];
 #pragma unroll
   for (int g = 0; g < NG; ++g)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[g][i] = 0.0f;
+    for (int i = 0; i < 4; ++i) {
+      acc[g][i] = 0.0f;
+      best[g][i] = -INFINITY;
+      bidx[g][i] = INT_MAX;
+    }
 
   // One (row group, segment) step; with REFILL each block's registers are
   // reloaded for step u + 1 right after their last use. REFILL is a
@@ -202,24 +237,116 @@ __global__ __launch_bounds__(kMThreads) void q4_multi_kernel(const uint8_t* __re
           s += __shfl_xor(s, 16);
           s += __shfl_xor(s, 32);
           const int v = 4 * g + i;
-          if (grp == 0 && row < n && v < m) y[size_t(v) * size_t(n) + row] = s * ef[v];
+          if constexpr (MODE == kMultiGemv) {
+            if (grp == 0 && row < n && v < m) y[size_t(v) * size_t(n) + row] = s * ef[v];
+          } else {
+            const float val = s * ef[v];
+            if (row < n && v < m && better(val, row, best[g][i], bidx[g][i])) {
+              best[g][i] = val;
+              bidx[g][i] = row;
+            }
+          }
           acc[g][i] = 0.0f;
         }
     }
   };
   for (int u = 0; u + 1 < units; ++u) step(u, std::true_type{});
   if (units > 0) step(units - 1, std::false_type{});
+
+  if constexpr (MODE == kMultiHead) {
+    // the workgroup's best (value, row) per vector into its partial slots
+    __shared__ float sv[kMWaves][4 * NG];
+    __shared__ int si[kMWaves][4 * NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float b = best[g][i];
+        int bi = bidx[g][i];
+        multi_wave_best(b, bi);
+        if (lane == 0) {
+          sv[wave][4 * g + i] = b;
+          si[wave][4 * g + i] = bi;
+        }
+      }
+    __syncthreads();
+    if (threadIdx.x < m) {
+      const int v = threadIdx.x;
+      float b = sv[0][v];
+      int bi = si[0][v];
+      for (int w = 1; w < kMWaves; ++w)
+        if (better(sv[w][v], si[w][v], b, bi)) {
+          b = sv[w][v];
+          bi = si[w][v];
+        }
+      partials[size_t(blockIdx.x) * kMultiVecs + v] = make_uint2(__builtin_bit_cast(uint32_t, b), uint32_t(bi));
+    }
+  }
 }
 
-template <int NG, bool FULL>
+// Second head launch: workgroup v reduces the partials of vector v and caps
+// the winner (the cap is increasing, so capping the winner alone gives the
+// capped maximum). Each thread issues its loads in batches of 16 before
+// comparing; the comparator is a total order, so the order does not matter.
+constexpr int kMRedBatch = 16;
+__global__ __launch_bounds__(kMThreads) void lmhead_multi_reduce_kernel(const uint2* __restrict__ partials, int g,
+                                                                        float cap, int32_t* __restrict__ idx_out,
+                                                                        float* __restrict__ val_out) {
+  const int v = blockIdx.x;
+  float best = -INFINITY;
+  int bidx = INT_MAX;
+  for (int base = 0; base < g; base += kMThreads * kMRedBatch) {
+    uint2 p[kMRedBatch];
+#pragma unroll
+    for (int j = 0; j < kMRedBatch; ++j) {
+      const int i = base + threadIdx.x + j * kMThreads;
+      p[j] = i < g ? partials[size_t(i) * kMultiVecs + v]
+                   : make_uint2(__builtin_bit_cast(uint32_t, -INFINITY), uint32_t(INT_MAX));
+    }
+#pragma unroll
+    for (int j = 0; j < kMRedBatch; ++j) {
+      const float pv = __builtin_bit_cast(float, p[j].x);
+      const int pi = int(p[j].y);
+      if (better(pv, pi, best, bidx)) {
+        best = pv;
+        bidx = pi;
+      }
+    }
+  }
+  multi_wave_best(best, bidx);
+  __shared__ float sv[kMWaves];
+  __shared__ int si[kMWaves];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    sv[wave] = best;
+    si[wave] = bidx;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kMWaves; ++w)
+      if (better(sv[w], si[w], best, bidx)) {
+        best = sv[w];
+        bidx = si[w];
+      }
+    if (bidx == INT_MAX) {
+      idx_out[v] = -1;
+      val_out[v] = __builtin_nanf("");
+    } else {
+      idx_out[v] = bidx;
+      val_out[v] = cap > 0.0f ? cap * tanhf(best / cap) : best;
+    }
+  }
+}
+
+template <int NG, int MODE, bool FULL>
 const void* pick_multi(int bpl) {
   switch (bpl) {
-    case 1: return reinterpret_cast<const void*>(&q4_multi_kernel<1, NG, FULL>);
-    case 2: return reinterpret_cast<const void*>(&q4_multi_kernel<2, NG, FULL>);
-    case 3: return reinterpret_cast<const void*>(&q4_multi_kernel<3, NG, FULL>);
-    case 4: return reinterpret_cast<const void*>(&q4_multi_kernel<4, NG, FULL>);
-    case 5: return reinterpret_cast<const void*>(&q4_multi_kernel<5, NG, FULL>);
-    case 6: return reinterpret_cast<const void*>(&q4_multi_kernel<6, NG, FULL>);
+    case 1: return reinterpret_cast<const void*>(&q4_multi_kernel<1, NG, MODE, FULL>);
+    case 2: return reinterpret_cast<const void*>(&q4_multi_kernel<2, NG, MODE, FULL>);
+    case 3: return reinterpret_cast<const void*>(&q4_multi_kernel<3, NG, MODE, FULL>);
+    case 4: return reinterpret_cast<const void*>(&q4_multi_kernel<4, NG, MODE, FULL>);
+    case 5: return reinterpret_cast<const void*>(&q4_multi_kernel<5, NG, MODE, FULL>);
+    case 6: return reinterpret_cast<const void*>(&q4_multi_kernel<6, NG, MODE, FULL>);
     default: return nullptr;
   }
 }
@@ -239,6 +366,59 @@ int multi_blocks_per_cu(const void* fn, size_t lds) {
   return nb;
 }
 
+// Largest LDS allocation one workgroup may make on the current device.
+size_t max_lds_per_block_bytes() {
+  int dev = 0, v = 0;
+  (void)hipGetDevice(&dev);
+  if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0) v = 65536;
+  return size_t(v);
+}
+
+struct MultiPlan {
+  const void* fn;
+  int nseg, ipw, grid;
+  size_t lds;
+};
+
+template <int MODE>
+MultiPlan multi_plan(int64_t n, int64_t k, int m) {
+  MultiPlan p{};
+  const int B = int(k / 32);
+  p.nseg = (B + 16 * kMaxBpl - 1) / (16 * kMaxBpl);
+  const int bpl = (B + 16 * p.nseg - 1) / (16 * p.nseg);
+  const bool full = B == 16 * bpl * p.nseg;
+  const int ng = (m + 3) / 4;
+  p.fn = ng == 1 ? (full ? pick_multi<1, MODE, true>(bpl) : pick_multi<1, MODE, false>(bpl))
+                 : (full ? pick_multi<2, MODE, true>(bpl) : pick_multi<2, MODE, false>(bpl));
+  if (!p.fn) return p;
+  p.lds = multi_mfma_lds_bytes(m, k);
+  const int rg = int((n + 3) / 4);
+  const int cus = device_cu_count();
+  const int waves_max = cus * multi_blocks_per_cu(p.fn, p.lds) * kMWaves;
+  p.ipw = (rg + waves_max - 1) / waves_max;
+  // every workgroup stages all m vectors: a wave walks up to three row
+  // groups while the grid still covers 80% of the CUs, to spread that cost
+  for (int want = 3; want > p.ipw; --want) {
+    const int64_t g = ((rg + want - 1) / want + kMWaves - 1) / kMWaves;
+    if (g * 5 >= int64_t(cus) * 4) {
+      p.ipw = want;
+      break;
+    }
+  }
+  const int waves = (rg + p.ipw - 1) / p.ipw;
+  p.grid = (waves + kMWaves - 1) / kMWaves;
+  return p;
+}
+
+int multi_run(const MultiPlan& p, const uint8_t* nib, const uint16_t* scl, int64_t n, int64_t k, const uint16_t* x,
+              int m, float* y, uint2* partials, hipStream_t stream, const char* name) {
+  int ni = int(n), ki = int(k), mi = m, ns = p.nseg, ip = p.ipw;
+  void* args[] = {&nib, &scl, &x, &ni, &ki, &mi, &ns, &ip, &y, &partials};
+  hipError_t e = hipLaunchKernel(p.fn, dim3(p.grid), dim3(kMThreads), args, p.lds, stream);
+  if (e != hipSuccess) return fail(Q4DEC_ERR_HIP, "%s: kernel launch failed: %s", name, hipGetErrorString(e));
+  return launch_status(name);
+}
+
 }  // namespace
 
 size_t multi_mfma_lds_bytes(int m, int64_t k) {
@@ -248,35 +428,59 @@ size_t multi_mfma_lds_bytes(int m, int64_t k) {
 
 int multi_mfma_launch(const uint8_t* nib, const uint16_t* scl, int64_t n, int64_t k, const uint16_t* x, int m,
                       float* y, hipStream_t stream) {
-  const int B = int(k / 32);
-  const int nseg = (B + 16 * kMaxBpl - 1) / (16 * kMaxBpl);
-  const int bpl = (B + 16 * nseg - 1) / (16 * nseg);
-  const bool full = B == 16 * bpl * nseg;
-  const int ng = (m + 3) / 4;
-  const void* fn = ng == 1 ? (full ? pick_multi<1, true>(bpl) : pick_multi<1, false>(bpl))
-                           : (full ? pick_multi<2, true>(bpl) : pick_multi<2, false>(bpl));
-  if (!fn) return fail(Q4DEC_ERR_UNSUPPORTED, "q4_gemv_multi: no kernel for k=%lld", (long long)k);
-  const size_t lds = multi_mfma_lds_bytes(m, k);
-  const int rg = int((n + 3) / 4);
-  const int cus = device_cu_count();
-  const int waves_max = cus * multi_blocks_per_cu(fn, lds) * kMWaves;
-  int ipw = (rg + waves_max - 1) / waves_max;
-  // every workgroup stages all m vectors: a wave walks up to three row
-  // groups while the grid still covers 80% of the CUs, to spread that cost
-  for (int want = 3; want > ipw; --want) {
-    const int64_t g = ((rg + want - 1) / want + kMWaves - 1) / kMWaves;
-    if (g * 5 >= int64_t(cus) * 4) {
-      ipw = want;
-      break;
-    }
-  }
-  const int waves = (rg + ipw - 1) / ipw;
-  const int grid = (waves + kMWaves - 1) / kMWaves;
-  int ni = int(n), ki = int(k), mi = m, ns = nseg, ip = ipw;
-  void* args[] = {&nib, &scl, &x, &ni, &ki, &mi, &ns, &ip, &y};
-  hipError_t e = hipLaunchKernel(fn, dim3(grid), dim3(kMThreads), args, lds, stream);
-  if (e != hipSuccess) return fail(Q4DEC_ERR_HIP, "q4_gemv_multi: kernel launch failed: %s", hipGetErrorString(e));
-  return launch_status("q4_gemv_multi");
+  const MultiPlan p = multi_plan<kMultiGemv>(n, k, m);
+  if (!p.fn) return fail(Q4DEC_ERR_UNSUPPORTED, "q4_gemv_multi: no kernel for k=%lld", (long long)k);
+  return multi_run(p, nib, scl, n, k, x, m, y, nullptr, stream, "q4_gemv_multi");
 }
 
 }  // namespace q4dec
+
+extern "C" size_t lmhead_multi_workspace_bytes(int64_t vocab, int64_t k, int64_t m) {
+  (void)vocab;
+  (void)k;
+  (void)m;
+  return size_t(q4dec::kMultiPartials) * q4dec::kMultiVecs * sizeof(uint2);
+}
+
+extern "C" int lmhead_softcap_argmax_multi(const void* packed, int64_t vocab, int64_t k, const uint16_t* x,
+                                           int64_t m, float cap, void* ws, size_t ws_bytes, int32_t* idx_out,
+                                           float* val_out, void* stream) {
+  using namespace q4dec;
+  const char* name = "lmhead_softcap_argmax_multi";
+  if (!packed) return fail(Q4DEC_ERR_NULL, "%s: packed is NULL", name);
+  if (!x) return fail(Q4DEC_ERR_NULL, "%s: x is NULL", name);
+  if (!ws) return fail(Q4DEC_ERR_NULL, "%s: ws is NULL", name);
+  if (!idx_out) return fail(Q4DEC_ERR_NULL, "%s: idx_out is NULL", name);
+  if (!val_out) return fail(Q4DEC_ERR_NULL, "%s: val_out is NULL", name);
+  if (vocab <= 0 || vocab >= (int64_t(1) << 31))
+    return fail(Q4DEC_ERR_SHAPE, "%s: vocab must be in [1, 2^31) (got %lld)", name, (long long)vocab);
+  if (k <= 0 || k % 32)
+    return fail(Q4DEC_ERR_SHAPE, "%s: k must be a positive multiple of 32 (got %lld)", name, (long long)k);
+  if (k > Q4DEC_MAX_K)
+    return fail(Q4DEC_ERR_UNSUPPORTED, "%s: k must be <= %d (got %lld)", name, Q4DEC_MAX_K, (long long)k);
+  if (m < 1 || m > kMultiVecs)
+    return fail(Q4DEC_ERR_SHAPE, "%s: m must be in [1, %d] (got %lld)", name, kMultiVecs, (long long)m);
+  if (!aligned(packed, 16)) return fail(Q4DEC_ERR_ALIGN, "%s: packed must be 16-byte aligned", name);
+  if (!aligned(x, 16)) return fail(Q4DEC_ERR_ALIGN, "%s: x must be 16-byte aligned", name);
+  if (!aligned(ws, 8)) return fail(Q4DEC_ERR_ALIGN, "%s: ws must be 8-byte aligned", name);
+  if (!aligned(idx_out, 4) || !aligned(val_out, 4))
+    return fail(Q4DEC_ERR_ALIGN, "%s: idx_out and val_out must be 4-byte aligned", name);
+  const size_t need = lmhead_multi_workspace_bytes(vocab, k, m);
+  if (ws_bytes < need) return fail(Q4DEC_ERR_WORKSPACE, "%s: ws_bytes %zu < required %zu", name, ws_bytes, need);
+  const size_t lds = multi_mfma_lds_bytes(int(m), k);
+  if (lds > max_lds_per_block_bytes())
+    return fail(Q4DEC_ERR_UNSUPPORTED, "%s: m * k too large (%zu bytes of LDS, device allows %zu)", name, lds,
+                max_lds_per_block_bytes());
+  const MultiPlan p = multi_plan<kMultiHead>(vocab, k, int(m));
+  if (!p.fn) return fail(Q4DEC_ERR_UNSUPPORTED, "%s: no kernel for k=%lld", name, (long long)k);
+  if (p.grid > kMultiPartials) return fail(Q4DEC_ERR_UNSUPPORTED, "%s: too many workgroups", name);
+  const uint8_t* nib = static_cast<const uint8_t*>(packed);
+  const uint16_t* scl = reinterpret_cast<const uint16_t*>(nib + nib_plane_bytes(vocab, k));
+  uint2* partials = static_cast<uint2*>(ws);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  int rc = multi_run(p, nib, scl, vocab, k, x, int(m), nullptr, partials, st, name);
+  if (rc) return rc;
+  hipLaunchKernelGGL(lmhead_multi_reduce_kernel, dim3(unsigned(m)), dim3(kMThreads), 0, st, partials, p.grid, cap,
+                     idx_out, val_out);
+  return launch_status(name);
+}

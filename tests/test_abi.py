@@ -12,7 +12,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(q4.LIB_PATH), reason="libq4de
 
 EXPECTED = {
     "q4dec_abi_version", "q4dec_last_error", "q4_packed_bytes", "q4_pack", "q4_quantize", "q4_gemv", "q4_gemv_gelu_mul", "q4_gemv_multi", "rowq_gemv", "rowq_gemv_gelu_mul",
-    "q4_gemm_s64", "q4_gemm_workspace_bytes", "lmhead_workspace_bytes", "lmhead_softcap_argmax", "ple_gather",
+    "q4_gemm_s64", "q4_gemm_workspace_bytes", "lmhead_workspace_bytes", "lmhead_softcap_argmax", "lmhead_multi_workspace_bytes", "lmhead_softcap_argmax_multi", "ple_gather",
 }
 
 
@@ -171,6 +171,33 @@ def test_rowq_gemv_gelu_mul_validation():
     assert call(3, 96)[0] == q4.ERR_SHAPE
     assert call(6, FAKE + 1)[0] == q4.ERR_ALIGN
     assert call(1, FAKE + 2)[0] == q4.ERR_ALIGN
+
+
+def test_lmhead_multi_validation():
+    L = q4.lib()
+    need = L.lmhead_multi_workspace_bytes(262144, 1536, 4)
+    assert need >= 8 * 8 * 1024
+    ok = [FAKE, 1000, 1536, FAKE, 4, 30.0, FAKE, need, FAKE, FAKE, None]
+
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return _rc_and_msg(L.lmhead_softcap_argmax_multi(*a))
+
+    for i, name in [(0, "packed"), (3, "x"), (6, "ws"), (8, "idx_out"), (9, "val_out")]:
+        rc, msg = call(i, None)
+        assert rc == q4.ERR_NULL and name in msg
+    rc, msg = call(4, 9)
+    assert rc == q4.ERR_SHAPE and "m" in msg
+    assert call(4, 0)[0] == q4.ERR_SHAPE
+    assert call(1, 0)[0] == q4.ERR_SHAPE
+    assert call(2, 48)[0] == q4.ERR_SHAPE
+    assert call(2, q4.MAX_K + 32)[0] == q4.ERR_UNSUPPORTED
+    rc, msg = call(7, need - 8)
+    assert rc == q4.ERR_WORKSPACE and "ws_bytes" in msg
+    assert call(6, FAKE + 4)[0] == q4.ERR_ALIGN
+    assert call(3, FAKE + 8)[0] == q4.ERR_ALIGN
+    assert call(8, FAKE + 2)[0] == q4.ERR_ALIGN
 
 
 def test_pack_validation():

@@ -446,6 +446,13 @@ def _check_head_batch(codes, sb, xs, cap=30.0):
     for x in xs:
         i, v = q4.lmhead_softcap_argmax(packed, vocab, k, d(x), cap, ws)
         got.append((int(i.item()), float(v.item())))
+    return _check_head_results(codes, sb, xs, got, cap)
+
+
+def _check_head_results(codes, sb, xs, got, cap=30.0):
+    """got[s] = (idx, val) for xs[s]: the index must be the oracle's wherever
+    the top-2 margin of the capped logits is at least 1e-3, the value within
+    the GEMV bar of the oracle's maximum. Returns the excluded count."""
     z, a = oracle.gemm(codes, sb, np.stack(xs))
     excluded = 0
     for s, (gi, gv) in enumerate(got):
@@ -510,6 +517,65 @@ def test_lmhead_e4b_head_shape():
     codes, sb = synth.q4_weights(rng, 262144, 2560)
     xs = [synth.bf16_normal(rng, 2560) for _ in range(4)]
     _check_head_batch(codes, sb, xs)
+
+
+def _multi_head(packed, vocab, k, xs, cap=30.0, ws=None):
+    i, v = q4.lmhead_softcap_argmax_multi(packed, vocab, k, d(np.stack(xs)), cap, ws)
+    return list(zip(i.cpu().numpy().tolist(), v.cpu().numpy().tolist()))
+
+
+def test_lmhead_multi_e2b_full_100_vectors():
+    """The verify head: the E2B head with the 100 vectors in batches of 8, 4,
+    3 and 2 (both matrix-core chains, ragged batches)."""
+    s = synth.SHAPES["head_e2b"]
+    rng = synth.rng_for(0, 3)
+    codes, sb = synth.q4_weights(rng, s["vocab"], s["k"])
+    xs = [synth.bf16_normal(rng, s["k"]) for _ in range(s["n_vectors"])]
+    packed = pack(codes, sb)
+    ws = torch.zeros(q4.lmhead_multi_workspace_bytes(s["vocab"], s["k"], 8), dtype=torch.uint8, device=DEV)
+    got, i = [], 0
+    for m in [8] * 11 + [4, 3, 2, 3]:
+        got += _multi_head(packed, s["vocab"], s["k"], xs[i:i + m], ws=ws)
+        i += m
+    assert i == len(xs)
+    excluded = _check_head_results(codes, sb, xs, got)
+    assert excluded <= 5
+
+
+def test_lmhead_multi_e4b_and_ragged_vocab():
+    for vocab, k, m in [(262144, 2560, 4), (1, 64, 2), (3, 32, 8), (1000, 1536, 5), (4099, 2560, 7),
+                        (777, 10240, 4), (70001, 2048, 6)]:
+        rng = synth.rng_for(14, vocab, k, m)
+        codes, sb = synth.q4_weights(rng, vocab, k)
+        xs = [synth.bf16_normal(rng, k) for _ in range(m)]
+        got = _multi_head(pack(codes, sb), vocab, k, xs)
+        _check_head_results(codes, sb, xs, got)
+
+
+def test_lmhead_multi_planted_ties_per_vector():
+    """Equal maxima in several rows: each vector's lowest winning row, with
+    vectors that pick different rows (x and -x) in one call; cap <= 0 gives
+    the raw maxima, exact for integer inputs."""
+    vocab, k = 262144, 1536
+    rng = synth.rng_for(15)
+    codes = rng.integers(-2, 3, size=(vocab, k), dtype=np.int8)
+    sb = np.full((vocab, k // 32), fp16_bits(2.0 ** -7), dtype=np.uint16)
+    xi = rng.integers(-3, 4, size=k)
+    up = np.where(xi > 0, 7, np.where(xi < 0, -8, 0)).astype(np.int8)    # the maximum for x
+    down = np.where(xi > 0, -8, np.where(xi < 0, 7, 0)).astype(np.int8)  # the maximum for -x
+    for r in (70000, 5, 262143):
+        codes[r] = up
+    for r in (262143, 1024, 1023):
+        codes[r] = down
+    packed = pack(codes, sb)
+    x, xn = bf16_bits_of_ints(xi), bf16_bits_of_ints(-xi)
+    got = _multi_head(packed, vocab, k, [x, xn, x], cap=0.0)
+    zu = float(sum(int(up[j]) * int(xi[j]) for j in range(k))) / 128.0
+    zd = float(sum(int(down[j]) * int(-xi[j]) for j in range(k))) / 128.0
+    assert got == [(5, zu), (1023, zd), (5, zu)]
+    got = _multi_head(packed, vocab, k, [xn, x], cap=30.0)
+    assert [g[0] for g in got] == [1023, 5]
+    assert abs(got[1][1] - float(oracle.softcap(zu))) <= 1e-6 + 1e-4 * abs(zu)
 
 
 def test_lmhead_shared_workspace_and_graph_replays():
