@@ -24,6 +24,7 @@
 // within about 66 times the codes' own contribution (six of fp32's 24 bits).
 #include <math.h>
 
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -367,8 +368,13 @@ RPlan rowq_plan(int64_t n, int64_t k) {
   const int64_t units = MODE == kRowqGelu ? n / 2 : n;
   const int upw = MODE == kRowqGelu ? p.rpw / 2 : p.rpw;
   p.rg = int((units + upw - 1) / upw);
-  const int waves_max = device_cu_count() * rowq_blocks_per_cu(p.fn) * kRWaves;
+  const int cus = device_cu_count();
+  const int waves_max = cus * rowq_blocks_per_cu(p.fn) * kRWaves;
   p.ipw = (p.rg + waves_max - 1) / waves_max;
+  // one-row waves: every workgroup stages all of x for 4 rows per step, so
+  // walk rows until the grid is about one workgroup per CU (INT2 [1536,
+  // 12288]: 6.2 -> 5.3 us; INT4 [2560, 10240]: 7.4 -> 6.6 us)
+  if (p.rpw == 1) p.ipw = std::max(p.ipw, (p.rg + cus * kRWaves - 1) / (cus * kRWaves));
   const int waves = (p.rg + p.ipw - 1) / p.ipw;
   p.grid = (waves + kRWaves - 1) / kRWaves;
   return p;
