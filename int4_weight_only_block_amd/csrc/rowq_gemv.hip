@@ -129,7 +129,7 @@ __device__ __forceinline__ void stage_block(const uint16_t* __restrict__ xb, uin
     for (int f = 0; f < F::kPairs; ++f) {
       const int e0 = F::elem(d, f), s = F::shift(f);
       const half2_t h = {(_Float16)ldexpf(elem(e0), -e - s), (_Float16)ldexpf(elem(e0 + F::kSecond), -e - s)};
-      const _Float16 bias = (_Float16)(1024 + (F::kOffset << s));  // 1152 or 1536, exact
+      const _Float16 bias = (_Float16)(1024 + (F::kOffset << s));  // 1056, 1152 or 1536, exact
       const half2_t bb = {bias, bias};
       c = __builtin_amdgcn_fdot2(h, bb, c, false);
       out[d * F::kPairs + f] = __builtin_bit_cast(uint32_t, h);
