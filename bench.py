@@ -373,6 +373,143 @@ def probe_rowq(torch, dev, seed: int, reps: int = 20):
             "frac_of_hbm_peak": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
+def probe_configs(torch, dev, wl: Workload, seed: int, reps: int = 10):
+    """The smaller workloads, each in its own HIP graph over distinct copies
+    so no launch finds its weights in the infinity cache:
+
+    * gemv_1536: 768 distinct q4_0 [1536, 1536] matrices (1.02 GB) back to
+      back, plus the latency of one launch alone (one-launch graph replayed,
+      and an eager launch between two events, median of 100);
+    * ffn_e2b: 64 distinct E2B FFN pairs, the fused gate/up GELU launch
+      [12288, 1536] then the down GEMV [1536, 6144] on its bf16 output;
+    * head_e2b: the E2B-shaped head [262144, 1536] with softcap + argmax,
+      100 activation vectors over 3 copies of the head, one vector per call,
+      and the same 100 vectors 8 per call (13 calls of the multi-vector head);
+    * ple: the E2B table [262144, 8960] for 1 and 64 ids, the E4B table
+      [262144, 10752] for 64 ids."""
+    import int4_weight_only_block_amd as q4
+    import synth
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed + 5)
+
+    def packed(n, k):
+        codes, scales = synth.torch_q4_weights(g, n, k, dev)
+        return q4.q4_pack(codes, scales)
+
+    def time_graph(fn, r=reps):
+        fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(r):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del graph
+        return e0.elapsed_time(e1) / r * 1e3  # us per replay
+
+    def rate(b, us):
+        return {"achieved_GBs": round(b / us / 1e3, 1), "frac_of_hbm_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+    out = {}
+    # --- one small GEMV
+    n = k = 1536
+    mats = [packed(n, k) for _ in range(768)]
+    x = synth.torch_bf16_normal(g, k, dev)
+    y = torch.empty(n, dtype=torch.float32, device=dev)
+
+    def run_gemv():
+        for p in mats:
+            q4.q4_gemv(p, n, k, x, y)
+
+    us = time_graph(run_gemv) / len(mats)
+    one_graph_us = time_graph(lambda: q4.q4_gemv(mats[0], n, k, x, y), 200)
+    eager = []
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(100):
+        e0.record()
+        q4.q4_gemv(mats[i], n, k, x, y)
+        e1.record()
+        torch.cuda.synchronize()
+        eager.append(e0.elapsed_time(e1) * 1e3)
+    eager.sort()
+    out["gemv_1536"] = {"shape": [n, k], "matrices": len(mats), "avg_launch_us": round(us, 3),
+                        "bytes_per_launch": q4_bytes(n, k), **rate(q4_bytes(n, k), us),
+                        "single_launch_graph_us": round(one_graph_us, 3),
+                        "single_launch_eager_us_median": round(eager[len(eager) // 2], 3)}
+    del mats
+    # --- E2B FFN pair
+    H, D = 6144, 1536
+    pairs = [(packed(2 * H, D), packed(D, H)) for _ in range(64)]
+    a = torch.empty(H, dtype=torch.int16, device=dev)
+
+    def run_ffn():
+        for gu, dn in pairs:
+            q4.q4_gemv_gelu_mul(gu, 2 * H, D, x, a)
+            q4.q4_gemv(dn, D, H, a, y)
+
+    us = time_graph(run_ffn) / len(pairs)
+    b = weight_bytes(2 * H, D) + 2 * D + 2 * H + weight_bytes(D, H) + 2 * H + 4 * D
+    out["ffn_e2b"] = {"gate_up": [2 * H, D], "down": [D, H], "pairs": len(pairs), "launches_per_pair": 2,
+                      "avg_pair_us": round(us, 3), "bytes_per_pair": b, **rate(b, us)}
+    del pairs
+    # --- E2B-shaped head, 100 vectors
+    V = 262144
+    heads = [packed(V, D) for _ in range(3)]
+    xs = synth.torch_bf16_normal(g, (100, D), dev)
+    ws = torch.zeros(q4.lmhead_workspace_bytes(V, D), dtype=torch.uint8, device=dev)
+    idx = torch.empty(100, dtype=torch.int32, device=dev)
+    val = torch.empty(100, dtype=torch.float32, device=dev)
+
+    def run_head():
+        for i in range(100):
+            q4.lmhead_softcap_argmax(heads[i % 3], V, D, xs[i], 30.0, ws, idx[i:i + 1], val[i:i + 1])
+
+    us = time_graph(run_head, 3) / 100
+    b = weight_bytes(V, D) + 2 * D + 8
+    wsm = torch.zeros(q4.lmhead_multi_workspace_bytes(V, D, 8), dtype=torch.uint8, device=dev)
+    batches = [(s, min(8, 100 - s)) for s in range(0, 100, 8)]
+
+    def run_head_multi():
+        for j, (s, m) in enumerate(batches):
+            q4.lmhead_softcap_argmax_multi(heads[j % 3], V, D, xs[s:s + m], 30.0, wsm, idx[s:s + m], val[s:s + m])
+
+    us_m = time_graph(run_head_multi, 3)
+    out["head_e2b"] = {"shape": [V, D], "vectors": 100, "copies": 3, "avg_call_us": round(us, 3),
+                       "bytes_per_call": b, **rate(b, us),
+                       "multi_8_per_call_us_for_100": round(us_m, 2), "multi_calls": len(batches)}
+    del heads
+    # --- PLE gathers
+    s2 = synth.SHAPES["ple_e2b"]
+    t2 = torch.randint(-127, 128, (s2["vocab"], s2["dim"]), dtype=torch.int8, device=dev, generator=g)
+    sc2 = torch.empty(s2["vocab"], dtype=torch.float32, device=dev).uniform_(1e-3, 1e-2, generator=g)
+    ple = {}
+    for name, table, scale in (("e2b", t2, sc2), ("e4b", wl.table, wl.scale)):
+        vocab, dim = table.shape
+        for T in ((1, 64) if name == "e2b" else (64,)):
+            ids = torch.randint(0, vocab, (32, T), dtype=torch.int32, device=dev, generator=g)
+            o = torch.empty((T, dim), dtype=torch.float32, device=dev)
+
+            def run_ple(table=table, scale=scale, ids=ids, o=o):
+                for r in range(ids.shape[0]):
+                    q4.ple_gather(table, scale, ids[r], 16.0, out=o)
+
+            us = time_graph(run_ple) / ids.shape[0]
+            b = T * (dim + 4 + 4 * dim + 4)
+            ple[f"{name}_T{T}"] = {"table": [vocab, dim], "ids": T, "avg_launch_us": round(us, 3),
+                                   "bytes_per_launch": b, "achieved_GBs": round(b / us / 1e3, 1)}
+    out["ple"] = ple
+    del t2, sc2
+    torch.cuda.synchronize()
+    return out
+
+
 def cpu_baseline(seconds: float):
     """fp64 oracle on a bounded sample of the decode step: whole matrices of
     layer 0 (QKV, O, gate+up, down) and then row slices of the head until the
@@ -612,6 +749,7 @@ def main():
         result["verify_m4"] = probe_verify_m4(torch, wl, args.seed)
         result["quantize_e4b_gate_up"] = probe_quantize(torch, dev, args.seed)
         result["rowq_int2_kprobe"] = probe_rowq(torch, dev, args.seed)
+        result["configs"] = probe_configs(torch, dev, wl, args.seed)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
