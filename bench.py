@@ -272,6 +272,44 @@ def probe_verify_m4(torch, wl: Workload, seed: int, reps: int = 10):
             "head_4_vectors_us": round(head_us, 2), "head_weight_GBs": round(hb / head_us / 1e3, 1)}
 
 
+def probe_head_s64(torch, wl: Workload, reps: int = 10):
+    """The head for every row of a 64-token prefill chunk
+    (lmhead_softcap_argmax_s64: the S=64 MFMA kernel with a per-token argmax
+    epilogue) on the E4B head, rotating over three copies of it so no call
+    finds its weights in the infinity cache; reported per call (64 tokens)."""
+    q4 = wl.q4
+    hn, hk = wl.head_nk
+    wl.head_copies_launches()  # makes the three copies of the head
+    ws = torch.zeros(q4.lmhead_s64_workspace_bytes(hn, hk), dtype=torch.uint8, device=wl.p_head_x.device)
+    idx = torch.empty(64, dtype=torch.int32, device=ws.device)
+    val = torch.empty(64, dtype=torch.float32, device=ws.device)
+
+    def run():
+        for p in wl._head_copies:
+            q4.lmhead_softcap_argmax_s64(p, hn, hk, wl.p_head_x, 30.0, ws, idx, val)
+
+    run()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * len(wl._head_copies))
+    del graph
+    wb = weight_bytes(hn, hk)
+    flops = 2 * 64 * hn * hk
+    return {"shape": [hn, hk], "tokens": 64, "avg_call_us": round(us, 2),
+            "weight_GBs": round(wb / us / 1e3, 1), "TFLOPs": round(flops / us / 1e6, 1),
+            "us_per_token": round(us / 64, 3)}
+
+
 def probe_quantize(torch, dev, seed: int, reps: int = 20):
     """q4_quantize on an E4B gate+up sized bf16 matrix [20480, 2560] (the
     export step, not part of a decode step): bf16 read + int8 codes + fp16
@@ -744,6 +782,8 @@ def main():
                          "mfma_fp16_floor_ms": round(flops / 2.5e15 * 1e3, 4)},
         }
         del pgraph
+        if not args.no_probe:
+            result["prefill_s64"]["head_all_64_rows"] = probe_head_s64(torch, wl)
 
     if not args.no_probe:
         result["verify_m4"] = probe_verify_m4(torch, wl, args.seed)

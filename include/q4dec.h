@@ -260,6 +260,35 @@ int lmhead_softcap_argmax_multi(const void* packed, int64_t vocab, int64_t k,
                                 void* ws, size_t ws_bytes, int32_t* idx_out,
                                 float* val_out, void* stream);
 
+/* Workspace bytes lmhead_softcap_argmax_s64 needs for a [vocab, k] head (0
+ * for invalid shapes). */
+size_t lmhead_s64_workspace_bytes(int64_t vocab, int64_t k);
+
+/* lmhead_softcap_argmax_s64: the LM head for every row of a prefill chunk of
+ * n_tok <= 64 tokens: for each s < n_tok, lmhead_softcap_argmax on x[s]
+ * (model card: the prefill entry point has a static query width of 64 and
+ * outputs logits for every position; E2B card: the head is fused with its
+ * argmax, no logit readback). The logits are those of q4_gemm_s64 (same
+ * kernel, same numerics) and are never written out: each workgroup keeps per
+ * token the best (logit, row) of its 128 rows. Launches on `stream`: the
+ * activation conversion, the MFMA kernel, then one workgroup per token
+ * reduces the partials and caps the winner.
+ *   packed   from q4_pack with (n = vocab, k); 16-byte aligned.
+ *   x        bf16 [n_tok, k] row-major, 16-byte aligned.
+ *   cap      30.0 for Gemma 4; cap <= 0 returns the raw maximum logits.
+ *   ws       device workspace, ws_bytes >= lmhead_s64_workspace_bytes(vocab,
+ *            k), 256-byte aligned, caller-owned, no initial contents needed;
+ *            calls sharing one ws must not overlap.
+ *   idx_out  device int32 [n_tok]; val_out device fp32 [n_tok]; per token as
+ *            lmhead_softcap_argmax (lowest row among equal maxima, NaN never
+ *            wins, -1 and NaN when no logit compares).
+ * Errors: NULL pointer, vocab <= 0 or >= 2^31, k % 32 != 0, k > Q4DEC_MAX_K,
+ *         n_tok not in [1, 64], workspace too small, misalignment. */
+int lmhead_softcap_argmax_s64(const void* packed, int64_t vocab, int64_t k,
+                              const uint16_t* x, int64_t n_tok, float cap,
+                              void* ws, size_t ws_bytes, int32_t* idx_out,
+                              float* val_out, void* stream);
+
 /* ple_gather: Per-Layer-Embedding row gather
  * out[t, j] = RN_fp32(table[ids[t], j] * row_scale[ids[t]] * mult)
  * (model card, PLE gather-table sidecar section: int8 table [V, L*ld], fp32

@@ -55,6 +55,9 @@ _SIGNATURES = {
                                                    ctypes.c_size_t, _c_p, _c_p, _c_p]),
     "lmhead_softcap_argmax": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, ctypes.c_float, _c_p,
                                              ctypes.c_size_t, _c_p, _c_p, _c_p]),
+    "lmhead_s64_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
+    "lmhead_softcap_argmax_s64": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, ctypes.c_float, _c_p,
+                                                 ctypes.c_size_t, _c_p, _c_p, _c_p]),
     "ple_gather": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_i64, ctypes.c_float, _c_p,
                                   _c_p, _c_p]),
 }
@@ -325,6 +328,35 @@ def lmhead_softcap_argmax_multi(packed: torch.Tensor, vocab: int, k: int, x: tor
     pv = _dev(val_out, "val_out", _F32, m)
     _check(lib().lmhead_softcap_argmax_multi(pp, vocab, k, px, m, float(cap), pw,
                                              ws.numel() * ws.element_size(), pi, pv, _stream(x)))
+    return idx_out, val_out
+
+
+def lmhead_s64_workspace_bytes(vocab: int, k: int) -> int:
+    return int(lib().lmhead_s64_workspace_bytes(vocab, k))
+
+
+def lmhead_softcap_argmax_s64(packed: torch.Tensor, vocab: int, k: int, x: torch.Tensor,
+                              cap: float = 30.0, ws: torch.Tensor | None = None,
+                              idx_out: torch.Tensor | None = None,
+                              val_out: torch.Tensor | None = None):
+    """(idx int32 [s], val fp32 [s]): the softcapped head maximum for each of
+    the s <= 64 bf16 token rows x [s, k] of a prefill chunk."""
+    n_tok = x.shape[0] if x.dim() == 2 else 1
+    pp = _dev(packed, "packed", _BYTES)
+    _check_packed(packed, vocab, k)
+    px = _dev(x, "x", _U16, n_tok * k)
+    need = lmhead_s64_workspace_bytes(vocab, k)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    pw = _dev(ws, "ws", _BYTES)
+    if idx_out is None:
+        idx_out = torch.empty(n_tok, dtype=torch.int32, device=x.device)
+    if val_out is None:
+        val_out = torch.empty(n_tok, dtype=torch.float32, device=x.device)
+    pi = _dev(idx_out, "idx_out", _I32, n_tok)
+    pv = _dev(val_out, "val_out", _F32, n_tok)
+    _check(lib().lmhead_softcap_argmax_s64(pp, vocab, k, px, n_tok, float(cap), pw,
+                                           ws.numel() * ws.element_size(), pi, pv, _stream(x)))
     return idx_out, val_out
 
 

@@ -22,6 +22,12 @@
 // current chunk runs on the matrix cores. Small-N matrices split K over
 // several workgroups; their partial sums go to the workspace and a second
 // kernel adds them in a fixed order, so results are deterministic.
+//
+// The same kernel, with an argmax epilogue instead of the output store, is
+// the LM head over a chunk of up to 64 tokens: each workgroup keeps, per
+// token, the best (logit, row) of its 128 rows, and a second launch reduces
+// those per token and caps the winner, so no logits are written.
+#include <limits.h>
 #include <math.h>
 
 #include <algorithm>
@@ -44,7 +50,14 @@ struct GemmPlan {
   size_t xh_off, xf_off, part_off, total;  // workspace: fp16 activations, token factors, partials
 };
 
-static GemmPlan gemm_plan(int64_t n, int64_t k) {
+// what the MFMA kernel does with its output tile
+enum GemmMode : int {
+  kGemmOut = 0,     // Y[s, r] (fp32)
+  kGemmSlices = 1,  // the K slice's partial Y into the workspace
+  kGemmHead = 2,    // per token, the tile's best (logit, row) into the workspace
+};
+
+static GemmPlan gemm_plan(int64_t n, int64_t k, bool split = true) {
   GemmPlan p{};
   const int B = int(k / 32);
   const int64_t tiles = (n + kTileN - 1) / kTileN;
@@ -52,7 +65,7 @@ static GemmPlan gemm_plan(int64_t n, int64_t k) {
   // idle, in slices of whole chunks (a partial last chunk runs its MFMAs on
   // zeroed scales). Matrices with >= 128 tiles are not split, so they need
   // no second launch.
-  const int64_t s_target = std::max<int64_t>(1, 256 / tiles);
+  const int64_t s_target = split ? std::max<int64_t>(1, 256 / tiles) : 1;
   const int per = int((B + s_target - 1) / s_target);
   p.bps = ((per + kChunk - 1) / kChunk) * kChunk;
   p.slices = (B + p.bps - 1) / p.bps;
@@ -243,11 +256,11 @@ __device__ __forceinline__ void mma_chunk(float4_t (&t)[kSub][4], const uint4 (&
   }
 }
 
-template <bool PARTIAL>
+template <int MODE>
 __global__ __launch_bounds__(256) void q4_gemm_kernel(const uint8_t* __restrict__ nib, const uint16_t* __restrict__ scl,
                                                       const uint8_t* __restrict__ rexp, const _Float16* __restrict__ xh,
                                                       const float* __restrict__ xf, int n, int k, int n_tok, int bps,
-                                                      float* __restrict__ out) {
+                                                      void* __restrict__ out) {
   __shared__ uint4 xs[kChunk][kTok][4];  // [block][token][k quarter, swizzled], 32 KB
   const int B = k >> 5;
   const int lane = threadIdx.x & 63;
@@ -332,20 +345,71 @@ __global__ __launch_bounds__(256) void q4_gemm_kernel(const uint8_t* __restrict_
   if (b0 < b_end) run(ra, b0);
 
   // lane holds tokens s = 16m + 4q + i of output rows rows[u]
-#pragma unroll
-  for (int u = 0; u < kSub; ++u) {
-    if (rows[u] >= n) continue;
-    const float rf = ldexpf(1.0f, shift[u]);
+  if constexpr (MODE == kGemmHead) {
+    // per token: the best (logit, row) of the lane's two rows, then of the
+    // 16 lanes of its lane group (the tile's 16 columns), then of the waves
+    __shared__ float hv[4][kTok];
+    __shared__ int hr[4][kTok];
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int s = 16 * m + 4 * q + i;
-        const float v = acc[u][m][i] * (tf[4 * m + i] * rf);
-        if (PARTIAL) {
-          out[(size_t(blockIdx.y) * kTok + s) * size_t(n) + rows[u]] = v;
-        } else if (s < n_tok) {
-          out[size_t(s) * size_t(n) + rows[u]] = v;
+        float bv = -INFINITY;
+        int br = INT_MAX;
+#pragma unroll
+        for (int u = 0; u < kSub; ++u) {
+          const float v = acc[u][m][i] * (tf[4 * m + i] * ldexpf(1.0f, shift[u]));
+          if (rows[u] < n && better(v, rows[u], bv, br)) {
+            bv = v;
+            br = rows[u];
+          }
+        }
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+          const float ov = __shfl_xor(bv, off);
+          const int orow = __shfl_xor(br, off);
+          if (better(ov, orow, bv, br)) {
+            bv = ov;
+            br = orow;
+          }
+        }
+        if (col == 0) {
+          hv[wave][16 * m + 4 * q + i] = bv;
+          hr[wave][16 * m + 4 * q + i] = br;
+        }
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x < n_tok) {
+      const int s = threadIdx.x;
+      float bv = hv[0][s];
+      int br = hr[0][s];
+#pragma unroll
+      for (int w = 1; w < 4; ++w)
+        if (better(hv[w][s], hr[w][s], bv, br)) {
+          bv = hv[w][s];
+          br = hr[w][s];
+        }
+      static_cast<uint2*>(out)[size_t(blockIdx.x) * kTok + s] = make_uint2(__builtin_bit_cast(uint32_t, bv),
+                                                                            uint32_t(br));
+    }
+  } else {
+    float* y = static_cast<float*>(out);
+#pragma unroll
+    for (int u = 0; u < kSub; ++u) {
+      if (rows[u] >= n) continue;
+      const float rf = ldexpf(1.0f, shift[u]);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = 16 * m + 4 * q + i;
+          const float v = acc[u][m][i] * (tf[4 * m + i] * rf);
+          if (MODE == kGemmSlices) {
+            y[(size_t(blockIdx.y) * kTok + s) * size_t(n) + rows[u]] = v;
+          } else if (s < n_tok) {
+            y[size_t(s) * size_t(n) + rows[u]] = v;
+          }
         }
       }
     }
@@ -415,14 +479,73 @@ extern "C" int q4_gemm_s64(const void* packed, int64_t n, int64_t k, const uint1
   hipLaunchKernelGGL(gemm_x_prep_kernel, dim3(kTok), dim3(256), 0, st, x, int(k), int(n_tok), xh, xf);
   const dim3 grid(unsigned((n + kTileN - 1) / kTileN), unsigned(p.slices));
   if (p.slices == 1) {
-    hipLaunchKernelGGL(q4_gemm_kernel<false>, grid, dim3(256), 0, st, nib, scl, rexp, xh, xf, int(n), int(k),
-                       int(n_tok), p.bps, y);
+    hipLaunchKernelGGL(q4_gemm_kernel<kGemmOut>, grid, dim3(256), 0, st, nib, scl, rexp, xh, xf, int(n), int(k),
+                       int(n_tok), p.bps, static_cast<void*>(y));
   } else {
-    hipLaunchKernelGGL(q4_gemm_kernel<true>, grid, dim3(256), 0, st, nib, scl, rexp, xh, xf, int(n), int(k),
-                       int(n_tok), p.bps, part);
+    hipLaunchKernelGGL(q4_gemm_kernel<kGemmSlices>, grid, dim3(256), 0, st, nib, scl, rexp, xh, xf, int(n), int(k),
+                       int(n_tok), p.bps, static_cast<void*>(part));
     const size_t total = size_t(n_tok) * size_t(n);
     const unsigned rgrid = unsigned(std::min<size_t>((total + 255) / 256, 4096));
     hipLaunchKernelGGL(gemm_reduce_kernel, dim3(rgrid), dim3(256), 0, st, part, p.slices, int(n), int(n_tok), y);
   }
   return launch_status("q4_gemm_s64");
+}
+
+// ------------------------------------------------------ head over 64 tokens
+namespace q4dec {
+// workspace of the head over S tokens: the scaled activations and token
+// factors as for q4_gemm_s64, then one (logit, row) partial per row tile and
+// token slot
+static size_t head_s64_partials_off(int64_t vocab, int64_t k) { return gemm_plan(vocab, k, false).part_off; }
+static size_t head_s64_ws_bytes(int64_t vocab, int64_t k) {
+  const int64_t tiles = (vocab + kTileN - 1) / kTileN;
+  return head_s64_partials_off(vocab, k) + align256(size_t(tiles) * kTok * sizeof(uint2));
+}
+}  // namespace q4dec
+
+extern "C" size_t lmhead_s64_workspace_bytes(int64_t vocab, int64_t k) {
+  if (vocab <= 0 || vocab >= (int64_t(1) << 31) || k <= 0 || k % 32 || k > Q4DEC_MAX_K) return 0;
+  return q4dec::head_s64_ws_bytes(vocab, k);
+}
+
+extern "C" int lmhead_softcap_argmax_s64(const void* packed, int64_t vocab, int64_t k, const uint16_t* x,
+                                         int64_t n_tok, float cap, void* ws, size_t ws_bytes, int32_t* idx_out,
+                                         float* val_out, void* stream) {
+  using namespace q4dec;
+  const char* name = "lmhead_softcap_argmax_s64";
+  if (!packed) return fail(Q4DEC_ERR_NULL, "%s: packed is NULL", name);
+  if (!x) return fail(Q4DEC_ERR_NULL, "%s: x is NULL", name);
+  if (!ws) return fail(Q4DEC_ERR_NULL, "%s: ws is NULL", name);
+  if (!idx_out) return fail(Q4DEC_ERR_NULL, "%s: idx_out is NULL", name);
+  if (!val_out) return fail(Q4DEC_ERR_NULL, "%s: val_out is NULL", name);
+  if (vocab <= 0 || vocab >= (int64_t(1) << 31))
+    return fail(Q4DEC_ERR_SHAPE, "%s: vocab must be in [1, 2^31) (got %lld)", name, (long long)vocab);
+  if (k <= 0 || k % 32)
+    return fail(Q4DEC_ERR_SHAPE, "%s: k must be a positive multiple of 32 (got %lld)", name, (long long)k);
+  if (k > Q4DEC_MAX_K)
+    return fail(Q4DEC_ERR_UNSUPPORTED, "%s: k must be <= %d (got %lld)", name, Q4DEC_MAX_K, (long long)k);
+  if (n_tok < 1 || n_tok > kTok)
+    return fail(Q4DEC_ERR_SHAPE, "%s: n_tok must be in [1, %d] (got %lld)", name, kTok, (long long)n_tok);
+  if (!aligned(packed, 16)) return fail(Q4DEC_ERR_ALIGN, "%s: packed must be 16-byte aligned", name);
+  if (!aligned(x, 16)) return fail(Q4DEC_ERR_ALIGN, "%s: x must be 16-byte aligned", name);
+  if (!aligned(ws, 256)) return fail(Q4DEC_ERR_ALIGN, "%s: ws must be 256-byte aligned", name);
+  if (!aligned(idx_out, 4) || !aligned(val_out, 4))
+    return fail(Q4DEC_ERR_ALIGN, "%s: idx_out and val_out must be 4-byte aligned", name);
+  const size_t need = head_s64_ws_bytes(vocab, k);
+  if (ws_bytes < need) return fail(Q4DEC_ERR_WORKSPACE, "%s: ws_bytes %zu < required %zu", name, ws_bytes, need);
+  const GemmPlan p = gemm_plan(vocab, k, false);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  _Float16* xh = reinterpret_cast<_Float16*>(w8 + p.xh_off);
+  float* xf = reinterpret_cast<float*>(w8 + p.xf_off);
+  uint2* part = reinterpret_cast<uint2*>(w8 + head_s64_partials_off(vocab, k));
+  const uint8_t* nib = static_cast<const uint8_t*>(packed);
+  const uint16_t* scl = reinterpret_cast<const uint16_t*>(nib + nib_plane_bytes(vocab, k));
+  const uint8_t* rexp = nib + nib_plane_bytes(vocab, k) + scale_plane_bytes(vocab, k);
+  const int tiles = int((vocab + kTileN - 1) / kTileN);
+  hipLaunchKernelGGL(gemm_x_prep_kernel, dim3(kTok), dim3(256), 0, st, x, int(k), int(n_tok), xh, xf);
+  hipLaunchKernelGGL(q4_gemm_kernel<kGemmHead>, dim3(unsigned(tiles), 1u), dim3(256), 0, st, nib, scl, rexp, xh, xf,
+                     int(vocab), int(k), int(n_tok), p.bps, static_cast<void*>(part));
+  reduce_argmax_partials(part, tiles, kTok, int(n_tok), cap, idx_out, val_out, st);
+  return launch_status(name);
 }

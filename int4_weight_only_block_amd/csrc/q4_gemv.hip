@@ -501,10 +501,6 @@ extern "C" int q4_gemv_gelu_mul(const void* packed, int64_t n, int64_t k, const 
   return launch_status("q4_gemv_gelu_mul");
 }
 
-namespace q4dec {
-
-}  // namespace q4dec
-
 extern "C" int q4_gemv_multi(const void* packed, int64_t n, int64_t k, const uint16_t* x, int64_t m, float* y,
                              void* stream) {
   using namespace q4dec;

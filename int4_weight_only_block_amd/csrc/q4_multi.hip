@@ -290,7 +290,8 @@ __global__ __launch_bounds__(kMThreads) void q4_multi_kernel(const uint8_t* __re
 // comparing; the comparator is a total order, so the order does not matter.
 constexpr int kMRedBatch = 16;
 __global__ __launch_bounds__(kMThreads) void lmhead_multi_reduce_kernel(const uint2* __restrict__ partials, int g,
-                                                                        float cap, int32_t* __restrict__ idx_out,
+                                                                        int stride, float cap,
+                                                                        int32_t* __restrict__ idx_out,
                                                                         float* __restrict__ val_out) {
   const int v = blockIdx.x;
   float best = -INFINITY;
@@ -300,7 +301,7 @@ __global__ __launch_bounds__(kMThreads) void lmhead_multi_reduce_kernel(const ui
 #pragma unroll
     for (int j = 0; j < kMRedBatch; ++j) {
       const int i = base + threadIdx.x + j * kMThreads;
-      p[j] = i < g ? partials[size_t(i) * kMultiVecs + v]
+      p[j] = i < g ? partials[size_t(i) * size_t(stride) + v]
                    : make_uint2(__builtin_bit_cast(uint32_t, -INFINITY), uint32_t(INT_MAX));
     }
 #pragma unroll
@@ -421,6 +422,12 @@ int multi_run(const MultiPlan& p, const uint8_t* nib, const uint16_t* scl, int64
 
 }  // namespace
 
+void reduce_argmax_partials(const uint2* partials, int g, int stride, int nvec, float cap, int32_t* idx_out,
+                            float* val_out, hipStream_t st) {
+  hipLaunchKernelGGL(lmhead_multi_reduce_kernel, dim3(unsigned(nvec)), dim3(kMThreads), 0, st, partials, g, stride,
+                     cap, idx_out, val_out);
+}
+
 size_t multi_mfma_lds_bytes(int m, int64_t k) {
   const int ng = (m + 3) / 4;
   return size_t(4 * ng) * size_t(x_stride(int(k))) * 2;
@@ -480,7 +487,6 @@ extern "C" int lmhead_softcap_argmax_multi(const void* packed, int64_t vocab, in
   hipStream_t st = static_cast<hipStream_t>(stream);
   int rc = multi_run(p, nib, scl, vocab, k, x, int(m), nullptr, partials, st, name);
   if (rc) return rc;
-  hipLaunchKernelGGL(lmhead_multi_reduce_kernel, dim3(unsigned(m)), dim3(kMThreads), 0, st, partials, p.grid, cap,
-                     idx_out, val_out);
+  reduce_argmax_partials(partials, p.grid, kMultiVecs, int(m), cap, idx_out, val_out, st);
   return launch_status(name);
 }

@@ -148,6 +148,13 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Per-vector argmax over per-workgroup (value bits, row) partials: vector v's
+// entries sit at partials[w * stride + v] for w < g. One workgroup per
+// vector writes idx_out[v] and cap * tanh(best / cap) (the raw best for
+// cap <= 0) to val_out[v]; idx -1 and NaN when no value compares.
+void reduce_argmax_partials(const uint2* partials, int g, int stride, int nvec, float cap, int32_t* idx_out,
+                            float* val_out, hipStream_t st);
+
 // (value desc, index asc) comparator for the argmax; NaN never wins.
 __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);

@@ -12,7 +12,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(q4.LIB_PATH), reason="libq4de
 
 EXPECTED = {
     "q4dec_abi_version", "q4dec_last_error", "q4_packed_bytes", "q4_pack", "q4_quantize", "q4_gemv", "q4_gemv_gelu_mul", "q4_gemv_multi", "rowq_gemv", "rowq_gemv_gelu_mul",
-    "q4_gemm_s64", "q4_gemm_workspace_bytes", "lmhead_workspace_bytes", "lmhead_softcap_argmax", "lmhead_multi_workspace_bytes", "lmhead_softcap_argmax_multi", "ple_gather",
+    "q4_gemm_s64", "q4_gemm_workspace_bytes", "lmhead_workspace_bytes", "lmhead_softcap_argmax", "lmhead_multi_workspace_bytes", "lmhead_softcap_argmax_multi", "lmhead_s64_workspace_bytes", "lmhead_softcap_argmax_s64", "ple_gather",
 }
 
 
@@ -253,6 +253,33 @@ def test_gemm_validation():
     assert call(7, need - 1) == q4.ERR_WORKSPACE
     assert call(6, FAKE + 16) == q4.ERR_ALIGN
     assert call(0, FAKE + 8) == q4.ERR_ALIGN
+
+
+def test_head_s64_validation():
+    L = q4.lib()
+    need = q4.lmhead_s64_workspace_bytes(1000, 64)
+    assert need > 0 and q4.lmhead_s64_workspace_bytes(1000, 40) == 0
+    assert q4.lmhead_s64_workspace_bytes(0, 64) == 0
+    # packed, vocab, k, x, n_tok, cap, ws, ws_bytes, idx_out, val_out, stream
+    ok = [FAKE, 1000, 64, FAKE, 64, 30.0, FAKE, need, FAKE, FAKE, None]
+
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return L.lmhead_softcap_argmax_s64(*a)
+
+    for i, name in [(0, "packed"), (3, "x"), (6, "ws"), (8, "idx_out"), (9, "val_out")]:
+        assert call(i, None) == q4.ERR_NULL and name in q4.q4dec_last_error()
+    assert call(4, 0) == q4.ERR_SHAPE and "n_tok" in q4.q4dec_last_error()
+    assert call(4, 65) == q4.ERR_SHAPE
+    assert call(1, 0) == q4.ERR_SHAPE and "vocab" in q4.q4dec_last_error()
+    assert call(2, 48) == q4.ERR_SHAPE
+    assert call(2, q4.MAX_K + 32) == q4.ERR_UNSUPPORTED
+    assert call(7, need - 1) == q4.ERR_WORKSPACE
+    assert call(6, FAKE + 16) == q4.ERR_ALIGN
+    assert call(0, FAKE + 8) == q4.ERR_ALIGN
+    assert call(3, FAKE + 8) == q4.ERR_ALIGN
+    assert call(8, FAKE + 2) == q4.ERR_ALIGN
 
 
 def test_ple_validation():

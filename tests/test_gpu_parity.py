@@ -578,6 +578,76 @@ def test_lmhead_multi_planted_ties_per_vector():
     assert abs(got[1][1] - float(oracle.softcap(zu))) <= 1e-6 + 1e-4 * abs(zu)
 
 
+# ------------------------------------------------ head over 64 tokens --
+@pytest.mark.parametrize("vocab,k,n_tok", [(40000, 1536, 64), (40000, 1536, 17), (3001, 2560, 1),
+                                           (130, 10240, 64)])
+def test_lmhead_s64_against_oracle(vocab, k, n_tok):
+    rng = synth.rng_for(90, vocab, k, n_tok)
+    codes, sb = synth.q4_weights(rng, vocab, k)
+    xs = synth.bf16_normal(rng, n_tok * k).reshape(n_tok, k)
+    i, v = q4.lmhead_softcap_argmax_s64(pack(codes, sb), vocab, k, d(xs), 30.0)
+    got = list(zip(i.cpu().tolist(), v.cpu().tolist()))
+    excluded = _check_head_results(codes, sb, list(xs), got)
+    assert excluded <= max(2, n_tok // 10)
+
+
+def test_lmhead_s64_planted_ties_and_raw_values():
+    """Integer inputs, so every logit is exact: rows 5, 77 and 9999 hold the
+    same maximum for x (the lowest, 5, must win), row 1023 holds the maximum
+    for -x, and tokens alternate between x and -x in one call; cap <= 0 gives
+    the raw logits exactly."""
+    vocab, k, n_tok = 10000, 1536, 64
+    rng = synth.rng_for(91)
+    codes = rng.integers(-2, 3, size=(vocab, k), dtype=np.int8)
+    sb = np.full((vocab, k // 32), fp16_bits(2.0 ** -7), dtype=np.uint16)
+    xi = rng.integers(-3, 4, size=k)
+    up = np.where(xi > 0, 7, np.where(xi < 0, -8, 0)).astype(np.int8)
+    down = np.where(xi > 0, -8, np.where(xi < 0, 7, 0)).astype(np.int8)
+    for r in (5, 77, 9999):
+        codes[r] = up
+    codes[1023] = down
+    packed = pack(codes, sb)
+    xs = np.stack([bf16_bits_of_ints(xi if t % 2 == 0 else -xi) for t in range(n_tok)])
+    zu = float(np.dot(up.astype(np.int64), xi)) / 128.0
+    zd = float(np.dot(down.astype(np.int64), -xi)) / 128.0
+    i, v = q4.lmhead_softcap_argmax_s64(packed, vocab, k, d(xs), 0.0)
+    assert i.cpu().tolist() == [5 if t % 2 == 0 else 1023 for t in range(n_tok)]
+    assert v.cpu().tolist() == [zu if t % 2 == 0 else zd for t in range(n_tok)]
+    i, v = q4.lmhead_softcap_argmax_s64(packed, vocab, k, d(xs), 30.0)
+    assert i.cpu().tolist() == [5 if t % 2 == 0 else 1023 for t in range(n_tok)]
+    assert abs(float(v[0].item()) - float(oracle.softcap(zu))) <= 1e-6 + 1e-4 * abs(zu)
+
+
+def test_lmhead_s64_e4b_head_sampled_tokens():
+    """The E4B head [262144, 2560] for a 64-token chunk. Four tokens are
+    checked against the whole oracle head. For every token, the value must
+    match the oracle's logit of the returned row, and that row must match the
+    single-token head's row or hold an exact logit within both error bars of
+    it."""
+    vocab, k, n_tok = 262144, 2560, 64
+    rng = synth.rng_for(92)
+    codes, sb = synth.q4_weights(rng, vocab, k)
+    packed = pack(codes, sb)
+    xs = synth.bf16_normal(rng, n_tok * k).reshape(n_tok, k)
+    i, v = q4.lmhead_softcap_argmax_s64(packed, vocab, k, d(xs), 30.0)
+    idx, val = i.cpu().tolist(), v.cpu().tolist()
+    for t in (0, 21, 42, 63):
+        ref = oracle.lmhead(codes, sb, xs[t])
+        if ref["margin"] >= 1e-3:
+            assert idx[t] == ref["idx"], (t, idx[t], ref["idx"])
+        assert abs(val[t] - ref["val"]) <= 1e-4 * ref["a_idx"] + 1e-6
+    ws = torch.zeros(q4.lmhead_workspace_bytes(vocab, k), dtype=torch.uint8, device=DEV)
+    for t in range(n_tok):
+        r = idx[t]
+        z, a = oracle.gemv(codes[r:r + 1], sb[r:r + 1], xs[t])
+        assert abs(val[t] - float(oracle.softcap(z[0]))) <= 1e-4 * a[0] + 1e-6, t
+        i1, _ = q4.lmhead_softcap_argmax(packed, vocab, k, d(xs[t]), 30.0, ws)
+        r1 = int(i1.item())
+        if r1 != r:
+            z1, a1 = oracle.gemv(codes[r1:r1 + 1], sb[r1:r1 + 1], xs[t])
+            assert abs(z1[0] - z[0]) <= 1e-4 * (a[0] + a1[0]) + 2e-6, (t, r, r1)
+
+
 def test_lmhead_shared_workspace_and_graph_replays():
     """One workspace serves calls of different sizes back to back and the
     replays of a captured call; every call writes a fresh result (outputs are
