@@ -594,6 +594,51 @@ def cpu_baseline(seconds: float):
     }
 
 
+def cpu_oracle_configs():
+    """The fp64 oracle on each smaller workload, one call each (wall time on
+    the host cores): the [1536, 1536] GEMV, the E2B FFN pair (gate/up GEMV
+    with the GELU product, then the down GEMV), the E2B-shaped head for one
+    vector, and the PLE gather of 64 ids from an E2B-wide table (4096 rows:
+    the gather's work depends on the ids and the row width, not the row
+    count)."""
+    import oracle
+    import synth
+
+    rng = synth.rng_for(0, 98)
+    out = {}
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    c, sb = synth.q4_weights(rng, 1536, 1536)
+    x = synth.bf16_normal(rng, 1536)
+    dt = min(timed(lambda: oracle.gemv(c, sb, x)) for _ in range(3))
+    out["gemv_1536"] = {"seconds": round(dt, 5), "GBs": round(q4_bytes(1536, 1536) / dt / 1e9, 3)}
+    H, D = 6144, 1536
+    cg, sg = synth.q4_weights(rng, 2 * H, D)
+    cd, sd = synth.q4_weights(rng, D, H)
+
+    def ffn():
+        _, g, u, _, _ = oracle.gelu_mul(cg, sg, x)
+        oracle.gemv(cd, sd, oracle.ffn_down_input_bits(g, u))
+
+    dt = min(timed(ffn) for _ in range(2))
+    b = weight_bytes(2 * H, D) + weight_bytes(D, H)
+    out["ffn_e2b"] = {"seconds": round(dt, 4), "GBs": round(b / dt / 1e9, 3)}
+    del cg, sg, cd, sd
+    ch, shb = synth.q4_weights(rng, synth.VOCAB, D)
+    dt = timed(lambda: oracle.lmhead(ch, shb, x))
+    out["head_e2b"] = {"seconds": round(dt, 3), "GBs": round(weight_bytes(synth.VOCAB, D) / dt / 1e9, 3)}
+    del ch, shb
+    dim = synth.SHAPES["ple_e2b"]["dim"]
+    table, scale, ids = synth.ple_inputs(rng, 4096, dim, 64)
+    dt = min(timed(lambda: oracle.ple_gather(table, scale, ids)) for _ in range(3))
+    out["ple_e2b_T64"] = {"seconds": round(dt, 5), "GBs": round(64 * (dim + 4 + 4 * dim + 4) / dt / 1e9, 3)}
+    return out
+
+
 def load_traffic(kernel: str, launches_per_step: dict):
     """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
     summaries, scaled by the copy-kernel calibration; None when absent or
@@ -793,6 +838,7 @@ def main():
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        result["cpu_oracle_configs"] = cpu_oracle_configs()
 
     print(json.dumps(result), flush=True)
 
