@@ -23,6 +23,7 @@ from .q4_oracle import (  # noqa: F401
     ple_gather,
     q4_quantize,
     rowq_gelu_mul,
+    rowq_gather,
     rowq_gemv,
     rowq_pack,
     rowq_unpack,

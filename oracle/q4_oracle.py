@@ -288,6 +288,34 @@ def ple_gather(table, row_scale, ids, mult: float = 16.0):
     return out, err
 
 
+def rowq_gather(w_bytes, scales, bits: int, group: int, ids, mult: float = 16.0):
+    """Row gather on the dense per-row formats: out[t, j] = RN_fp32(c[id_t, j]
+    * s[id_t, j // group] * mult). [MIX] bundle table and mixed-bit map: the
+    input embedding (tied with the head) is INT2 [262144, 1536] with one scale
+    per row, and the PLE table stores each row as 35 layer-major 128-byte INT4
+    blocks with one scale per (row, layer); the codes follow rowq_unpack.
+    ``scales`` is fp32 [V, dim / group]. The product of a code, an fp32 scale
+    and the fp32 multiplier is exact in 80-bit extended precision (at most
+    4 + 24 + 24 significant bits) and is rounded once to fp32. Ids outside
+    [0, V) give a zero row and set the returned error flag. Returns
+    (out float32 [T, dim], err int)."""
+    sc = np.asarray(scales, dtype=np.float32)
+    v, ng = sc.shape
+    dim = ng * group
+    w = np.ascontiguousarray(w_bytes).view(np.uint8).reshape(v, dim * bits // 8)
+    ids = np.asarray(ids, dtype=np.int64).reshape(-1)
+    out = np.zeros((ids.size, dim), dtype=np.float32)
+    ok = (ids >= 0) & (ids < v)
+    err = int((~ok).any())
+    if ok.any():
+        rows = ids[ok]
+        c = rowq_unpack(w[rows], rows.size, dim, bits).astype(np.longdouble)
+        s = np.repeat(sc[rows].astype(np.longdouble), group, axis=1)
+        m = np.longdouble(np.float32(mult))
+        out[ok] = (c * s * m).astype(np.float32)
+    return out, err
+
+
 # --------------------------------------------------------- FFN host glue --
 def gelu_tanh_f32(g):
     """tanh-approximation GELU evaluated in fp32 ([MIX] fused gate/up kernel:

@@ -339,6 +339,9 @@ def test_page_shape_constants():
     assert synth.VOCAB * synth.SHAPES["ple_e2b"]["dim"] == 2_348_810_240
     assert synth.VOCAB * 4 == 1_048_576
     assert synth.SHAPES["ple_e2b"]["dim"] == 8960
+    # the mixed-bit PLE table: 35 layer-major 128-byte INT4 blocks per row
+    # (4480 bytes) hold the same 35 x 256 values per token
+    assert 35 * 128 == 4480 and 4480 * 2 == synth.SHAPES["ple_e2b"]["dim"] == 35 * 256
     assert synth.SHAPES["ple_e4b"]["dim"] == 10752
     assert 16.0 == math.sqrt(256)
     assert f"{np.float32(math.sqrt(1536)):.6f}" == "39.191837"
@@ -594,6 +597,47 @@ def test_rowq_gemv_bruteforce_fraction(bits):
         ae = abs(Fraction(float(sc[r]))) * sum(abs(Fraction(c) * v) for c, v in zip(codes, xs))
         assert abs(Fraction(y[r]) - ye) <= Fraction(1, 10 ** 12) * ae
         assert abs(Fraction(a[r]) - ae) <= Fraction(1, 10 ** 12) * ae
+
+
+def test_rowq_gather_hand_decoded_rows():
+    # INT2 row 0xE4 -> codes 0, 1, -2, -1; scale 0.5, multiplier 2 -> the codes
+    w = np.array([[0xE4], [0x1B]], dtype=np.uint8)
+    out, err = oracle.rowq_gather(w, np.array([[0.5], [3.0]], dtype=np.float32), 2, 4, [0, 1, 0], 2.0)
+    assert err == 0
+    assert out.tolist() == [[0, 1, -2, -1], [-6, -12, 6, 0], [0, 1, -2, -1]]
+    # INT4, two groups of two codes: 0x8F 0x70 -> -1, -8 | 0, 7 with scales
+    # 0.25 and 4 per group, multiplier 1
+    w = np.array([[0x8F, 0x70]], dtype=np.uint8)
+    out, err = oracle.rowq_gather(w, np.array([[0.25, 4.0]], dtype=np.float32), 4, 2, [0], 1.0)
+    assert err == 0 and out.tolist() == [[-0.25, -2.0, 0.0, 28.0]]
+    # an id outside the table: zero row and the flag
+    out, err = oracle.rowq_gather(w, np.array([[0.25, 4.0]], dtype=np.float32), 4, 2, [1, 0, -1], 1.0)
+    assert err == 1 and out[0].tolist() == [0, 0, 0, 0] and out[2].tolist() == [0, 0, 0, 0]
+    assert out[1].tolist() == [-0.25, -2.0, 0.0, 28.0]
+
+
+@pytest.mark.parametrize("bits,group", [(2, 64), (2, 256), (4, 32), (4, 128)])
+def test_rowq_gather_bruteforce_fraction(bits, group):
+    # bytes decoded bit by bit, the product rounded from the exact rational;
+    # multipliers 16 (PLE), fp32(sqrt(1536)) (token embedding) and 0.3
+    rng = np.random.default_rng(75 + bits + group)
+    v, dim = 6, 256
+    w = rng.integers(0, 256, size=(v, dim * bits // 8), dtype=np.uint8)
+    sc = rng.uniform(1e-3, 1e-2, size=(v, dim // group)).astype(np.float32)
+    ids = np.array([5, 0, 3, 3], dtype=np.int32)
+    for mult in (16.0, float(np.float32(math.sqrt(1536))), 0.3):
+        out, err = oracle.rowq_gather(w, sc, bits, group, ids, mult)
+        assert err == 0
+        m = Fraction(float(np.float32(mult)))
+        for t, r in enumerate(ids.tolist()):
+            codes = []
+            for byte in w[r].tolist():
+                for i in range(8 // bits):
+                    u = (byte >> (i * bits)) & ((1 << bits) - 1)
+                    codes.append(u - (1 << bits) if u >= (1 << (bits - 1)) else u)
+            for j in range(dim):
+                ref = rn32(codes[j] * Fraction(float(sc[r, j // group])) * m)
+                assert f32_bits(float(out[t, j])) == f32_bits(ref), (bits, group, mult, t, j)
 
 
 def test_rowq_gelu_mul_pairs_gate_row_j_with_up_row_h_plus_j():
