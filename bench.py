@@ -424,7 +424,9 @@ def probe_configs(torch, dev, wl: Workload, seed: int, reps: int = 10):
       100 activation vectors over 3 copies of the head, one vector per call,
       and the same 100 vectors 8 per call (13 calls of the multi-vector head);
     * ple: the E2B table [262144, 8960] for 1 and 64 ids, the E4B table
-      [262144, 10752] for 64 ids."""
+      [262144, 10752] for 64 ids;
+    * rowq_gather: the mixed-bit INT2 token embedding [262144, 1536] and the
+      INT4 PLE table [262144, 35 x 256], for 1 and 64 ids."""
     import int4_weight_only_block_amd as q4
     import synth
 
@@ -544,6 +546,27 @@ def probe_configs(torch, dev, wl: Workload, seed: int, reps: int = 10):
                                    "bytes_per_launch": b, "achieved_GBs": round(b / us / 1e3, 1)}
     out["ple"] = ple
     del t2, sc2
+    # --- mixed-bit tables: INT2 token embedding, INT4 PLE table
+    rg = {}
+    for name, bits, dim, group, mult in (("int2_embed", 2, 1536, 1536, 39.191837), ("int4_ple", 4, 8960, 256, 16.0)):
+        V = synth.VOCAB
+        w = torch.randint(0, 256, (V, dim * bits // 8), dtype=torch.uint8, device=dev, generator=g)
+        sc = torch.empty((V, dim // group), dtype=torch.float32, device=dev).uniform_(1e-3, 1e-2, generator=g)
+        for T in (1, 64):
+            ids = torch.randint(0, V, (32, T), dtype=torch.int32, device=dev, generator=g)
+            o = torch.empty((T, dim), dtype=torch.float32, device=dev)
+
+            def run_rg(w=w, sc=sc, ids=ids, o=o, bits=bits, group=group, mult=mult):
+                for r in range(ids.shape[0]):
+                    q4.rowq_gather(w, sc, bits, group, ids[r], mult, out=o)
+
+            us = time_graph(run_rg) / ids.shape[0]
+            b = T * (dim * bits // 8 + 4 * (dim // group) + 4 + 4 * dim)
+            rg[f"{name}_T{T}"] = {"table": [V, dim], "bits": bits, "group": group, "ids": T,
+                                  "avg_launch_us": round(us, 3), "bytes_per_launch": b,
+                                  "achieved_GBs": round(b / us / 1e3, 1)}
+        del w, sc
+    out["rowq_gather"] = rg
     torch.cuda.synchronize()
     return out
 

@@ -306,6 +306,31 @@ int ple_gather(const int8_t* table, const float* row_scale, int64_t vocab,
                int64_t dim, const int32_t* ids, int64_t n_ids, float mult,
                float* out, int32_t* err_flag, void* stream);
 
+/* rowq_gather: row gather on the dense per-row INT2 / INT4 packing of
+ * rowq_gemv, with one fp32 scale per group of columns:
+ * out[t, j] = RN_fp32(c[ids[t], j] * scales[ids[t], j / group] * mult)
+ * (mixed-bit page, bundle table and mixed-bit map: the input embedding, tied
+ * with the head, is INT2 [262144, 1536] with one scale per row, group = dim,
+ * mult = sqrt(1536); the PLE table stores each row as 35 layer-major
+ * 128-byte INT4 blocks with one scale per row and layer, group = 256,
+ * mult = 16). The product is rounded once to fp32, as in ple_gather.
+ *   w        [vocab, dim * bits / 8] bytes, codes as rowq_gemv (INT2: 4 per
+ *            byte, first code in bits [1:0]; INT4: low nibble first; two's
+ *            complement); 16-byte aligned.
+ *   scales   fp32 [vocab, dim / group].
+ *   bits     2 or 4.
+ *   group    columns per scale: divides dim, a multiple of 64 (INT2) or 32
+ *            (INT4).
+ *   ids      int32 [n_ids]; an id outside [0, vocab) yields a zero row and
+ *            sets *err_flag = 1 (when err_flag is not NULL).
+ *   out      fp32 [n_ids, dim] row-major, 16-byte aligned.
+ * Errors: NULL pointer (err_flag may be NULL), bits not 2 or 4, vocab <= 0,
+ *         dim not a positive multiple of 64 / 32, group invalid, n_ids not
+ *         in [0, 65535], misalignment. */
+int rowq_gather(const void* w, const float* scales, int64_t vocab, int64_t dim,
+                int32_t bits, int64_t group, const int32_t* ids, int64_t n_ids,
+                float mult, float* out, int32_t* err_flag, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -60,6 +60,8 @@ _SIGNATURES = {
                                                  ctypes.c_size_t, _c_p, _c_p, _c_p]),
     "ple_gather": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_i64, ctypes.c_float, _c_p,
                                   _c_p, _c_p]),
+    "rowq_gather": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, ctypes.c_int32, _c_i64, _c_p, _c_i64,
+                                   ctypes.c_float, _c_p, _c_p, _c_p]),
 }
 
 _lib = None
@@ -374,4 +376,24 @@ def ple_gather(table: torch.Tensor, row_scale: torch.Tensor, ids: torch.Tensor,
     po = _dev(out, "out", _F32, n_ids * dim)
     pe = _dev(err_flag, "err_flag", _I32, 1) if err_flag is not None else None
     _check(lib().ple_gather(pt, psc, vocab, dim, pi, n_ids, float(mult), po, pe, _stream(table)))
+    return out
+
+
+def rowq_gather(w: torch.Tensor, scales: torch.Tensor, bits: int, group: int, ids: torch.Tensor,
+                mult: float = 16.0, out: torch.Tensor | None = None,
+                err_flag: torch.Tensor | None = None) -> torch.Tensor:
+    """out[t, :] fp32 = codes[ids[t]] * scales[ids[t], j // group] * mult,
+    rounded once; w holds the dense INT2 / INT4 rows, scales is fp32
+    [vocab, dim / group]."""
+    vocab, ngroups = scales.shape
+    dim = ngroups * group
+    pw = _dev(w, "w", _BYTES, vocab * dim * bits // 8)
+    ps = _dev(scales, "scales", _F32)
+    pi = _dev(ids, "ids", _I32)
+    n_ids = ids.numel()
+    if out is None:
+        out = torch.empty((n_ids, dim), dtype=torch.float32, device=w.device)
+    po = _dev(out, "out", _F32, n_ids * dim)
+    pe = _dev(err_flag, "err_flag", _I32, 1) if err_flag is not None else None
+    _check(lib().rowq_gather(pw, ps, vocab, dim, bits, group, pi, n_ids, float(mult), po, pe, _stream(w)))
     return out

@@ -12,7 +12,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(q4.LIB_PATH), reason="libq4de
 
 EXPECTED = {
     "q4dec_abi_version", "q4dec_last_error", "q4_packed_bytes", "q4_pack", "q4_quantize", "q4_gemv", "q4_gemv_gelu_mul", "q4_gemv_multi", "rowq_gemv", "rowq_gemv_gelu_mul",
-    "q4_gemm_s64", "q4_gemm_workspace_bytes", "lmhead_workspace_bytes", "lmhead_softcap_argmax", "lmhead_multi_workspace_bytes", "lmhead_softcap_argmax_multi", "lmhead_s64_workspace_bytes", "lmhead_softcap_argmax_s64", "ple_gather",
+    "q4_gemm_s64", "q4_gemm_workspace_bytes", "lmhead_workspace_bytes", "lmhead_softcap_argmax", "lmhead_multi_workspace_bytes", "lmhead_softcap_argmax_multi", "lmhead_s64_workspace_bytes", "lmhead_softcap_argmax_s64", "ple_gather", "rowq_gather",
 }
 
 
@@ -280,6 +280,33 @@ def test_head_s64_validation():
     assert call(0, FAKE + 8) == q4.ERR_ALIGN
     assert call(3, FAKE + 8) == q4.ERR_ALIGN
     assert call(8, FAKE + 2) == q4.ERR_ALIGN
+
+
+def test_rowq_gather_validation():
+    L = q4.lib()
+    # w, scales, vocab, dim, bits, group, ids, n_ids, mult, out, err_flag, stream
+    ok = [FAKE, FAKE, 100, 1536, 2, 1536, FAKE, 4, 39.19, FAKE, None, None]
+
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return L.rowq_gather(*a)
+
+    for i, name in [(0, "w"), (1, "scales"), (6, "ids"), (9, "out")]:
+        assert call(i, None) == q4.ERR_NULL and name in q4.q4dec_last_error()
+    assert call(4, 8) == q4.ERR_SHAPE and "bits" in q4.q4dec_last_error()
+    assert call(2, 0) == q4.ERR_SHAPE and "vocab" in q4.q4dec_last_error()
+    assert call(3, 1504) == q4.ERR_SHAPE and "dim" in q4.q4dec_last_error()   # not a multiple of 64
+    assert call(5, 96) == q4.ERR_SHAPE and "group" in q4.q4dec_last_error()   # INT2 groups of 64
+    assert call(5, 1000) == q4.ERR_SHAPE                                       # does not divide dim
+    assert call(7, -1) == q4.ERR_SHAPE and "n_ids" in q4.q4dec_last_error()
+    assert call(7, 0) == q4.OK                                                 # no-op
+    assert call(0, FAKE + 8) == q4.ERR_ALIGN
+    assert call(9, FAKE + 4) == q4.ERR_ALIGN
+    a = list(ok)
+    a[4], a[3], a[5] = 4, 8960, 256   # the INT4 PLE layout is accepted
+    a[7] = 0
+    assert L.rowq_gather(*a) == q4.OK
 
 
 def test_ple_validation():

@@ -763,6 +763,76 @@ def test_ple_gather_out_of_range_ids():
     assert int(flag.item()) == 0
 
 
+# ------------------------------------ mixed-bit INT2 / INT4 row gathers --
+@pytest.mark.parametrize("bits,dim,group,mult", [(2, 1536, 1536, 39.191837),  # INT2 token embedding
+                                                 (4, 8960, 256, 16.0)])       # INT4 PLE table
+def test_rowq_gather_full_tables(bits, dim, group, mult):
+    """The mixed-bit recipe's tables at full size: the INT2 input embedding
+    [262144, 1536] with a per-row scale and sqrt(1536), and the INT4 PLE table
+    [262144, 35 x 256] with one scale per row and layer and 16.0; 1 and 64 ids
+    with the first and last rows and a duplicate. Bit-exact."""
+    vocab = synth.VOCAB
+    g = torch.Generator(device=DEV)
+    g.manual_seed(77 + bits)
+    w = torch.randint(0, 256, (vocab, dim * bits // 8), dtype=torch.uint8, device=DEV, generator=g)
+    sc = torch.empty((vocab, dim // group), dtype=torch.float32, device=DEV).uniform_(1e-3, 1e-2, generator=g)
+    rng = synth.rng_for(78, bits)
+    for n_ids in (1, 64):
+        ids = synth.ple_ids(rng, vocab, n_ids)
+        if n_ids == 64:
+            ids[:4] = [0, vocab - 1, ids[10], ids[10]]
+        idt = d(ids)
+        out = q4.rowq_gather(w, sc, bits, group, idt, mult).cpu().numpy()
+        ref, err = oracle.rowq_gather(w[idt.long()].cpu().numpy(), sc[idt.long()].cpu().numpy(), bits, group,
+                                      np.arange(n_ids, dtype=np.int32), mult)
+        assert err == 0
+        assert np.array_equal(out.view(np.uint32), ref.view(np.uint32)), (bits, n_ids)
+
+
+@pytest.mark.parametrize("bits,dim,group", [(2, 64, 64), (2, 4096, 128), (2, 1536, 64), (4, 32, 32),
+                                            (4, 96, 32), (4, 4096, 2048), (4, 8960, 256)])
+def test_rowq_gather_shapes_and_multipliers(bits, dim, group):
+    rng = synth.rng_for(79, bits, dim, group)
+    vocab = 3000
+    w = rng.integers(0, 256, size=(vocab, dim * bits // 8), dtype=np.uint8)
+    sc = rng.uniform(1e-3, 1e-2, size=(vocab, dim // group)).astype(np.float32)
+    ids = synth.ple_ids(rng, vocab, 37)
+    for mult in (16.0, float(np.float32(np.sqrt(1536.0))), 0.3):
+        out = q4.rowq_gather(d(w), d(sc), bits, group, d(ids), mult).cpu().numpy()
+        ref, _ = oracle.rowq_gather(w, sc, bits, group, ids, mult)
+        assert np.array_equal(out.view(np.uint32), ref.view(np.uint32)), (bits, dim, group, mult)
+
+
+def test_rowq_gather_int2_extreme_scales():
+    """INT2 scales near the top of the fp32 range (where code * scale alone
+    would overflow but the product with mult < 1 is finite), at the bottom
+    (subnormal) and around 2^126, with multipliers below and above one."""
+    rng = synth.rng_for(81)
+    w = rng.integers(0, 256, size=(8, 16), dtype=np.uint8)   # INT2, dim 64
+    sc = np.array([[3.0e38], [2.0 ** 126], [2.0 ** 126 * 0.999], [1.0e-40], [1.5e-45], [-3.0e38], [1.0], [0.0]],
+                  dtype=np.float32)
+    ids = np.arange(8, dtype=np.int32)
+    for mult in (0.3, 16.0, float(np.float32(np.sqrt(1536.0)))):
+        out = q4.rowq_gather(d(w), d(sc), 2, 64, d(ids), mult).cpu().numpy()
+        ref, _ = oracle.rowq_gather(w, sc, 2, 64, ids, mult)
+        assert np.array_equal(out.view(np.uint32), ref.view(np.uint32)), mult
+
+
+def test_rowq_gather_out_of_range_ids():
+    rng = synth.rng_for(80)
+    w = rng.integers(0, 256, size=(50, 128), dtype=np.uint8)   # INT4, dim 256
+    sc = rng.uniform(1e-3, 1e-2, size=(50, 2)).astype(np.float32)
+    ids = np.array([3, -1, 50, 49], dtype=np.int32)
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    out = q4.rowq_gather(d(w), d(sc), 4, 128, d(ids), 16.0, err_flag=flag).cpu().numpy()
+    ref, err = oracle.rowq_gather(w, sc, 4, 128, ids, 16.0)
+    assert int(flag.item()) == 1 and err == 1
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+    flag.zero_()
+    q4.rowq_gather(d(w), d(sc), 4, 128, d(np.array([0, 49], np.int32)), 16.0, err_flag=flag)
+    assert int(flag.item()) == 0
+
+
 # ----------------------------------------------------------- S=64 GEMM --
 @pytest.mark.parametrize("n,k,n_tok", [(1536, 1536, 64), (64, 32, 64), (100, 96, 1), (300, 2560, 37),
                                        (3072, 2560, 64), (2560, 10240, 64), (77, 16384, 5),
