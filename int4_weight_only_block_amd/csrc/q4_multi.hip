@@ -284,15 +284,16 @@ __global__ __launch_bounds__(kMThreads) void q4_multi_kernel(const uint8_t* __re
   }
 }
 
-// Second head launch: workgroup v reduces the partials of vector v and caps
-// the winner (the cap is increasing, so capping the winner alone gives the
-// capped maximum). Each thread issues its loads in batches of 16 before
+// Second launch of the multi-vector head and of the 64-token head:
+// workgroup v reduces the partials of vector v (entries w * stride + v) and
+// caps the winner (the cap is increasing, so capping the winner alone gives
+// the capped maximum). Each thread issues its loads in batches of 16 before
 // comparing; the comparator is a total order, so the order does not matter.
 constexpr int kMRedBatch = 16;
-__global__ __launch_bounds__(kMThreads) void lmhead_multi_reduce_kernel(const uint2* __restrict__ partials, int g,
-                                                                        int stride, float cap,
-                                                                        int32_t* __restrict__ idx_out,
-                                                                        float* __restrict__ val_out) {
+__global__ __launch_bounds__(kMThreads) void argmax_partials_reduce_kernel(const uint2* __restrict__ partials,
+                                                                           int g, int stride, float cap,
+                                                                           int32_t* __restrict__ idx_out,
+                                                                           float* __restrict__ val_out) {
   const int v = blockIdx.x;
   float best = -INFINITY;
   int bidx = INT_MAX;
@@ -424,7 +425,7 @@ int multi_run(const MultiPlan& p, const uint8_t* nib, const uint16_t* scl, int64
 
 void reduce_argmax_partials(const uint2* partials, int g, int stride, int nvec, float cap, int32_t* idx_out,
                             float* val_out, hipStream_t st) {
-  hipLaunchKernelGGL(lmhead_multi_reduce_kernel, dim3(unsigned(nvec)), dim3(kMThreads), 0, st, partials, g, stride,
+  hipLaunchKernelGGL(argmax_partials_reduce_kernel, dim3(unsigned(nvec)), dim3(kMThreads), 0, st, partials, g, stride,
                      cap, idx_out, val_out);
 }
 
