@@ -833,6 +833,93 @@ def test_rowq_gather_out_of_range_ids():
     assert int(flag.item()) == 0
 
 
+# ------------------------------------------------------- graph replays --
+def test_every_entry_point_replays_in_a_graph():
+    """One call of every entry point captured in a HIP graph, replayed four
+    times with fresh inputs and eager work between replays; each replay must
+    equal an eager run of the same calls bit for bit (nothing in the library
+    records a memset or depends on state left by a previous call)."""
+    rng = synth.rng_for(95)
+    n, k, m = 1000, 2560, 4
+    codes, sb = synth.q4_weights(rng, 2 * n, k)
+    packed = pack(codes, sb)
+    w2 = d(rng.integers(0, 256, size=(n, k // 4), dtype=np.uint8))
+    s2 = d(rng.uniform(1e-3, 1e-2, size=n).astype(np.float32))
+    table, scale, _ = synth.ple_inputs(rng, 5000, 256, 1)
+    table, scale = d(table), d(scale)
+    x = torch.zeros(k, dtype=torch.int16, device=DEV)
+    xm = torch.zeros((m, k), dtype=torch.int16, device=DEV)
+    x64 = torch.zeros((64, k), dtype=torch.int16, device=DEV)
+    ids = torch.zeros(8, dtype=torch.int32, device=DEV)
+    xb = torch.zeros((1, k), dtype=torch.int16, device=DEV)
+    outs = {
+        "y": torch.empty(2 * n, dtype=torch.float32, device=DEV),
+        "a": torch.empty(n, dtype=torch.int16, device=DEV),
+        "ym": torch.empty((m, 2 * n), dtype=torch.float32, device=DEV),
+        "yg": torch.empty((64, 2 * n), dtype=torch.float32, device=DEV),
+        "yr": torch.empty(n, dtype=torch.float32, device=DEV),
+        "hi": torch.empty(1, dtype=torch.int32, device=DEV), "hv": torch.empty(1, dtype=torch.float32, device=DEV),
+        "mi": torch.empty(m, dtype=torch.int32, device=DEV), "mv": torch.empty(m, dtype=torch.float32, device=DEV),
+        "si": torch.empty(64, dtype=torch.int32, device=DEV), "sv": torch.empty(64, dtype=torch.float32, device=DEV),
+        "pg": torch.empty((8, 256), dtype=torch.float32, device=DEV),
+        "rg": torch.empty((8, k), dtype=torch.float32, device=DEV),
+        "qc": torch.empty((1, k), dtype=torch.int8, device=DEV),
+        "qs": torch.empty((1, k // 32), dtype=torch.int16, device=DEV),
+        "pk": torch.empty(q4.q4_packed_bytes(64, k), dtype=torch.uint8, device=DEV),
+    }
+    pack_codes = torch.zeros((64, k), dtype=torch.int8, device=DEV)
+    pack_scales = torch.zeros((64, k // 32), dtype=torch.int16, device=DEV)
+    ws_g = torch.empty(q4.q4_gemm_workspace_bytes(2 * n, k), dtype=torch.uint8, device=DEV)
+    ws_h = torch.empty(q4.lmhead_workspace_bytes(2 * n, k), dtype=torch.uint8, device=DEV)
+    ws_m = torch.empty(q4.lmhead_multi_workspace_bytes(2 * n, k, m), dtype=torch.uint8, device=DEV)
+    ws_s = torch.empty(q4.lmhead_s64_workspace_bytes(2 * n, k), dtype=torch.uint8, device=DEV)
+    w_int2_rows = d(rng.integers(0, 256, size=(5000, k // 4), dtype=np.uint8))
+    s_int2_rows = d(rng.uniform(1e-3, 1e-2, size=(5000, 1)).astype(np.float32))
+
+    def calls():
+        q4.q4_gemv(packed, 2 * n, k, x, outs["y"])
+        q4.q4_gemv_gelu_mul(packed, 2 * n, k, x, outs["a"])
+        q4.q4_gemv_multi(packed, 2 * n, k, xm, outs["ym"])
+        q4.q4_gemm_s64(packed, 2 * n, k, x64, outs["yg"], ws_g)
+        q4.rowq_gemv(w2, s2, n, k, 2, x, outs["yr"])
+        q4.lmhead_softcap_argmax(packed, 2 * n, k, x, 30.0, ws_h, outs["hi"], outs["hv"])
+        q4.lmhead_softcap_argmax_multi(packed, 2 * n, k, xm, 30.0, ws_m, outs["mi"], outs["mv"])
+        q4.lmhead_softcap_argmax_s64(packed, 2 * n, k, x64, 30.0, ws_s, outs["si"], outs["sv"])
+        q4.ple_gather(table, scale, ids, 16.0, out=outs["pg"])
+        q4.rowq_gather(w_int2_rows, s_int2_rows, 2, k, ids, 39.191837, out=outs["rg"])
+        q4.q4_quantize(xb, q4.QUANT_Q4_0, codes=outs["qc"], scales=outs["qs"])
+        q4.q4_pack(pack_codes, pack_scales, packed=outs["pk"])
+
+    def fresh_inputs(rep):
+        r = synth.rng_for(96, rep)
+        x.copy_(d(synth.bf16_normal(r, k)))
+        xm.copy_(d(synth.bf16_normal(r, (m, k))))
+        x64.copy_(d(synth.bf16_normal(r, (64, k))))
+        xb.copy_(d(synth.bf16_normal(r, (1, k))))
+        ids.copy_(d(synth.ple_ids(r, 5000, 8)))
+        c, sc = synth.q4_weights(r, 64, k)
+        pack_codes.copy_(d(c))
+        pack_scales.copy_(d(sc))
+
+    fresh_inputs(0)
+    calls()  # warm-up outside capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        calls()
+    for rep in range(1, 5):
+        fresh_inputs(rep)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = {name: t.clone() for name, t in outs.items()}
+        q4.q4_gemv(packed, 2 * n, k, x64[0], outs["y"])  # unrelated eager work between replays
+        calls()
+        torch.cuda.synchronize()
+        for name, t in outs.items():
+            assert torch.equal(got[name], t), (rep, name)
+
+
 # ----------------------------------------------------------- S=64 GEMM --
 @pytest.mark.parametrize("n,k,n_tok", [(1536, 1536, 64), (64, 32, 64), (100, 96, 1), (300, 2560, 37),
                                        (3072, 2560, 64), (2560, 10240, 64), (77, 16384, 5),
