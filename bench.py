@@ -343,6 +343,40 @@ def probe_quantize(torch, dev, seed: int, reps: int = 20):
             "achieved_GBs": round(b / us / 1e3, 1), "frac_of_hbm_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
 
 
+def probe_pack(torch, dev, seed: int, reps: int = 20):
+    """q4_pack on an E4B gate+up sized matrix [20480, 2560] (load time, not
+    part of a decode step): int8 codes and fp16 scales read, the packed
+    nibble, scale and row-exponent planes written, four distinct inputs in
+    rotation. The call is the nibble packing kernel plus the row-exponent
+    kernel."""
+    import int4_weight_only_block_amd as q4
+    import synth
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed + 6)
+    n, k = 20480, 2560
+    ins = [synth.torch_q4_weights(g, n, k, dev) for _ in range(4)]
+    packed = torch.empty(q4.q4_packed_bytes(n, k), dtype=torch.uint8, device=dev)
+    q4.q4_pack(ins[0][0], ins[0][1], packed)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for c, sc in ins:
+            q4.q4_pack(c, sc, packed)
+    graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (reps * len(ins))
+    b = n * k + n * (k // 32) * 2 + weight_bytes(n, k) + n
+    return {"shape": [n, k], "avg_call_us": round(us, 3), "bytes_per_call": b,
+            "achieved_GBs": round(b / us / 1e3, 1), "frac_of_hbm_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+
 def probe_rowq(torch, dev, seed: int, reps: int = 20):
     """Per-row symmetric INT2 GEMVs on the mobile mixed-bit kernel-probe
     workload: six INT2 FFNs (gate and up [12288, 1536], down [1536, 12288])
@@ -856,6 +890,7 @@ def main():
     if not args.no_probe:
         result["verify_m4"] = probe_verify_m4(torch, wl, args.seed)
         result["quantize_e4b_gate_up"] = probe_quantize(torch, dev, args.seed)
+        result["pack_e4b_gate_up"] = probe_pack(torch, dev, args.seed)
         result["rowq_int2_kprobe"] = probe_rowq(torch, dev, args.seed)
         result["configs"] = probe_configs(torch, dev, wl, args.seed)
 
