@@ -91,9 +91,12 @@ def rowq_unpack(w_bytes, n: int, k: int, bits: int) -> np.ndarray:
     recipe: per-channel symmetric linear, all zero points 0, bytes = elements *
     bits / 8; packing convention: INT2 holds 4 codes per byte with the first
     code in bits [1:0], two's complement in [-2, 1]; INT4 is the same with
-    nibbles, low nibble first, in [-8, 7])."""
+    nibbles, low nibble first, in [-8, 7]; the INT8 PLE gate / projection
+    matrices are plain signed bytes, [-128, 127])."""
+    if bits == 8:
+        return np.ascontiguousarray(w_bytes).view(np.int8).reshape(n, k).copy()
     if bits not in (2, 4):
-        raise ValueError("bits must be 2 or 4")
+        raise ValueError("bits must be 2, 4 or 8")
     per = 8 // bits
     b = np.ascontiguousarray(w_bytes).view(np.uint8).reshape(n, k // per)
     shifts = np.arange(per, dtype=np.uint8) * bits
@@ -108,6 +111,8 @@ def rowq_pack(codes, bits: int) -> np.ndarray:
     lo, hi = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
     if ((c < lo) | (c > hi)).any():
         raise ValueError("codes out of range")
+    if bits == 8:
+        return c.astype(np.int8).view(np.uint8)
     per = 8 // bits
     n, k = c.shape
     u = (c & ((1 << bits) - 1)).astype(np.uint8).reshape(n, k // per, per)

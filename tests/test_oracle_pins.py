@@ -571,13 +571,16 @@ def test_rowq_unpack_bytes_follow_the_stated_convention():
     # INT4: low nibble first, two's complement: 0x8F -> -1, -8 ; 0x70 -> 0, 7
     b = np.array([[0x8F, 0x70]], dtype=np.uint8)
     assert oracle.rowq_unpack(b, 1, 4, 4).tolist() == [[-1, -8, 0, 7]]
+    # INT8: signed bytes: 0x80 -> -128, 0x7F -> 127, 0xFF -> -1
+    b = np.array([[0x80, 0x7F, 0xFF, 0x01]], dtype=np.uint8)
+    assert oracle.rowq_unpack(b, 1, 4, 8).tolist() == [[-128, 127, -1, 1]]
     rng = np.random.default_rng(70)
-    for bits in (2, 4):
+    for bits in (2, 4, 8):
         c = rng.integers(-(1 << (bits - 1)), 1 << (bits - 1), size=(3, 64)).astype(np.int8)
         assert np.array_equal(oracle.rowq_unpack(oracle.rowq_pack(c, bits), 3, 64, bits), c)
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 4, 8])
 def test_rowq_gemv_bruteforce_fraction(bits):
     rng = np.random.default_rng(71 + bits)
     n, k = 5, 128
