@@ -460,7 +460,9 @@ def probe_configs(torch, dev, wl: Workload, seed: int, reps: int = 10):
     * ple: the E2B table [262144, 8960] for 1 and 64 ids, the E4B table
       [262144, 10752] for 64 ids;
     * rowq_gather: the mixed-bit INT2 token embedding [262144, 1536] and the
-      INT4 PLE table [262144, 35 x 256], for 1 and 64 ids."""
+      INT4 PLE table [262144, 35 x 256], for 1 and 64 ids;
+    * rowq_int8: the mixed-bit INT8 per-row GEMVs (PLE gate [256, 1536],
+      projection [1536, 256], model projection [8960, 1536])."""
     import int4_weight_only_block_amd as q4
     import synth
 
@@ -601,6 +603,25 @@ def probe_configs(torch, dev, wl: Workload, seed: int, reps: int = 10):
                                   "achieved_GBs": round(b / us / 1e3, 1)}
         del w, sc
     out["rowq_gather"] = rg
+    # --- INT8 per-row GEMVs of the mixed-bit recipe (PLE gate, PLE projection,
+    # per-layer model projection), 35 distinct copies each (one per layer)
+    r8 = {}
+    for name, n, k in (("ple_gate", 256, 1536), ("ple_proj", 1536, 256), ("model_proj", 8960, 1536)):
+        ws8 = [torch.randint(0, 256, (n, k), dtype=torch.uint8, device=dev, generator=g) for _ in range(35)]
+        sc8 = torch.empty(n, dtype=torch.float32, device=dev).uniform_(1e-3, 1e-2, generator=g)
+        x8 = synth.torch_bf16_normal(g, k, dev)
+        y8 = torch.empty(n, dtype=torch.float32, device=dev)
+
+        def run_r8(ws8=ws8, sc8=sc8, x8=x8, y8=y8, n=n, k=k):
+            for w8 in ws8:
+                q4.rowq_gemv(w8, sc8, n, k, 8, x8, y8)
+
+        us = time_graph(run_r8) / len(ws8)
+        b = n * k + 4 * n + 2 * k + 4 * n
+        r8[name] = {"shape": [n, k], "avg_launch_us": round(us, 3), "bytes_per_launch": b,
+                    "achieved_GBs": round(b / us / 1e3, 1)}
+        del ws8
+    out["rowq_int8"] = r8
     torch.cuda.synchronize()
     return out
 

@@ -137,20 +137,21 @@ int q4_gemv(const void* packed, int64_t n, int64_t k, const uint16_t* x,
 int q4_gemv_multi(const void* packed, int64_t n, int64_t k, const uint16_t* x,
                   int64_t m, float* y, void* stream);
 
-/* rowq_gemv: per-row symmetric INT4 / INT2 matvec on the dense packing of the
- * mixed-bit recipe (mixed-bit page: decode recipe, per-channel symmetric
- * linear weights with all zero points 0; packing convention: INT2 holds 4
- * codes per byte, first code in bits [1:0], two's complement in [-2, 1];
- * INT4 likewise with nibbles, low nibble first, in [-8, 7]; receiving-end
+/* rowq_gemv: per-row symmetric INT8 / INT4 / INT2 matvec on the dense packing
+ * of the mixed-bit recipe (mixed-bit page: decode recipe, per-channel
+ * symmetric linear weights with all zero points 0; packing convention: INT2
+ * holds 4 codes per byte, first code in bits [1:0], two's complement in
+ * [-2, 1]; INT4 likewise with nibbles, low nibble first, in [-8, 7]; the
+ * INT8 PLE gate / projection matrices are signed bytes; receiving-end
  * design: the integer-weighted sum is scaled once per row):
  *   y[r] = row_scale[r] * sum_k c[r, k] * x[k]   (fp32 accumulation).
  * The raw packed bytes are the kernel's layout (no repacking).
  *   w          [n, k * bits / 8] bytes row-major, 16-byte aligned.
  *   row_scale  fp32 [n], 4-byte aligned.
- *   bits       2 or 4; k a multiple of 64 (INT2) or 32 (INT4).
+ *   bits       2, 4 or 8; k a multiple of 64 (INT2) or 32 (INT4, INT8).
  *   x          bf16 [k], 16-byte aligned.   y  fp32 [n], 4-byte aligned.
- * Errors: NULL pointer, bits not 2 or 4, n <= 0 or >= 2^31, k not a
- *         multiple of the 16-byte code chunk, k > Q4DEC_MAX_K, misalignment. */
+ * Errors: NULL pointer, bits not 2, 4 or 8, n <= 0 or >= 2^31, k not a
+ *         multiple of the code chunk, k > Q4DEC_MAX_K, misalignment. */
 int rowq_gemv(const void* w, const float* row_scale, int64_t n, int64_t k,
               int32_t bits, const uint16_t* x, float* y, void* stream);
 
@@ -160,7 +161,8 @@ int rowq_gemv(const void* w, const float* row_scale, int64_t n, int64_t k,
  * dispatch). With h = n / 2 and the rowq_gemv sums,
  *   g_j = y[j],  u_j = y[h + j]  (each row with its own scale),
  *   a[j] = RN_bf16(gelu(g_j) * u_j), gelu as in q4_gemv_gelu_mul, j < h.
- *   w, row_scale, bits, x  as rowq_gemv, n rows ([gate; up]), n even.
+ *   w, row_scale, bits, x  as rowq_gemv (bits 2, 4 or 8), n rows
+ *          ([gate; up]), n even.
  *   a          bf16 bit patterns [n / 2], 2-byte aligned, caller-owned.
  * Errors: those of rowq_gemv, n odd, k > Q4DEC_GELU_MAX_K (unsupported). */
 int rowq_gemv_gelu_mul(const void* w, const float* row_scale, int64_t n,

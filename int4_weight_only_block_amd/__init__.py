@@ -215,7 +215,7 @@ def q4_gemv_multi(packed: torch.Tensor, n: int, k: int, x: torch.Tensor,
 def rowq_gemv(w: torch.Tensor, row_scale: torch.Tensor, n: int, k: int, bits: int, x: torch.Tensor,
               y: torch.Tensor | None = None) -> torch.Tensor:
     """y fp32 [n] = row_scale * (codes @ x) for dense-packed per-row INT2 /
-    INT4 codes w [n, k * bits / 8] (uint8)."""
+    INT4 / INT8 codes w [n, k * bits / 8] (uint8)."""
     pw = _dev(w, "w", _BYTES, n * k * bits // 8)
     ps = _dev(row_scale, "row_scale", _F32, n)
     px = _dev(x, "x", _U16, k)

@@ -1,13 +1,15 @@
-// rowq_gemv: per-row symmetric INT4 / INT2 matvec on the dense packing of the
-// mixed-bit recipe ("Gemma-4 E2B mobile mixed-bit QAT weights" knowledge page:
+// rowq_gemv: per-row symmetric INT8 / INT4 / INT2 matvec on the dense packing
+// of the mixed-bit recipe ("Gemma-4 E2B mobile mixed-bit QAT weights" knowledge page:
 // decode recipe with per-channel symmetric linear weights, all zero points 0,
 // bytes = elements * bits / 8; packing convention: INT2 holds 4 codes per byte
 // with the first code in bits [1:0], two's complement, INT4 likewise with
-// nibbles, low nibble first; receiving-end design: the integer-weighted sum is
-// scaled by the row's scale once).
+// nibbles, low nibble first; the INT8 PLE gate / projection matrices are
+// signed bytes; receiving-end design: the integer-weighted sum is scaled by
+// the row's scale once).
 //
-// The weight stream follows q4_gemv: lane t of a row group owns 16-byte chunks
-// t, t + LPR, ... of its row (64 INT2 or 32 INT4 codes each) and walks down
+// The weight stream follows q4_gemv: lane t of a row group owns chunks t,
+// t + LPR, ... of its row (16 bytes: 64 INT2 or 32 INT4 codes; 32 bytes: 32
+// INT8 codes, so every chunk holds whole 32-wide blocks) and walks down
 // the rows with one row group of loads in flight. Because a lane meets the
 // same chunks on every row, its share of x lives in registers: the workgroup
 // converts x once into LDS, each lane copies its blocks out, and the row loop
@@ -15,13 +17,14 @@
 //
 // Codes are not converted to fp16 on their own. Each field is read at bit
 // offset s of an fp16 whose exponent is that of 1024 (OR with 0x6400), so the
-// half holds 1024 + 2^s * u exactly, u = code + 2 (INT2) or code + 8 (INT4)
-// after an XOR of the packed word. The matching activation is stored
-// pre-multiplied by 2^-s, so the dot product yields code * x plus
-// (1024 * 2^-s + offset) * x, a term that depends on x alone: each block's sum
-// of those terms is computed once at staging and starts the block's fp32
-// accumulator with the opposite sign. Offsets s of 4 to 8 keep that term
-// within about 66 times the codes' own contribution (six of fp32's 24 bits).
+// half holds 1024 + 2^s * u exactly, u = code + 2 (INT2), code + 8 (INT4) or
+// code + 128 (INT8, s = 0) after an XOR of the packed word. The matching
+// activation is stored pre-multiplied by 2^-s, so the dot product yields
+// code * x plus (1024 * 2^-s + offset) * x, a term that depends on x alone:
+// each block's sum of those terms is computed once at staging and starts the
+// block's fp32 accumulator with the opposite sign. For INT2 and INT4 offsets s of 4 to 8
+// keep that term within about 66 times the codes' own contribution (six of
+// fp32's 24 bits); for INT8 the ratio is 1152 / |code|.
 #include <math.h>
 
 #include <algorithm>
@@ -95,6 +98,27 @@ struct Fields<4> {
   }
 };
 
+template <>
+struct Fields<8> {
+  static constexpr int kPairs = 2;
+  static constexpr int kDwords = 8;
+  static constexpr int kSecond = 2;
+  static constexpr int kOffset = 128;  // u = code + 128
+  __device__ static constexpr int elem(int d, int f) { return 4 * d + f; }
+  // bytes 0 and 2 of a word are read in place, bytes 1 and 3 after w >> 8
+  __device__ static constexpr int shift(int) { return 0; }
+  __device__ __forceinline__ static float dot(uint32_t w, const uint32_t* xp, float p, uint32_t magic) {
+    w ^= 0x80808080u;
+    p = dot2(field(w, 0x00FF00FFu, magic), xp[0], p);
+    p = dot2(field(w >> 8, 0x00FF00FFu, magic), xp[1], p);
+    return p;
+  }
+};
+
+// 16-byte loads per chunk: one for INT2 / INT4, two for INT8
+template <int BITS>
+constexpr int kChunkLoads = BITS == 8 ? 2 : 1;
+
 // Stage block b of x: its 16 activation pairs, element e scaled by 2^-(E + s)
 // where 2^E brings the block's largest bf16 exponent to 2^14 (as in q4_gemv)
 // and s is the shift of the field the element meets; quarter i of the 64
@@ -166,6 +190,7 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
                                                               const uint16_t* __restrict__ x, int n, int k, int ipw,
                                                               void* __restrict__ out) {
   using F = Fields<BITS>;
+  constexpr int CH = kChunkLoads<BITS>;
   constexpr int RPW = 64 / LPR;
   static_assert(MODE != kRowqGelu || RPW >= 2, "the gate/up pairing needs two rows per wave step");
   constexpr int UPW = MODE == kRowqGelu ? RPW / 2 : RPW;  // outputs per wave step
@@ -174,7 +199,7 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
   constexpr int MAXB = LPR * NB;
   __shared__ uint32_t xs[MAXB * 16];
   __shared__ float2 xc[MAXB];
-  const int U = (k * BITS) >> 7;  // 16-byte chunks per row
+  const int U = (k * BITS) / (128 * CH);  // chunks per row
   const int B = k >> 5;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -183,7 +208,7 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
   const int units = MODE == kRowqGelu ? n / 2 : n;
   const int RG = (units + UPW - 1) / UPW;
   const int rg_base = blockIdx.x * kRWaves * ipw + wave;
-  const size_t row_bytes = size_t(U) * 16;
+  const size_t row_bytes = size_t(U) * 16 * CH;
   const int iters = rg_base < RG ? min(ipw, (RG - rg_base + kRWaves - 1) / kRWaves) : 0;
   auto row_of = [&](int i) {
     if constexpr (MODE == kRowqGelu) {
@@ -195,15 +220,18 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
     }
   };
 
-  uint4 qa[CPL], qb[CPL];
-  auto load = [&](uint4(&q)[CPL], int row) {
+  uint4 qa[CPL][CH], qb[CPL][CH];
+  auto load = [&](uint4(&q)[CPL][CH], int row) {
     const u32x4* p = reinterpret_cast<const u32x4*>(w + size_t(row) * row_bytes);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int c = j * LPR + t;
       if (FULL || c < U) {
-        const u32x4 v = __builtin_nontemporal_load(p + c);
-        q[j] = make_uint4(v.x, v.y, v.z, v.w);
+#pragma unroll
+        for (int h = 0; h < CH; ++h) {
+          const u32x4 v = __builtin_nontemporal_load(p + c * CH + h);
+          q[j][h] = make_uint4(v.x, v.y, v.z, v.w);
+        }
       }
     }
   };
@@ -239,14 +267,18 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
   uint32_t magic;
   asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 
-  auto dot = [&](uint4(&q)[CPL], bool refill, int row_next) -> float {
+  auto dot = [&](uint4(&q)[CPL][CH], bool refill, int row_next) -> float {
     const u32x4* pn = reinterpret_cast<const u32x4*>(w + size_t(row_next) * row_bytes);
     float acc = 0.0f;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int c = j * LPR + t;
       if (FULL || c < U) {
-        const uint32_t wd[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
+        uint32_t wd[4 * CH];
+#pragma unroll
+        for (int h = 0; h < CH; ++h) {
+          wd[4 * h] = q[j][h].x; wd[4 * h + 1] = q[j][h].y; wd[4 * h + 2] = q[j][h].z; wd[4 * h + 3] = q[j][h].w;
+        }
 #pragma unroll
         for (int bb = 0; bb < BPC; ++bb) {
           const int l = j * BPC + bb;
@@ -260,8 +292,11 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
         asm volatile("" : "+v"(acc));
         __builtin_amdgcn_sched_barrier(0);
         if (refill) {
-          const u32x4 v = __builtin_nontemporal_load(pn + c);
-          q[j] = make_uint4(v.x, v.y, v.z, v.w);
+#pragma unroll
+          for (int h = 0; h < CH; ++h) {
+            const u32x4 v = __builtin_nontemporal_load(pn + c * CH + h);
+            q[j][h] = make_uint4(v.x, v.y, v.z, v.w);
+          }
         }
       }
     }
@@ -318,14 +353,15 @@ const void* pick_rowq(int lpr, int cpl) {
   }
   if constexpr (BITS == 2) {
     RQ_CASE(8, 1) RQ_CASE(8, 2) RQ_CASE(8, 3)
-    RQ_CASE(16, 2) RQ_CASE(16, 3)
-    RQ_CASE(32, 2) RQ_CASE(32, 3)
-    RQ_CASE(64, 2) RQ_CASE(64, 3) RQ_CASE(64, 4)
-  } else {
+    RQ_CASE(16, 1) RQ_CASE(16, 2) RQ_CASE(16, 3)
+    RQ_CASE(32, 1) RQ_CASE(32, 2) RQ_CASE(32, 3)
+    RQ_CASE(64, 1) RQ_CASE(64, 2) RQ_CASE(64, 3) RQ_CASE(64, 4)
+  } else {  // INT4 and INT8: one 32-wide block per chunk
     RQ_CASE(8, 1) RQ_CASE(8, 2) RQ_CASE(8, 3) RQ_CASE(8, 4) RQ_CASE(8, 5) RQ_CASE(8, 6)
-    RQ_CASE(16, 4) RQ_CASE(16, 5) RQ_CASE(16, 6)
-    RQ_CASE(32, 4) RQ_CASE(32, 5) RQ_CASE(32, 6)
-    RQ_CASE(64, 4) RQ_CASE(64, 5) RQ_CASE(64, 6) RQ_CASE(64, 7) RQ_CASE(64, 8)
+    RQ_CASE(16, 1) RQ_CASE(16, 2) RQ_CASE(16, 3) RQ_CASE(16, 4) RQ_CASE(16, 5) RQ_CASE(16, 6)
+    RQ_CASE(32, 1) RQ_CASE(32, 2) RQ_CASE(32, 3) RQ_CASE(32, 4) RQ_CASE(32, 5) RQ_CASE(32, 6)
+    RQ_CASE(64, 1) RQ_CASE(64, 2) RQ_CASE(64, 3) RQ_CASE(64, 4) RQ_CASE(64, 5) RQ_CASE(64, 6) RQ_CASE(64, 7)
+    RQ_CASE(64, 8)
   }
 #undef RQ_CASE
   return nullptr;
@@ -346,20 +382,12 @@ int rowq_blocks_per_cu(const void* fn) {
   return nb;
 }
 
+// The plan for U chunks per row at a given split: chunks per lane, kernel,
+// row groups, row walk and grid.
 template <int BITS, int MODE>
-RPlan rowq_plan(int64_t n, int64_t k) {
-  constexpr int BPC = BITS == 2 ? 2 : 1;
-  const int U = int((k * BITS) >> 7);
+RPlan rowq_plan_at(int64_t n, int U, int lpr) {
   RPlan p{};
-  // smallest split of at least 8 lanes (128 contiguous bytes per row and
-  // instruction) whose lanes hold at most 6 activation blocks (108 VGPRs);
-  // rows too wide for that take 64 lanes and up to 8 blocks
-  p.lpr = 64;
-  for (int l = 8; l <= 64; l *= 2)
-    if ((U + l - 1) / l * BPC <= 6) {
-      p.lpr = l;
-      break;
-    }
+  p.lpr = lpr;
   p.cpl = (U + p.lpr - 1) / p.lpr;
   const bool full = U == p.lpr * p.cpl;
   p.fn = full ? pick_rowq<BITS, MODE, true>(p.lpr, p.cpl) : pick_rowq<BITS, MODE, false>(p.lpr, p.cpl);
@@ -380,6 +408,32 @@ RPlan rowq_plan(int64_t n, int64_t k) {
   return p;
 }
 
+template <int BITS, int MODE>
+RPlan rowq_plan(int64_t n, int64_t k) {
+  constexpr int BPC = BITS == 2 ? 2 : 1;
+  const int U = int((k * BITS) / (128 * kChunkLoads<BITS>));
+  // smallest split of at least 8 lanes (128 contiguous bytes per row and
+  // instruction) whose lanes hold at most 6 activation blocks (108 VGPRs);
+  // rows too wide for that take 64 lanes and up to 8 blocks
+  int lpr = 64;
+  for (int l = 8; l <= 64; l *= 2)
+    if ((U + l - 1) / l * BPC <= 6) {
+      lpr = l;
+      break;
+    }
+  RPlan p = rowq_plan_at<BITS, MODE>(n, U, lpr);
+  // a matrix too small to give every CU a workgroup spreads each row over
+  // more lanes: more, shorter waves (INT8 [256, 1536]: 4.0 -> 2.7 us; INT4
+  // [2048, 1536]: 3.5 -> 3.0 us)
+  const int cus = device_cu_count();
+  while (p.fn && p.grid < cus && p.lpr < 64) {
+    const RPlan q = rowq_plan_at<BITS, MODE>(n, U, 2 * p.lpr);
+    if (!q.fn || q.grid <= p.grid) break;
+    p = q;
+  }
+  return p;
+}
+
 // argument checks shared by both entry points; returns 0 or an error code
 int rowq_check(const char* name, const void* w, const float* row_scale, int64_t n, int64_t k, int32_t bits,
                const uint16_t* x, const void* out, const char* out_name, int64_t max_k) {
@@ -387,10 +441,11 @@ int rowq_check(const char* name, const void* w, const float* row_scale, int64_t 
   if (!row_scale) return fail(Q4DEC_ERR_NULL, "%s: row_scale is NULL", name);
   if (!x) return fail(Q4DEC_ERR_NULL, "%s: x is NULL", name);
   if (!out) return fail(Q4DEC_ERR_NULL, "%s: %s is NULL", name, out_name);
-  if (bits != 2 && bits != 4) return fail(Q4DEC_ERR_SHAPE, "%s: bits must be 2 or 4 (got %d)", name, int(bits));
+  if (bits != 2 && bits != 4 && bits != 8)
+    return fail(Q4DEC_ERR_SHAPE, "%s: bits must be 2, 4 or 8 (got %d)", name, int(bits));
   if (n <= 0 || n >= (int64_t(1) << 31))
     return fail(Q4DEC_ERR_SHAPE, "%s: n must be in [1, 2^31) (got %lld)", name, (long long)n);
-  const int64_t kq = bits == 2 ? 64 : 32;  // one 16-byte chunk of codes
+  const int64_t kq = bits == 2 ? 64 : 32;  // one chunk of codes
   if (k <= 0 || k % kq)
     return fail(Q4DEC_ERR_SHAPE, "%s: k must be a positive multiple of %lld for %d-bit codes (got %lld)", name,
                 (long long)kq, int(bits), (long long)k);
@@ -405,7 +460,7 @@ int rowq_check(const char* name, const void* w, const float* row_scale, int64_t 
 template <int MODE>
 int rowq_launch(const char* name, const void* w, const float* row_scale, int64_t n, int64_t k, int32_t bits,
                 const uint16_t* x, void* out, void* stream) {
-  const RPlan p = bits == 2 ? rowq_plan<2, MODE>(n, k) : rowq_plan<4, MODE>(n, k);
+  const RPlan p = bits == 2 ? rowq_plan<2, MODE>(n, k) : bits == 4 ? rowq_plan<4, MODE>(n, k) : rowq_plan<8, MODE>(n, k);
   if (!p.fn) return fail(Q4DEC_ERR_UNSUPPORTED, "%s: no kernel for k=%lld", name, (long long)k);
   const uint8_t* wp = static_cast<const uint8_t*>(w);
   int ni = int(n), ki = int(k), ipw = p.ipw;

@@ -144,6 +144,10 @@ def test_rowq_gemv_validation():
     a = list(ok); a[3] = 48; a[4] = 4
     rc, msg = _rc_and_msg(L.rowq_gemv(*a))
     assert rc == q4.ERR_SHAPE and "32" in msg  # INT4 in 32-wide ones
+    a[4] = 8
+    rc, msg = _rc_and_msg(L.rowq_gemv(*a))
+    assert rc == q4.ERR_SHAPE and "32" in msg  # INT8 in 32-wide 32-byte ones
+    assert call(4, 16)[0] == q4.ERR_SHAPE
     assert call(2, 0)[0] == q4.ERR_SHAPE
     assert call(3, q4.MAX_K + 64)[0] == q4.ERR_UNSUPPORTED
     assert call(0, FAKE + 8)[0] == q4.ERR_ALIGN
@@ -167,7 +171,7 @@ def test_rowq_gemv_gelu_mul_validation():
     assert rc == q4.ERR_SHAPE and "even" in msg
     rc, msg = call(3, q4.GELU_MAX_K + 64)
     assert rc == q4.ERR_UNSUPPORTED and str(q4.GELU_MAX_K) in msg
-    assert call(4, 8)[0] == q4.ERR_SHAPE
+    assert call(4, 16)[0] == q4.ERR_SHAPE and "bits" in call(4, 16)[1]
     assert call(3, 96)[0] == q4.ERR_SHAPE
     assert call(6, FAKE + 1)[0] == q4.ERR_ALIGN
     assert call(1, FAKE + 2)[0] == q4.ERR_ALIGN

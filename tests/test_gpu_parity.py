@@ -209,7 +209,11 @@ def _rowq_inputs(rng, n, k, bits):
 # L0-14 and attention q/o), ragged row counts, and every lane split
 @pytest.mark.parametrize("bits,n,k", [(2, 12288, 1536), (2, 1536, 12288), (2, 262144, 1536), (4, 6144, 1536),
                                       (4, 1536, 6144), (4, 2048, 1536), (4, 1536, 2048), (2, 77, 64), (4, 301, 32),
-                                      (2, 515, 4096), (4, 1000, 16384), (2, 33, 16384), (4, 129, 960)])
+                                      (2, 515, 4096), (4, 1000, 16384), (2, 33, 16384), (4, 129, 960),
+                                      # INT8: PLE gate [256, 1536], projection [1536, 256] and the
+                                      # per-layer model projection [8960, 1536]; ragged and wide
+                                      (8, 256, 1536), (8, 1536, 256), (8, 8960, 1536), (8, 77, 32), (8, 301, 96),
+                                      (8, 1000, 16384), (8, 3000, 5120)])
 def test_rowq_gemv_tolerance(bits, n, k):
     rng = synth.rng_for(80, bits, n, k)
     w, sc, x = _rowq_inputs(rng, n, k, bits)
@@ -218,7 +222,7 @@ def test_rowq_gemv_tolerance(bits, n, k):
     assert_within_tol(y, yr, a, f"rowq int{bits}")
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 4, 8])
 def test_rowq_gemv_integer_exact(bits):
     n, k = 700, 3072
     rng = synth.rng_for(81, bits)
@@ -233,7 +237,8 @@ def test_rowq_gemv_integer_exact(bits):
 # fused [gate; up] GELU on the per-row formats: the E2B INT2 and INT4 FFN
 # halves, ragged output counts, and the widest supported k
 @pytest.mark.parametrize("bits,h,k", [(2, 12288, 1536), (4, 6144, 1536), (2, 77, 64), (4, 301, 32),
-                                      (2, 515, 6144), (4, 1000, 6144), (2, 33, 4096), (4, 129, 960)])
+                                      (2, 515, 6144), (4, 1000, 6144), (2, 33, 4096), (4, 129, 960),
+                                      (8, 256, 1536), (8, 77, 96), (8, 1000, 6144)])
 def test_rowq_gelu_mul_tolerance(bits, h, k):
     rng = synth.rng_for(82, bits, h, k)
     w, sc, x = _rowq_inputs(rng, 2 * h, k, bits)

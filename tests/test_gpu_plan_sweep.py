@@ -117,16 +117,17 @@ def test_gelu_plans_within_bound(h, blocks):
     assert bad.size == 0, (h, k, bad[:5])
 
 
-# per-row formats: k in steps of one 16-byte chunk (64 INT2 or 32 INT4 codes)
+# per-row formats: k in steps of one chunk (64 INT2, 32 INT4 or 32 INT8 codes)
 # through every lane split and chunk count, short and tall matrices
 ROWQ = ([(2, 23, c) for c in [1, 2, 3, 4, 5, 8, 9, 16, 17, 24, 25, 32, 33, 48, 49, 64, 96, 128, 129, 192, 256]]
         + [(4, 23, c) for c in [1, 2, 3, 5, 6, 8, 9, 16, 17, 24, 48, 49, 96, 97, 192, 193, 256, 320, 384, 448, 512]]
-        + [(2, 30000, 24), (2, 3000, 192), (4, 30000, 48), (4, 3000, 512)])
+        + [(8, 23, c) for c in [1, 2, 3, 5, 6, 8, 9, 16, 17, 24, 48, 49, 96, 97, 192, 193, 256, 320, 384, 448, 512]]
+        + [(2, 30000, 24), (2, 3000, 192), (4, 30000, 48), (4, 3000, 512), (8, 30000, 48), (8, 3000, 512)])
 
 
 @pytest.mark.parametrize("bits,n,chunks", ROWQ)
 def test_rowq_plans_exact(bits, n, chunks):
-    k = chunks * (128 // bits)
+    k = chunks * (64 if bits == 2 else 32)  # codes per chunk: 16 bytes of INT2 / INT4, 32 bytes of INT8
     rng = synth.rng_for(404, bits, n, chunks)
     w = rng.integers(0, 256, size=(n, k * bits // 8), dtype=np.uint8)
     sc = (2.0 ** rng.integers(-6, -2, size=n)).astype(np.float32)
