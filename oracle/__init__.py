@@ -24,6 +24,7 @@ from .q4_oracle import (  # noqa: F401
     q4_quantize,
     rowq_gelu_mul,
     rowq_gather,
+    rowq_lmhead,
     rowq_gemv,
     rowq_pack,
     rowq_unpack,

@@ -130,8 +130,26 @@ def rowq_gemv(w_bytes, row_scale, bits: int, x_bits):
     k = x.size
     sc = np.asarray(row_scale, dtype=np.float32).astype(np.float64)
     n = sc.size
-    c = rowq_unpack(w_bytes, n, k, bits).astype(np.float64)
-    return sc * (c @ x), np.abs(sc) * (np.abs(c) @ np.abs(x))
+    w = np.ascontiguousarray(w_bytes).view(np.uint8).reshape(n, k * bits // 8)
+    y = np.empty(n, dtype=np.float64)
+    a = np.empty(n, dtype=np.float64)
+    ax = np.abs(x)
+    for r0 in range(0, n, ROW_CHUNK):
+        c = rowq_unpack(w[r0:r0 + ROW_CHUNK], min(ROW_CHUNK, n - r0), k, bits).astype(np.float64)
+        y[r0:r0 + len(c)] = sc[r0:r0 + len(c)] * (c @ x)
+        a[r0:r0 + len(c)] = np.abs(sc[r0:r0 + len(c)]) * (np.abs(c) @ ax)
+    return y, a
+
+
+def rowq_lmhead(w_bytes, row_scale, bits: int, x_bits, cap: float = 30.0):
+    """The head on the per-row formats ([MIX] mixed-bit map: the INT2
+    [262144, 1536] input embedding is tied with the head): logits from
+    rowq_gemv, the softcap and the first argmax of the capped logits, as in
+    lmhead. Returns dict(idx, val, margin, a_idx, z, capped)."""
+    z, a = rowq_gemv(w_bytes, row_scale, bits, x_bits)
+    c = softcap(z, cap)
+    i = first_argmax(c)
+    return dict(idx=i, val=float(c[i]), margin=top2_margin(c), a_idx=float(a[i]), z=z, capped=c)
 
 
 # --------------------------------------------------------------- quantiser --

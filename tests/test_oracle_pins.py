@@ -602,6 +602,26 @@ def test_rowq_gemv_bruteforce_fraction(bits):
         assert abs(Fraction(a[r]) - ae) <= Fraction(1, 10 ** 12) * ae
 
 
+def test_rowq_lmhead_planted_rows_and_ties():
+    # INT2, k = 64, x = +1 on the first 32 elements and -1 on the rest. Row
+    # codes: 1 on the +1 half and -2 on the -1 half give 32 + 64 = 96 per unit
+    # scale, the row maximum. Rows 3 and 6 hold it with scale 1 (a tie: the
+    # lower, 3, wins); row 5 holds it with scale 0.5 (48); the other rows are
+    # zero codes. cap 0 gives the raw value; cap 30 gives 30 tanh(96 / 30).
+    n, k = 8, 64
+    best = np.array([1] * 32 + [-2] * 32, dtype=np.int8)
+    codes = np.zeros((n, k), dtype=np.int8)
+    codes[3] = codes[5] = codes[6] = best
+    w = oracle.rowq_pack(codes, 2)
+    sc = np.array([1, 1, 1, 1, 1, 0.5, 1, 1], dtype=np.float32)
+    x = np.array([0x3F80] * 32 + [0xBF80] * 32, dtype=np.uint16)  # bf16 +1, -1
+    r = oracle.rowq_lmhead(w, sc, 2, x, 0.0)
+    assert r["idx"] == 3 and r["val"] == 96.0 and r["margin"] == 0.0
+    r = oracle.rowq_lmhead(w, sc, 2, x, 30.0)
+    assert r["idx"] == 3 and abs(r["val"] - 30.0 * math.tanh(96.0 / 30.0)) < 1e-12
+    assert r["z"].tolist() == [0, 0, 0, 96, 0, 48, 96, 0]
+
+
 def test_rowq_gather_hand_decoded_rows():
     # INT2 row 0xE4 -> codes 0, 1, -2, -1; scale 0.5, multiplier 2 -> the codes
     w = np.array([[0xE4], [0x1B]], dtype=np.uint8)
