@@ -383,7 +383,8 @@ def probe_rowq(torch, dev, seed: int, reps: int = 20):
     and the INT2 262,144-row head [262144, 1536], 185 MB of codes per run,
     one HIP graph. Each FFN runs as the fused gate/up GELU launch plus the
     down GEMV (13 launches); the unfused run (gate, up and down as separate
-    GEMVs, 19 launches) is timed too. Not part of the q4_0 decode step. Bytes
+    GEMVs, 19 launches) and a run whose head is the fused softcap + argmax
+    (no logits written; 14 launches) are timed too. Not part of the q4_0 decode step. Bytes
     counted: packed codes + fp32 row scales + bf16 x + the outputs."""
     import int4_weight_only_block_amd as q4
 
@@ -411,6 +412,16 @@ def probe_rowq(torch, dev, seed: int, reps: int = 20):
             q4.rowq_gemv(w_dn, s_dn, D, H, 2, a, y)
         q4.rowq_gemv(head, head_sc, V, D, 2, x, logits)
 
+    ws = torch.empty(q4.rowq_head_workspace_bytes(V, D, 2), dtype=torch.uint8, device=dev)
+    hi = torch.empty(1, dtype=torch.int32, device=dev)
+    hv = torch.empty(1, dtype=torch.float32, device=dev)
+
+    def run_argmax():
+        for w_gu, s_gu, w_dn, s_dn in ffn:
+            q4.rowq_gemv_gelu_mul(w_gu, s_gu, 2 * H, D, 2, x, a)
+            q4.rowq_gemv(w_dn, s_dn, D, H, 2, a, y)
+        q4.rowq_softcap_argmax(head, head_sc, V, D, 2, x, 30.0, ws, hi, hv)
+
     def run_unfused():
         for w_gu, s_gu, w_dn, s_dn in ffn:
             q4.rowq_gemv(w_gu[:H], s_gu[:H], H, D, 2, x, gu[:H])
@@ -436,11 +447,13 @@ def probe_rowq(torch, dev, seed: int, reps: int = 20):
 
     ms = time_graph(run_fused)
     ms_unfused = time_graph(run_unfused)
+    ms_argmax = time_graph(run_argmax)
     code_bytes = 6 * (2 * H * D + D * H) // 4 + V * D // 4
     b = (code_bytes + 4 * (6 * (2 * H + D) + V) + 2 * (6 * (D + H) + D)
          + 6 * (2 * H + 4 * D) + 4 * V)
     return {"workload": "int2_kprobe_6ffn_plus_head", "launches": 13, "ms_per_run": round(ms, 4),
-            "ms_per_run_unfused_19_launches": round(ms_unfused, 4), "code_bytes": code_bytes,
+            "ms_per_run_unfused_19_launches": round(ms_unfused, 4),
+            "ms_per_run_head_fused_argmax_14_launches": round(ms_argmax, 4), "code_bytes": code_bytes,
             "bytes_per_run": b, "achieved_GBs": round(b / (ms * 1e-3) / 1e9, 1),
             "frac_of_hbm_peak": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
@@ -462,7 +475,9 @@ def probe_configs(torch, dev, wl: Workload, seed: int, reps: int = 10):
     * rowq_gather: the mixed-bit INT2 token embedding [262144, 1536] and the
       INT4 PLE table [262144, 35 x 256], for 1 and 64 ids;
     * rowq_int8: the mixed-bit INT8 per-row GEMVs (PLE gate [256, 1536],
-      projection [1536, 256], model projection [8960, 1536])."""
+      projection [1536, 256], model projection [8960, 1536]);
+    * rowq_head_int2: the tied INT2 head [262144, 1536] with softcap + argmax,
+      100 vectors over 3 copies, and its logits-only GEMV."""
     import int4_weight_only_block_amd as q4
     import synth
 
@@ -622,6 +637,29 @@ def probe_configs(torch, dev, wl: Workload, seed: int, reps: int = 10):
                     "achieved_GBs": round(b / us / 1e3, 1)}
         del ws8
     out["rowq_int8"] = r8
+    # --- the tied INT2 head [262144, 1536] with softcap + argmax, 100 vectors
+    # over 3 copies, one vector per call; the logits-only GEMV beside it
+    V = synth.VOCAB
+    h2 = [torch.randint(0, 256, (V, D // 4), dtype=torch.uint8, device=dev, generator=g) for _ in range(3)]
+    hs2 = torch.empty(V, dtype=torch.float32, device=dev).uniform_(1e-3, 1e-2, generator=g)
+    wsr = torch.zeros(q4.rowq_head_workspace_bytes(V, D, 2), dtype=torch.uint8, device=dev)
+    lg = torch.empty(V, dtype=torch.float32, device=dev)
+
+    def run_rhead():
+        for i in range(100):
+            q4.rowq_softcap_argmax(h2[i % 3], hs2, V, D, 2, xs[i], 30.0, wsr, idx[i:i + 1], val[i:i + 1])
+
+    def run_rlogits():
+        for i in range(100):
+            q4.rowq_gemv(h2[i % 3], hs2, V, D, 2, xs[i], lg)
+
+    us = time_graph(run_rhead, 3) / 100
+    us_l = time_graph(run_rlogits, 3) / 100
+    b = V * D // 4 + 4 * V + 2 * D + 8
+    out["rowq_head_int2"] = {"shape": [V, D], "vectors": 100, "copies": 3, "launches_per_call": 2,
+                             "avg_call_us": round(us, 3), "bytes_per_call": b, **rate(b, us),
+                             "logits_only_gemv_us": round(us_l, 3)}
+    del h2
     torch.cuda.synchronize()
     return out
 

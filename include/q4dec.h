@@ -169,6 +169,32 @@ int rowq_gemv_gelu_mul(const void* w, const float* row_scale, int64_t n,
                        int64_t k, int32_t bits, const uint16_t* x,
                        uint16_t* a, void* stream);
 
+/* Workspace bytes rowq_softcap_argmax needs (a fixed 64 KiB: at most 8192
+ * per-workgroup partials). */
+size_t rowq_head_workspace_bytes(int64_t vocab, int64_t k, int32_t bits);
+
+/* rowq_softcap_argmax: the LM head on the per-row formats (mixed-bit page:
+ * the INT2 [262144, 1536] input embedding with its per-row scale is tied
+ * with the head; E2B card: the head is fused with its argmax). The logits
+ * z[r] are those of rowq_gemv (same kernel, same numerics) and are never
+ * written out; the index and capped value of the maximum follow
+ * lmhead_softcap_argmax: lowest index among equal maxima, the argmax taken
+ * on z, only the winner capped, NaN never wins, idx_out = -1 and
+ * val_out = NaN when no logit compares. Two launches on `stream`: each
+ * workgroup of the first leaves the best (value, row) of its rows in ws,
+ * one workgroup of the second reduces them.
+ *   w, row_scale, bits, x  as rowq_gemv with n = vocab.
+ *   cap      30.0 for Gemma 4; cap <= 0 returns the raw maximum logit.
+ *   ws       device workspace, ws_bytes >= rowq_head_workspace_bytes,
+ *            8-byte aligned, caller-owned, no initial contents needed;
+ *            calls sharing one ws must not overlap.
+ *   idx_out  device int32 [1]; val_out device fp32 [1], 4-byte aligned.
+ * Errors: those of rowq_gemv, workspace too small, misalignment. */
+int rowq_softcap_argmax(const void* w, const float* row_scale, int64_t vocab,
+                        int64_t k, int32_t bits, const uint16_t* x, float cap,
+                        void* ws, size_t ws_bytes, int32_t* idx_out,
+                        float* val_out, void* stream);
+
 /* q4_gemv_gelu_mul: fused gate/up matvec with the GELU-tanh * up epilogue
  * (mixed-bit page, fused gate/up kernels: one launch over the concatenated
  * [gate; up] rows, fp32 tanh-form GELU in the epilogue). With h = n / 2,

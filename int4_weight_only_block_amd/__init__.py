@@ -47,6 +47,9 @@ _SIGNATURES = {
     "q4_gemv_multi": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p]),
     "rowq_gemv": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, ctypes.c_int32, _c_p, _c_p, _c_p]),
     "rowq_gemv_gelu_mul": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, ctypes.c_int32, _c_p, _c_p, _c_p]),
+    "rowq_head_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64, ctypes.c_int32]),
+    "rowq_softcap_argmax": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, ctypes.c_int32, _c_p, ctypes.c_float, _c_p,
+                                           ctypes.c_size_t, _c_p, _c_p, _c_p]),
     "q4_gemm_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
     "q4_gemm_s64": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, _c_p, _c_p, ctypes.c_size_t, _c_p]),
     "lmhead_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
@@ -228,7 +231,7 @@ def rowq_gemv(w: torch.Tensor, row_scale: torch.Tensor, n: int, k: int, bits: in
 
 def rowq_gemv_gelu_mul(w: torch.Tensor, row_scale: torch.Tensor, n: int, k: int, bits: int, x: torch.Tensor,
                        a: torch.Tensor | None = None) -> torch.Tensor:
-    """a[j] = bf16(gelu_tanh(g_j) * u_j) for per-row INT2 / INT4 [gate; up]
+    """a[j] = bf16(gelu_tanh(g_j) * u_j) for per-row INT2 / INT4 / INT8 [gate; up]
     rows (g = rows 0 .. n/2-1, u = rows n/2 .. n-1, each scaled by its own
     row scale); returns bf16 bits (int16)."""
     pw = _dev(w, "w", _BYTES, n * k * bits // 8)
@@ -239,6 +242,33 @@ def rowq_gemv_gelu_mul(w: torch.Tensor, row_scale: torch.Tensor, n: int, k: int,
     pa = _dev(a, "a", _U16, max(n // 2, 1))
     _check(lib().rowq_gemv_gelu_mul(pw, ps, n, k, int(bits), px, pa, _stream(x)))
     return a
+
+
+def rowq_head_workspace_bytes(vocab: int, k: int, bits: int) -> int:
+    return int(lib().rowq_head_workspace_bytes(vocab, k, int(bits)))
+
+
+def rowq_softcap_argmax(w: torch.Tensor, row_scale: torch.Tensor, vocab: int, k: int, bits: int,
+                        x: torch.Tensor, cap: float = 30.0, ws: torch.Tensor | None = None,
+                        idx_out: torch.Tensor | None = None, val_out: torch.Tensor | None = None):
+    """(idx int32 [1], val fp32 [1]): the softcapped maximum of the per-row
+    INT2 / INT4 / INT8 head logits row_scale * (codes @ x), lowest index on
+    ties."""
+    pw = _dev(w, "w", _BYTES, vocab * k * bits // 8)
+    ps = _dev(row_scale, "row_scale", _F32, vocab)
+    px = _dev(x, "x", _U16, k)
+    if ws is None:
+        ws = torch.empty(rowq_head_workspace_bytes(vocab, k, bits), dtype=torch.uint8, device=x.device)
+    pws = _dev(ws, "ws", _BYTES)
+    if idx_out is None:
+        idx_out = torch.empty(1, dtype=torch.int32, device=x.device)
+    if val_out is None:
+        val_out = torch.empty(1, dtype=torch.float32, device=x.device)
+    pi = _dev(idx_out, "idx_out", _I32, 1)
+    pv = _dev(val_out, "val_out", _F32, 1)
+    _check(lib().rowq_softcap_argmax(pw, ps, vocab, k, int(bits), px, float(cap), pws,
+                                     ws.numel() * ws.element_size(), pi, pv, _stream(x)))
+    return idx_out, val_out
 
 
 def q4_gemv_gelu_mul(packed: torch.Tensor, n: int, k: int, x: torch.Tensor,

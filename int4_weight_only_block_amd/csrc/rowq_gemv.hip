@@ -25,6 +25,7 @@
 // block's fp32 accumulator with the opposite sign. For INT2 and INT4 offsets s of 4 to 8
 // keep that term within about 66 times the codes' own contribution (six of
 // fp32's 24 bits); for INT8 the ratio is 1152 / |code|.
+#include <limits.h>
 #include <math.h>
 
 #include <algorithm>
@@ -165,7 +166,23 @@ __device__ __forceinline__ void stage_block(const uint16_t* __restrict__ xb, uin
   *cx = make_float2(-c, ldexpf(1.0f, e));
 }
 
-enum RowqMode { kRowqGemv = 0, kRowqGelu = 1 };
+enum RowqMode { kRowqGemv = 0, kRowqGelu = 1, kRowqHead = 2 };
+
+// Most workgroups (partials) of one head launch.
+constexpr int kRowqMaxPartials = 8192;
+
+// Best (value, row) of the wave into every lane.
+__device__ __forceinline__ void rq_wave_best(float& best, int& bidx) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(best, off);
+    const int oi = __shfl_xor(bidx, off);
+    if (better(ov, oi, best, bidx)) {
+      best = ov;
+      bidx = oi;
+    }
+  }
+}
 
 // fused [gate; up] epilogue: tanh-form GELU in fp32 and the bf16 rounding of
 // the product (same definitions as the q4_0 fused kernel)
@@ -183,7 +200,8 @@ __device__ __forceinline__ uint16_t rq_bf16_rne(float v) {
 // writes y[row] (fp32); kRowqGelu reads the n rows as [gate; up] and writes
 // bf16(gelu(g_j) * u_j) for j < n / 2: lane groups r < RPW / 2 take gate
 // rows, the others the up rows of the same outputs, so each pair of sums is
-// 32 lanes apart after the row reduction.
+// 32 lanes apart after the row reduction; kRowqHead keeps the best (scaled
+// sum, row) of the workgroup's rows and writes it to out[blockIdx.x].
 template <int BITS, int LPR, int CPL, int DEPTH, int MODE, bool FULL>
 __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __restrict__ w,
                                                               const float* __restrict__ row_scale,
@@ -302,9 +320,20 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
     }
     return acc;
   };
+  float best = -INFINITY;
+  int bidx = INT_MAX;
   auto emit = [&](int i, float acc) {
     acc = group_sum<LPR>(acc);
-    if constexpr (MODE == kRowqGelu) {
+    if constexpr (MODE == kRowqHead) {
+      const int row = (rg_base + i * kRWaves) * RPW + r;
+      if (row < n) {
+        const float v = acc * row_scale[row];
+        if (better(v, row, best, bidx)) {
+          best = v;
+          bidx = row;
+        }
+      }
+    } else if constexpr (MODE == kRowqGelu) {
       const float v = acc * row_scale[row_of(i)];
       const float up = __shfl_xor(v, 32);  // the up row's scaled sum
       const int j = (rg_base + i * kRWaves) * UPW + r;
@@ -333,6 +362,24 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
       if (i + 1 < iters) emit(i + 1, dot(qb, false, 0));
     }
   }
+  if constexpr (MODE == kRowqHead) {
+    rq_wave_best(best, bidx);
+    __shared__ float sv[kRWaves];
+    __shared__ int si[kRWaves];
+    if (lane == 0) {
+      sv[wave] = best;
+      si[wave] = bidx;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      for (int v = 1; v < kRWaves; ++v)
+        if (better(sv[v], si[v], best, bidx)) {
+          best = sv[v];
+          bidx = si[v];
+        }
+      static_cast<uint2*>(out)[blockIdx.x] = make_uint2(__builtin_bit_cast(uint32_t, best), uint32_t(bidx));
+    }
+  }
 }
 
 struct RPlan {
@@ -346,7 +393,7 @@ template <int BITS, int MODE, bool FULL>
 const void* pick_rowq(int lpr, int cpl) {
 #define RQ_CASE(L, C)                                                                                  \
   if (lpr == L && cpl == C) {                                                                          \
-    if constexpr (MODE == kRowqGemv || L <= 32)                                                        \
+    if constexpr (MODE != kRowqGelu || L <= 32)                                                        \
       return reinterpret_cast<const void*>(&rowq_rows_kernel<BITS, L, C, 1, MODE, FULL>);              \
     else                                                                                               \
       return nullptr;                                                                                  \
@@ -489,4 +536,40 @@ extern "C" int rowq_gemv_gelu_mul(const void* w, const float* row_scale, int64_t
                          (long long)n);
   if (!aligned(a, 2)) return fail(Q4DEC_ERR_ALIGN, "rowq_gemv_gelu_mul: a must be 2-byte aligned");
   return rowq_launch<kRowqGelu>("rowq_gemv_gelu_mul", w, row_scale, n, k, bits, x, a, stream);
+}
+
+extern "C" size_t rowq_head_workspace_bytes(int64_t vocab, int64_t k, int32_t bits) {
+  (void)vocab;
+  (void)k;
+  (void)bits;
+  return size_t(q4dec::kRowqMaxPartials) * sizeof(uint2);
+}
+
+extern "C" int rowq_softcap_argmax(const void* w, const float* row_scale, int64_t vocab, int64_t k, int32_t bits,
+                                   const uint16_t* x, float cap, void* ws, size_t ws_bytes, int32_t* idx_out,
+                                   float* val_out, void* stream) {
+  using namespace q4dec;
+  const char* name = "rowq_softcap_argmax";
+  if (int rc = rowq_check(name, w, row_scale, vocab, k, bits, x, ws, "ws", Q4DEC_MAX_K)) return rc;
+  if (!idx_out) return fail(Q4DEC_ERR_NULL, "%s: idx_out is NULL", name);
+  if (!val_out) return fail(Q4DEC_ERR_NULL, "%s: val_out is NULL", name);
+  if (!aligned(ws, 8)) return fail(Q4DEC_ERR_ALIGN, "%s: ws must be 8-byte aligned", name);
+  if (!aligned(idx_out, 4) || !aligned(val_out, 4))
+    return fail(Q4DEC_ERR_ALIGN, "%s: idx_out and val_out must be 4-byte aligned", name);
+  const size_t need = rowq_head_workspace_bytes(vocab, k, bits);
+  if (ws_bytes < need) return fail(Q4DEC_ERR_WORKSPACE, "%s: ws_bytes %zu < required %zu", name, ws_bytes, need);
+  const RPlan p = bits == 2   ? rowq_plan<2, kRowqHead>(vocab, k)
+                  : bits == 4 ? rowq_plan<4, kRowqHead>(vocab, k)
+                              : rowq_plan<8, kRowqHead>(vocab, k);
+  if (!p.fn) return fail(Q4DEC_ERR_UNSUPPORTED, "%s: no kernel for k=%lld", name, (long long)k);
+  if (p.grid > kRowqMaxPartials) return fail(Q4DEC_ERR_UNSUPPORTED, "%s: too many workgroups", name);
+  const uint8_t* wp = static_cast<const uint8_t*>(w);
+  int ni = int(vocab), ki = int(k), ipw = p.ipw;
+  void* part = ws;
+  void* args[] = {&wp, &row_scale, &x, &ni, &ki, &ipw, &part};
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t e = hipLaunchKernel(p.fn, dim3(p.grid), dim3(kRThreads), args, 0, st);
+  if (e != hipSuccess) return fail(Q4DEC_ERR_HIP, "%s: kernel launch failed: %s", name, hipGetErrorString(e));
+  reduce_argmax_partials(static_cast<const uint2*>(ws), p.grid, 1, 1, cap, idx_out, val_out, st);
+  return launch_status(name);
 }

@@ -12,6 +12,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(q4.LIB_PATH), reason="libq4de
 
 EXPECTED = {
     "q4dec_abi_version", "q4dec_last_error", "q4_packed_bytes", "q4_pack", "q4_quantize", "q4_gemv", "q4_gemv_gelu_mul", "q4_gemv_multi", "rowq_gemv", "rowq_gemv_gelu_mul",
+    "rowq_head_workspace_bytes", "rowq_softcap_argmax",
     "q4_gemm_s64", "q4_gemm_workspace_bytes", "lmhead_workspace_bytes", "lmhead_softcap_argmax", "lmhead_multi_workspace_bytes", "lmhead_softcap_argmax_multi", "lmhead_s64_workspace_bytes", "lmhead_softcap_argmax_s64", "ple_gather", "rowq_gather",
 }
 
@@ -284,6 +285,33 @@ def test_head_s64_validation():
     assert call(0, FAKE + 8) == q4.ERR_ALIGN
     assert call(3, FAKE + 8) == q4.ERR_ALIGN
     assert call(8, FAKE + 2) == q4.ERR_ALIGN
+
+
+def test_rowq_head_validation():
+    L = q4.lib()
+    need = q4.rowq_head_workspace_bytes(262144, 1536, 2)
+    assert need == 8192 * 8
+    # w, row_scale, vocab, k, bits, x, cap, ws, ws_bytes, idx_out, val_out, stream
+    ok = [FAKE, FAKE, 262144, 1536, 2, FAKE, 30.0, FAKE, need, FAKE, FAKE, None]
+
+    def call(i, v):
+        a = list(ok)
+        a[i] = v
+        return L.rowq_softcap_argmax(*a)
+
+    for i, name in [(0, "w"), (1, "row_scale"), (5, "x"), (7, "ws"), (9, "idx_out"), (10, "val_out")]:
+        assert call(i, None) == q4.ERR_NULL and name in q4.q4dec_last_error()
+    assert call(4, 3) == q4.ERR_SHAPE and "bits" in q4.q4dec_last_error()
+    assert call(4, 16) == q4.ERR_SHAPE
+    assert call(2, 0) == q4.ERR_SHAPE and "n" in q4.q4dec_last_error()
+    assert call(3, 32) == q4.ERR_SHAPE  # INT2 chunks hold 64 codes
+    assert call(3, q4.MAX_K + 64) == q4.ERR_UNSUPPORTED
+    assert call(8, need - 1) == q4.ERR_WORKSPACE
+    assert call(7, FAKE + 4) == q4.ERR_ALIGN
+    assert call(0, FAKE + 8) == q4.ERR_ALIGN
+    assert call(5, FAKE + 8) == q4.ERR_ALIGN
+    assert call(9, FAKE + 2) == q4.ERR_ALIGN
+    assert call(10, FAKE + 1) == q4.ERR_ALIGN
 
 
 def test_rowq_gather_validation():

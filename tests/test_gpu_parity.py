@@ -292,6 +292,74 @@ def test_rowq_int2_ffn_chain():
     assert_within_tol(y, yr, am, "rowq int2 down")
 
 
+# the tied per-row head: softcap + argmax fused over the rowq logits
+def _check_rowq_head(w, sc, bits, x, cap=30.0, ws=None):
+    vocab = w.shape[0]
+    k = x.size
+    i, v = q4.rowq_softcap_argmax(d(w), d(sc), vocab, k, bits, d(x), cap, ws)
+    gi, gv = int(i.item()), float(v.item())
+    ref = oracle.rowq_lmhead(w, sc, bits, x, cap)
+    c, ri = ref["capped"], ref["idx"]
+    if ref["margin"] >= 1e-3:
+        assert gi == ri, (vocab, k, bits, gi, ri, ref["margin"])
+    else:
+        _, am = oracle.rowq_gemv(w, sc, bits, x)  # the GEMV bar's sum of |terms| per row
+        assert 0 <= gi < vocab and c[ri] - c[gi] < 1e-3 + 1e-4 * am[gi] + 1e-6
+    assert abs(gv - ref["val"]) <= 1e-4 * ref["a_idx"] + 1e-6, (gv, ref["val"])
+    return ref["margin"] < 1e-3
+
+
+def test_rowq_head_e2b_int2_tied_head():
+    """The INT2 [262144, 1536] embedding used as the head, four vectors."""
+    rng = synth.rng_for(85)
+    w, sc, _ = _rowq_inputs(rng, 262144, 1536, 2)
+    ws = torch.zeros(q4.rowq_head_workspace_bytes(262144, 1536, 2), dtype=torch.uint8, device=DEV)
+    excluded = sum(_check_rowq_head(w, sc, 2, synth.bf16_normal(rng, 1536), ws=ws) for _ in range(4))
+    assert excluded <= 1
+
+
+@pytest.mark.parametrize("bits,vocab,k", [(2, 1, 64), (2, 3, 128), (2, 1000, 1536), (2, 70001, 2048),
+                                          (2, 4099, 12288), (4, 1, 32), (4, 777, 1536), (4, 70001, 2560),
+                                          (4, 3000, 16384), (8, 5, 32), (8, 20001, 1536), (8, 999, 10240)])
+def test_rowq_head_shapes(bits, vocab, k):
+    rng = synth.rng_for(86, bits, vocab, k)
+    w, sc, x = _rowq_inputs(rng, vocab, k, bits)
+    _check_rowq_head(w, sc, bits, x)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_rowq_head_planted_ties_and_raw_values(bits):
+    """Integer activations and a power-of-two scale make every logit exact:
+    rows planted with the sign pattern of x hold the unique maximum, the
+    lowest planted row must win across and within workgroups, and cap <= 0
+    returns the exact raw logit."""
+    vocab, k = (262144, 1536) if bits == 2 else (40000, 1536)
+    rng = synth.rng_for(87, bits)
+    lo, hi = -(1 << (bits - 1)), (1 << (bits - 1)) - 1
+    w0 = rng.integers(0, 256, size=(vocab, k * bits // 8), dtype=np.uint8)
+    w0[:, 0] &= np.uint8((0xFF << bits) & 0xFF)  # code 0 of every row is 0 ...
+    xi = rng.integers(-3, 4, size=k)
+    xi[0] = 4  # ... so no random row reaches the planted sum
+    planted = np.where(xi > 0, hi, np.where(xi < 0, lo, 0)).astype(np.int8)
+    prow = oracle.rowq_pack(planted[None, :], bits)[0]
+    sc = np.full(vocab, 2.0 ** -9, dtype=np.float32)
+    scd = d(sc)
+    x = d(bf16_bits_of_ints(xi))
+    zr = float(int(planted.astype(np.int64) @ xi)) * 2.0 ** -9
+    last = vocab - 1
+    for rows, expect in [((5, 77777 % vocab, last), 5), ((last,), last), ((0, last), 0),
+                         ((1023, 1024, 4096), 1023), ((64, 63), 63)]:
+        ww = w0.copy()
+        for r in rows:
+            ww[r] = prow
+        w = d(ww)
+        i, v = q4.rowq_softcap_argmax(w, scd, vocab, k, bits, x, 30.0)
+        assert int(i.item()) == expect, rows
+        assert abs(float(v.item()) - float(oracle.softcap(zr))) <= 1e-6 + 1e-4 * abs(zr)
+        i, v = q4.rowq_softcap_argmax(w, scd, vocab, k, bits, x, 0.0)
+        assert int(i.item()) == expect and float(v.item()) == zr
+
+
 # -------------------------------------------------------------- quantiser --
 def _quantize_gpu(x, rule):
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
@@ -866,6 +934,8 @@ def test_every_entry_point_replays_in_a_graph():
         "hi": torch.empty(1, dtype=torch.int32, device=DEV), "hv": torch.empty(1, dtype=torch.float32, device=DEV),
         "mi": torch.empty(m, dtype=torch.int32, device=DEV), "mv": torch.empty(m, dtype=torch.float32, device=DEV),
         "si": torch.empty(64, dtype=torch.int32, device=DEV), "sv": torch.empty(64, dtype=torch.float32, device=DEV),
+        "ri": torch.empty(1, dtype=torch.int32, device=DEV), "rv": torch.empty(1, dtype=torch.float32, device=DEV),
+        "ra": torch.empty(n // 2, dtype=torch.int16, device=DEV),
         "pg": torch.empty((8, 256), dtype=torch.float32, device=DEV),
         "rg": torch.empty((8, k), dtype=torch.float32, device=DEV),
         "qc": torch.empty((1, k), dtype=torch.int8, device=DEV),
@@ -878,6 +948,7 @@ def test_every_entry_point_replays_in_a_graph():
     ws_h = torch.empty(q4.lmhead_workspace_bytes(2 * n, k), dtype=torch.uint8, device=DEV)
     ws_m = torch.empty(q4.lmhead_multi_workspace_bytes(2 * n, k, m), dtype=torch.uint8, device=DEV)
     ws_s = torch.empty(q4.lmhead_s64_workspace_bytes(2 * n, k), dtype=torch.uint8, device=DEV)
+    ws_r = torch.empty(q4.rowq_head_workspace_bytes(n, k, 2), dtype=torch.uint8, device=DEV)
     w_int2_rows = d(rng.integers(0, 256, size=(5000, k // 4), dtype=np.uint8))
     s_int2_rows = d(rng.uniform(1e-3, 1e-2, size=(5000, 1)).astype(np.float32))
 
@@ -887,6 +958,8 @@ def test_every_entry_point_replays_in_a_graph():
         q4.q4_gemv_multi(packed, 2 * n, k, xm, outs["ym"])
         q4.q4_gemm_s64(packed, 2 * n, k, x64, outs["yg"], ws_g)
         q4.rowq_gemv(w2, s2, n, k, 2, x, outs["yr"])
+        q4.rowq_gemv_gelu_mul(w2, s2, n, k, 2, x, outs["ra"])
+        q4.rowq_softcap_argmax(w2, s2, n, k, 2, x, 30.0, ws_r, outs["ri"], outs["rv"])
         q4.lmhead_softcap_argmax(packed, 2 * n, k, x, 30.0, ws_h, outs["hi"], outs["hv"])
         q4.lmhead_softcap_argmax_multi(packed, 2 * n, k, xm, 30.0, ws_m, outs["mi"], outs["mv"])
         q4.lmhead_softcap_argmax_s64(packed, 2 * n, k, x64, 30.0, ws_s, outs["si"], outs["sv"])

@@ -136,3 +136,19 @@ def test_rowq_plans_exact(bits, n, chunks):
     yr, _ = oracle.rowq_gemv(w, sc, bits, x)
     bad = np.nonzero(y.astype(np.float64) != yr)[0]
     assert bad.size == 0, (bits, n, k, bad[:5], y[bad[:3]], yr[bad[:3]])
+
+
+# the per-row head through the same plans; with exact logits and no cap the
+# index is the oracle's lowest winning row (ties are common at these sizes)
+# and the value its raw maximum, bit for bit
+@pytest.mark.parametrize("bits,n,chunks", [c for c in ROWQ if c[2] in (1, 3, 16, 17, 48, 96, 192, 256, 512)])
+def test_rowq_head_plans_exact(bits, n, chunks):
+    k = chunks * (64 if bits == 2 else 32)
+    rng = synth.rng_for(405, bits, n, chunks)
+    w = rng.integers(0, 256, size=(n, k * bits // 8), dtype=np.uint8)
+    sc = (2.0 ** rng.integers(-6, -2, size=n)).astype(np.float32)
+    x = int_bf16(rng.integers(-4, 5, size=k))
+    i, v = q4.rowq_softcap_argmax(d(w), d(sc), n, k, bits, d(x), 0.0)
+    ref = oracle.rowq_lmhead(w, sc, bits, x, 0.0)
+    assert int(i.item()) == ref["idx"], (bits, n, k, int(i.item()), ref["idx"])
+    assert float(v.item()) == ref["val"]
