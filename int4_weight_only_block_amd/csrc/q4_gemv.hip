@@ -129,6 +129,56 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
   return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// Stage x (bf16 [32 B]) into LDS as block-scaled fp16 pairs (block b at
+// xs[16 b], quarter i in slot i ^ (b & 3), 2^E in xf[b]); E puts the block's
+// largest magnitude in [2^14, 2^15), so every bf16 value keeps its 8-bit
+// significand unless it lies below 2^-31 times that maximum. Four lanes share a
+// 32-wide block, one 16-byte quarter each, and agree on the block's largest
+// exponent with two xor shuffles. The loads are issued first (stage_x_load,
+// NXL quarters per thread) and converted later (stage_x_store): vector memory
+// counters retire in order, so loads issued before the weight loads can be
+// waited for while the weights are still in flight.
+template <int NT, int NXL>
+__device__ __forceinline__ void stage_x_load(const uint16_t* __restrict__ x, int B, uint4 (&v)[NXL]) {
+  const uint4* src = reinterpret_cast<const uint4*>(x);
+  // unconditional (a clamped index past the end), so the wait for these
+  // loads can be counted past the weight loads that follow
+#pragma unroll
+  for (int u = 0; u < NXL; ++u) v[u] = src[min(int(threadIdx.x) + u * NT, 4 * B - 1)];
+}
+
+template <int NT, int NXL>
+__device__ __forceinline__ void stage_x_store(const uint4 (&v)[NXL], int B, uint32_t* __restrict__ xs,
+                                              float* __restrict__ xf) {
+  // every lane converts (a clamped duplicate past the end, not stored): a
+  // conditional use would let the compiler sink the load past the weights
+#pragma unroll
+  for (int u = 0; u < NXL; ++u) {
+    const int qi = int(threadIdx.x) + u * NT;
+    {
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      uint32_t emax = 1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) emax = max(emax, max((w[i] >> 7) & 0xFFu, (w[i] >> 23) & 0xFFu));
+      emax = max(emax, uint32_t(__shfl_xor(int(emax), 1)));
+      emax = max(emax, uint32_t(__shfl_xor(int(emax), 2)));
+      const int e = int(emax) - 127 - 14;
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const half2_t h = {(_Float16)ldexpf(bf16_to_f32(w[i] & 0xFFFFu), -e),
+                           (_Float16)ldexpf(bf16_to_f32(w[i] >> 16), -e)};
+        o[i] = __builtin_bit_cast(uint32_t, h);
+      }
+      const int b = qi >> 2, q = qi & 3;
+      if (qi < 4 * B) {
+        reinterpret_cast<uint4*>(xs + 16 * b)[q ^ (b & 3)] = make_uint4(o[0], o[1], o[2], o[3]);
+        if (q == 0) xf[b] = ldexpf(1.0f, e);
+      }
+    }
+  }
+}
+
 template <int LPR, int BPL, int MODE, bool FULL>
 __global__ __launch_bounds__(kThreads) void q4_rows_kernel(const uint8_t* __restrict__ nib,
                                                            const uint16_t* __restrict__ scl,
@@ -167,19 +217,15 @@ __global__ __launch_bounds__(kThreads) void q4_rows_kernel(const uint8_t* __rest
     }
   };
 
+  // Activation loads first, then the first row group's weights; the
+  // activations are converted while the weights are in flight.
+  constexpr int NXL = (4 * MAXB + kThreads - 1) / kThreads;  // x quarters per thread
+  uint4 xv[NXL];
+  stage_x_load<kThreads, NXL>(x, B, xv);
   Lane<LPR, BPL, FULL> L;
-  // The first row group's weights do not depend on x: put them in flight
-  // before the activations are staged.
-  if (iters > 0) L.load(nib, scl, row_of(0), t, B, row_bytes);
-
-  // Stage the activations once per workgroup as block-scaled fp16 pairs.
-  for (int b = threadIdx.x; b < B; b += kThreads) {
-    uint32_t tmp[16];
-    xf[b] = convert_x_block(x + 32 * b, tmp);
-    uint4* d4 = reinterpret_cast<uint4*>(xs + 16 * b);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) d4[i ^ (b & 3)] = make_uint4(tmp[4 * i], tmp[4 * i + 1], tmp[4 * i + 2], tmp[4 * i + 3]);
-  }
+  // (a wave with no rows loads the clamped last row and never uses it)
+  L.load(nib, scl, row_of(0), t, B, row_bytes);
+  stage_x_store<kThreads, NXL>(xv, B, xs, xf);
   __syncthreads();
 
   float fr[BPL];

@@ -101,35 +101,6 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h16) {
   return __builtin_bit_cast(float, h16 << 16);
 }
 
-// Convert the 32 bf16 activations of one block into 16 fp16 pairs scaled by
-// 2^-E, with E chosen from the block's largest exponent so the largest
-// magnitude lands in [2^14, 2^15): every bf16 value keeps its 8-bit
-// significand unless it is below max * 2^-31. Returns 2^E as fp32.
-__device__ __forceinline__ float convert_x_block(const uint16_t* xb, uint32_t* out16) {
-  const uint4* src = reinterpret_cast<const uint4*>(xb);
-  uint32_t w[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint4 v = src[i];
-    w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
-  }
-  uint32_t emax = 1;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    uint32_t lo = (w[i] >> 7) & 0xFFu, hi = (w[i] >> 23) & 0xFFu;
-    emax = max(emax, max(lo, hi));
-  }
-  const int e = int(emax) - 127 - 14;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float a = ldexpf(bf16_to_f32(w[i] & 0xFFFFu), -e);
-    float b = ldexpf(bf16_to_f32(w[i] >> 16), -e);
-    half2_t h = {(_Float16)a, (_Float16)b};
-    out16[i] = __builtin_bit_cast(uint32_t, h);
-  }
-  return ldexpf(1.0f, e);
-}
-
 // ---- cross-lane sums ------------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
