@@ -128,11 +128,10 @@ constexpr int kChunkLoads = BITS == 8 ? 2 : 1;
 // the dot-product instruction forms each product exactly and C carries only
 // the fp32 rounding of its sums.
 template <int BITS>
-__device__ __forceinline__ void stage_block(const uint16_t* __restrict__ xb, uint32_t* __restrict__ dst, int sw,
-                                            float2* __restrict__ cx) {
+__device__ __forceinline__ void stage_block(const uint4 (&src)[4], uint32_t* __restrict__ dst, int sw,
+                                            float2* __restrict__ cx, bool store) {
   using F = Fields<BITS>;
   uint32_t raw[16];
-  const uint4* src = reinterpret_cast<const uint4*>(xb);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint4 v = src[i];
@@ -160,10 +159,12 @@ __device__ __forceinline__ void stage_block(const uint16_t* __restrict__ xb, uin
       out[d * F::kPairs + f] = __builtin_bit_cast(uint32_t, h);
     }
   }
-  uint4* d4 = reinterpret_cast<uint4*>(dst);
+  if (store) {
+    uint4* d4 = reinterpret_cast<uint4*>(dst);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) d4[i ^ (sw & 3)] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
-  *cx = make_float2(-c, ldexpf(1.0f, e));
+    for (int i = 0; i < 4; ++i) d4[i ^ (sw & 3)] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
+    *cx = make_float2(-c, ldexpf(1.0f, e));
+  }
 }
 
 enum RowqMode { kRowqGemv = 0, kRowqGelu = 1, kRowqHead = 2 };
@@ -253,10 +254,38 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
       }
     }
   };
-  if (iters > 0) load(qa, row_of(0));
-  if (DEPTH == 2 && iters > 1) load(qb, row_of(1));
+  // Activation loads first (vector memory counters retire in order, so the
+  // staging below waits only for these), then the first row groups' weights.
+  // Loads and conversions are unconditional, on clamped indices, and only the
+  // stores are guarded, so the compiler cannot sink a load past the weights;
+  // a wave with no rows loads the clamped last row and never uses it.
+  constexpr int NXB = (MAXB + kRThreads - 1) / kRThreads;  // x blocks per thread
+  u32x4 xr[NXB][4];
+#pragma unroll
+  for (int u = 0; u < NXB; ++u) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(x) + 4 * min(int(threadIdx.x) + u * kRThreads, B - 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xr[u][i] = src[i];
+  }
+  load(qa, row_of(0));
+  if (DEPTH == 2) load(qb, row_of(1));
+  // an unconditional use of the activation registers here keeps their loads
+  // ahead of the weight loads (the conversion feeds only guarded stores, which
+  // would otherwise let the compiler move the loads into the guarded block)
+#pragma unroll
+  for (int u = 0; u < NXB; ++u)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(xr[u][i]));
 
-  for (int b = threadIdx.x; b < B; b += kRThreads) stage_block<BITS>(x + 32 * b, xs + 16 * b, b / BPC, xc + b);
+#pragma unroll
+  for (int u = 0; u < NXB; ++u) {
+    const int b = int(threadIdx.x) + u * kRThreads, bc = min(b, B - 1);
+    const uint4 v4[4] = {make_uint4(xr[u][0].x, xr[u][0].y, xr[u][0].z, xr[u][0].w),
+                         make_uint4(xr[u][1].x, xr[u][1].y, xr[u][1].z, xr[u][1].w),
+                         make_uint4(xr[u][2].x, xr[u][2].y, xr[u][2].z, xr[u][2].w),
+                         make_uint4(xr[u][3].x, xr[u][3].y, xr[u][3].z, xr[u][3].w)};
+    stage_block<BITS>(v4, xs + 16 * bc, bc / BPC, xc + bc, b < B);
+  }
   // LDS writes done and visible; the weight loads above stay in flight
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
