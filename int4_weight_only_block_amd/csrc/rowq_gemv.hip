@@ -49,6 +49,20 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
 }
 
+// Codes enter the dot product exactly: a field read at bit offset S of each
+// half is the fp16 value 1024 + 2^S * u with u = code + OFF, so subtracting
+// the exact constant 1024 + OFF * 2^S leaves 2^S * code (|2^S code| <= 1024,
+// exact); the activation was staged pre-multiplied by 2^-S. (Leaving the
+// constant in and removing its sum per block saves this add, but then the
+// error grows with sum |x| instead of sum |code * x|, which breaks the GEMV
+// bound on rows whose codes are mostly zero.)
+template <int S, int OFF>
+__device__ __forceinline__ float dotc(uint32_t fld, uint32_t b, float c) {
+  constexpr _Float16 k = _Float16(-(1024 + (OFF << S)));
+  const half2_t kk = {k, k};
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, fld) + kk, __builtin_bit_cast(half2_t, b), c, false);
+}
+
 // One dword of codes against its activation pairs. Pair f of dword d of a
 // 32-code block holds block elements elem(d, f) and elem(d, f) + kSecond,
 // matching the low-half and high-half field that one AND-OR isolates.
@@ -69,14 +83,14 @@ struct Fields<2> {
   __device__ __forceinline__ static float dot(uint32_t w, const uint32_t* xp, float p, uint32_t magic) {
     w ^= 0xAAAAAAAAu;
     const uint32_t a = w << 4, c = w >> 6;
-    p = dot2(field(a, 0x00300030u, magic), xp[0], p);
-    p = dot2(field(a, 0x00C000C0u, magic), xp[1], p);
-    p = dot2(field(a, 0x03000300u, magic), xp[2], p);
-    p = dot2(field(w, 0x00C000C0u, magic), xp[3], p);
-    p = dot2(field(w, 0x03000300u, magic), xp[4], p);
-    p = dot2(field(c, 0x00300030u, magic), xp[5], p);
-    p = dot2(field(c, 0x00C000C0u, magic), xp[6], p);
-    p = dot2(field(c, 0x03000300u, magic), xp[7], p);
+    p = dotc<4, kOffset>(field(a, 0x00300030u, magic), xp[0], p);
+    p = dotc<6, kOffset>(field(a, 0x00C000C0u, magic), xp[1], p);
+    p = dotc<8, kOffset>(field(a, 0x03000300u, magic), xp[2], p);
+    p = dotc<6, kOffset>(field(w, 0x00C000C0u, magic), xp[3], p);
+    p = dotc<8, kOffset>(field(w, 0x03000300u, magic), xp[4], p);
+    p = dotc<4, kOffset>(field(c, 0x00300030u, magic), xp[5], p);
+    p = dotc<6, kOffset>(field(c, 0x00C000C0u, magic), xp[6], p);
+    p = dotc<8, kOffset>(field(c, 0x03000300u, magic), xp[7], p);
     return p;
   }
 };
@@ -94,7 +108,7 @@ struct Fields<4> {
     w ^= 0x88888888u;
     const uint32_t s[4] = {w << 4, w, w >> 4, w >> 8};  // nibbles 0 1 2 3
 #pragma unroll
-    for (int f = 0; f < 4; ++f) p = dot2(field(s[f], 0x00F000F0u, magic), xp[f], p);
+    for (int f = 0; f < 4; ++f) p = dotc<4, kOffset>(field(s[f], 0x00F000F0u, magic), xp[f], p);
     return p;
   }
 };
@@ -110,8 +124,8 @@ struct Fields<8> {
   __device__ static constexpr int shift(int) { return 0; }
   __device__ __forceinline__ static float dot(uint32_t w, const uint32_t* xp, float p, uint32_t magic) {
     w ^= 0x80808080u;
-    p = dot2(field(w, 0x00FF00FFu, magic), xp[0], p);
-    p = dot2(field(w >> 8, 0x00FF00FFu, magic), xp[1], p);
+    p = dotc<0, kOffset>(field(w, 0x00FF00FFu, magic), xp[0], p);
+    p = dotc<0, kOffset>(field(w >> 8, 0x00FF00FFu, magic), xp[1], p);
     return p;
   }
 };
@@ -123,13 +137,12 @@ constexpr int kChunkLoads = BITS == 8 ? 2 : 1;
 // Stage block b of x: its 16 activation pairs, element e scaled by 2^-(E + s)
 // where 2^E brings the block's largest bf16 exponent to 2^14 (as in q4_gemv)
 // and s is the shift of the field the element meets; quarter i of the 64
-// bytes goes to slot i ^ (sw & 3). cx receives (-C, 2^E), C being the block's
-// sum of (1024 + offset * 2^s) * x'. Both factors are exact fp16 values, so
-// the dot-product instruction forms each product exactly and C carries only
-// the fp32 rounding of its sums.
+// bytes goes to slot i ^ (sw & 3); xe receives 2^E. The codes met in the dot
+// product are exact fp16 values 2^s * code, so each product is exact and
+// only the fp32 accumulation rounds.
 template <int BITS>
 __device__ __forceinline__ void stage_block(const uint4 (&src)[4], uint32_t* __restrict__ dst, int sw,
-                                            float2* __restrict__ cx, bool store) {
+                                            float* __restrict__ xe, bool store) {
   using F = Fields<BITS>;
   uint32_t raw[16];
 #pragma unroll
@@ -146,16 +159,12 @@ __device__ __forceinline__ void stage_block(const uint4 (&src)[4], uint32_t* __r
   for (int i = 0; i < 16; ++i) emax = max(emax, max((raw[i] >> 7) & 0xFFu, (raw[i] >> 23) & 0xFFu));
   const int e = int(emax) - 127 - 14;
   uint32_t out[16];
-  float c = 0.0f;
 #pragma unroll
   for (int d = 0; d < F::kDwords; ++d) {
 #pragma unroll
     for (int f = 0; f < F::kPairs; ++f) {
       const int e0 = F::elem(d, f), s = F::shift(f);
       const half2_t h = {(_Float16)ldexpf(elem(e0), -e - s), (_Float16)ldexpf(elem(e0 + F::kSecond), -e - s)};
-      const _Float16 bias = (_Float16)(1024 + (F::kOffset << s));  // 1056, 1152 or 1536, exact
-      const half2_t bb = {bias, bias};
-      c = __builtin_amdgcn_fdot2(h, bb, c, false);
       out[d * F::kPairs + f] = __builtin_bit_cast(uint32_t, h);
     }
   }
@@ -163,7 +172,7 @@ __device__ __forceinline__ void stage_block(const uint4 (&src)[4], uint32_t* __r
     uint4* d4 = reinterpret_cast<uint4*>(dst);
 #pragma unroll
     for (int i = 0; i < 4; ++i) d4[i ^ (sw & 3)] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
-    *cx = make_float2(-c, ldexpf(1.0f, e));
+    *xe = ldexpf(1.0f, e);
   }
 }
 
@@ -217,7 +226,7 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
   constexpr int NB = CPL * BPC;           // blocks held by one lane
   constexpr int MAXB = LPR * NB;
   __shared__ uint32_t xs[MAXB * 16];
-  __shared__ float2 xc[MAXB];
+  __shared__ float xc[MAXB];
   const int U = (k * BITS) / (128 * CH);  // chunks per row
   const int B = k >> 5;
   const int lane = threadIdx.x & 63;
@@ -290,7 +299,7 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
   uint32_t xp[NB][16];
-  float cneg[NB], xf[NB];
+  float xf[NB];
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     const int c = j * LPR + t;
@@ -304,9 +313,7 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
           const uint4 v = s4[i ^ (c & 3)];
           xp[l][4 * i] = v.x; xp[l][4 * i + 1] = v.y; xp[l][4 * i + 2] = v.z; xp[l][4 * i + 3] = v.w;
         }
-        const float2 cc = xc[b];
-        cneg[l] = cc.x;
-        xf[l] = cc.y;
+        xf[l] = xc[b];
       }
     }
   }
@@ -329,7 +336,7 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
 #pragma unroll
         for (int bb = 0; bb < BPC; ++bb) {
           const int l = j * BPC + bb;
-          float p = cneg[l];
+          float p = 0.0f;
 #pragma unroll
           for (int d = 0; d < F::kDwords; ++d) p = F::dot(wd[bb * F::kDwords + d], &xp[l][d * F::kPairs], p, magic);
           acc = fmaf(p, xf[l], acc);

@@ -234,6 +234,26 @@ def test_rowq_gemv_integer_exact(bits):
     assert np.array_equal(y.astype(np.float64), (codes @ xi) / 32.0)
 
 
+@pytest.mark.parametrize("bits,n,k", [(2, 1536, 1536), (2, 12288, 1536), (2, 1536, 12288), (4, 2048, 1536),
+                                      (4, 1536, 6144), (8, 256, 1536), (8, 8960, 1536)])
+def test_rowq_gemv_degenerate_rows(bits, n, k):
+    """Rows whose codes are all zero (and rows with a single nonzero code)
+    among random rows, with N(0,1) activations: every output, the zero rows'
+    included, must meet the GEMV bar, whose floor is 1e-6 where sum|w x| is
+    zero; zero activations give exactly zero."""
+    rng = synth.rng_for(88, bits, n, k)
+    w, sc, x = _rowq_inputs(rng, n, k, bits)
+    w[::3] = 0
+    one = np.arange(1, n, 7)
+    w[one] = 0
+    w[one, rng.integers(0, w.shape[1], size=one.size)] = 1  # one code of 1 per row
+    y = q4.rowq_gemv(d(w), d(sc), n, k, bits, d(x)).cpu().numpy()
+    yr, a = oracle.rowq_gemv(w, sc, bits, x)
+    assert_within_tol(y, yr, a, f"rowq int{bits} degenerate rows")
+    y0 = q4.rowq_gemv(d(w), d(sc), n, k, bits, d(np.zeros(k, np.uint16))).cpu().numpy()
+    assert (y0 == 0).all()
+
+
 # fused [gate; up] GELU on the per-row formats: the E2B INT2 and INT4 FFN
 # halves, ragged output counts, and the widest supported k
 @pytest.mark.parametrize("bits,h,k", [(2, 12288, 1536), (4, 6144, 1536), (2, 77, 64), (4, 301, 32),
