@@ -248,8 +248,12 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
     }
   };
 
+  // a row group's weights and its per-row scale are loaded together; the
+  // scale is then at hand when the sum is ready, instead of a load issued
+  // behind the next group's weights and waited for with them
   uint4 qa[CPL][CH], qb[CPL][CH];
-  auto load = [&](uint4(&q)[CPL][CH], int row) {
+  float sa = 0.0f, sb = 0.0f;
+  auto load = [&](uint4(&q)[CPL][CH], float& sc, int row) {
     const u32x4* p = reinterpret_cast<const u32x4*>(w + size_t(row) * row_bytes);
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
@@ -262,6 +266,7 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
         }
       }
     }
+    sc = row_scale[row];
   };
   // Activation loads first (vector memory counters retire in order, so the
   // staging below waits only for these), then the first row groups' weights.
@@ -276,8 +281,8 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
 #pragma unroll
     for (int i = 0; i < 4; ++i) xr[u][i] = src[i];
   }
-  load(qa, row_of(0));
-  if (DEPTH == 2) load(qb, row_of(1));
+  load(qa, sa, row_of(0));
+  if (DEPTH == 2) load(qb, sb, row_of(1));
   // an unconditional use of the activation registers here keeps their loads
   // ahead of the weight loads (the conversion feeds only guarded stores, which
   // would otherwise let the compiler move the loads into the guarded block)
@@ -321,8 +326,9 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
   uint32_t magic;
   asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 
-  auto dot = [&](uint4(&q)[CPL][CH], bool refill, int row_next) -> float {
+  auto dot = [&](uint4(&q)[CPL][CH], float& sc, bool refill, int row_next) -> float {
     const u32x4* pn = reinterpret_cast<const u32x4*>(w + size_t(row_next) * row_bytes);
+    if (refill) sc = row_scale[row_next];
     float acc = 0.0f;
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
@@ -358,44 +364,50 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
   };
   float best = -INFINITY;
   int bidx = INT_MAX;
-  auto emit = [&](int i, float acc) {
+  auto emit = [&](int i, float acc, float sc) {
     acc = group_sum<LPR>(acc);
     if constexpr (MODE == kRowqHead) {
       const int row = (rg_base + i * kRWaves) * RPW + r;
       if (row < n) {
-        const float v = acc * row_scale[row];
+        const float v = acc * sc;
         if (better(v, row, best, bidx)) {
           best = v;
           bidx = row;
         }
       }
     } else if constexpr (MODE == kRowqGelu) {
-      const float v = acc * row_scale[row_of(i)];
+      const float v = acc * sc;
       const float up = __shfl_xor(v, 32);  // the up row's scaled sum
       const int j = (rg_base + i * kRWaves) * UPW + r;
       if (t == 0 && r < UPW && j < units) static_cast<uint16_t*>(out)[j] = rq_bf16_rne(rq_gelu_tanh(v) * up);
     } else {
       const int row = (rg_base + i * kRWaves) * RPW + r;
-      if (t == 0 && row < n) static_cast<float*>(out)[row] = acc * row_scale[row];
+      if (t == 0 && row < n) static_cast<float*>(out)[row] = acc * sc;
     }
   };
+  // row group i: its scale is read before dot() may refill it for a later group
+  auto step = [&](int i, uint4(&q)[CPL][CH], float& sc, bool refill, int row_next) {
+    const float s_i = sc;
+    const float acc = dot(q, sc, refill, row_next);
+    emit(i, acc, s_i);
+  };
   if constexpr (DEPTH == 1) {
-    for (int i = 0; i + 1 < iters; ++i) emit(i, dot(qa, true, row_of(i + 1)));
-    if (iters > 0) emit(iters - 1, dot(qa, false, 0));
+    for (int i = 0; i + 1 < iters; ++i) step(i, qa, sa, true, row_of(i + 1));
+    if (iters > 0) step(iters - 1, qa, sa, false, 0);
   } else {
     // qa holds row group i, qb row group i + 1; each refills two ahead
     int i = 0;
     for (; i + 3 < iters; i += 2) {
-      emit(i, dot(qa, true, row_of(i + 2)));
-      emit(i + 1, dot(qb, true, row_of(i + 3)));
+      step(i, qa, sa, true, row_of(i + 2));
+      step(i + 1, qb, sb, true, row_of(i + 3));
     }
     if (i + 2 < iters) {  // three left
-      emit(i, dot(qa, true, row_of(i + 2)));
-      emit(i + 1, dot(qb, false, 0));
-      emit(i + 2, dot(qa, false, 0));
+      step(i, qa, sa, true, row_of(i + 2));
+      step(i + 1, qb, sb, false, 0);
+      step(i + 2, qa, sa, false, 0);
     } else {
-      if (i < iters) emit(i, dot(qa, false, 0));
-      if (i + 1 < iters) emit(i + 1, dot(qb, false, 0));
+      if (i < iters) step(i, qa, sa, false, 0);
+      if (i + 1 < iters) step(i + 1, qb, sb, false, 0);
     }
   }
   if constexpr (MODE == kRowqHead) {
