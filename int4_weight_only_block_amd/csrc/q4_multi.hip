@@ -41,6 +41,7 @@ constexpr int kMaxBpl = 6;  // blocks per lane per row segment
 
 constexpr int kMultiVecs = 8;         // most vectors of one launch
 constexpr int kMultiPartials = 8192;  // most workgroups of one head launch
+constexpr int kMXLoads = 5;           // x pieces per thread loaded ahead of the weights
 
 // halves per activation row in LDS: k plus 8 (16 bytes), so the 4 vectors a
 // 4-lane group reads sit in different bank quads
@@ -112,26 +113,52 @@ __global__ __launch_bounds__(kMThreads) void q4_multi_kernel(const uint8_t* __re
       }
     }
   };
-  // the first weights do not depend on x: in flight before the staging
-  if (units > 0) load(0);
-
   // Stage x: the raw bf16 rows go to LDS while each vector's largest bf16
   // exponent is found; then each row is rewritten in place as fp16 scaled by
   // the power of two that puts its largest value at 2^14 (x is read from
-  // memory once). Rows v >= m are zeros.
+  // memory once). Rows v >= m are zeros. The first kMXLoads 16-byte pieces of
+  // each thread are loaded before the first weights (vector memory counters
+  // retire in order, so the staging then waits for these loads only); the
+  // loads are unconditional on a clamped index and an empty asm use after the
+  // weight loads keeps the compiler from moving them behind the weights.
   const int k8 = k >> 3;
-  for (int v = 0; v < m; ++v) {
-    const uint4* s4 = reinterpret_cast<const uint4*>(x + size_t(v) * size_t(k));
-    uint32_t emax = 1;
-    for (int i = threadIdx.x; i < k8; i += kMThreads) {
-      const uint4 w = s4[i];
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+  const int tot = m * k8;  // 16-byte pieces of x
+  const uint4* xq = reinterpret_cast<const uint4*>(x);
+  uint4 xr[kMXLoads];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) emax = max(emax, max((ws[e] >> 7) & 0xFFu, (ws[e] >> 23) & 0xFFu));
-      *reinterpret_cast<uint4*>(xs + size_t(v) * xsn + 8 * i) = w;
-    }
-    for (int off = 32; off >= 1; off >>= 1) emax = max(emax, uint32_t(__shfl_xor(int(emax), off)));
-    if (lane == 0) red[wave][v] = emax;
+  for (int u = 0; u < kMXLoads; ++u) xr[u] = xq[min(int(threadIdx.x) + u * kMThreads, tot - 1)];
+  // (a wave with no rows loads the clamped last row and never uses it)
+  load(0);
+#pragma unroll
+  for (int u = 0; u < kMXLoads; ++u) asm volatile("" : "+v"(xr[u].x), "+v"(xr[u].y), "+v"(xr[u].z), "+v"(xr[u].w));
+
+  uint32_t emax[kMultiVecs];
+#pragma unroll
+  for (int v = 0; v < kMultiVecs; ++v) emax[v] = 1;
+  auto take = [&](int idx, const uint4& w) {
+    const int v = idx / k8, i = idx - v * k8;
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    uint32_t e = 1;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) e = max(e, max((ws[c] >> 7) & 0xFFu, (ws[c] >> 23) & 0xFFu));
+#pragma unroll
+    for (int vv = 0; vv < kMultiVecs; ++vv)
+      if (vv == v) emax[vv] = max(emax[vv], e);
+    *reinterpret_cast<uint4*>(xs + size_t(v) * xsn + 8 * i) = w;
+  };
+#pragma unroll
+  for (int u = 0; u < kMXLoads; ++u) {
+    const int idx = int(threadIdx.x) + u * kMThreads;
+    if (idx < tot) take(idx, xr[u]);
+  }
+  for (int idx = int(threadIdx.x) + kMXLoads * kMThreads; idx < tot; idx += kMThreads) take(idx, xq[idx]);
+  for (int v = 0; v < m; ++v) {
+    uint32_t e = emax[0];
+#pragma unroll
+    for (int vv = 1; vv < kMultiVecs; ++vv)
+      if (vv == v) e = emax[vv];
+    for (int off = 32; off >= 1; off >>= 1) e = max(e, uint32_t(__shfl_xor(int(e), off)));
+    if (lane == 0) red[wave][v] = e;
   }
   __syncthreads();
   for (int idx = threadIdx.x; idx < 4 * NG * k8; idx += kMThreads) {
