@@ -151,7 +151,15 @@ __global__ __launch_bounds__(kMThreads) void q4_multi_kernel(const uint8_t* __re
     const int idx = int(threadIdx.x) + u * kMThreads;
     if (idx < tot) take(idx, xr[u]);
   }
-  for (int idx = int(threadIdx.x) + kMXLoads * kMThreads; idx < tot; idx += kMThreads) take(idx, xq[idx]);
+  // the rest (long rows, many vectors) in batches of four loads in flight
+  for (int base = int(threadIdx.x) + kMXLoads * kMThreads; base < tot; base += 4 * kMThreads) {
+    uint4 r[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) r[u] = xq[min(base + u * kMThreads, tot - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (base + u * kMThreads < tot) take(base + u * kMThreads, r[u]);
+  }
   for (int v = 0; v < m; ++v) {
     uint32_t e = emax[0];
 #pragma unroll
