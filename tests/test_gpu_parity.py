@@ -71,6 +71,44 @@ def test_gemv_integer_exact(k):
     assert np.array_equal(y.astype(np.float64), yr)
 
 
+def test_degenerate_inputs_all_q4_paths():
+    """All-zero codes and all-zero activations through the multi-vector GEMV,
+    the S=64 GEMM, the fused GELU and the three heads: every sum is exactly
+    zero, so outputs are exact zeros, GELU(0) * 0 is +0 in bf16, and each
+    head returns row 0 (the lowest of equal maxima) with value 0. Extreme
+    codes -8 / 7 stay within the GEMV bar on the matrix-core paths."""
+    rng = synth.rng_for(2)
+    n, k = 300, 2560
+    codes, sb = synth.q4_weights(rng, n, k)
+    zero_w = pack(np.zeros_like(codes), sb)
+    packed = pack(codes, sb)
+    xs = synth.bf16_normal(rng, (64, k))
+    zx = np.zeros((64, k), np.uint16)
+    for w, x in ((zero_w, xs), (packed, zx)):
+        for m in (2, 4, 8):
+            assert (q4.q4_gemv_multi(w, n, k, d(x[:m])).cpu().numpy() == 0).all(), m
+        for t in (1, 17, 64):
+            assert (q4.q4_gemm_s64(w, n, k, d(x[:t])).cpu().numpy() == 0).all(), t
+        a = q4.q4_gemv_gelu_mul(w, n, k, d(x[0])).cpu().numpy().view(np.uint16)
+        assert (a == 0).all()
+        i, v = q4.lmhead_softcap_argmax(w, n, k, d(x[0]), 30.0)
+        assert int(i.item()) == 0 and float(v.item()) == 0.0
+        i, v = q4.lmhead_softcap_argmax_multi(w, n, k, d(x[:5]), 30.0)
+        assert (i.cpu().numpy() == 0).all() and (v.cpu().numpy() == 0).all()
+        i, v = q4.lmhead_softcap_argmax_s64(w, n, k, d(x[:33]), 30.0)
+        assert (i.cpu().numpy() == 0).all() and (v.cpu().numpy() == 0).all()
+    for c in (-8, 7):
+        cc = np.full_like(codes, c)
+        w = pack(cc, sb)
+        yr, a = oracle.gemm(cc, sb, xs[:4])
+        y = q4.q4_gemv_multi(w, n, k, d(xs[:4])).cpu().numpy()
+        for r in range(4):
+            assert_within_tol(y[r], yr[r], a[r], f"multi codes {c}")
+        y = q4.q4_gemm_s64(w, n, k, d(xs[:4])).cpu().numpy()
+        for r in range(4):
+            assert_within_tol(y[r], yr[r], a[r], f"gemm codes {c}")
+
+
 @pytest.mark.parametrize("n,k", [(1536, 1536), (1, 1536), (3, 32), (1000, 2560), (513, 10240), (64, 16384)])
 def test_gemv_random_tolerance(n, k):
     rng = synth.rng_for(0, n, k)
