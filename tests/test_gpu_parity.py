@@ -288,8 +288,21 @@ def test_rowq_gemv_degenerate_rows(bits, n, k):
     y = q4.rowq_gemv(d(w), d(sc), n, k, bits, d(x)).cpu().numpy()
     yr, a = oracle.rowq_gemv(w, sc, bits, x)
     assert_within_tol(y, yr, a, f"rowq int{bits} degenerate rows")
-    y0 = q4.rowq_gemv(d(w), d(sc), n, k, bits, d(np.zeros(k, np.uint16))).cpu().numpy()
+    zx = d(np.zeros(k, np.uint16))
+    y0 = q4.rowq_gemv(d(w), d(sc), n, k, bits, zx).cpu().numpy()
     assert (y0 == 0).all()
+    # the head and the fused GELU on the same rows: all logits 0 -> row 0, value 0
+    i, v = q4.rowq_softcap_argmax(d(w), d(sc), n, k, bits, zx, 30.0)
+    assert int(i.item()) == 0 and float(v.item()) == 0.0
+    if n % 2 == 0 and k <= q4.GELU_MAX_K:
+        a = q4.rowq_gemv_gelu_mul(d(w), d(sc), n, k, bits, zx).cpu().numpy().view(np.uint16)
+        assert (a == 0).all()
+    # degenerate rows through the head: the winner is the oracle's when clear
+    ref = oracle.rowq_lmhead(w, sc, bits, x, 30.0)
+    i, v = q4.rowq_softcap_argmax(d(w), d(sc), n, k, bits, d(x), 30.0)
+    if ref["margin"] >= 1e-3:
+        assert int(i.item()) == ref["idx"]
+    assert abs(float(v.item()) - ref["val"]) <= 1e-4 * ref["a_idx"] + 1e-6
 
 
 # fused [gate; up] GELU on the per-row formats: the E2B INT2 and INT4 FFN
