@@ -305,7 +305,7 @@ __global__ __launch_bounds__(kMThreads) void q4_multi_kernel(const uint8_t* __re
         }
       }
     __syncthreads();
-    if (threadIdx.x < m) {
+    if (int(threadIdx.x) < m) {
       const int v = threadIdx.x;
       float b = sv[0][v];
       int bi = si[0][v];

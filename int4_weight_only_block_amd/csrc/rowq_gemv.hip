@@ -45,10 +45,6 @@ constexpr int kRThreads = 64 * kRWaves;
 // itself and so knows the hazards between it and the dot product
 __device__ __forceinline__ uint32_t field(uint32_t a, uint32_t mask, uint32_t magic) { return (a & mask) | magic; }
 
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
-}
-
 // Codes enter the dot product exactly: a field read at bit offset S of each
 // half is the fp16 value 1024 + 2^S * u with u = code + OFF, so subtracting
 // the exact constant 1024 + OFF * 2^S leaves 2^S * code (|2^S code| <= 1024,
