@@ -380,7 +380,7 @@ __global__ __launch_bounds__(256) void q4_gemm_kernel(const uint8_t* __restrict_
       }
     }
     __syncthreads();
-    if (threadIdx.x < n_tok) {
+    if (int(threadIdx.x) < n_tok) {
       const int s = threadIdx.x;
       float bv = hv[0][s];
       int br = hr[0][s];
