@@ -775,7 +775,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the hot path is built and measured on one GPU's share; see DESIGN.md for sharding)",
+              "(the hot path is built and measured on one GPU's share)",
               file=sys.stderr)
         sys.exit(2)
     import torch
