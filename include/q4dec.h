@@ -48,7 +48,7 @@ extern "C" {
 #define Q4DEC_ERR_SHAPE -2       /* n, k, vocab, dim, s or n_ids out of range */
 #define Q4DEC_ERR_ALIGN -3       /* pointer misaligned (see each call) */
 #define Q4DEC_ERR_WORKSPACE -4   /* workspace smaller than required */
-#define Q4DEC_ERR_UNSUPPORTED -5 /* valid request this build does not handle */
+#define Q4DEC_ERR_UNSUPPORTED -5 /* valid request the library does not handle */
 #define Q4DEC_ERR_HIP -6         /* HIP runtime error at launch */
 
 /* Largest K (input dimension) the GEMV, head and GEMM kernels accept. */
