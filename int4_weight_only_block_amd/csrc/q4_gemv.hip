@@ -460,10 +460,12 @@ static Plan make_plan(int64_t n, int64_t k) {
   }
   Plan p = plan_for<MODE>(n, B, lpr);
   // A matrix that fits one resident round at this split takes the widest
-  // split that still fills every lane: shorter block chains per wave and more
-  // waves to cover the load latency.
+  // split up to 32 lanes that still fills every lane: shorter block chains
+  // per wave and more waves to cover the load latency. (64-lane rows with
+  // few blocks per lane measured slower: E2B down [1536, 6144] 3.78 us at 64
+  // lanes against 3.43 at 32, E4B O [2560, 2048] 2.91 against 2.70.)
   if (p.fn && p.ipw == 1) {
-    for (int wide = 64; wide > lpr; wide /= 2) {
+    for (int wide = 32; wide > lpr; wide /= 2) {
       if (B % wide || B / wide < 1) continue;
       const Plan q = plan_for<MODE>(n, B, wide);
       if (q.fn && q.ipw == 1) return q;
