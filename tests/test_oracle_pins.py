@@ -370,6 +370,63 @@ def test_gelu_tanh_identities():
         torch.tensor(gel1 * 2.0, dtype=torch.float32).to(torch.bfloat16).float())
 
 
+def _bf16_rne_fraction(v: float) -> int:
+    """bf16 bit pattern nearest to the finite float v, ties to an even last
+    significand bit, found in exact rational arithmetic: the two bf16 values
+    around v are the upper half of v's fp32 pattern and the next one away
+    from zero; compare |v - lo| with |hi - v| as fractions."""
+    from fractions import Fraction
+
+    u = struct.unpack("<I", struct.pack("<f", v))[0]
+    lo_bits = u >> 16
+    hi_bits = lo_bits + 1  # one bf16 step further from zero (same sign)
+
+    def val(b16: int) -> Fraction:
+        return Fraction(struct.unpack("<f", struct.pack("<I", b16 << 16))[0])
+
+    fv, lo, hi = Fraction(v), val(lo_bits), val(hi_bits)
+    dlo, dhi = abs(fv - lo), abs(hi - fv)
+    if dlo < dhi:
+        return lo_bits
+    if dhi < dlo:
+        return hi_bits
+    return lo_bits if lo_bits % 2 == 0 else hi_bits
+
+
+def test_ffn_down_input_bits_round_half_even():
+    """The down GEMV's input is the fp32 product gelu(g) * u rounded to bf16
+    by round-to-nearest-even (mixed-bit page, fused gate/up kernel: fp32 GELU
+    in the epilogue; the bf16 activation format of the configs). Pinned
+    against an exact-rational rounding, on random products and on products
+    planted exactly half-way between two bf16 values with even and with odd
+    lower neighbours, both signs, plus values that are bf16 already."""
+    rng = np.random.default_rng(77)
+    g = rng.normal(0, 2.5, size=4000).astype(np.float32)
+    u = rng.normal(0, 1.0, size=4000).astype(np.float32)
+    # For g >= 16 the fp32 tanh of the GELU's argument is exactly 1, so
+    # gelu(g) = g exactly and g * 1 = g: plant exact ties and exact values.
+    ties = []
+    for hi16 in (0x4180, 0x4181, 0x4203, 0x4204, 0x4400, 0x43FF):
+        ties.append(struct.unpack("<f", struct.pack("<I", (hi16 << 16) | 0x8000))[0])  # half-way
+        ties.append(struct.unpack("<f", struct.pack("<I", (hi16 << 16) | 0x7FFF))[0])  # just below
+        ties.append(struct.unpack("<f", struct.pack("<I", (hi16 << 16) | 0x8001))[0])  # just above
+        ties.append(struct.unpack("<f", struct.pack("<I", hi16 << 16))[0])             # exact
+    gt = np.array(ties * 2, dtype=np.float32)
+    ut = np.array([1.0] * len(ties) + [-1.0] * len(ties), dtype=np.float32)
+    assert (oracle.gelu_tanh_f32(gt) == gt).all()
+    g = np.concatenate([g, gt])
+    u = np.concatenate([u, ut])
+    bits = oracle.ffn_down_input_bits(g, u)
+    prod = oracle.gelu_tanh_f32(g) * u  # numpy fp32 product
+    want = np.array([_bf16_rne_fraction(float(p)) for p in prod], dtype=np.uint16)
+    assert np.array_equal(bits, want)
+    # the half-way products (every fourth planted value) land on even bf16
+    # patterns, the lower neighbour for 0x4180 and the upper one for 0x4181
+    n_t = len(ties)
+    assert {int(b) & 1 for b in want[4000:4000 + n_t:4]} == {0}
+    assert want[4000] == 0x4180 and want[4004] == 0x4182
+
+
 def test_decoders_exact():
     for v in (0.0, 1.0, -2.5, 65504.0, 2.0 ** -24, 6.1e-5):
         b = fp16_bits(v)
