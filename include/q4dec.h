@@ -110,7 +110,11 @@ int q4_pack(const int8_t* codes, const uint16_t* scales, int64_t n, int64_t k,
             void* packed, int32_t* err_flag, void* stream);
 
 /* q4_gemv: S=1 decode matvec y[r] = sum_k c[r,k] * d[r,k/32] * x[k]
- * (fp32 accumulation; model card Provenance table, S=1 decode).
+ * (fp32 accumulation; model card Provenance table, S=1 decode). Results are
+ * within |y - y_exact| <= 1e-4 * sum_k |w x| + 1e-6 for every finite x: x is
+ * staged as fp16 scaled by one power of two per 32-wide block, and when a
+ * block's nonzero values span more than 31 binades (a value would lose bits
+ * there) the whole call reads x as stored instead (exact path, slower).
  *   packed  from q4_pack with the same (n, k); 16-byte aligned.
  *   x       bf16 [k], 16-byte aligned.
  *   y       fp32 [n], 4-byte aligned; must not overlap packed or x.
@@ -127,7 +131,9 @@ int q4_gemv(const void* packed, int64_t n, int64_t k, const uint16_t* x,
  * vector is converted once to fp16 scaled by one power of two (its largest
  * value lands in [2^14, 2^15)), codes times activations accumulate in fp32
  * per block, and each block sum is scaled by d; results are within the
- * q4_gemv bar of the exact sums.
+ * q4_gemv bar of the exact sums for every finite x: when a vector's nonzero
+ * values span more than 31 binades the call reads x as stored instead
+ * (exact path, slower).
  *   packed  from q4_pack with the same (n, k); 16-byte aligned.
  *   x       bf16 [m, k] row-major, 16-byte aligned.
  *   y       fp32 [m, n] row-major, 4-byte aligned, caller-owned.
@@ -145,7 +151,12 @@ int q4_gemv_multi(const void* packed, int64_t n, int64_t k, const uint16_t* x,
  * INT8 PLE gate / projection matrices are signed bytes; receiving-end
  * design: the integer-weighted sum is scaled once per row):
  *   y[r] = row_scale[r] * sum_k c[r, k] * x[k]   (fp32 accumulation).
- * The raw packed bytes are the kernel's layout (no repacking).
+ * The raw packed bytes are the kernel's layout (no repacking). Within the
+ * q4_gemv bar for every finite x: x is staged per 32-wide block as fp16
+ * scaled by a power of two and by the field offset 2^-s the codes are read
+ * at (s <= 8 for INT2, 4 for INT4, 0 for INT8); when a block's nonzero values
+ * span more than 31 - s binades the call reads x as stored instead (exact
+ * path, slower).
  *   w          [n, k * bits / 8] bytes row-major, 16-byte aligned.
  *   row_scale  fp32 [n], 4-byte aligned.
  *   bits       2, 4 or 8; k a multiple of 64 (INT2) or 32 (INT4, INT8).
@@ -221,8 +232,10 @@ size_t q4_gemm_workspace_bytes(int64_t n, int64_t k);
  * kernel: each fp16 block scale d is split exactly into d_hi (top 7
  * significant bits) and d_lo = d - d_hi, so c * d_hi and c * d_lo are exact
  * fp16 values; activations enter as fp16 scaled by a per-token power of two;
- * two MFMAs per product accumulate in fp32. Deterministic (fixed summation
- * order). Launches on `stream`: an activation conversion, the MFMA kernel
+ * two MFMAs per product accumulate in fp32. Within the q4_gemv bar for every
+ * finite x: when a token's nonzero values span more than 31 binades the call
+ * reads X as stored instead (exact path, slower). Deterministic (fixed
+ * summation order). Launches on `stream`: an activation conversion, the MFMA kernel
  * and, when K is split over several workgroups, an in-order slice sum.
  *   packed  from q4_pack with the same (n, k); 16-byte aligned.
  *   x       bf16 [n_tok, k] row-major, 16-byte aligned.
@@ -329,7 +342,8 @@ int lmhead_softcap_argmax_s64(const void* packed, int64_t vocab, int64_t k,
  *   mult       16.0 for the PLE table.
  *   out        fp32 [n_ids, dim] row-major.
  * Errors: NULL pointer (err_flag may be NULL), vocab <= 0, dim <= 0,
- *         n_ids < 0 (n_ids == 0 is a no-op), vocab or dim >= 2^31. */
+ *         n_ids not in [0, 65535] (n_ids == 0 is a no-op), vocab or
+ *         dim >= 2^31, row_scale, ids or out not 4-byte aligned. */
 int ple_gather(const int8_t* table, const float* row_scale, int64_t vocab,
                int64_t dim, const int32_t* ids, int64_t n_ids, float mult,
                float* out, int32_t* err_flag, void* stream);

@@ -99,18 +99,28 @@ __global__ __launch_bounds__(256) void gemm_x_prep_kernel(const uint16_t* __rest
     const int i = threadIdx.x + 256 * r;
     v[r] = i < k8 ? s4[i] : make_uint4(0u, 0u, 0u, 0u);
   }
-  uint32_t emax = 1;
+  uint32_t emax = 1, emin = 255;
 #pragma unroll
   for (int r = 0; r < kPrepVec; ++r) {
     const uint32_t w[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) emax = max(emax, max((w[j] >> 7) & 0xFFu, (w[j] >> 23) & 0xFFu));
+    for (int j = 0; j < 4; ++j) {
+      emax = max(emax, max((w[j] >> 7) & 0xFFu, (w[j] >> 23) & 0xFFu));
+      emin = min(emin, min(bf16_exp_nz(w[j] & 0xFFFFu), bf16_exp_nz(w[j] >> 16)));
+    }
   }
-  for (int off = 32; off >= 1; off >>= 1) emax = max(emax, uint32_t(__shfl_xor(int(emax), off)));
-  __shared__ uint32_t wm[4];
-  if ((threadIdx.x & 63) == 0) wm[threadIdx.x >> 6] = emax;
+  for (int off = 32; off >= 1; off >>= 1) {
+    emax = max(emax, uint32_t(__shfl_xor(int(emax), off)));
+    emin = min(emin, uint32_t(__shfl_xor(int(emin), off)));
+  }
+  __shared__ uint32_t wm[4], wn[4];
+  if ((threadIdx.x & 63) == 0) {
+    wm[threadIdx.x >> 6] = emax;
+    wn[threadIdx.x >> 6] = emin;
+  }
   __syncthreads();
   emax = max(max(wm[0], wm[1]), max(wm[2], wm[3]));
+  emin = min(min(wn[0], wn[1]), min(wn[2], wn[3]));
   const int e = int(emax) - 127 - 14;
 #pragma unroll
   for (int r = 0; r < kPrepVec; ++r) {
@@ -126,7 +136,10 @@ __global__ __launch_bounds__(256) void gemm_x_prep_kernel(const uint16_t* __rest
     }
     dst[i] = make_uint4(o[0], o[1], o[2], o[3]);
   }
-  if (threadIdx.x == 0) xf[s] = ldexpf(1.0f, e);
+  // a token whose nonzero values span more binades than its scaled fp16
+  // copy keeps is marked by a negative factor: the GEMM then reads X as
+  // stored (exact path)
+  if (threadIdx.x == 0) xf[s] = int(emax) - int(emin) > kMaxSpan ? -1.0f : ldexpf(1.0f, e);
 }
 
 __device__ __forceinline__ half8_t codes_f16x8(uint32_t w, uint32_t m_lo, uint32_t m_hi, uint32_t magic) {
@@ -259,8 +272,8 @@ __device__ __forceinline__ void mma_chunk(float4_t (&t)[kSub][4], const uint4 (&
 template <int MODE>
 __global__ __launch_bounds__(256) void q4_gemm_kernel(const uint8_t* __restrict__ nib, const uint16_t* __restrict__ scl,
                                                       const uint8_t* __restrict__ rexp, const _Float16* __restrict__ xh,
-                                                      const float* __restrict__ xf, int n, int k, int n_tok, int bps,
-                                                      void* __restrict__ out) {
+                                                      const float* __restrict__ xf, const uint16_t* __restrict__ x,
+                                                      int n, int k, int n_tok, int bps, void* __restrict__ out) {
   __shared__ uint4 xs[kChunk][kTok][4];  // [block][token][k quarter, swizzled], 32 KB
   const int B = k >> 5;
   const int lane = threadIdx.x & 63;
@@ -304,6 +317,61 @@ __global__ __launch_bounds__(256) void q4_gemm_kernel(const uint8_t* __restrict_
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[u][m] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
+  // A wide token (negative factor from the prep kernel) puts the whole
+  // workgroup on the exact path.
+  __shared__ int wide_w[4];
+  {
+    const bool wide_t = int(threadIdx.x) < n_tok && xf[threadIdx.x & (kTok - 1)] < 0.0f;
+    const bool wide_wave = __ballot(wide_t) != 0;
+    if (lane == 0) wide_w[wave] = wide_wave;
+  }
+  __syncthreads();
+  // uniform by construction; readfirstlane lets the compiler branch on it
+  // as a scalar, so the two paths do not hold registers at the same time
+  const bool exact = __builtin_amdgcn_readfirstlane(wide_w[0] | wide_w[1] | wide_w[2] | wide_w[3]) != 0;
+  if (exact) {
+    // Each lane's outputs (rows rows[u], tokens 16m + 4q + i) summed over the
+    // slice's blocks in fp32 with X as stored: every code-activation product
+    // is exact, each block sum is scaled by its fp16 d. One block at a time.
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tf[4 * m + i] = 1.0f;
+#pragma unroll
+    for (int u = 0; u < kSub; ++u) shift[u] = 0;
+#pragma unroll 1
+    for (int b = b_begin; b < b_end; ++b) {
+#pragma unroll
+      for (int u = 0; u < kSub; ++u) {
+        const uint4 wq = wrow[u][b];
+        const uint32_t wd[4] = {wq.x, wq.y, wq.z, wq.w};
+        const float d = float(__builtin_bit_cast(_Float16, srow[u][b]));
+#pragma unroll 1
+        for (int mi = 0; mi < 16; ++mi) {
+          const int tok = 16 * (mi >> 2) + 4 * q + (mi & 3);
+          if (tok >= n_tok) continue;
+          const uint4* xb = reinterpret_cast<const uint4*>(x + size_t(tok) * size_t(k) + size_t(b) * 32);
+          float sum = 0.0f;
+#pragma unroll
+          for (int dd = 0; dd < 4; ++dd) {
+            const uint4 xv = xb[dd];
+            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+            const CodePairs cp = unpack_dword(wd[dd], m_lo, m_hi, magic);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+              sum = fmaf(float(cp.p[jj][0]), bf16_to_f32(xw[jj] & 0xFFFFu), sum);
+              sum = fmaf(float(cp.p[jj][1]), bf16_to_f32(xw[jj] >> 16), sum);
+            }
+          }
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (4 * m + i == mi) acc[u][m][i] = fmaf(d, sum, acc[u][m][i]);
+        }
+      }
+    }
+  } else {
   // two chunks in flight: A holds chunks 0, 2, 4, ..., B holds 1, 3, 5, ...
   // (every slice holds at least one block; a chunk past the slice's end is
   // replaced by its first chunk, which is loaded but never used)
@@ -343,6 +411,7 @@ __global__ __launch_bounds__(256) void q4_gemm_kernel(const uint8_t* __restrict_
     run(rb, b0 + kChunk);
   }
   if (b0 < b_end) run(ra, b0);
+  }
 
   // lane holds tokens s = 16m + 4q + i of output rows rows[u]
   if constexpr (MODE == kGemmHead) {
@@ -479,11 +548,11 @@ extern "C" int q4_gemm_s64(const void* packed, int64_t n, int64_t k, const uint1
   hipLaunchKernelGGL(gemm_x_prep_kernel, dim3(kTok), dim3(256), 0, st, x, int(k), int(n_tok), xh, xf);
   const dim3 grid(unsigned((n + kTileN - 1) / kTileN), unsigned(p.slices));
   if (p.slices == 1) {
-    hipLaunchKernelGGL(q4_gemm_kernel<kGemmOut>, grid, dim3(256), 0, st, nib, scl, rexp, xh, xf, int(n), int(k),
-                       int(n_tok), p.bps, static_cast<void*>(y));
+    hipLaunchKernelGGL(q4_gemm_kernel<kGemmOut>, grid, dim3(256), 0, st, nib, scl, rexp, xh, xf, x, int(n),
+                       int(k), int(n_tok), p.bps, static_cast<void*>(y));
   } else {
-    hipLaunchKernelGGL(q4_gemm_kernel<kGemmSlices>, grid, dim3(256), 0, st, nib, scl, rexp, xh, xf, int(n), int(k),
-                       int(n_tok), p.bps, static_cast<void*>(part));
+    hipLaunchKernelGGL(q4_gemm_kernel<kGemmSlices>, grid, dim3(256), 0, st, nib, scl, rexp, xh, xf, x, int(n),
+                       int(k), int(n_tok), p.bps, static_cast<void*>(part));
     const size_t total = size_t(n_tok) * size_t(n);
     const unsigned rgrid = unsigned(std::min<size_t>((total + 255) / 256, 4096));
     hipLaunchKernelGGL(gemm_reduce_kernel, dim3(rgrid), dim3(256), 0, st, part, p.slices, int(n), int(n_tok), y);
@@ -545,7 +614,7 @@ extern "C" int lmhead_softcap_argmax_s64(const void* packed, int64_t vocab, int6
   const int tiles = int((vocab + kTileN - 1) / kTileN);
   hipLaunchKernelGGL(gemm_x_prep_kernel, dim3(kTok), dim3(256), 0, st, x, int(k), int(n_tok), xh, xf);
   hipLaunchKernelGGL(q4_gemm_kernel<kGemmHead>, dim3(unsigned(tiles), 1u), dim3(256), 0, st, nib, scl, rexp, xh, xf,
-                     int(vocab), int(k), int(n_tok), p.bps, static_cast<void*>(part));
+                     x, int(vocab), int(k), int(n_tok), p.bps, static_cast<void*>(part));
   reduce_argmax_partials(part, tiles, kTok, int(n_tok), cap, idx_out, val_out, st);
   return launch_status(name);
 }

@@ -88,6 +88,30 @@ struct Lane {
     }
     return acc;
   }
+
+  // The same row sum with the activations read as stored (bf16 from x,
+  // converted to fp32 exactly) and each block loaded on its own: the path
+  // for an x whose blocks span too many binades for the scaled fp16 copy.
+  // One block at a time (no unrolling), so it needs fewer registers than
+  // the streaming path beside it.
+  __device__ __forceinline__ float dot_exact(const uint8_t* __restrict__ nib, const uint16_t* __restrict__ scl,
+                                             const uint16_t* __restrict__ x, int row, int t, int B,
+                                             size_t row_bytes, uint32_t m_lo, uint32_t m_hi, uint32_t magic) {
+    const u32x4* np = reinterpret_cast<const u32x4*>(nib + size_t(row) * row_bytes);
+    const uint16_t* sp = scl + size_t(row) * size_t(B);
+    float acc = 0.0f;
+#pragma unroll 1
+    for (int j = 0; j < BPL; ++j) {
+      const int b = j * LPR + t;
+      if (FULL || b < B) {
+        const u32x4 v = np[b];
+        const float p = block_dot_exact(make_uint4(v.x, v.y, v.z, v.w), reinterpret_cast<const uint4*>(x + 32 * b),
+                                        m_lo, m_hi, magic);
+        acc = fmaf(float(__builtin_bit_cast(_Float16, sp[b])), p, acc);
+      }
+    }
+    return acc;
+  }
 };
 
 // Most activation vectors one multi-vector GEMV launch takes.
@@ -147,9 +171,14 @@ __device__ __forceinline__ void stage_x_load(const uint16_t* __restrict__ x, int
   for (int u = 0; u < NXL; ++u) v[u] = src[min(int(threadIdx.x) + u * NT, 4 * B - 1)];
 }
 
+// Returns true if one of this thread's blocks is "wide": a nonzero value lies
+// more than 31 binades below the block's largest exponent, so its scaled fp16
+// copy would lose significand bits (or flush to zero). The kernel then reads
+// x as stored instead (exact path).
 template <int NT, int NXL>
-__device__ __forceinline__ void stage_x_store(const uint4 (&v)[NXL], int B, uint32_t* __restrict__ xs,
+__device__ __forceinline__ bool stage_x_store(const uint4 (&v)[NXL], int B, uint32_t* __restrict__ xs,
                                               float* __restrict__ xf) {
+  bool wide = false;
   // every lane converts (a clamped duplicate past the end, not stored): a
   // conditional use would let the compiler sink the load past the weights
 #pragma unroll
@@ -157,11 +186,21 @@ __device__ __forceinline__ void stage_x_store(const uint4 (&v)[NXL], int B, uint
     const int qi = int(threadIdx.x) + u * NT;
     {
       const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-      uint32_t emax = 1;
+      uint32_t emax = 1, emin = 255;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) emax = max(emax, max((w[i] >> 7) & 0xFFu, (w[i] >> 23) & 0xFFu));
+      for (int i = 0; i < 4; ++i) {
+        emax = max(emax, max((w[i] >> 7) & 0xFFu, (w[i] >> 23) & 0xFFu));
+        emin = min(emin, min(bf16_exp_nz(w[i] & 0xFFFFu), bf16_exp_nz(w[i] >> 16)));
+      }
       emax = max(emax, uint32_t(__shfl_xor(int(emax), 1)));
       emax = max(emax, uint32_t(__shfl_xor(int(emax), 2)));
+      emin = min(emin, uint32_t(__shfl_xor(int(emin), 1)));
+      emin = min(emin, uint32_t(__shfl_xor(int(emin), 2)));
+      // the span test right here (pinned by the empty asm), so the exponent
+      // fields die before the conversion
+      int w_u = int(emax) - int(emin) > kMaxSpan;
+      asm volatile("" : "+v"(w_u));
+      wide |= w_u != 0;
       const int e = int(emax) - 127 - 14;
       uint32_t o[4];
 #pragma unroll
@@ -177,6 +216,7 @@ __device__ __forceinline__ void stage_x_store(const uint4 (&v)[NXL], int B, uint
       }
     }
   }
+  return wide;
 }
 
 template <int LPR, int BPL, int MODE, bool FULL>
@@ -225,8 +265,16 @@ __global__ __launch_bounds__(kThreads) void q4_rows_kernel(const uint8_t* __rest
   Lane<LPR, BPL, FULL> L;
   // (a wave with no rows loads the clamped last row and never uses it)
   L.load(nib, scl, row_of(0), t, B, row_bytes);
-  stage_x_store<kThreads, NXL>(xv, B, xs, xf);
+  // a wide block anywhere in x puts every workgroup (all stage the same x)
+  // on the exact path
+  __shared__ int wide_w[kWaves];
+  const bool wide_t = stage_x_store<kThreads, NXL>(xv, B, xs, xf);
+  const bool wide_wave = __ballot(wide_t) != 0;
+  if (lane == 0) wide_w[wave] = wide_wave;
   __syncthreads();
+  // uniform by construction; readfirstlane lets the compiler branch on it
+  // as a scalar, so the two paths do not hold registers at the same time
+  const bool exact = __builtin_amdgcn_readfirstlane(wide_w[0] | wide_w[1] | wide_w[2] | wide_w[3]) != 0;
 
   float fr[BPL];
 #pragma unroll
@@ -260,13 +308,18 @@ __global__ __launch_bounds__(kThreads) void q4_rows_kernel(const uint8_t* __rest
         static_cast<uint16_t*>(out)[v] = f32_to_bf16_rne(gelu_tanh(acc) * up);
     }
   };
-  for (int i = 0; i + 1 < iters; ++i) {
-    const float acc = L.template dot<true>(nib, scl, xs, fr, row_of(i + 1), t, B, row_bytes, m_lo, m_hi, magic);
-    emit(i, acc);
-  }
-  if (iters > 0) {
-    const float acc = L.template dot<false>(nib, scl, xs, fr, 0, t, B, row_bytes, m_lo, m_hi, magic);
-    emit(iters - 1, acc);
+  if (exact) {
+    for (int i = 0; i < iters; ++i)
+      emit(i, L.dot_exact(nib, scl, x, row_of(i), t, B, row_bytes, m_lo, m_hi, magic));
+  } else {
+    for (int i = 0; i + 1 < iters; ++i) {
+      const float acc = L.template dot<true>(nib, scl, xs, fr, row_of(i + 1), t, B, row_bytes, m_lo, m_hi, magic);
+      emit(i, acc);
+    }
+    if (iters > 0) {
+      const float acc = L.template dot<false>(nib, scl, xs, fr, 0, t, B, row_bytes, m_lo, m_hi, magic);
+      emit(iters - 1, acc);
+    }
   }
 
   if constexpr (MODE == kHead) {

@@ -80,6 +80,7 @@ __global__ __launch_bounds__(kMThreads) void q4_multi_kernel(const uint8_t* __re
   const int xsn = x_stride(k);
   _Float16* xs = reinterpret_cast<_Float16*>(dyn_lds);  // [4 * NG][xsn]
   __shared__ uint32_t red[kMWaves][4 * NG];
+  __shared__ uint32_t redn[kMWaves][4 * NG];
   __shared__ float ef[4 * NG];
 
   const int lane = threadIdx.x & 63;
@@ -132,18 +133,27 @@ __global__ __launch_bounds__(kMThreads) void q4_multi_kernel(const uint8_t* __re
 #pragma unroll
   for (int u = 0; u < kMXLoads; ++u) asm volatile("" : "+v"(xr[u].x), "+v"(xr[u].y), "+v"(xr[u].z), "+v"(xr[u].w));
 
-  uint32_t emax[kMultiVecs];
+  uint32_t emax[kMultiVecs], emin[kMultiVecs];
 #pragma unroll
-  for (int v = 0; v < kMultiVecs; ++v) emax[v] = 1;
+  for (int v = 0; v < kMultiVecs; ++v) {
+    emax[v] = 1;
+    emin[v] = 255;
+  }
   auto take = [&](int idx, const uint4& w) {
     const int v = idx / k8, i = idx - v * k8;
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-    uint32_t e = 1;
+    uint32_t e = 1, en = 255;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) e = max(e, max((ws[c] >> 7) & 0xFFu, (ws[c] >> 23) & 0xFFu));
+    for (int c = 0; c < 4; ++c) {
+      e = max(e, max((ws[c] >> 7) & 0xFFu, (ws[c] >> 23) & 0xFFu));
+      en = min(en, min(bf16_exp_nz(ws[c] & 0xFFFFu), bf16_exp_nz(ws[c] >> 16)));
+    }
 #pragma unroll
     for (int vv = 0; vv < kMultiVecs; ++vv)
-      if (vv == v) emax[vv] = max(emax[vv], e);
+      if (vv == v) {
+        emax[vv] = max(emax[vv], e);
+        emin[vv] = min(emin[vv], en);
+      }
     *reinterpret_cast<uint4*>(xs + size_t(v) * xsn + 8 * i) = w;
   };
 #pragma unroll
@@ -161,19 +171,43 @@ __global__ __launch_bounds__(kMThreads) void q4_multi_kernel(const uint8_t* __re
       if (base + u * kMThreads < tot) take(base + u * kMThreads, r[u]);
   }
   for (int v = 0; v < m; ++v) {
-    uint32_t e = emax[0];
+    uint32_t e = emax[0], en = emin[0];
 #pragma unroll
     for (int vv = 1; vv < kMultiVecs; ++vv)
-      if (vv == v) e = emax[vv];
-    for (int off = 32; off >= 1; off >>= 1) e = max(e, uint32_t(__shfl_xor(int(e), off)));
-    if (lane == 0) red[wave][v] = e;
+      if (vv == v) {
+        e = emax[vv];
+        en = emin[vv];
+      }
+    for (int off = 32; off >= 1; off >>= 1) {
+      e = max(e, uint32_t(__shfl_xor(int(e), off)));
+      en = min(en, uint32_t(__shfl_xor(int(en), off)));
+    }
+    if (lane == 0) {
+      red[wave][v] = e;
+      redn[wave][v] = en;
+    }
   }
   __syncthreads();
+  // A vector whose nonzero values span more binades than the scaled fp16
+  // copy keeps exactly puts every workgroup (all stage the same x) on the
+  // exact path: the rows stay raw bf16 in LDS and are read as stored.
+  int wide = 0;
+  for (int v = 0; v < m; ++v) {
+    const uint32_t e = max(max(red[0][v], red[1][v]), max(red[2][v], red[3][v]));
+    const uint32_t en = min(min(redn[0][v], redn[1][v]), min(redn[2][v], redn[3][v]));
+    wide |= int(e) - int(en) > kMaxSpan;
+  }
+  // uniform by construction; readfirstlane lets the compiler branch on it as
+  // a scalar, so the two paths do not hold registers at the same time
+  const bool exact = __builtin_amdgcn_readfirstlane(wide) != 0;
   for (int idx = threadIdx.x; idx < 4 * NG * k8; idx += kMThreads) {
     const int v = idx / k8, i = idx - v * k8;
     uint4* slot = reinterpret_cast<uint4*>(xs + size_t(v) * xsn + 8 * i);
     uint4 o = make_uint4(0u, 0u, 0u, 0u);
-    if (v < m) {
+    if (v < m && exact) {
+      o = *slot;  // raw bf16, read as stored
+      if (i == 0) ef[v] = 1.0f;
+    } else if (v < m) {
       const uint32_t emax = max(max(red[0][v], red[1][v]), max(red[2][v], red[3][v]));
       const int e = int(emax) - 127 - 14;
       const uint4 w = *slot;
@@ -211,6 +245,36 @@ __global__ __launch_bounds__(kMThreads) void q4_multi_kernel(const uint8_t* __re
       best[g][i] = -INFINITY;
       bidx[g][i] = INT_MAX;
     }
+
+  // After the last segment of a row group: sum the 16 lane groups (lanes
+  // 4g + j for fixed j); lanes 0..3 hold the row group's results, vector
+  // 4 * g + i of row j in acc[g][i].
+  auto finish = [&](int u) {
+    if (u % nseg == nseg - 1) {
+      const int row = (rg_base + (u / nseg) * kMWaves) * 4 + j;
+#pragma unroll
+      for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float s = acc[g][i];
+          s += __shfl_xor(s, 4);
+          s += __shfl_xor(s, 8);
+          s += __shfl_xor(s, 16);
+          s += __shfl_xor(s, 32);
+          const int v = 4 * g + i;
+          if constexpr (MODE == kMultiGemv) {
+            if (grp == 0 && row < n && v < m) y[size_t(v) * size_t(n) + row] = s * ef[v];
+          } else {
+            const float val = s * ef[v];
+            if (row < n && v < m && better(val, row, best[g][i], bidx[g][i])) {
+              best[g][i] = val;
+              bidx[g][i] = row;
+            }
+          }
+          acc[g][i] = 0.0f;
+        }
+    }
+  };
 
   // One (row group, segment) step; with REFILL each block's registers are
   // reloaded for step u + 1 right after their last use. REFILL is a
@@ -258,35 +322,53 @@ __global__ __launch_bounds__(kMThreads) void q4_multi_kernel(const uint8_t* __re
         }
       }
     }
-    if (u % nseg == nseg - 1) {
-      // sum the 16 lane groups (lanes 4g + j for fixed j); lanes 0..3 hold
-      // the row group's results, vector 4 * g + i of row j in acc[g][i]
-      const int row = (rg_base + (u / nseg) * kMWaves) * 4 + j;
+    finish(u);
+  };
+  // The exact path's step: each block loaded on its own (no refill, no
+  // unrolling) and summed per vector against the raw bf16 rows in fp32,
+  // where every code-activation product is exact.
+  auto step_exact = [&](int u) {
+    const int row = row_of(u);
+    const u32x4* np = reinterpret_cast<const u32x4*>(nib + size_t(row) * row_bytes);
+    const uint16_t* sp = scl + size_t(row) * size_t(B);
+#pragma unroll 1
+    for (int t = 0; t < BPL; ++t) {
+      const int b = block_of(u, t);
+      if (FULL || b < B) {
+        const u32x4 qv = np[b];
+        const uint32_t wd[4] = {qv.x, qv.y, qv.z, qv.w};
+        const float d = float(__builtin_bit_cast(_Float16, sp[b]));
+#pragma unroll 1
+        for (int v = 0; v < m; ++v) {
+          const uint4* xb = reinterpret_cast<const uint4*>(xs + size_t(v) * xsn + 32 * b);
+          float sum = 0.0f;
 #pragma unroll
-      for (int g = 0; g < NG; ++g)
+          for (int dd = 0; dd < 4; ++dd) {
+            const uint4 xv = xb[dd];  // bf16 k = 8dd .. 8dd+7
+            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+            const CodePairs cp = unpack_dword(wd[dd], m_lo, m_hi, magic);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          float s = acc[g][i];
-          s += __shfl_xor(s, 4);
-          s += __shfl_xor(s, 8);
-          s += __shfl_xor(s, 16);
-          s += __shfl_xor(s, 32);
-          const int v = 4 * g + i;
-          if constexpr (MODE == kMultiGemv) {
-            if (grp == 0 && row < n && v < m) y[size_t(v) * size_t(n) + row] = s * ef[v];
-          } else {
-            const float val = s * ef[v];
-            if (row < n && v < m && better(val, row, best[g][i], bidx[g][i])) {
-              best[g][i] = val;
-              bidx[g][i] = row;
+            for (int jj = 0; jj < 4; ++jj) {
+              sum = fmaf(float(cp.p[jj][0]), bf16_to_f32(xw[jj] & 0xFFFFu), sum);
+              sum = fmaf(float(cp.p[jj][1]), bf16_to_f32(xw[jj] >> 16), sum);
             }
           }
-          acc[g][i] = 0.0f;
+#pragma unroll
+          for (int g = 0; g < NG; ++g)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (4 * g + i == v) acc[g][i] = fmaf(d, sum, acc[g][i]);
         }
+      }
     }
+    finish(u);
   };
-  for (int u = 0; u + 1 < units; ++u) step(u, std::true_type{});
-  if (units > 0) step(units - 1, std::false_type{});
+  if (exact) {
+    for (int u = 0; u < units; ++u) step_exact(u);
+  } else {
+    for (int u = 0; u + 1 < units; ++u) step(u, std::true_type{});
+    if (units > 0) step(units - 1, std::false_type{});
+  }
 
   if constexpr (MODE == kMultiHead) {
     // the workgroup's best (value, row) per vector into its partial slots

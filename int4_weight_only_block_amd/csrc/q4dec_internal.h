@@ -101,6 +101,41 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h16) {
   return __builtin_bit_cast(float, h16 << 16);
 }
 
+// Activation staging scales a group of bf16 values (a block, a vector or a
+// token) by the power of two that puts the group's largest exponent at 2^14
+// and stores fp16. A nonzero value with exponent field E keeps all its bits
+// only if emax - E <= kMaxSpan (its last significand bit, 2^(E - emax + 7)
+// after scaling, must not fall below fp16's smallest step 2^-24). A group
+// with a wider span is computed on the exact path instead.
+constexpr int kMaxSpan = 31;
+
+// Exponent field of a nonzero bf16 value (subnormals count as 1, whose last
+// significand bit they share); 255 for +-0, so it never lowers a minimum.
+__device__ __forceinline__ uint32_t bf16_exp_nz(uint32_t h16) {
+  const uint32_t e = (h16 >> 7) & 0xFFu;
+  return (h16 & 0x7FFFu) == 0u ? 255u : (e == 0u ? 1u : e);
+}
+
+// sum_{j<32} c_j * x_j for one block with x as stored (bf16 [32], 16-byte
+// aligned), in fp32: every product is exact, only the sum rounds.
+__device__ __forceinline__ float block_dot_exact(uint4 q, const uint4* __restrict__ xb, uint32_t m_lo,
+                                                 uint32_t m_hi, uint32_t magic) {
+  float acc = 0.0f;
+  const uint32_t ws[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 xv = xb[i];  // bf16 k = 8i .. 8i+7, two per word
+    const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
+    const CodePairs cp = unpack_dword(ws[i], m_lo, m_hi, magic);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc = fmaf(float(cp.p[j][0]), bf16_to_f32(xw[j] & 0xFFFFu), acc);
+      acc = fmaf(float(cp.p[j][1]), bf16_to_f32(xw[j] >> 16), acc);
+    }
+  }
+  return acc;
+}
+
 // ---- cross-lane sums ------------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {

@@ -18,13 +18,16 @@
 // Codes are not converted to fp16 on their own. Each field is read at bit
 // offset s of an fp16 whose exponent is that of 1024 (OR with 0x6400), so the
 // half holds 1024 + 2^s * u exactly, u = code + 2 (INT2), code + 8 (INT4) or
-// code + 128 (INT8, s = 0) after an XOR of the packed word. The matching
-// activation is stored pre-multiplied by 2^-s, so the dot product yields
-// code * x plus (1024 * 2^-s + offset) * x, a term that depends on x alone:
-// each block's sum of those terms is computed once at staging and starts the
-// block's fp32 accumulator with the opposite sign. For INT2 and INT4 offsets s of 4 to 8
-// keep that term within about 66 times the codes' own contribution (six of
-// fp32's 24 bits); for INT8 the ratio is 1152 / |code|.
+// code + 128 (INT8, s = 0) after an XOR of the packed word. Subtracting the
+// exact fp16 constant 1024 + 2^s * offset in the same packed add leaves
+// 2^s * code exactly (dotc below), and the matching activation is stored
+// pre-multiplied by 2^-s, so each product in the dot is code * x exactly and
+// only the fp32 accumulation rounds.
+//
+// Staging scales each 32-wide block by one power of two; a block whose
+// nonzero values span more binades than that copy holds exactly (31 minus
+// the largest field offset) sends the launch down an exact path that decodes
+// each code as a signed integer and reads x as stored.
 #include <limits.h>
 #include <math.h>
 
@@ -136,8 +139,16 @@ constexpr int kChunkLoads = BITS == 8 ? 2 : 1;
 // bytes goes to slot i ^ (sw & 3); xe receives 2^E. The codes met in the dot
 // product are exact fp16 values 2^s * code, so each product is exact and
 // only the fp32 accumulation rounds.
+// Largest field shift s of a format: the staged values carry an extra 2^-s,
+// which narrows the span of binades a block can hold exactly.
 template <int BITS>
-__device__ __forceinline__ void stage_block(const uint4 (&src)[4], uint32_t* __restrict__ dst, int sw,
+constexpr int kMaxShift = BITS == 2 ? 8 : BITS == 4 ? 4 : 0;
+
+// Returns true when the block is "wide": a nonzero value lies more than
+// kMaxSpan - kMaxShift binades below its largest exponent, so its scaled fp16
+// copy would lose bits; the kernel then reads x as stored (exact path).
+template <int BITS>
+__device__ __forceinline__ bool stage_block(const uint4 (&src)[4], uint32_t* __restrict__ dst, int sw,
                                             float* __restrict__ xe, bool store) {
   using F = Fields<BITS>;
   uint32_t raw[16];
@@ -150,9 +161,16 @@ __device__ __forceinline__ void stage_block(const uint4 (&src)[4], uint32_t* __r
     const uint32_t v = raw[e >> 1];
     return __builtin_bit_cast(float, (e & 1) ? (v & 0xFFFF0000u) : (v << 16));
   };
-  uint32_t emax = 1;
+  uint32_t emax = 1, emin = 255;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) emax = max(emax, max((raw[i] >> 7) & 0xFFu, (raw[i] >> 23) & 0xFFu));
+  for (int i = 0; i < 16; ++i) {
+    emax = max(emax, max((raw[i] >> 7) & 0xFFu, (raw[i] >> 23) & 0xFFu));
+    emin = min(emin, min(bf16_exp_nz(raw[i] & 0xFFFFu), bf16_exp_nz(raw[i] >> 16)));
+  }
+  // the span test right here (pinned by the empty asm), so the 32 exponent
+  // fields die before the conversion instead of living across it
+  int wide = int(emax) - int(emin) > kMaxSpan - kMaxShift<BITS>;
+  asm volatile("" : "+v"(wide));
   const int e = int(emax) - 127 - 14;
   uint32_t out[16];
 #pragma unroll
@@ -170,6 +188,7 @@ __device__ __forceinline__ void stage_block(const uint4 (&src)[4], uint32_t* __r
     for (int i = 0; i < 4; ++i) d4[i ^ (sw & 3)] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
     *xe = ldexpf(1.0f, e);
   }
+  return wide != 0;
 }
 
 enum RowqMode { kRowqGemv = 0, kRowqGelu = 1, kRowqHead = 2 };
@@ -287,6 +306,7 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
 #pragma unroll
     for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(xr[u][i]));
 
+  bool wide_t = false;
 #pragma unroll
   for (int u = 0; u < NXB; ++u) {
     const int b = int(threadIdx.x) + u * kRThreads, bc = min(b, B - 1);
@@ -294,13 +314,25 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
                          make_uint4(xr[u][1].x, xr[u][1].y, xr[u][1].z, xr[u][1].w),
                          make_uint4(xr[u][2].x, xr[u][2].y, xr[u][2].z, xr[u][2].w),
                          make_uint4(xr[u][3].x, xr[u][3].y, xr[u][3].z, xr[u][3].w)};
-    stage_block<BITS>(v4, xs + 16 * bc, bc / BPC, xc + bc, b < B);
+    wide_t |= stage_block<BITS>(v4, xs + 16 * bc, bc / BPC, xc + bc, b < B);
+  }
+  // a wide block anywhere in x puts every workgroup (all stage the same x)
+  // on the exact path
+  __shared__ int wide_w[kRWaves];
+  {
+    const bool wide_wave = __ballot(wide_t) != 0;
+    if (lane == 0) wide_w[wave] = wide_wave;
   }
   // LDS writes done and visible; the weight loads above stay in flight
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  // uniform by construction; readfirstlane lets the compiler branch on it
+  // as a scalar, so the two paths do not hold registers at the same time
+  const bool exact = __builtin_amdgcn_readfirstlane(wide_w[0] | wide_w[1] | wide_w[2] | wide_w[3]) != 0;
 
   uint32_t xp[NB][16];
   float xf[NB];
+  // the lane's activation blocks, copied out of LDS (streaming path only)
+  auto fetch_x = [&]() {
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     const int c = j * LPR + t;
@@ -318,6 +350,7 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
       }
     }
   }
+  };
 
   uint32_t magic;
   asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
@@ -387,10 +420,47 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
     const float acc = dot(q, sc, refill, row_next);
     emit(i, acc, s_i);
   };
-  if constexpr (DEPTH == 1) {
+  // The exact path's row sum: each chunk loaded on its own, every code
+  // decoded as a signed integer (two's complement field, first code in the
+  // lowest bits) and multiplied by x as stored in fp32, where the product is
+  // exact; one chunk at a time.
+  auto dot_exact = [&](int row) -> float {
+    constexpr int NE = 128 * CH / BITS;  // codes per chunk
+    constexpr int PER = 32 / BITS;       // codes per dword
+    float acc = 0.0f;
+#pragma unroll 1
+    for (int j = 0; j < CPL; ++j) {
+      const int c = j * LPR + t;
+      if (FULL || c < U) {
+        const uint32_t* wp = reinterpret_cast<const uint32_t*>(w + size_t(row) * row_bytes + size_t(c) * 16 * CH);
+#pragma unroll 1
+        for (int d = 0; d < 4 * CH; ++d) {
+          const uint32_t word = wp[d];
+          const uint16_t* xd = x + size_t(c) * NE + d * PER;
+          // field f sign-extended by a left shift and an arithmetic right
+          // shift (the sbfe builtin's result was converted to float as if
+          // unsigned, so plain C is used)
+#pragma unroll
+          for (int f = 0; f < PER; ++f) {
+            const int code = int(word << (32 - BITS - f * BITS)) >> (32 - BITS);
+            acc = fmaf(float(code), bf16_to_f32(xd[f]), acc);
+          }
+        }
+      }
+    }
+    return acc;
+  };
+  if (exact) {
+    for (int i = 0; i < iters; ++i) {
+      const int row = row_of(i);
+      emit(i, dot_exact(row), row_scale[row]);
+    }
+  } else if constexpr (DEPTH == 1) {
+    fetch_x();
     for (int i = 0; i + 1 < iters; ++i) step(i, qa, sa, true, row_of(i + 1));
     if (iters > 0) step(iters - 1, qa, sa, false, 0);
   } else {
+    fetch_x();
     // qa holds row group i, qb row group i + 1; each refills two ahead
     int i = 0;
     for (; i + 3 < iters; i += 2) {

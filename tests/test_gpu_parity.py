@@ -1071,7 +1071,8 @@ def test_every_entry_point_replays_in_a_graph():
 
 # ----------------------------------------------------------- S=64 GEMM --
 @pytest.mark.parametrize("n,k,n_tok", [(1536, 1536, 64), (64, 32, 64), (100, 96, 1), (300, 2560, 37),
-                                       (3072, 2560, 64), (2560, 10240, 64), (77, 16384, 5),
+                                       # the four E4B layer shapes: QKV, O, down (split K) ...
+                                       (3072, 2560, 64), (2560, 2048, 64), (2560, 10240, 64), (77, 16384, 5),
                                        # >= 128 row tiles: one K slice, no reduce (E4B gate+up; a
                                        # ragged last tile)
                                        (20480, 2560, 64), (16400, 512, 17)])
