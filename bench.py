@@ -72,9 +72,13 @@ def parse():
 
 
 class Workload:
-    """Resident inputs of one decode step (drawn on the GPU, seeded)."""
+    """Resident inputs of one decode step (drawn on the GPU, seeded).
 
-    def __init__(self, dev, seed: int):
+    ``keep`` names matrix indices (into ``mats``) whose unpacked codes and
+    scales stay resident in ``kept`` so a test can check the step's outputs
+    against the oracle."""
+
+    def __init__(self, dev, seed: int, keep=()):
         import torch
 
         import int4_weight_only_block_amd as q4
@@ -85,9 +89,12 @@ class Workload:
         g.manual_seed(seed)
         self.mats = synth.stack_e4b_matrices()
         self.packed, self.xs, self.ys = [], [], []
-        for _, n, k in self.mats:
+        self.kept = {}
+        for i, (_, n, k) in enumerate(self.mats):
             codes, scales = synth.torch_q4_weights(g, n, k, dev)
             self.packed.append(q4.q4_pack(codes, scales))
+            if i in keep:
+                self.kept[i] = (codes, scales)
             del codes, scales
             self.xs.append(synth.torch_bf16_normal(g, k, dev))
             self.ys.append(torch.empty(n, dtype=torch.float32, device=dev))
@@ -180,6 +187,17 @@ class Workload:
 
     def prefill_flops(self) -> int:
         return sum(2 * 64 * n * k for _, n, k in self.mats[:-1]) + 2 * self.head_nk[0] * self.head_nk[1]
+
+
+def capture_step(torch, wl: Workload):
+    """One eager pass (lazy initialisation), then the decode step captured
+    in a HIP graph on the current stream."""
+    wl.step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        wl.step()
+    return graph
 
 
 def probe_kernels(torch, wl: Workload, reps: int = 20):
@@ -793,11 +811,7 @@ def main():
         return
 
     wl = Workload(dev, args.seed)
-    wl.step()  # eager pass: lazy init, device property cache
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        wl.step()
+    graph = capture_step(torch, wl)
     for _ in range(max(args.warmup, 0)):
         graph.replay()
     torch.cuda.synchronize()
