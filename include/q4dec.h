@@ -24,7 +24,8 @@
  *    Validation errors return before anything is enqueued.
  *    q4dec_last_error() then names the offending argument (thread-local).
  *  - Calls are stateless and thread-safe; the only library state is a cache
- *    of per-device properties (compute-unit count).
+ *    of per-device properties (compute-unit count) and the partials array of
+ *    lmhead_softcap_argmax_noalloc (see there).
  *  - Activations are bf16 bit patterns (uint16), outputs fp32.
  *  - q4_0 weights enter as unpacked int8 codes c in [-8, 7] plus fp16 scale
  *    bit patterns, one per 32 consecutive weights of a row; q4_pack converts
@@ -275,6 +276,27 @@ int lmhead_softcap_argmax(const void* packed, int64_t vocab, int64_t k,
                           const uint16_t* x, float cap, void* ws,
                           size_t ws_bytes, int32_t* idx_out, float* val_out,
                           void* stream);
+
+/* lmhead_softcap_argmax_noalloc: lmhead_softcap_argmax with no workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc). The
+ * per-workgroup partials live in a device array inside the library: 8192
+ * entries of 8 bytes (64 KiB) on every GPU the library runs on, held until
+ * the process ends. The call itself allocates nothing; the first call on a
+ * device looks up that array's device address. All calls on one GPU share
+ * the array, so calls that overlap in time on one GPU (several streams,
+ * several host threads) race and must be serialised by the caller; the
+ * array needs no initial contents. Same results as lmhead_softcap_argmax
+ * (the same kernels).
+ *   packed, vocab, k, x, cap, idx_out, val_out  as lmhead_softcap_argmax.
+ * Errors: as lmhead_softcap_argmax (no workspace errors);
+ *         Q4DEC_ERR_UNSUPPORTED if the head would need more than 8192
+ *         workgroup partials; Q4DEC_ERR_HIP if the array's address cannot be
+ *         looked up. */
+int lmhead_softcap_argmax_noalloc(const void* packed, int64_t vocab, int64_t k,
+                                  const uint16_t* x, float cap,
+                                  int32_t* idx_out, float* val_out,
+                                  void* stream);
 
 /* Workspace bytes lmhead_softcap_argmax_multi needs (m <= 8 vectors). */
 size_t lmhead_multi_workspace_bytes(int64_t vocab, int64_t k, int64_t m);

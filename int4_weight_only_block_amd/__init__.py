@@ -58,6 +58,8 @@ _SIGNATURES = {
                                                    ctypes.c_size_t, _c_p, _c_p, _c_p]),
     "lmhead_softcap_argmax": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, ctypes.c_float, _c_p,
                                              ctypes.c_size_t, _c_p, _c_p, _c_p]),
+    "lmhead_softcap_argmax_noalloc": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, ctypes.c_float, _c_p, _c_p,
+                                                     _c_p]),
     "lmhead_s64_workspace_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
     "lmhead_softcap_argmax_s64": (ctypes.c_int, [_c_p, _c_i64, _c_i64, _c_p, _c_i64, ctypes.c_float, _c_p,
                                                  ctypes.c_size_t, _c_p, _c_p, _c_p]),
@@ -331,6 +333,24 @@ def lmhead_softcap_argmax(packed: torch.Tensor, vocab: int, k: int, x: torch.Ten
     pv = _dev(val_out, "val_out", _F32, 1)
     _check(lib().lmhead_softcap_argmax(pp, vocab, k, px, float(cap), pw,
                                        ws.numel() * ws.element_size(), pi, pv, _stream(x)))
+    return idx_out, val_out
+
+
+def lmhead_softcap_argmax_noalloc(packed: torch.Tensor, vocab: int, k: int, x: torch.Tensor,
+                                  cap: float = 30.0, idx_out: torch.Tensor | None = None,
+                                  val_out: torch.Tensor | None = None):
+    """lmhead_softcap_argmax with the library's own partials array (no
+    workspace). Calls that overlap on one GPU race."""
+    pp = _dev(packed, "packed", _BYTES)
+    _check_packed(packed, vocab, k)
+    px = _dev(x, "x", _U16, k)
+    if idx_out is None:
+        idx_out = torch.empty(1, dtype=torch.int32, device=x.device)
+    if val_out is None:
+        val_out = torch.empty(1, dtype=torch.float32, device=x.device)
+    pi = _dev(idx_out, "idx_out", _I32, 1)
+    pv = _dev(val_out, "val_out", _F32, 1)
+    _check(lib().lmhead_softcap_argmax_noalloc(pp, vocab, k, px, float(cap), pi, pv, _stream(x)))
     return idx_out, val_out
 
 

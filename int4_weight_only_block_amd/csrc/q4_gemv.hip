@@ -572,31 +572,91 @@ extern "C" size_t lmhead_workspace_bytes(int64_t vocab, int64_t k) {
   return size_t(q4dec::kMaxPartials) * sizeof(uint2);
 }
 
-extern "C" int lmhead_softcap_argmax(const void* packed, int64_t vocab, int64_t k, const uint16_t* x, float cap,
-                                     void* ws, size_t ws_bytes, int32_t* idx_out, float* val_out, void* stream) {
-  using namespace q4dec;
-  int rc = check_common("lmhead_softcap_argmax", packed, vocab, "vocab", k, x);
+namespace q4dec {
+
+// Checks shared by the two head entry points (everything but the workspace).
+static int head_check(const char* fn, const void* packed, int64_t vocab, int64_t k, const uint16_t* x,
+                      const int32_t* idx_out, const float* val_out) {
+  int rc = check_common(fn, packed, vocab, "vocab", k, x);
   if (rc) return rc;
-  if (!ws) return fail(Q4DEC_ERR_NULL, "lmhead_softcap_argmax: ws is NULL");
-  if (!idx_out) return fail(Q4DEC_ERR_NULL, "lmhead_softcap_argmax: idx_out is NULL");
-  if (!val_out) return fail(Q4DEC_ERR_NULL, "lmhead_softcap_argmax: val_out is NULL");
-  if (!aligned(ws, 8)) return fail(Q4DEC_ERR_ALIGN, "lmhead_softcap_argmax: ws must be 8-byte aligned");
+  if (!idx_out) return fail(Q4DEC_ERR_NULL, "%s: idx_out is NULL", fn);
+  if (!val_out) return fail(Q4DEC_ERR_NULL, "%s: val_out is NULL", fn);
   if (!aligned(idx_out, 4) || !aligned(val_out, 4))
-    return fail(Q4DEC_ERR_ALIGN, "lmhead_softcap_argmax: idx_out and val_out must be 4-byte aligned");
-  const size_t need = lmhead_workspace_bytes(vocab, k);
-  if (ws_bytes < need)
-    return fail(Q4DEC_ERR_WORKSPACE, "lmhead_softcap_argmax: ws_bytes %zu < required %zu", ws_bytes, need);
+    return fail(Q4DEC_ERR_ALIGN, "%s: idx_out and val_out must be 4-byte aligned", fn);
+  return Q4DEC_OK;
+}
+
+// Both passes of the head, with the per-workgroup partials in `partials`
+// (at least kMaxPartials entries; the plan never needs more).
+static int head_run(const char* fn, const void* packed, int64_t vocab, int64_t k, const uint16_t* x, float cap,
+                    uint2* partials, int32_t* idx_out, float* val_out, hipStream_t st) {
   const Plan p = make_plan<kHead>(vocab, k);
-  if (p.grid > kMaxPartials) return fail(Q4DEC_ERR_UNSUPPORTED, "lmhead_softcap_argmax: too many workgroups");
+  if (p.grid > kMaxPartials)
+    return fail(Q4DEC_ERR_UNSUPPORTED, "%s: the head needs %d workgroup partials, more than the %d it holds", fn,
+                p.grid, kMaxPartials);
   const uint8_t* nib = static_cast<const uint8_t*>(packed);
   const uint16_t* scl = reinterpret_cast<const uint16_t*>(nib + nib_plane_bytes(vocab, k));
-  uint2* partials = static_cast<uint2*>(ws);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  rc = launch_rows(p, nib, scl, x, int(vocab), int(k), nullptr, partials, st);
+  int rc = launch_rows(p, nib, scl, x, int(vocab), int(k), nullptr, partials, st);
   if (rc) return rc;
   hipLaunchKernelGGL(lmhead_reduce_kernel, dim3(1), dim3(kReduceThreads), 0, st, partials, p.grid, cap, idx_out,
                      val_out);
-  return launch_status("lmhead_softcap_argmax");
+  return launch_status(fn);
+}
+
+// Partials of lmhead_softcap_argmax_noalloc: a file-scope device array in
+// place of a caller workspace (kMaxPartials entries, 64 KiB on every GPU the
+// library runs on, held until the process ends). In host code `scratch`
+// names a host-side stand-in, not the device memory: kernels get the device
+// address that hipGetSymbolAddress returns for the current device, looked
+// up once per device and kept.
+static __device__ __align__(256) uint2 scratch[kMaxPartials];
+
+static int scratch_partials(const char* fn, uint2** out) {
+  static std::mutex mu;
+  static uint2* ptr[64] = {nullptr};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(Q4DEC_ERR_HIP, "%s: hipGetDevice failed: %s", fn, hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(Q4DEC_ERR_UNSUPPORTED, "%s: device %d out of range", fn, dev);
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(Q4DEC_ERR_HIP, "%s: scratch address lookup failed on device %d: %s", fn, dev,
+                  hipGetErrorString(e));
+    ptr[dev] = static_cast<uint2*>(p);
+  }
+  *out = ptr[dev];
+  return Q4DEC_OK;
+}
+
+}  // namespace q4dec
+
+extern "C" int lmhead_softcap_argmax(const void* packed, int64_t vocab, int64_t k, const uint16_t* x, float cap,
+                                     void* ws, size_t ws_bytes, int32_t* idx_out, float* val_out, void* stream) {
+  using namespace q4dec;
+  const char* fn = "lmhead_softcap_argmax";
+  int rc = head_check(fn, packed, vocab, k, x, idx_out, val_out);
+  if (rc) return rc;
+  if (!ws) return fail(Q4DEC_ERR_NULL, "%s: ws is NULL", fn);
+  if (!aligned(ws, 8)) return fail(Q4DEC_ERR_ALIGN, "%s: ws must be 8-byte aligned", fn);
+  const size_t need = lmhead_workspace_bytes(vocab, k);
+  if (ws_bytes < need) return fail(Q4DEC_ERR_WORKSPACE, "%s: ws_bytes %zu < required %zu", fn, ws_bytes, need);
+  return head_run(fn, packed, vocab, k, x, cap, static_cast<uint2*>(ws), idx_out, val_out,
+                  static_cast<hipStream_t>(stream));
+}
+
+extern "C" int lmhead_softcap_argmax_noalloc(const void* packed, int64_t vocab, int64_t k, const uint16_t* x,
+                                             float cap, int32_t* idx_out, float* val_out, void* stream) {
+  using namespace q4dec;
+  const char* fn = "lmhead_softcap_argmax_noalloc";
+  int rc = head_check(fn, packed, vocab, k, x, idx_out, val_out);
+  if (rc) return rc;
+  uint2* partials = nullptr;
+  rc = scratch_partials(fn, &partials);
+  if (rc) return rc;
+  return head_run(fn, packed, vocab, k, x, cap, partials, idx_out, val_out, static_cast<hipStream_t>(stream));
 }
 
 extern "C" int q4_gemv_gelu_mul(const void* packed, int64_t n, int64_t k, const uint16_t* x, uint16_t* a,

@@ -13,7 +13,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(q4.LIB_PATH), reason="libq4de
 EXPECTED = {
     "q4dec_abi_version", "q4dec_last_error", "q4_packed_bytes", "q4_pack", "q4_quantize", "q4_gemv", "q4_gemv_gelu_mul", "q4_gemv_multi", "rowq_gemv", "rowq_gemv_gelu_mul",
     "rowq_head_workspace_bytes", "rowq_softcap_argmax",
-    "q4_gemm_s64", "q4_gemm_workspace_bytes", "lmhead_workspace_bytes", "lmhead_softcap_argmax", "lmhead_multi_workspace_bytes", "lmhead_softcap_argmax_multi", "lmhead_s64_workspace_bytes", "lmhead_softcap_argmax_s64", "ple_gather", "rowq_gather",
+    "q4_gemm_s64", "q4_gemm_workspace_bytes", "lmhead_workspace_bytes", "lmhead_softcap_argmax", "lmhead_softcap_argmax_noalloc", "lmhead_multi_workspace_bytes", "lmhead_softcap_argmax_multi", "lmhead_s64_workspace_bytes", "lmhead_softcap_argmax_s64", "ple_gather", "rowq_gather",
 }
 
 
@@ -236,6 +236,31 @@ def test_lmhead_validation():
     assert call(k=40) == q4.ERR_SHAPE
     assert call(ws=FAKE + 4) == q4.ERR_ALIGN
     assert call(idx=FAKE + 2) == q4.ERR_ALIGN
+
+
+def test_lmhead_noalloc_validation():
+    """Argument errors return before the scratch lookup or any launch."""
+    L = q4.lib()
+    args = [FAKE, 1024, 64, FAKE, 30.0, FAKE, FAKE, None]
+
+    def call(**kw):
+        a = list(args)
+        names = ["packed", "vocab", "k", "x", "cap", "idx", "val", "stream"]
+        for key, v in kw.items():
+            a[names.index(key)] = v
+        return L.lmhead_softcap_argmax_noalloc(*a)
+
+    assert call(packed=None) == q4.ERR_NULL and "packed" in q4.q4dec_last_error()
+    assert call(x=None) == q4.ERR_NULL
+    assert call(idx=None) == q4.ERR_NULL and "idx_out" in q4.q4dec_last_error()
+    assert call(val=None) == q4.ERR_NULL
+    assert call(vocab=0) == q4.ERR_SHAPE and "vocab" in q4.q4dec_last_error()
+    assert call(vocab=1 << 31) == q4.ERR_SHAPE
+    assert call(k=40) == q4.ERR_SHAPE
+    assert call(k=q4.MAX_K + 32) == q4.ERR_UNSUPPORTED
+    assert call(packed=FAKE + 8) == q4.ERR_ALIGN
+    assert call(idx=FAKE + 2) == q4.ERR_ALIGN
+    assert "lmhead_softcap_argmax_noalloc" in q4.q4dec_last_error()
 
 
 def test_gemm_validation():
