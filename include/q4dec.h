@@ -251,6 +251,87 @@ int q4_gemm_s64(const void* packed, int64_t n, int64_t k, const uint16_t* x,
                 int64_t n_tok, float* y, void* ws, size_t ws_bytes,
                 void* stream);
 
+/* ---- q4_gemv_chain: one persistent launch over a chain of S=1 GEMVs ----
+ * A decode step reads every layer's weights once per token (E4B card,
+ * bandwidth cost-model paragraph: bytes per token over the bandwidth plus a
+ * fixed per-step cost); with one launch per matrix each of the 169 E4B
+ * matrices pays a fixed dispatch cost and starts its weight stream only
+ * after the previous kernel has drained (mixed-bit page, fused gate/up
+ * paragraph: fewer dispatches per layer help the device). A chain runs its
+ * links in one launch: every workgroup walks the links in order, issues the
+ * weight loads of its first rows of link i + 1 as soon as it has finished
+ * link i, and only then waits (when link i + 1 waits) for every workgroup to
+ * finish link i, so the wait runs under the weight stream. Per link the
+ * arithmetic is q4_gemv's (and q4_gemv_gelu_mul's, lmhead_softcap_argmax's),
+ * with the same results bar. */
+#define Q4DEC_LINK_GEMV 0 /* out = fp32 y[n] = W x (q4_gemv) */
+#define Q4DEC_LINK_GELU 1 /* out = bf16 a[n/2] (q4_gemv_gelu_mul; k <= Q4DEC_CHAIN_GELU_MAX_K) */
+#define Q4DEC_LINK_HEAD 2 /* last link only: softcap + argmax to idx_out / val_out */
+#define Q4DEC_CHAIN_MAX_LINKS 4096
+#define Q4DEC_CHAIN_MAX_K 10240
+#define Q4DEC_CHAIN_GELU_MAX_K 5120
+
+typedef struct q4_chain_link {
+  const void* packed;  /* q4_pack output for (n, k); 16-byte aligned */
+  const uint16_t* x;   /* bf16 [k], 16-byte aligned; may be an earlier link's output */
+  void* out;           /* fp32 [n] (GEMV) or bf16 [n/2] (GELU); unused for HEAD */
+  int64_t n, k;
+  int32_t mode;        /* Q4DEC_LINK_* */
+  int32_t wait;        /* nonzero: stage x only after every workgroup has
+                          finished every earlier link (required when x is an
+                          earlier link's output) */
+} q4_chain_link;
+
+/* Bytes of a chain table for n_links links (0 if n_links is out of range). */
+size_t q4_chain_table_bytes(int64_t n_links);
+
+/* Bytes of the chain workspace (error word, arrival counters, head
+ * partials). Zero it once before the first call; the kernel leaves it clear
+ * after every call that succeeds. */
+size_t q4_chain_workspace_bytes(void);
+
+/* q4_chain_build: validates a host array of links and writes the chain table
+ * (host memory, q4_chain_table_bytes(n_links) bytes) that q4_gemv_chain
+ * runs; the caller copies it once to device memory. Host-only: the links'
+ * buffers are not touched. Per link it picks the lane split of the S=1 GEMV.
+ * It rejects a chain in which an output shares a 256-byte line with the input
+ * of the same or an earlier link or with another link's output, or in which
+ * a link reads an earlier output with no waiting link in between (later
+ * links read earlier outputs with ordinary cached loads, which is safe only
+ * for lines nothing has read before in the launch).
+ *   cap      softcap of a head link (30.0; <= 0 disables it).
+ *   spin_us  bound on each wait, in microseconds (0: 500000). A wait that
+ *            runs out sets the workspace's error word (see q4_gemv_chain).
+ *   table    host output, 8-byte aligned.
+ * Errors: NULL pointer, n_links out of range, a link's n, k, mode, wait or
+ *         alignment invalid (as the matching single-matrix call), k >
+ *         Q4DEC_CHAIN_MAX_K, a head link not last, the line rules above,
+ *         table too small. */
+int q4_chain_build(const q4_chain_link* links, int64_t n_links, float cap,
+                   int64_t spin_us, void* table, size_t table_bytes);
+
+/* q4_gemv_chain: runs a built chain as one launch on `stream`: one workgroup
+ * of 1024 threads per compute unit, all resident at once (nothing else may
+ * occupy the device's compute units while it runs, or its waits run out).
+ *   table_host  the table q4_chain_build wrote (checked: tag, checksum).
+ *   table_dev   a device copy of it, 64-byte aligned; the kernel checks its
+ *               tag, link count and checksum against table_host before use.
+ *   ws          q4_chain_workspace_bytes() bytes, 256-byte aligned, zeroed
+ *               before the first call and owned by this chain's calls (calls
+ *               that share a workspace must not overlap).
+ *   idx_out, val_out  device int32 [1] / fp32 [1] for a chain that ends in a
+ *               head link (may be NULL otherwise).
+ * The first 4 bytes of ws are an error word the kernel sets: 1 when a wait
+ * ran out (another workgroup did not arrive in time), 2 when table_dev does
+ * not match table_host. While it is nonzero every call returns at once
+ * without writing outputs; zero the whole workspace to clear it.
+ * Errors: NULL pointer, misalignment, workspace too small, table_host not a
+ *         valid built table or built on a device with another compute-unit
+ *         count, a head chain without idx_out / val_out. */
+int q4_gemv_chain(const void* table_host, const void* table_dev, void* ws,
+                  size_t ws_bytes, int32_t* idx_out, float* val_out,
+                  void* stream);
+
 /* Workspace bytes lmhead_softcap_argmax needs for a [vocab, k] head. */
 size_t lmhead_workspace_bytes(int64_t vocab, int64_t k);
 

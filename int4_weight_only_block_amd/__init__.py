@@ -15,6 +15,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -68,6 +69,21 @@ _SIGNATURES = {
     "rowq_gather": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, ctypes.c_int32, _c_i64, _c_p, _c_i64,
                                    ctypes.c_float, _c_p, _c_p, _c_p]),
 }
+
+
+
+class ChainLink(ctypes.Structure):
+    """q4_chain_link of include/q4dec.h."""
+    _fields_ = [("packed", ctypes.c_void_p), ("x", ctypes.c_void_p), ("out", ctypes.c_void_p),
+                ("n", ctypes.c_int64), ("k", ctypes.c_int64), ("mode", ctypes.c_int32), ("wait", ctypes.c_int32)]
+
+
+_SIGNATURES.update({
+    "q4_chain_table_bytes": (ctypes.c_size_t, [_c_i64]),
+    "q4_chain_workspace_bytes": (ctypes.c_size_t, []),
+    "q4_chain_build": (ctypes.c_int, [_c_p, _c_i64, ctypes.c_float, _c_i64, _c_p, ctypes.c_size_t]),
+    "q4_gemv_chain": (ctypes.c_int, [_c_p, _c_p, _c_p, ctypes.c_size_t, _c_p, _c_p, _c_p]),
+})
 
 _lib = None
 
@@ -447,3 +463,74 @@ def rowq_gather(w: torch.Tensor, scales: torch.Tensor, bits: int, group: int, id
     pe = _dev(err_flag, "err_flag", _I32, 1) if err_flag is not None else None
     _check(lib().rowq_gather(pw, ps, vocab, dim, bits, group, pi, n_ids, float(mult), po, pe, _stream(w)))
     return out
+
+
+# ------------------------------------------------------------- GEMV chain
+LINK_GEMV, LINK_GELU, LINK_HEAD = 0, 1, 2
+CHAIN_MAX_K = 10240
+CHAIN_GELU_MAX_K = 5120
+
+
+class Chain:
+    """A chain built by q4_chain_build: the host table, its device copy, the
+    workspace (zeroed), and references that keep every link's tensors alive.
+    ``err()`` reads the workspace's error word (synchronises)."""
+
+    def __init__(self, table_host, table_dev, ws, keep, head):
+        self.table_host, self.table_dev, self.ws, self._keep, self.head = table_host, table_dev, ws, keep, head
+
+    def err(self) -> int:
+        return int(self.ws[:4].view(torch.int32).item())
+
+    def clear(self):
+        self.ws.zero_()
+
+
+def chain_link(packed: torch.Tensor, n: int, k: int, x: torch.Tensor, out: torch.Tensor | None = None,
+               mode: int = LINK_GEMV, wait: bool = True) -> dict:
+    """One link: GEMV (out fp32 [n]), GELU (out bf16 [n/2]) or HEAD (last link, no out)."""
+    return dict(packed=packed, n=n, k=k, x=x, out=out, mode=mode, wait=wait)
+
+
+def q4_chain_build(links, cap: float = 30.0, spin_us: int = 0) -> Chain:
+    arr = (ChainLink * len(links))()
+    keep = []
+    for i, l in enumerate(links):
+        n, k, mode = int(l["n"]), int(l["k"]), int(l["mode"])
+        pp = _dev(l["packed"], f"links[{i}].packed", _BYTES)
+        _check_packed(l["packed"], n, k)
+        px = _dev(l["x"], f"links[{i}].x", _U16, k)
+        po = 0
+        if mode == LINK_GEMV:
+            po = _dev(l["out"], f"links[{i}].out", _F32, n)
+        elif mode == LINK_GELU:
+            po = _dev(l["out"], f"links[{i}].out", _U16, n // 2)
+        arr[i] = ChainLink(pp, px, po, n, k, mode, 1 if l.get("wait", True) else 0)
+        keep += [l["packed"], l["x"], l["out"]]
+    nb = int(lib().q4_chain_table_bytes(len(links)))
+    if nb == 0:
+        raise ValueError(f"chain of {len(links)} links out of range")
+    host = np.zeros((nb + 7) // 8, dtype=np.uint64)
+    _check(lib().q4_chain_build(ctypes.cast(arr, ctypes.c_void_p), len(links), float(cap), int(spin_us),
+                                host.ctypes.data, host.nbytes))
+    dev = links[0]["x"].device
+    table_dev = torch.from_numpy(host.view(np.uint8)).to(dev)
+    ws = torch.zeros(int(lib().q4_chain_workspace_bytes()), dtype=torch.uint8, device=dev)
+    return Chain(host, table_dev, ws, keep, head=int(links[-1]["mode"]) == LINK_HEAD)
+
+
+def q4_gemv_chain(chain: Chain, idx_out: torch.Tensor | None = None, val_out: torch.Tensor | None = None):
+    """Run a built chain (one launch on the current stream). Returns (idx,
+    val) for a chain ending in a head, else None."""
+    dev = chain.table_dev.device
+    pi = pv = 0
+    if chain.head:
+        if idx_out is None:
+            idx_out = torch.empty(1, dtype=torch.int32, device=dev)
+        if val_out is None:
+            val_out = torch.empty(1, dtype=torch.float32, device=dev)
+        pi = _dev(idx_out, "idx_out", _I32, 1)
+        pv = _dev(val_out, "val_out", _F32, 1)
+    _check(lib().q4_gemv_chain(chain.table_host.ctypes.data, chain.table_dev.data_ptr(), chain.ws.data_ptr(),
+                               chain.ws.numel(), pi, pv, _stream(chain.table_dev)))
+    return (idx_out, val_out) if chain.head else None

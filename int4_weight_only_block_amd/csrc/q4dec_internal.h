@@ -154,6 +154,103 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// (value desc, index asc) comparator for the argmax; NaN never wins.
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+// Best (value, row) of the wave into every lane.
+__device__ __forceinline__ void wave_best(float& best, int& bidx) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(best, off);
+    const int oi = __shfl_xor(bidx, off);
+    if (better(ov, oi, best, bidx)) {
+      best = ov;
+      bidx = oi;
+    }
+  }
+}
+
+// tanh-form GELU in fp32: 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))).
+__device__ __forceinline__ float gelu_tanh(float g) {
+  const float k0 = 0.7978845608028654f, k1 = 0.044715f;
+  return 0.5f * g * (1.0f + tanhf(k0 * (g + k1 * g * g * g)));
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float v) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return uint16_t((u >> 16) | 0x40u);
+  return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+// Stage x (bf16 [32 B]) into LDS as block-scaled fp16 pairs (block b at
+// xs[16 b], quarter i in slot i ^ (b & 3), 2^E in xf[b]); E puts the block's
+// largest magnitude in [2^14, 2^15), so every bf16 value keeps its 8-bit
+// significand unless it lies below 2^-31 times that maximum. Four lanes share a
+// 32-wide block, one 16-byte quarter each, and agree on the block's largest
+// exponent with two xor shuffles. The loads are issued first (stage_x_load,
+// NXL quarters per thread) and converted later (stage_x_store): vector memory
+// counters retire in order, so loads issued before the weight loads can be
+// waited for while the weights are still in flight.
+template <int NT, int NXL>
+__device__ __forceinline__ void stage_x_load(const uint16_t* __restrict__ x, int B, uint4 (&v)[NXL]) {
+  const uint4* src = reinterpret_cast<const uint4*>(x);
+  // unconditional (a clamped index past the end), so the wait for these
+  // loads can be counted past the weight loads that follow
+#pragma unroll
+  for (int u = 0; u < NXL; ++u) v[u] = src[min(int(threadIdx.x) + u * NT, 4 * B - 1)];
+}
+
+// Returns true if one of this thread's blocks is "wide": a nonzero value lies
+// more than 31 binades below the block's largest exponent, so its scaled fp16
+// copy would lose significand bits (or flush to zero). The kernel then reads
+// x as stored instead (exact path).
+template <int NT, int NXL>
+__device__ __forceinline__ bool stage_x_store(const uint4 (&v)[NXL], int B, uint32_t* __restrict__ xs,
+                                              float* __restrict__ xf) {
+  bool wide = false;
+  // every lane converts (a clamped duplicate past the end, not stored): a
+  // conditional use would let the compiler sink the load past the weights
+#pragma unroll
+  for (int u = 0; u < NXL; ++u) {
+    const int qi = int(threadIdx.x) + u * NT;
+    {
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+      uint32_t emax = 1, emin = 255;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        emax = max(emax, max((w[i] >> 7) & 0xFFu, (w[i] >> 23) & 0xFFu));
+        emin = min(emin, min(bf16_exp_nz(w[i] & 0xFFFFu), bf16_exp_nz(w[i] >> 16)));
+      }
+      emax = max(emax, uint32_t(__shfl_xor(int(emax), 1)));
+      emax = max(emax, uint32_t(__shfl_xor(int(emax), 2)));
+      emin = min(emin, uint32_t(__shfl_xor(int(emin), 1)));
+      emin = min(emin, uint32_t(__shfl_xor(int(emin), 2)));
+      // the span test right here (pinned by the empty asm), so the exponent
+      // fields die before the conversion
+      int w_u = int(emax) - int(emin) > kMaxSpan;
+      asm volatile("" : "+v"(w_u));
+      wide |= w_u != 0;
+      const int e = int(emax) - 127 - 14;
+      uint32_t o[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const half2_t h = {(_Float16)ldexpf(bf16_to_f32(w[i] & 0xFFFFu), -e),
+                           (_Float16)ldexpf(bf16_to_f32(w[i] >> 16), -e)};
+        o[i] = __builtin_bit_cast(uint32_t, h);
+      }
+      const int b = qi >> 2, q = qi & 3;
+      if (qi < 4 * B) {
+        reinterpret_cast<uint4*>(xs + 16 * b)[q ^ (b & 3)] = make_uint4(o[0], o[1], o[2], o[3]);
+        if (q == 0) xf[b] = ldexpf(1.0f, e);
+      }
+    }
+  }
+  return wide;
+}
+
 // Per-vector argmax over per-workgroup (value bits, row) partials: vector v's
 // entries sit at partials[w * stride + v] for w < g. One workgroup per
 // vector writes idx_out[v] and cap * tanh(best / cap) (the raw best for
@@ -161,9 +258,5 @@ __device__ __forceinline__ float group_sum(float v) {
 void reduce_argmax_partials(const uint2* partials, int g, int stride, int nvec, float cap, int32_t* idx_out,
                             float* val_out, hipStream_t st);
 
-// (value desc, index asc) comparator for the argmax; NaN never wins.
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
-}
 
 }  // namespace q4dec

@@ -13,7 +13,8 @@ pytestmark = pytest.mark.skipif(not os.path.exists(q4.LIB_PATH), reason="libq4de
 EXPECTED = {
     "q4dec_abi_version", "q4dec_last_error", "q4_packed_bytes", "q4_pack", "q4_quantize", "q4_gemv", "q4_gemv_gelu_mul", "q4_gemv_multi", "rowq_gemv", "rowq_gemv_gelu_mul",
     "rowq_head_workspace_bytes", "rowq_softcap_argmax",
-    "q4_gemm_s64", "q4_gemm_workspace_bytes", "lmhead_workspace_bytes", "lmhead_softcap_argmax", "lmhead_softcap_argmax_noalloc", "lmhead_multi_workspace_bytes", "lmhead_softcap_argmax_multi", "lmhead_s64_workspace_bytes", "lmhead_softcap_argmax_s64", "ple_gather", "rowq_gather",
+    "q4_gemm_s64", "q4_gemm_workspace_bytes", "lmhead_workspace_bytes", "lmhead_softcap_argmax", "lmhead_softcap_argmax_noalloc", "lmhead_multi_workspace_bytes",
+    "q4_chain_table_bytes", "q4_chain_workspace_bytes", "q4_chain_build", "q4_gemv_chain", "lmhead_softcap_argmax_multi", "lmhead_s64_workspace_bytes", "lmhead_softcap_argmax_s64", "ple_gather", "rowq_gather",
 }
 
 
@@ -387,3 +388,60 @@ def test_binding_rejects_host_tensors():
 
     with pytest.raises(ValueError):
         q4.q4_gemv(torch.zeros(100, dtype=torch.uint8), 2, 32, torch.zeros(32, dtype=torch.int16))
+
+
+def test_chain_build_validation():
+    """q4_chain_build is host-only; every rejection below returns before any
+    device query (fake, never dereferenced addresses)."""
+    import numpy as np
+
+    L = q4.lib()
+    MB = 1 << 20
+
+    def link(i, **kw):
+        d = dict(packed=FAKE + (10 + 4 * i) * MB, x=FAKE + (11 + 4 * i) * MB, out=FAKE + (12 + 4 * i) * MB,
+                 n=256, k=2560, mode=q4.LINK_GEMV, wait=1)
+        d.update(kw)
+        return q4.ChainLink(d["packed"], d["x"], d["out"], d["n"], d["k"], d["mode"], d["wait"])
+
+    def build(links, table_bytes=None, n=None):
+        arr = (q4.ChainLink * len(links))(*links)
+        nl = len(links) if n is None else n
+        tb = int(L.q4_chain_table_bytes(max(nl, 1))) if table_bytes is None else table_bytes
+        host = np.zeros(max(tb, 8) // 8 + 1, dtype=np.uint64)
+        return L.q4_chain_build(arr, nl, 30.0, 0, host.ctypes.data, tb)
+
+    assert L.q4_chain_table_bytes(0) == 0 and L.q4_chain_table_bytes(169) == 64 + 169 * 64
+    assert L.q4_chain_workspace_bytes() >= 256 + 16 * 256
+    assert build([link(0)], n=0) == q4.ERR_SHAPE
+    assert build([link(0)], table_bytes=64) == q4.ERR_WORKSPACE
+    assert build([link(0, k=40)]) == q4.ERR_SHAPE and "k must be" in q4.q4dec_last_error()
+    assert build([link(0, k=q4.CHAIN_MAX_K + 32)]) == q4.ERR_UNSUPPORTED
+    assert build([link(0, n=0)]) == q4.ERR_SHAPE
+    assert build([link(0, mode=7)]) == q4.ERR_SHAPE
+    assert build([link(0, mode=q4.LINK_HEAD), link(1)]) == q4.ERR_SHAPE and "last" in q4.q4dec_last_error()
+    assert build([link(0, mode=q4.LINK_GELU, n=255)]) == q4.ERR_SHAPE
+    assert build([link(0, mode=q4.LINK_GELU, k=q4.CHAIN_GELU_MAX_K + 32)]) == q4.ERR_SHAPE
+    assert build([link(0, packed=FAKE + 10 * MB + 8)]) == q4.ERR_ALIGN
+    assert build([link(0, out=0)]) == q4.ERR_NULL
+    # an output in a line its own link reads
+    assert build([link(0, out=FAKE + 11 * MB + 4096)]) == q4.ERR_SHAPE and "line" in q4.q4dec_last_error()
+    # an output in a line an earlier link reads
+    assert build([link(0), link(1, out=FAKE + 11 * MB)]) == q4.ERR_SHAPE
+    # two outputs sharing a line
+    assert build([link(0), link(1, out=FAKE + 12 * MB + 128)]) == q4.ERR_SHAPE
+    # a later link reading an earlier output without a wait in between
+    assert build([link(0), link(1, x=FAKE + 12 * MB, wait=0)]) == q4.ERR_SHAPE and "wait" in q4.q4dec_last_error()
+
+
+def test_chain_run_validation():
+    import numpy as np
+
+    L = q4.lib()
+    host = np.zeros(64, dtype=np.uint64)
+    ws_bytes = int(L.q4_chain_workspace_bytes())
+    assert L.q4_gemv_chain(None, FAKE, FAKE, ws_bytes, FAKE, FAKE, None) == q4.ERR_NULL
+    assert L.q4_gemv_chain(host.ctypes.data, FAKE, FAKE, ws_bytes - 1, FAKE, FAKE, None) == q4.ERR_WORKSPACE
+    assert L.q4_gemv_chain(host.ctypes.data, FAKE, FAKE + 64, ws_bytes, FAKE, FAKE, None) == q4.ERR_ALIGN
+    # a table that q4_chain_build did not write
+    assert L.q4_gemv_chain(host.ctypes.data, FAKE, FAKE, ws_bytes, FAKE, FAKE, None) == q4.ERR_SHAPE
