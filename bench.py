@@ -236,6 +236,49 @@ def probe_kernels(torch, wl: Workload, reps: int = 20):
     return out
 
 
+def probe_chain(torch, wl: Workload, graph, reps: int = 10):
+    """The same decode step as one persistent chain launch (q4_gemv_chain:
+    the 168 layer GEMVs and the head as links, each waiting for the one
+    before) after the PLE gather, timed in a HIP graph and eagerly, beside
+    the eager sequence of the step's 171 launches and the graph of it (the
+    timed step). Eager timings include the host's launch cost."""
+    q4 = wl.q4
+    hn, hk = wl.head_nk
+    links = [q4.chain_link(wl.packed[i], n, k, wl.xs[i], wl.ys[i], q4.LINK_GEMV, wait=True)
+             for i, (_, n, k) in enumerate(wl.mats[:-1])]
+    links.append(q4.chain_link(wl.packed[-1], hn, hk, wl.xs[-1], None, q4.LINK_HEAD, wait=True))
+    ch = q4.q4_chain_build(links, cap=30.0)
+
+    def chain_step():
+        q4.ple_gather(wl.table, wl.scale, wl.ids, 16.0, out=wl.ple_out)
+        q4.q4_gemv_chain(ch, wl.idx, wl.val)
+
+    def timed(fn, r):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(r):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / r
+
+    chain_step()
+    torch.cuda.synchronize()
+    cg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(cg):
+        chain_step()
+    cg.replay()
+    out = {"links": len(links), "launches_per_step": 2,
+           "graph_ms": round(timed(cg.replay, reps), 4),
+           "eager_ms": round(timed(chain_step, reps), 4),
+           "launch_sequence_eager_ms": round(timed(wl.step, reps), 4),
+           "launch_sequence_graph_ms": round(timed(graph.replay, reps), 4),
+           "err_word": ch.err()}
+    del cg
+    return out
+
+
 def probe_verify_m4(torch, wl: Workload, seed: int, reps: int = 10):
     """A 4-token verify pass: the 168 layer GEMVs with m = 4 activation
     vectors each (q4_gemv_multi: every weight read once for the 4 tokens)
@@ -725,7 +768,20 @@ def cpu_baseline(seconds: float):
                    f"[{head_rows}-row slices of 262144x2560 with softcap+argmax]; "
                    f"{done_bytes / 1e9:.3f} GB of q4_0 weights in {dt:.1f} s"),
         "host_cpus": os.cpu_count(),
+        "host_cpu_model": host_cpu_model(),
     }
+
+
+def host_cpu_model() -> str:
+    """The host CPU's model name (as lscpu reports it, read from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_oracle_configs():
@@ -773,17 +829,18 @@ def cpu_oracle_configs():
     return out
 
 
-def load_traffic(kernel: str, launches_per_step: dict):
-    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    summaries, scaled by the copy-kernel calibration; None when absent or
-    when the kernel source changed since the counters were taken."""
+def load_traffic(shape: str):
+    """HBM bytes per launch of one launch shape, from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summaries scaled by the copy-kernel calibration;
+    None when absent or when the kernel source changed since the counters
+    were taken."""
     if not os.path.exists(COUNTERS_FILE):
         return None
     with open(COUNTERS_FILE) as f:
         c = json.load(f)
     if c.get("kernel_source_hash") != kernel_source_hash():
         return None
-    k = c.get("kernels", {}).get(kernel)
+    k = c.get("shapes", {}).get(shape)
     if not k:
         return None
     return k.get("hbm_bytes_per_launch")
@@ -854,74 +911,70 @@ def main():
     if not args.no_probe:
         per_kind = probe_kernels(torch, wl)
         shapes = {name.split(".")[-1] if "." in name else name: (n, k) for name, n, k in wl.mats}
-        groups = {
-            # kernel instantiation -> launch kinds it serves
-            "q4_rows_kernel gemv (K=2560: qkv, gate_up)": ["qkv", "gate_up"],
-            "q4_rows_kernel gemv (K=2048: o)": ["o"],
-            "q4_rows_kernel gemv (K=10240: down)": ["down"],
-            "q4_rows_kernel head + reduce (K=2560)": ["head"],
-            "ple_gather_kernel": ["ple"],
-            "q4_rows_kernel gelu (K=2560: gate_up with fused GELU*up epilogue, not in the step)": ["gate_up_gelu"],
-        }
+        step_kinds = [kk for kk, _ in wl.launches()]
         kernels = {}
-        for gname, kinds in groups.items():
-            tot_ms, tot_bytes, count = 0.0, 0, 0
-            for kind in kinds:
-                if kind not in per_kind:
-                    continue
-                mean = per_kind[kind]
-                per_step = sum(1 for kk, _ in wl.launches() if kk == kind) or (42 if kind == "gate_up_gelu" else 0)
-                if kind == "ple":
-                    b = 4 + 4 + wl.ple_dim * (1 + 4)
-                elif kind == "gate_up_gelu":
-                    n, k = shapes["gate_up"]
-                    b = weight_bytes(n, k) + 2 * k + 2 * (n // 2)
-                else:
-                    n, k = shapes[kind] if kind != "head" else wl.head_nk
-                    # the head writes one (index, value) pair, not n fp32 outputs
-                    b = q4_bytes(n, k) if kind != "head" else weight_bytes(n, k) + 2 * k + 8
-                tot_ms += mean * per_step
-                tot_bytes += b * per_step
-                count += per_step
-            if count:
-                avg_ms = tot_ms / count
-                kernels[gname] = {
-                    "launches_per_step": count,
-                    "avg_launch_us": round(avg_ms * 1e3, 3),
-                    "ms_per_step": round(tot_ms, 4),
-                    "bytes_per_launch": tot_bytes // count,
-                    "achieved_GBs": round(tot_bytes / count / (avg_ms * 1e-3) / 1e9, 1),
-                }
-        gk = "q4_rows_kernel gelu (K=2560: gate_up with fused GELU*up epilogue, not in the step)"
-        if gk in kernels:
-            fused = kernels.pop(gk)
-            fused.pop("ms_per_step", None)
-            fused["frac_of_hbm_peak"] = round(fused["achieved_GBs"] / HBM_PEAK_GBS, 4)
-            result["fused_gate_up_gelu"] = fused
+        for kind, mean_ms in per_kind.items():
+            if kind == "ple":
+                b = 4 + 4 + wl.ple_dim * (1 + 4)
+                desc = f"ple_gather_kernel, 1 id, table [{wl.vocab}, {wl.ple_dim}] int8"
+            elif kind == "gate_up_gelu":
+                n, k = shapes["gate_up"]
+                b = weight_bytes(n, k) + 2 * k + 2 * (n // 2)
+                desc = f"q4_rows_kernel GELU mode [{n}, {k}] (fused gate/up GELU, not in the step)"
+            elif kind == "head":
+                n, k = wl.head_nk
+                # pass 1 (weights, x, partials) + pass 2; the call returns (index, value)
+                b = weight_bytes(n, k) + 2 * k + 8
+                desc = f"q4_rows_kernel head mode [{n}, {k}] + lmhead_reduce_kernel (both passes)"
+            else:
+                n, k = shapes[kind]
+                b = q4_bytes(n, k)
+                desc = f"q4_rows_kernel GEMV [{n}, {k}]"
+            per_step = step_kinds.count(kind)
+            ach = b / (mean_ms * 1e-3) / 1e9
+            kernels[kind] = {
+                "kernel": desc,
+                "launches_per_step": per_step,
+                "avg_launch_us": round(mean_ms * 1e3, 3),
+                "ms_per_step": round(mean_ms * per_step, 4),
+                "bytes_per_launch": b,
+                "achieved_GBs": round(ach, 1),
+                "frac_of_hbm_peak": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": load_traffic(kind),
+            }
+        gelu = kernels.pop("gate_up_gelu", None)
+        if gelu:
+            gelu.pop("ms_per_step", None)
+            result["fused_gate_up_gelu"] = gelu
         result["kernels"] = kernels
-        dominant = max((g for g in kernels if not g.startswith("ple")), key=lambda g: kernels[g]["ms_per_step"])
+        result["kernel_timing"] = ("per launch shape: the step's launches of that shape (42 distinct matrices; "
+                                   "the head over 3 distinct copies), repeated to >= 24, captured in one HIP "
+                                   "graph and replayed between HIP events on the launch stream")
+        dominant = max((kk for kk in kernels if kk != "ple"), key=lambda kk: kernels[kk]["ms_per_step"])
         kd = kernels[dominant]
         result["roofline"] = {
-            "kernel": dominant,
+            "kernel": f"{dominant}: {kd['kernel']}",
             "bound": "hbm",
             "achieved": kd["achieved_GBs"],
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(kd["achieved_GBs"] / HBM_PEAK_GBS, 4),
-            "traffic": load_traffic(dominant, kd),
+            "frac": kd["frac_of_hbm_peak"],
+            "traffic": kd["traffic"],
             "avg_launch_us": kd["avg_launch_us"],
             "bytes_per_launch": kd["bytes_per_launch"],
         }
-        hk = "q4_rows_kernel head + reduce (K=2560)"
-        if hk in kernels:
-            kh = kernels[hk]
-            result["roofline_lmhead"] = {
-                "bound": "hbm", "achieved": kh["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(kh["achieved_GBs"] / HBM_PEAK_GBS, 4), "traffic": load_traffic(hk, kh),
-                "avg_launch_us": kh["avg_launch_us"], "bytes_per_launch": kh["bytes_per_launch"],
-            }
+        result["roofline_by_shape"] = {kk: {"achieved": v["achieved_GBs"], "frac": v["frac_of_hbm_peak"],
+                                            "avg_launch_us": v["avg_launch_us"], "ms_per_step": v["ms_per_step"]}
+                                       for kk, v in kernels.items()}
+        kh = kernels["head"]
+        result["roofline_lmhead"] = {
+            "bound": "hbm", "achieved": kh["achieved_GBs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": kh["frac_of_hbm_peak"], "traffic": kh["traffic"],
+            "avg_launch_us": kh["avg_launch_us"], "bytes_per_launch": kh["bytes_per_launch"],
+        }
         result["kernel_time_sum_ms"] = round(sum(v["ms_per_step"] for v in kernels.values()), 4)
         result["launch_gap_ms_per_step"] = round(ms_step - result["kernel_time_sum_ms"], 4)
+        result["decode_step_chain"] = probe_chain(torch, wl, graph)
 
     if not args.no_prefill:
         g2 = torch.Generator(device=dev)

@@ -32,15 +32,19 @@ def test_algorithmic_bytes():
 
 
 def test_traffic_is_gated_on_the_kernel_sources(tmp_path, monkeypatch):
-    name = "q4_rows_kernel gemv (K=2560: qkv, gate_up)"
     good = {"kernel_source_hash": bench.kernel_source_hash(),
-            "kernels": {name: {"hbm_bytes_per_launch": 12345}}}
+            "shapes": {"gate_up": {"hbm_bytes_per_launch": 12345}}}
     path = tmp_path / "counters.json"
     monkeypatch.setattr(bench, "COUNTERS_FILE", str(path))
-    assert bench.load_traffic(name, {}) is None  # no file
+    assert bench.load_traffic("gate_up") is None  # no file
     path.write_text(json.dumps(good))
-    assert bench.load_traffic(name, {}) == 12345
-    assert bench.load_traffic("no such kernel", {}) is None
+    assert bench.load_traffic("gate_up") == 12345
+    assert bench.load_traffic("no such shape") is None
     stale = dict(good, kernel_source_hash="0" * 16)
     path.write_text(json.dumps(stale))
-    assert bench.load_traffic(name, {}) is None
+    assert bench.load_traffic("gate_up") is None
+
+
+def test_host_cpu_model_is_named():
+    m = bench.host_cpu_model()
+    assert isinstance(m, str) and m
