@@ -230,21 +230,21 @@ size_t q4_gemm_workspace_bytes(int64_t n, int64_t k);
 /* q4_gemm_s64: chunked-prefill product Y[s, r] = sum_k X[s, k] * w[r, k] for
  * s < n_tok <= 64 (model card, Provenance table: the prefill entry point has a
  * static query width of 64; the weights are read once per 64 tokens). MFMA
- * kernel: each fp16 block scale d is split exactly into d_hi (top 7
- * significant bits) and d_lo = d - d_hi, so c * d_hi and c * d_lo are exact
- * fp16 values; activations enter as fp16 scaled by a per-token power of two;
- * two MFMAs per product accumulate in fp32. Within the q4_gemv bar for every
- * finite x: when a token's nonzero values span more than 31 binades the call
- * reads X as stored instead (exact path, slower). Deterministic (fixed
- * summation order). Launches on `stream`: an activation conversion, the MFMA kernel
- * and, when K is split over several workgroups, an in-order slice sum.
+ * kernel: per 32-wide block, v_mfma_f32_16x16x32_bf16 multiplies the
+ * activations as stored (bf16) by 16 * c (exact in bf16), so every product is
+ * exact and each block's sum is formed in fp32; the block sum is then scaled
+ * by its fp16 d in fp32 and accumulated, and 1/16 is applied at the end.
+ * No activation conversion and no range limit on X short of fp32 overflow:
+ * within the q4_gemv bar whenever every |x| < 2^100 (the largest product and
+ * block sum then stay finite). Deterministic (fixed summation order). Launches on
+ * `stream`: the MFMA kernel and, when K is split over several workgroups,
+ * an in-order slice sum.
  *   packed  from q4_pack with the same (n, k); 16-byte aligned.
  *   x       bf16 [n_tok, k] row-major, 16-byte aligned.
  *   y       fp32 [n_tok, n] row-major, 4-byte aligned.
  *   ws      device workspace of ws_bytes >= q4_gemm_workspace_bytes(n, k),
- *           256-byte aligned, caller-owned (converted activations and split-K
- *           partial sums; no initial contents needed). Calls that share one
- *           ws must not overlap.
+ *           256-byte aligned, caller-owned (split-K partial sums; no initial
+ *           contents needed). Calls that share one ws must not overlap.
  * Errors: NULL pointer, n <= 0, k % 32 != 0, k > Q4DEC_MAX_K, n_tok not in
  *         [1, 64], workspace too small, misalignment. */
 int q4_gemm_s64(const void* packed, int64_t n, int64_t k, const uint16_t* x,
@@ -414,9 +414,9 @@ size_t lmhead_s64_workspace_bytes(int64_t vocab, int64_t k);
  * outputs logits for every position; E2B card: the head is fused with its
  * argmax, no logit readback). The logits are those of q4_gemm_s64 (same
  * kernel, same numerics) and are never written out: each workgroup keeps per
- * token the best (logit, row) of its 128 rows. Launches on `stream`: the
- * activation conversion, the MFMA kernel, then one workgroup per token
- * reduces the partials and caps the winner.
+ * token the best (logit, row) of its rows. Launches on `stream`: the MFMA
+ * kernel, then one workgroup per token reduces the partials and caps the
+ * winner.
  *   packed   from q4_pack with (n = vocab, k); 16-byte aligned.
  *   x        bf16 [n_tok, k] row-major, 16-byte aligned.
  *   cap      30.0 for Gemma 4; cap <= 0 returns the raw maximum logits.

@@ -3,29 +3,36 @@
 // point has a static query width of 64 and reads the weights once per 64
 // tokens).
 //
-// Numerics. A single fp16 or bf16 copy of c * d would round the 15-bit
-// product, so each fp16 block scale d is split into d_hi (its top 7
-// significant bits) and d_lo = d - d_hi (at most 4 bits). Both c * d_hi and
-// c * d_lo are exact in fp16, and the two v_mfma_f32_16x16x32_f16 products
-// accumulate straight into fp32, so the sum is exact up to fp32 accumulation
-// and no per-block fold runs on the VALU. Activations are converted once per
-// call into fp16 scaled by a per-token power of two (the token's largest
-// magnitude lands in [2^14, 2^15)) by a small prep kernel, so the conversion
-// is not repeated by every workgroup; a row whose largest scale would let
-// c * d_hi overflow fp16 is scaled down by a power of two. Both factors are
-// undone on the output.
+// Numerics. Codes and activations meet in v_mfma_f32_16x16x32_bf16, one MFMA
+// per 32-wide block and 16x16 (token, row) tile: the B operand holds 16 * c
+// for the block's codes (exact in bf16), the A operand the activations as
+// stored (bf16), so every product is exact and the matrix core sums one
+// block in fp32. Each block's tile is then folded into fp32 accumulators
+// with the row's scale d, one FMA per output and block, and the factor 1/16
+// is applied once at the end (exact). There is no activation conversion and
+// no range limit on X beyond fp32's own.
 //
-// Work split. A workgroup (4 waves) owns 128 output rows (32 per wave, two
-// MFMA column tiles) for all 64 token slots and one K slice. Activations move
-// through LDS in chunks of 8 blocks shared by the 4 waves; the weights and
-// activations of the next two chunks are in flight in registers while the
-// current chunk runs on the matrix cores. Small-N matrices split K over
-// several workgroups; their partial sums go to the workspace and a second
-// kernel adds them in a fixed order, so results are deterministic.
+// Codes. q4_pack's dword q of a block holds the codes of k = 8q .. 8q+7,
+// which is one lane's B operand (lane group q supplies k = 8q .. 8q+7 of the
+// MFMA's 32). XOR with 0x88888888 turns the nibbles into 4-bit two's
+// complement codes; moved to the top half of each byte they read as signed
+// bytes 16 * c, which convert to fp32 one byte at a time and to bf16 in
+// pairs.
+//
+// Work split. When k is a multiple of 256 (every model shape) the chunked
+// kernel runs: the 4 waves of a workgroup own consecutive groups of rows and
+// share each chunk of 8 blocks of activations through LDS, whole 16-byte
+// blocks of codes are loaded two chunks ahead and transposed across lane
+// groups for the MFMAs (see below). Otherwise a workgroup owns one row tile
+// and its 4 waves take quarters of its K range, adding their partial tiles
+// in LDS in a fixed order. Matrices with too few row tiles to occupy the
+// chip also split K across workgroups: their partial tiles go to the
+// workspace and a second kernel adds them in slice order, so results are
+// deterministic.
 //
 // The same kernel, with an argmax epilogue instead of the output store, is
 // the LM head over a chunk of up to 64 tokens: each workgroup keeps, per
-// token, the best (logit, row) of its 128 rows, and a second launch reduces
+// token, the best (logit, row) of its rows, and a second launch reduces
 // those per token and caps the winner, so no logits are written.
 #include <limits.h>
 #include <math.h>
@@ -36,387 +43,443 @@
 
 namespace q4dec {
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kTok = 64;     // token slots
-constexpr int kSub = 2;      // 16-row MFMA column tiles per wave
-constexpr int kTileN = 128;  // weight rows per workgroup (4 waves x kSub x 16)
-constexpr int kChunk = 8;    // 32-wide blocks per LDS chunk
+constexpr int kTok = 64;   // token slots
+constexpr int kChunk = 8;  // blocks per activation chunk of the chunked kernel
+constexpr int kGWaves = 4;
+constexpr int kGThreads = 64 * kGWaves;
 
 struct GemmPlan {
-  int slices;  // K slices
-  int bps;     // blocks per slice
-  size_t xh_off, xf_off, part_off, total;  // workspace: fp16 activations, token factors, partials
+  bool chunked;  // k % 256 == 0: the chunked kernel (rows per workgroup = 64 * sub)
+  int sub;       // 16-row MFMA tiles per wave
+  int tiles;     // row tiles
+  int slices;    // K slices across workgroups
+  int bps;       // blocks per slice
+  size_t total;  // workspace bytes (partials of split matrices)
 };
 
-// what the MFMA kernel does with its output tile
+// what the kernel does with its output tile
 enum GemmMode : int {
   kGemmOut = 0,     // Y[s, r] (fp32)
   kGemmSlices = 1,  // the K slice's partial Y into the workspace
   kGemmHead = 2,    // per token, the tile's best (logit, row) into the workspace
 };
 
+// Row tile width and K split. The estimated time of a launch is the number
+// of workgroup rounds (two workgroups per CU at once) times the work of one
+// wave, plus the cost of writing and re-reading split partials (64 x n fp32
+// per slice) and of the reduce launch. Ties go to the wider tile, which reads
+// the activations fewer times.
 static GemmPlan gemm_plan(int64_t n, int64_t k, bool split = true) {
-  GemmPlan p{};
-  const int B = int(k / 32);
-  const int64_t tiles = (n + kTileN - 1) / kTileN;
-  // About one workgroup per CU: split K when the row tiles alone leave CUs
-  // idle, in slices of whole chunks (a partial last chunk runs its MFMAs on
-  // zeroed scales). Matrices with >= 128 tiles are not split, so they need
-  // no second launch.
-  const int64_t s_target = split ? std::max<int64_t>(1, 256 / tiles) : 1;
-  const int per = int((B + s_target - 1) / s_target);
-  p.bps = ((per + kChunk - 1) / kChunk) * kChunk;
-  p.slices = (B + p.bps - 1) / p.bps;
-  p.xh_off = 0;
-  p.xf_off = align256(size_t(kTok) * size_t(k) * 2);
-  p.part_off = p.xf_off + 256;
-  p.total = p.part_off + (p.slices > 1 ? align256(size_t(p.slices) * kTok * size_t(n) * 4) : 0);
-  return p;
-}
-
-// One workgroup per token slot: find the token's largest exponent, convert
-// its row to scaled fp16, store 2^E. Slots >= n_tok are zero-filled. Rows are
-// read and written 8 values (16 bytes) at a time (x is 16-byte aligned and
-// k % 32 == 0); a thread keeps its at most kPrepVec vectors in registers
-// between the exponent scan and the conversion, so the row is read once.
-constexpr int kPrepVec = Q4DEC_MAX_K / 8 / 256;
-__global__ __launch_bounds__(256) void gemm_x_prep_kernel(const uint16_t* __restrict__ x, int k, int n_tok,
-                                                          _Float16* __restrict__ xh, float* __restrict__ xf) {
-  const int s = blockIdx.x;
-  uint4* dst = reinterpret_cast<uint4*>(xh + size_t(s) * size_t(k));
-  const int k8 = k >> 3;
-  if (s >= n_tok) {
-    for (int i = threadIdx.x; i < k8; i += 256) dst[i] = make_uint4(0u, 0u, 0u, 0u);
-    if (threadIdx.x == 0) xf[s] = 0.0f;
-    return;
-  }
-  const uint4* s4 = reinterpret_cast<const uint4*>(x + size_t(s) * size_t(k));
-  uint4 v[kPrepVec];
-#pragma unroll
-  for (int r = 0; r < kPrepVec; ++r) {
-    const int i = threadIdx.x + 256 * r;
-    v[r] = i < k8 ? s4[i] : make_uint4(0u, 0u, 0u, 0u);
-  }
-  uint32_t emax = 1, emin = 255;
-#pragma unroll
-  for (int r = 0; r < kPrepVec; ++r) {
-    const uint32_t w[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      emax = max(emax, max((w[j] >> 7) & 0xFFu, (w[j] >> 23) & 0xFFu));
-      emin = min(emin, min(bf16_exp_nz(w[j] & 0xFFFFu), bf16_exp_nz(w[j] >> 16)));
+  const int64_t B = k / 32;
+  const int64_t cus = std::max(1, device_cu_count());
+  const bool chunked = B % kChunk == 0;
+  GemmPlan best{};
+  best.chunked = chunked;
+  double best_cost = 0.0;
+  for (int sub : {4, 2, 1}) {
+    if (chunked && sub == 4) continue;
+    // chunked: 4 waves side by side over rows, each over the whole slice;
+    // otherwise one row tile per workgroup, its 4 waves over K quarters
+    const int64_t rows = chunked ? 64 * sub : 16 * sub;
+    const int64_t tiles = (n + rows - 1) / rows;
+    const int64_t unit = chunked ? kChunk : 1;
+    const int64_t smax = split ? std::max<int64_t>(1, std::min<int64_t>(16, B / (chunked ? 2 * kChunk : 8))) : 1;
+    for (int64_t s = 1; s <= smax; ++s) {
+      const int64_t bps = ((B + s - 1) / s + unit - 1) / unit * unit;
+      const int64_t slices = (B + bps - 1) / bps;
+      if (slices != s) continue;
+      const int64_t wgs = tiles * slices;
+      const int64_t rounds = (wgs + 2 * cus - 1) / (2 * cus);
+      const double per_wave = double(sub) * double(chunked ? bps : (bps + kGWaves - 1) / kGWaves);
+      // a u-block (16 rows x one block) costs about 300 cycles of one SIMD;
+      // partial traffic at about 4 TB/s, the reduce launch about 4 us
+      const double t_run = double(rounds) * 2.0 * per_wave * 300.0 / 2.4e3;  // us
+      const double t_part = slices > 1 ? double(slices) * 64.0 * double(n) * 8.0 / 4e6 + 4.0 : 0.0;
+      const double cost = t_run + t_part;
+      if (best.sub == 0 || cost < best_cost * 0.97) {
+        best_cost = cost;
+        best.sub = sub;
+        best.tiles = int(tiles);
+        best.slices = int(slices);
+        best.bps = int(bps);
+      }
     }
   }
-  for (int off = 32; off >= 1; off >>= 1) {
-    emax = max(emax, uint32_t(__shfl_xor(int(emax), off)));
-    emin = min(emin, uint32_t(__shfl_xor(int(emin), off)));
-  }
-  __shared__ uint32_t wm[4], wn[4];
-  if ((threadIdx.x & 63) == 0) {
-    wm[threadIdx.x >> 6] = emax;
-    wn[threadIdx.x >> 6] = emin;
-  }
-  __syncthreads();
-  emax = max(max(wm[0], wm[1]), max(wm[2], wm[3]));
-  emin = min(min(wn[0], wn[1]), min(wn[2], wn[3]));
-  const int e = int(emax) - 127 - 14;
-#pragma unroll
-  for (int r = 0; r < kPrepVec; ++r) {
-    const int i = threadIdx.x + 256 * r;
-    if (i >= k8) break;
-    const uint32_t w[4] = {v[r].x, v[r].y, v[r].z, v[r].w};
-    uint32_t o[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const half2_t h = {(_Float16)ldexpf(bf16_to_f32(w[j] & 0xFFFFu), -e),
-                         (_Float16)ldexpf(bf16_to_f32(w[j] >> 16), -e)};
-      o[j] = __builtin_bit_cast(uint32_t, h);
-    }
-    dst[i] = make_uint4(o[0], o[1], o[2], o[3]);
-  }
-  // a token whose nonzero values span more binades than its scaled fp16
-  // copy keeps is marked by a negative factor: the GEMM then reads X as
-  // stored (exact path)
-  if (threadIdx.x == 0) xf[s] = int(emax) - int(emin) > kMaxSpan ? -1.0f : ldexpf(1.0f, e);
+  best.total = best.slices > 1 ? align256(size_t(best.slices) * kTok * size_t(n) * 4) : 256;
+  return best;
 }
 
-__device__ __forceinline__ half8_t codes_f16x8(uint32_t w, uint32_t m_lo, uint32_t m_hi, uint32_t magic) {
-  const CodePairs cp = unpack_dword(w, m_lo, m_hi, magic);
-  half8_t r;
-  r[0] = cp.p[0][0]; r[1] = cp.p[0][1]; r[2] = cp.p[1][0]; r[3] = cp.p[1][1];
-  r[4] = cp.p[2][0]; r[5] = cp.p[2][1]; r[6] = cp.p[3][0]; r[7] = cp.p[3][1];
+// 16 * c for the 8 codes of one packed dword, in k order, as bf16.
+__device__ __forceinline__ bf16x8_t codes16_bf16(uint32_t w) {
+  const uint32_t t = w ^ 0x88888888u;  // two's complement 4-bit codes
+  const uint32_t lo = (t << 4) & 0xF0F0F0F0u, hi = t & 0xF0F0F0F0u;
+  // byte j of the dword: low nibble k = 8q + {0, 4, 1, 5}[j], high nibble
+  // k = 8q + {2, 6, 3, 7}[j]; as signed bytes in the top half, 16 * c
+  bf16x8_t r;
+  r[0] = (__bf16)(float)(int8_t)(lo);
+  r[1] = (__bf16)(float)(int8_t)(lo >> 16);
+  r[2] = (__bf16)(float)(int8_t)(hi);
+  r[3] = (__bf16)(float)(int8_t)(hi >> 16);
+  r[4] = (__bf16)(float)(int8_t)(lo >> 8);
+  r[5] = (__bf16)(float)(int8_t)(lo >> 24);
+  r[6] = (__bf16)(float)(int8_t)(hi >> 8);
+  r[7] = (__bf16)(float)(int8_t)(hi >> 24);
   return r;
 }
 
-// Registers of one chunk (kChunk = 8 blocks = 2 groups of 4). Lane (col, q)
-// holds block 4g + q of its rows: the k-slots of lane group q inside one MFMA
-// then come from block 4g + q, and the A operand follows the same mapping.
-// Mixing blocks inside one MFMA is exact because the scale is already inside
-// the fp16 B operand (c * d_hi, c * d_lo).
-struct ChunkRegs {
-  uint4 w[kSub][2];      // full 16-byte block (32 codes) per column tile and group
-  uint32_t sd[kSub][2];  // its fp16 scale bits
-  uint4 xr[(kChunk * kTok * 4) / 256];  // scaled fp16 activations
+// One block's registers for one lane: the activations of its 4 token tiles
+// (A operands) and, per row tile, the code dword and the fp16 scale.
+template <int SUB>
+struct BlockRegs {
+  uint4 a[4];
+  uint32_t w[SUB];
+  uint32_t s[SUB];
 };
 
-// LDS slot of activation quarter qq of a token: swizzled so the 16 lanes of a
-// ds_read_b128 (16 tokens, same quarter) hit 16 distinct bank groups.
-__device__ __forceinline__ int xslot(int tok, int qq) { return qq ^ ((tok >> 2) & 3); }
-
-// Thread tid stages token tid / 4, quarter tid % 4 of each block of a chunk.
-__device__ __forceinline__ void load_chunk(ChunkRegs& R, const uint4* const (&wrow)[kSub],
-                                           const uint16_t* const (&srow)[kSub], const _Float16* __restrict__ xh,
-                                           int k, int q, int b0, int b_end) {
-  // Every load is issued unconditionally and nothing is computed from the
-  // loaded values here, so the number of loads in flight is the same on
-  // every path and the wait before a chunk's first use only covers that
-  // chunk, not the chunk loaded after it. A block past the slice's end reads
-  // a valid block instead; its weight scale is zeroed when the chunk is used,
-  // which zeroes its products with the (finite) activations as well.
-#pragma unroll
-  for (int u = 0; u < kSub; ++u)
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const int bb = b0 + 4 * g + q;
-      const int bc = bb < b_end ? bb : b0;  // ragged tail: any valid block, zeroed by its scale
-      R.w[u][g] = wrow[u][bc];
-      R.sd[u][g] = srow[u][bc];  // zeroed at use when bb >= b_end
-    }
-  const int sx = threadIdx.x >> 2, qq = threadIdx.x & 3;
-#pragma unroll
-  for (int c = 0; c < kChunk; ++c) {
-    const int bb = b0 + c;
-    const int bc = bb < b_end ? bb : b0;
-    R.xr[c] = *reinterpret_cast<const uint4*>(xh + size_t(sx) * size_t(k) + size_t(bc) * 32 + qq * 8);
-  }
-}
-
-// Writes the staged chunk to LDS (thread tid: token tid / 4, quarter tid % 4).
-__device__ __forceinline__ void store_chunk(const ChunkRegs& R, uint4 (*xs)[kTok][4]) {
-  const int sx = threadIdx.x >> 2, qq = threadIdx.x & 3;
-#pragma unroll
-  for (int c = 0; c < kChunk; ++c) xs[c][sx][xslot(sx, qq)] = R.xr[c];
-}
-
-// exact split of one fp16 scale (already shifted into range): hi keeps the
-// top 7 significant bits, lo = d - hi
-__device__ __forceinline__ void split_scale(uint32_t dbits, half2_t& hi, half2_t& lo) {
-  const _Float16 d = __builtin_bit_cast(_Float16, uint16_t(dbits));
-  const _Float16 h = __builtin_bit_cast(_Float16, uint16_t(dbits & 0xFFF0u));
-  const _Float16 l = d - h;
-  hi = half2_t{h, h};
-  lo = half2_t{l, l};
-}
-
-// Activation tiles of step (g, j): the 4 token tiles' A operands.
-__device__ __forceinline__ void load_a(half8_t (&a)[4], const uint4 (*xs)[kTok][4], int g, int j, int q, int col) {
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int tok = 16 * m + col;
-    a[m] = __builtin_bit_cast(half8_t, xs[4 * g + q][tok][xslot(tok, j)]);
-  }
-}
-
-// One chunk on the matrix cores: 2 groups x 4 k-slices x kSub column tiles x
-// 4 token tiles x (hi, lo), accumulated into t. The A operands of the next
-// step are read from LDS before this step's products are issued, so the LDS
-// latency runs under the matrix-core work.
-__device__ __forceinline__ void mma_chunk(float4_t (&t)[kSub][4], const uint4 (&w)[kSub][2],
-                                          const uint32_t (&sd)[kSub][2], const int (&shift)[kSub],
-                                          const uint4 (*xs)[kTok][4], int q, int col, int ngroups,
-                                          uint32_t m_lo, uint32_t m_hi, uint32_t magic) {
-  half8_t a0[4], a1[4];
-  load_a(a0, xs, 0, 0, q, col);
-  half2_t dh[kSub], dl[kSub];
-#pragma unroll
-  for (int st = 0; st < 8; ++st) {
-    const int g = st >> 2, j = st & 3;
-    if (g >= ngroups) break;
-    half8_t(&cur)[4] = (st & 1) ? a1 : a0;
-    half8_t(&nxt)[4] = (st & 1) ? a0 : a1;
-    // the tiles past the last used group are valid LDS, read and ignored
-    if (st + 1 < 8) load_a(nxt, xs, (st + 1) >> 2, (st + 1) & 3, q, col);
-    if (j == 0) {
-#pragma unroll
-      for (int u = 0; u < kSub; ++u) {
-        uint32_t dbits = sd[u][g];
-        if (shift[u] > 0) {  // rare: rows with scales >= 2^11
-          const float df = ldexpf(float(__builtin_bit_cast(_Float16, uint16_t(dbits))), -shift[u]);
-          dbits = __builtin_bit_cast(uint16_t, (_Float16)df);
-        }
-        split_scale(dbits, dh[u], dl[u]);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kSub; ++u) {
-      const uint32_t wd = j == 0 ? w[u][g].x : j == 1 ? w[u][g].y : j == 2 ? w[u][g].z : w[u][g].w;
-      const CodePairs cp = unpack_dword(wd, m_lo, m_hi, magic);
-      half8_t bh, bl;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const half2_t ph = cp.p[jj] * dh[u];
-        const half2_t pl = cp.p[jj] * dl[u];
-        bh[2 * jj] = ph[0]; bh[2 * jj + 1] = ph[1];
-        bl[2 * jj] = pl[0]; bl[2 * jj + 1] = pl[1];
-      }
-#pragma unroll
-      for (int m = 0; m < 4; ++m) t[u][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[m], bh, t[u][m], 0, 0, 0);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) t[u][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(cur[m], bl, t[u][m], 0, 0, 0);
-    }
-  }
-}
-
-template <int MODE>
-__global__ __launch_bounds__(256) void q4_gemm_kernel(const uint8_t* __restrict__ nib, const uint16_t* __restrict__ scl,
-                                                      const uint8_t* __restrict__ rexp, const _Float16* __restrict__ xh,
-                                                      const float* __restrict__ xf, const uint16_t* __restrict__ x,
-                                                      int n, int k, int n_tok, int bps, void* __restrict__ out) {
-  __shared__ uint4 xs[kChunk][kTok][4];  // [block][token][k quarter, swizzled], 32 KB
+template <int SUB, int MODE>
+__global__ __launch_bounds__(kGThreads) void q4_gemm_kernel(const uint8_t* __restrict__ nib,
+                                                            const uint16_t* __restrict__ scl,
+                                                            const uint16_t* __restrict__ x, int n, int k, int n_tok,
+                                                            int bps, void* __restrict__ out) {
+  constexpr int kRows = 16 * SUB;
+  __shared__ float4_t red[2][SUB * 4][64];  // two partial tiles (SUB = 4: 32 KB)
   const int B = k >> 5;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int q = lane >> 4;    // lane group: block 4g + q of a chunk
-  const int col = lane & 15;  // row within a 16-row MFMA column tile
-  const int b_begin = blockIdx.y * bps;
-  const int b_end = min(B, b_begin + bps);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q = lane >> 4;    // lane group: k = 8q .. 8q+7 of a block; tokens 4q .. 4q+3 of a C tile
+  const int col = lane & 15;  // row of a 16-row tile (B, C) and token of a 16-token tile (A)
 
-  const uint4* wrow[kSub];
-  const uint16_t* srow[kSub];
-  int rows[kSub];
-  int shift[kSub];  // power-of-two range shift of the row's scales
+  // this wave's K range: a quarter of the workgroup's slice (may be empty)
+  const int s0 = blockIdx.y * bps;
+  const int s1 = min(B, s0 + bps);
+  const int per = (s1 - s0 + kGWaves - 1) / kGWaves;
+  const int wb0 = min(s1, s0 + wave * per);
+  const int wb1 = min(s1, wb0 + per);
+
+  // Byte offsets from uniform bases (the tile's first row, the call's first
+  // token), so each load is a scalar base plus a 32-bit lane offset.
+  const int r0 = blockIdx.x * kRows;
+  const uint8_t* wt = nib + size_t(r0) * size_t(k >> 1);
+  const uint8_t* st = reinterpret_cast<const uint8_t*>(scl) + size_t(r0) * size_t(B) * 2;
+  const uint8_t* xt = reinterpret_cast<const uint8_t*>(x);
+  uint32_t woff[SUB], soff[SUB], xoff[4];
 #pragma unroll
-  for (int u = 0; u < kSub; ++u) {
-    rows[u] = blockIdx.x * kTileN + (wave * kSub + u) * 16 + col;
-    const int rc = rows[u] < n ? rows[u] : n - 1;
-    wrow[u] = reinterpret_cast<const uint4*>(nib + size_t(rc) * size_t(k >> 1));
-    srow[u] = scl + size_t(rc) * size_t(B);
-    // largest fp16 exponent field of the row's scales (computed by q4_pack);
-    // keep every scale below 2^11 so |c * d_hi| < 2^14 stays finite in fp16
-    shift[u] = max(0, int(rexp[rc]) - 15 - 10);
+  for (int u = 0; u < SUB; ++u) {
+    const int rl = min(r0 + 16 * u + col, n - 1) - r0;  // rows past n repeat the last row; never stored
+    woff[u] = uint32_t(rl) * uint32_t(k >> 1) + 4u * uint32_t(q);
+    soff[u] = uint32_t(rl) * uint32_t(B) * 2u;
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int tok = min(16 * m + col, n_tok - 1);  // slots past n_tok repeat a real token; never stored
+    xoff[m] = (uint32_t(tok) * uint32_t(k) + 8u * uint32_t(q)) * 2u;
   }
 
-  uint32_t m_lo, m_hi, magic;
-  asm volatile("v_mov_b32 %0, 0x000F000F" : "=v"(m_lo));
-  asm volatile("v_mov_b32 %0, 0x00F000F0" : "=v"(m_hi));
-  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+  // a block past the wave's range reloads its last block (cache hits) and is
+  // never computed
+  const int blast = wb1 > wb0 ? wb1 - 1 : min(wb0, B - 1);
+  auto load = [&](BlockRegs<SUB>& R, int b) {
+    const uint32_t bc = uint32_t(min(b, blast));
+#pragma unroll
+    for (int m = 0; m < 4; ++m) R.a[m] = *reinterpret_cast<const uint4*>(xt + size_t(bc * 64u) + xoff[m]);
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      R.w[u] = *reinterpret_cast<const uint32_t*>(wt + size_t(bc * 16u) + woff[u]);
+      R.s[u] = *reinterpret_cast<const uint16_t*>(st + size_t(bc * 2u) + soff[u]);
+    }
+  };
 
-  // the lane's 16 token factors, loaded now so they arrive under the main
-  // loop instead of one dependent load per output at the end
-  float tf[16];
+  float4_t acc[SUB][4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) tf[4 * m + i] = xf[16 * m + 4 * q + i];
-
-  float4_t acc[kSub][4];
-#pragma unroll
-  for (int u = 0; u < kSub; ++u)
+  for (int u = 0; u < SUB; ++u)
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[u][m] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // A wide token (negative factor from the prep kernel) puts the whole
-  // workgroup on the exact path.
-  __shared__ int wide_w[4];
-  {
-    const bool wide_t = int(threadIdx.x) < n_tok && xf[threadIdx.x & (kTok - 1)] < 0.0f;
-    const bool wide_wave = __ballot(wide_t) != 0;
-    if (lane == 0) wide_w[wave] = wide_wave;
+  auto compute = [&](const BlockRegs<SUB>& R) {
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+      const float d = float(__builtin_bit_cast(_Float16, uint16_t(R.s[u])));
+      const bf16x8_t bc = codes16_bf16(R.w[u]);
+      float4_t c[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        c[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, R.a[m]), bc,
+                                                       float4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[u][m][i] = fmaf(d, c[m][i], acc[u][m][i]);
+    }
+  };
+
+  // two blocks in flight: ra holds blocks wb0, wb0 + 2, ..., rb the odd ones;
+  // each set is refilled two blocks ahead right after its use. The loop body
+  // has no condition, so every refill feeds an unconditional use and stays
+  // where it is issued; an odd last block runs after the loop.
+  BlockRegs<SUB> ra, rb;
+  load(ra, wb0);
+  load(rb, wb0 + 1);
+  int b = wb0;
+  // the scheduling fences keep each refill where it is written: left to
+  // itself the scheduler sinks loads next to their use
+  for (; b + 1 < wb1; b += 2) {
+    compute(ra);
+    __builtin_amdgcn_sched_barrier(0);
+    load(ra, b + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(rb);
+    __builtin_amdgcn_sched_barrier(0);
+    load(rb, b + 3);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (b < wb1) compute(ra);
+
+  // partial tiles of the 4 waves, added as (w0 + w2) + (w1 + w3)
+  if (wave < 2) {
+#pragma unroll
+    for (int u = 0; u < SUB; ++u)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) red[wave][4 * u + m][lane] = acc[u][m];
   }
   __syncthreads();
-  // uniform by construction; readfirstlane lets the compiler branch on it
-  // as a scalar, so the two paths do not hold registers at the same time
-  const bool exact = __builtin_amdgcn_readfirstlane(wide_w[0] | wide_w[1] | wide_w[2] | wide_w[3]) != 0;
-  if (exact) {
-    // Each lane's outputs (rows rows[u], tokens 16m + 4q + i) summed over the
-    // slice's blocks in fp32 with X as stored: every code-activation product
-    // is exact, each block sum is scaled by its fp16 d. One block at a time.
+  if (wave >= 2) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int u = 0; u < SUB; ++u)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tf[4 * m + i] = 1.0f;
+      for (int m = 0; m < 4; ++m) red[wave - 2][4 * u + m][lane] += acc[u][m];
+  }
+  __syncthreads();
+  // wave w finishes token tile m = w for every row tile: lane holds tokens
+  // 16w + 4q + i of rows r0 + 16u + col
+  float4_t v[SUB];
 #pragma unroll
-    for (int u = 0; u < kSub; ++u) shift[u] = 0;
-#pragma unroll 1
-    for (int b = b_begin; b < b_end; ++b) {
+  for (int u = 0; u < SUB; ++u) v[u] = (red[0][4 * u + wave][lane] + red[1][4 * u + wave][lane]) * 0.0625f;
+
+  if constexpr (MODE == kGemmHead) {
+    uint2* part = static_cast<uint2*>(out);
 #pragma unroll
-      for (int u = 0; u < kSub; ++u) {
-        const uint4 wq = wrow[u][b];
-        const uint32_t wd[4] = {wq.x, wq.y, wq.z, wq.w};
-        const float d = float(__builtin_bit_cast(_Float16, srow[u][b]));
-#pragma unroll 1
-        for (int mi = 0; mi < 16; ++mi) {
-          const int tok = 16 * (mi >> 2) + 4 * q + (mi & 3);
-          if (tok >= n_tok) continue;
-          const uint4* xb = reinterpret_cast<const uint4*>(x + size_t(tok) * size_t(k) + size_t(b) * 32);
-          float sum = 0.0f;
+    for (int i = 0; i < 4; ++i) {
+      float bv = -INFINITY;
+      int br = INT_MAX;
 #pragma unroll
-          for (int dd = 0; dd < 4; ++dd) {
-            const uint4 xv = xb[dd];
-            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-            const CodePairs cp = unpack_dword(wd[dd], m_lo, m_hi, magic);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              sum = fmaf(float(cp.p[jj][0]), bf16_to_f32(xw[jj] & 0xFFFFu), sum);
-              sum = fmaf(float(cp.p[jj][1]), bf16_to_f32(xw[jj] >> 16), sum);
-            }
-          }
-#pragma unroll
-          for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (4 * m + i == mi) acc[u][m][i] = fmaf(d, sum, acc[u][m][i]);
+      for (int u = 0; u < SUB; ++u) {
+        const int row = r0 + 16 * u + col;
+        const float val = v[u][i];
+        if (row < n && !(val != val) && better(val, row, bv, br)) {  // NaN never wins
+          bv = val;
+          br = row;
         }
       }
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) {  // the 16 lanes of the lane group
+        const float ov = __shfl_xor(bv, off);
+        const int orow = __shfl_xor(br, off);
+        if (better(ov, orow, bv, br)) {
+          bv = ov;
+          br = orow;
+        }
+      }
+      const int s = 16 * wave + 4 * q + i;
+      if (col == 0 && s < n_tok)
+        part[size_t(blockIdx.x) * kTok + s] = make_uint2(__builtin_bit_cast(uint32_t, bv), uint32_t(br));
     }
   } else {
-  // two chunks in flight: A holds chunks 0, 2, 4, ..., B holds 1, 3, 5, ...
-  // (every slice holds at least one block; a chunk past the slice's end is
-  // replaced by its first chunk, which is loaded but never used)
-  ChunkRegs ra, rb;
-  load_chunk(ra, wrow, srow, xh, k, q, b_begin, b_end);
-  load_chunk(rb, wrow, srow, xh, k, q, b_begin + kChunk < b_end ? b_begin + kChunk : b_begin, b_end);
-
-  auto run = [&](ChunkRegs& R, int b0) {
-    __syncthreads();  // previous chunk fully consumed
-    store_chunk(R, xs);
-    uint4 w[kSub][2];
-    uint32_t sd[kSub][2];
+    float* y = static_cast<float*>(out);
+    if (MODE == kGemmSlices) y += size_t(blockIdx.y) * kTok * size_t(n);
 #pragma unroll
-    for (int u = 0; u < kSub; ++u)
+    for (int u = 0; u < SUB; ++u) {
+      const int row = r0 + 16 * u + col;
+      if (row >= n) continue;
 #pragma unroll
-      for (int g = 0; g < 2; ++g) {
-        w[u][g] = R.w[u][g];
-        sd[u][g] = b0 + 4 * g + q < b_end ? R.sd[u][g] : 0u;
-        // opaque copy: w gets registers of its own, so the refill below
-        // lands in R's registers in place (otherwise the compiler reuses R's
-        // registers for w and moves the refilled values back at the end of
-        // the loop, waiting on their loads)
-        asm volatile("" : "+v"(w[u][g].x), "+v"(w[u][g].y), "+v"(w[u][g].z), "+v"(w[u][g].w));
+      for (int i = 0; i < 4; ++i) {
+        const int s = 16 * wave + 4 * q + i;
+        if (s < n_tok) y[size_t(s) * size_t(n) + row] = v[u][i];
       }
-    __syncthreads();
-    // refill this register set with the chunk after next (or, past the end,
-    // with the current chunk again: cache hits, never used)
-    load_chunk(R, wrow, srow, xh, k, q, b0 + 2 * kChunk < b_end ? b0 + 2 * kChunk : b0, b_end);
-    const int ngroups = (min(kChunk, b_end - b0) + 3) / 4;
-    mma_chunk(acc, w, sd, shift, xs, q, col, ngroups, m_lo, m_hi, magic);
-  };
-  // pairs of chunks with no conditional inside, so both register sets stay
-  // in place across iterations (no copies that would wait on their loads)
-  int b0 = b_begin;
-  for (; b0 + kChunk < b_end; b0 += 2 * kChunk) {
-    run(ra, b0);
-    run(rb, b0 + kChunk);
+    }
   }
-  if (b0 < b_end) run(ra, b0);
-  }
+}
 
-  // lane holds tokens s = 16m + 4q + i of output rows rows[u]
+
+// --------------------------------------------------------- chunked kernel
+// For k a multiple of 256 (8 blocks): the 4 waves of a workgroup own
+// consecutive groups of 16 * SUB rows and walk the same K range, so the
+// activations of a chunk of 8 blocks are loaded once per workgroup and
+// shared through LDS. A lane loads whole 16-byte blocks (lane group q: block
+// 4h + q of its row) and the 8 scales of its row for the chunk in one
+// 16-byte load; a 4 x 4 transpose across the lane groups then gives each
+// lane the dword of every block that its MFMA needs. The next chunk's
+// activations and the chunk after that's weights are in flight while a
+// chunk runs (the activations are issued first, so waiting for them does
+// not wait for the weights issued after them).
+// LDS slot of activation quarter qq of token tok, swizzled so that the 16
+// lanes of one ds_read_b128 (16 tokens, one quarter) hit distinct banks.
+__device__ __forceinline__ int xslot(int tok, int qq) { return qq ^ ((tok >> 2) & 3); }
+
+// On entry lane group g holds dword j of block g in r[j]; on exit lane group
+// g holds dword g of block j in r[j], which is block j's B operand.
+__device__ __forceinline__ void transpose_groups(uint32_t (&r)[4]) {
+  const auto a = __builtin_amdgcn_permlane32_swap(r[0], r[2], false, false);  // groups 0,1 <-> 2,3
+  const auto b = __builtin_amdgcn_permlane32_swap(r[1], r[3], false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);  // groups 0 <-> 1, 2 <-> 3
+  const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  r[0] = c[0];
+  r[1] = c[1];
+  r[2] = d[0];
+  r[3] = d[1];
+}
+
+struct ChunkX {
+  u32x4 v[kChunk];  // thread t: token t / 4, quarter t % 4 of each block of a chunk
+};
+
+// A copy of v in a register of its own, made where it is written: the
+// register set it came from is refilled right after, and the refill then
+// lands in that set's registers instead of being moved back at the end of
+// the loop (which would wait for it), and the uses of the copy cannot be
+// hoisted into the previous chunk (which would wait for its loads early).
+__device__ __forceinline__ uint32_t fresh_copy(uint32_t v) {
+  uint32_t o;
+  asm volatile("v_mov_b32 %0, %1" : "=&v"(o) : "v"(v));
+  return o;
+}
+
+template <int SUB>
+struct ChunkW {
+  u32x4 w[SUB][2];  // lane group q: block 4h + q of the lane's row, h = 0, 1
+  u32x4 sc[SUB];    // the row's 8 fp16 scales of the chunk
+};
+
+template <int SUB, int MODE>
+__global__ __launch_bounds__(kGThreads) void q4_gemm_chunk_kernel(const uint8_t* __restrict__ nib,
+                                                                  const uint16_t* __restrict__ scl,
+                                                                  const uint16_t* __restrict__ x, int n, int k,
+                                                                  int n_tok, int bps, void* __restrict__ out) {
+  __shared__ u32x4 xs[kChunk][kTok][4];  // [block][token][quarter, swizzled], 32 KB
+  const int B = k >> 5;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int q = lane >> 4;
+  const int col = lane & 15;
+  const int b_begin = blockIdx.y * bps;
+  const int nch = (min(B, b_begin + bps) - b_begin) / kChunk;  // >= 1: B and bps are multiples of 8
+  const int r0 = (blockIdx.x * 4 + wave) * 16 * SUB;            // the wave's first row
+
+  const uint8_t* wrow[SUB];
+  const uint8_t* srow[SUB];
+#pragma unroll
+  for (int u = 0; u < SUB; ++u) {
+    const int rc = min(r0 + 16 * u + col, n - 1);  // rows past n repeat the last row; never stored
+    wrow[u] = nib + size_t(rc) * size_t(k >> 1) + 16 * q;
+    srow[u] = reinterpret_cast<const uint8_t*>(scl) + size_t(rc) * size_t(B) * 2;
+  }
+  // activation staging: thread t holds token t / 4, quarter t % 4 of each block
+  const int sx = threadIdx.x >> 2, qq = threadIdx.x & 3;
+  const uint8_t* xrow = reinterpret_cast<const uint8_t*>(x) + size_t(min(sx, n_tok - 1)) * size_t(k) * 2 + 16 * qq;
+
+  auto load_w = [&](ChunkW<SUB>& R, int ci) {
+    const size_t b0 = size_t(b_begin + ci * kChunk);
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) R.w[u][h] = *reinterpret_cast<const u32x4*>(wrow[u] + (b0 + 4 * h) * 16);
+      R.sc[u] = *reinterpret_cast<const u32x4*>(srow[u] + b0 * 2);
+    }
+  };
+  auto load_x = [&](ChunkX& X, int ci) {
+    const size_t b0 = size_t(b_begin + ci * kChunk);
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) X.v[c] = *reinterpret_cast<const u32x4*>(xrow + (b0 + c) * 64);
+  };
+
+  float4_t acc[SUB][4];
+#pragma unroll
+  for (int u = 0; u < SUB; ++u)
+#pragma unroll
+    for (int m = 0; m < 4; ++m) acc[u][m] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto load_a = [&](u32x4 (&a)[4], int c) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int tok = 16 * m + col;
+      a[m] = xs[c][tok][xslot(tok, q)];
+    }
+  };
+
+  // One chunk: stage its activations into LDS, take the weights out of the
+  // register set (transposed), refill the set two chunks ahead and the
+  // activation staging one chunk ahead, then run the 8 blocks.
+  auto run = [&](ChunkW<SUB>& R, ChunkX& X, int ci) {
+    __syncthreads();  // every wave is done with the previous chunk
+#pragma unroll
+    for (int c = 0; c < kChunk; ++c) xs[c][sx][xslot(sx, qq)] = X.v[c];
+    uint32_t wt[SUB][2][4];
+    uint32_t sc[SUB][4];
+#pragma unroll
+    for (int u = 0; u < SUB; ++u) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t r[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r[j] = fresh_copy(R.w[u][h][j]);
+        transpose_groups(r);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wt[u][h][j] = r[j];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sc[u][j] = fresh_copy(R.sc[u][j]);
+    }
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(X, ci + 1 < nch ? ci + 1 : ci);  // past the end: this chunk again (cache hits, never used)
+    load_w(R, ci + 2 < nch ? ci + 2 : ci);
+    __builtin_amdgcn_sched_barrier(0);
+    // block c on the matrix cores; the activations of block c + 1 are read
+    // from LDS before block c's products are issued
+    auto block = [&](const u32x4 (&a)[4], int c) {
+#pragma unroll
+      for (int u = 0; u < SUB; ++u) {
+        const bf16x8_t bc = codes16_bf16(wt[u][c >> 2][c & 3]);
+        const uint32_t sw = sc[u][c >> 1];
+        const float d = float(__builtin_bit_cast(_Float16, uint16_t((c & 1) ? sw >> 16 : sw & 0xFFFFu)));
+        float4_t r[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          r[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[m]), bc,
+                                                         float4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[u][m][i] = fmaf(d, r[m][i], acc[u][m][i]);
+      }
+    };
+    u32x4 a0[4], a1[4];
+    load_a(a0, 0);
+#pragma unroll
+    for (int c = 0; c < kChunk; c += 2) {
+      load_a(a1, c + 1);
+      block(a0, c);
+      if (c + 2 < kChunk) load_a(a0, c + 2);
+      block(a1, c + 1);
+    }
+  };
+
+  ChunkW<SUB> ra, rb;
+  ChunkX xr;
+  load_w(ra, 0);
+  load_w(rb, nch > 1 ? 1 : 0);
+  load_x(xr, 0);
+  int ci = 0;
+  for (; ci + 1 < nch; ci += 2) {
+    run(ra, xr, ci);
+    run(rb, xr, ci + 1);
+  }
+  if (ci < nch) run(ra, xr, ci);
+
+  // lane holds tokens 16m + 4q + i of rows r0 + 16u + col
   if constexpr (MODE == kGemmHead) {
-    // per token: the best (logit, row) of the lane's two rows, then of the
-    // 16 lanes of its lane group (the tile's 16 columns), then of the waves
     __shared__ float hv[4][kTok];
     __shared__ int hr[4][kTok];
 #pragma unroll
@@ -426,11 +489,12 @@ __global__ __launch_bounds__(256) void q4_gemm_kernel(const uint8_t* __restrict_
         float bv = -INFINITY;
         int br = INT_MAX;
 #pragma unroll
-        for (int u = 0; u < kSub; ++u) {
-          const float v = acc[u][m][i] * (tf[4 * m + i] * ldexpf(1.0f, shift[u]));
-          if (rows[u] < n && better(v, rows[u], bv, br)) {
-            bv = v;
-            br = rows[u];
+        for (int u = 0; u < SUB; ++u) {
+          const int row = r0 + 16 * u + col;
+          const float val = acc[u][m][i] * 0.0625f;
+          if (row < n && !(val != val) && better(val, row, bv, br)) {  // NaN never wins
+            bv = val;
+            br = row;
           }
         }
 #pragma unroll
@@ -464,24 +528,44 @@ __global__ __launch_bounds__(256) void q4_gemm_kernel(const uint8_t* __restrict_
     }
   } else {
     float* y = static_cast<float*>(out);
+    if (MODE == kGemmSlices) y += size_t(blockIdx.y) * kTok * size_t(n);
 #pragma unroll
-    for (int u = 0; u < kSub; ++u) {
-      if (rows[u] >= n) continue;
-      const float rf = ldexpf(1.0f, shift[u]);
+    for (int u = 0; u < SUB; ++u) {
+      const int row = r0 + 16 * u + col;
+      if (row >= n) continue;
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int s = 16 * m + 4 * q + i;
-          const float v = acc[u][m][i] * (tf[4 * m + i] * rf);
-          if (MODE == kGemmSlices) {
-            y[(size_t(blockIdx.y) * kTok + s) * size_t(n) + rows[u]] = v;
-          } else if (s < n_tok) {
-            y[size_t(s) * size_t(n) + rows[u]] = v;
-          }
+          if (s < n_tok) y[size_t(s) * size_t(n) + row] = acc[u][m][i] * 0.0625f;
         }
-      }
     }
+  }
+}
+
+template <int MODE>
+static void launch_gemm(const GemmPlan& p, hipStream_t st, const uint8_t* nib, const uint16_t* scl,
+                        const uint16_t* x, int n, int k, int n_tok, void* out) {
+  const dim3 grid(unsigned(p.tiles), unsigned(p.slices));
+  const dim3 block(kGThreads);
+  if (p.chunked) {
+    if (p.sub == 2)
+      hipLaunchKernelGGL((q4_gemm_chunk_kernel<2, MODE>), grid, block, 0, st, nib, scl, x, n, k, n_tok, p.bps, out);
+    else
+      hipLaunchKernelGGL((q4_gemm_chunk_kernel<1, MODE>), grid, block, 0, st, nib, scl, x, n, k, n_tok, p.bps, out);
+    return;
+  }
+  switch (p.sub) {
+    case 4:
+      hipLaunchKernelGGL((q4_gemm_kernel<4, MODE>), grid, block, 0, st, nib, scl, x, n, k, n_tok, p.bps, out);
+      break;
+    case 2:
+      hipLaunchKernelGGL((q4_gemm_kernel<2, MODE>), grid, block, 0, st, nib, scl, x, n, k, n_tok, p.bps, out);
+      break;
+    default:
+      hipLaunchKernelGGL((q4_gemm_kernel<1, MODE>), grid, block, 0, st, nib, scl, x, n, k, n_tok, p.bps, out);
+      break;
   }
 }
 
@@ -538,21 +622,13 @@ extern "C" int q4_gemm_s64(const void* packed, int64_t n, int64_t k, const uint1
   if (ws_bytes < p.total)
     return fail(Q4DEC_ERR_WORKSPACE, "q4_gemm_s64: ws_bytes %zu < required %zu", ws_bytes, p.total);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  uint8_t* w8 = static_cast<uint8_t*>(ws);
-  _Float16* xh = reinterpret_cast<_Float16*>(w8 + p.xh_off);
-  float* xf = reinterpret_cast<float*>(w8 + p.xf_off);
-  float* part = reinterpret_cast<float*>(w8 + p.part_off);
   const uint8_t* nib = static_cast<const uint8_t*>(packed);
   const uint16_t* scl = reinterpret_cast<const uint16_t*>(nib + nib_plane_bytes(n, k));
-  const uint8_t* rexp = nib + nib_plane_bytes(n, k) + scale_plane_bytes(n, k);
-  hipLaunchKernelGGL(gemm_x_prep_kernel, dim3(kTok), dim3(256), 0, st, x, int(k), int(n_tok), xh, xf);
-  const dim3 grid(unsigned((n + kTileN - 1) / kTileN), unsigned(p.slices));
   if (p.slices == 1) {
-    hipLaunchKernelGGL(q4_gemm_kernel<kGemmOut>, grid, dim3(256), 0, st, nib, scl, rexp, xh, xf, x, int(n),
-                       int(k), int(n_tok), p.bps, static_cast<void*>(y));
+    launch_gemm<kGemmOut>(p, st, nib, scl, x, int(n), int(k), int(n_tok), y);
   } else {
-    hipLaunchKernelGGL(q4_gemm_kernel<kGemmSlices>, grid, dim3(256), 0, st, nib, scl, rexp, xh, xf, x, int(n),
-                       int(k), int(n_tok), p.bps, static_cast<void*>(part));
+    float* part = static_cast<float*>(ws);
+    launch_gemm<kGemmSlices>(p, st, nib, scl, x, int(n), int(k), int(n_tok), part);
     const size_t total = size_t(n_tok) * size_t(n);
     const unsigned rgrid = unsigned(std::min<size_t>((total + 255) / 256, 4096));
     hipLaunchKernelGGL(gemm_reduce_kernel, dim3(rgrid), dim3(256), 0, st, part, p.slices, int(n), int(n_tok), y);
@@ -562,13 +638,11 @@ extern "C" int q4_gemm_s64(const void* packed, int64_t n, int64_t k, const uint1
 
 // ------------------------------------------------------ head over 64 tokens
 namespace q4dec {
-// workspace of the head over S tokens: the scaled activations and token
-// factors as for q4_gemm_s64, then one (logit, row) partial per row tile and
-// token slot
-static size_t head_s64_partials_off(int64_t vocab, int64_t k) { return gemm_plan(vocab, k, false).part_off; }
+// workspace of the head over S tokens: one (logit, row) partial per row tile
+// and token slot (the head is never split along K)
 static size_t head_s64_ws_bytes(int64_t vocab, int64_t k) {
-  const int64_t tiles = (vocab + kTileN - 1) / kTileN;
-  return head_s64_partials_off(vocab, k) + align256(size_t(tiles) * kTok * sizeof(uint2));
+  const GemmPlan p = gemm_plan(vocab, k, false);
+  return align256(size_t(p.tiles) * kTok * sizeof(uint2));
 }
 }  // namespace q4dec
 
@@ -604,17 +678,10 @@ extern "C" int lmhead_softcap_argmax_s64(const void* packed, int64_t vocab, int6
   if (ws_bytes < need) return fail(Q4DEC_ERR_WORKSPACE, "%s: ws_bytes %zu < required %zu", name, ws_bytes, need);
   const GemmPlan p = gemm_plan(vocab, k, false);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  uint8_t* w8 = static_cast<uint8_t*>(ws);
-  _Float16* xh = reinterpret_cast<_Float16*>(w8 + p.xh_off);
-  float* xf = reinterpret_cast<float*>(w8 + p.xf_off);
-  uint2* part = reinterpret_cast<uint2*>(w8 + head_s64_partials_off(vocab, k));
+  uint2* part = static_cast<uint2*>(ws);
   const uint8_t* nib = static_cast<const uint8_t*>(packed);
   const uint16_t* scl = reinterpret_cast<const uint16_t*>(nib + nib_plane_bytes(vocab, k));
-  const uint8_t* rexp = nib + nib_plane_bytes(vocab, k) + scale_plane_bytes(vocab, k);
-  const int tiles = int((vocab + kTileN - 1) / kTileN);
-  hipLaunchKernelGGL(gemm_x_prep_kernel, dim3(kTok), dim3(256), 0, st, x, int(k), int(n_tok), xh, xf);
-  hipLaunchKernelGGL(q4_gemm_kernel<kGemmHead>, dim3(unsigned(tiles), 1u), dim3(256), 0, st, nib, scl, rexp, xh, xf,
-                     x, int(vocab), int(k), int(n_tok), p.bps, static_cast<void*>(part));
-  reduce_argmax_partials(part, tiles, kTok, int(n_tok), cap, idx_out, val_out, st);
+  launch_gemm<kGemmHead>(p, st, nib, scl, x, int(vocab), int(k), int(n_tok), part);
+  reduce_argmax_partials(part, p.tiles, kTok, int(n_tok), cap, idx_out, val_out, st);
   return launch_status(name);
 }

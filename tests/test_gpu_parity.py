@@ -1073,8 +1073,8 @@ def test_every_entry_point_replays_in_a_graph():
 @pytest.mark.parametrize("n,k,n_tok", [(1536, 1536, 64), (64, 32, 64), (100, 96, 1), (300, 2560, 37),
                                        # the four E4B layer shapes: QKV, O, down (split K) ...
                                        (3072, 2560, 64), (2560, 2048, 64), (2560, 10240, 64), (77, 16384, 5),
-                                       # >= 128 row tiles: one K slice, no reduce (E4B gate+up; a
-                                       # ragged last tile)
+                                       # many row tiles: one K slice, no reduce (E4B gate+up; a
+                                       # ragged last tile; k not a multiple of 256)
                                        (20480, 2560, 64), (16400, 512, 17)])
 def test_gemm_s64_tolerance(n, k, n_tok):
     rng = synth.rng_for(20, n, k, n_tok)
@@ -1119,8 +1119,8 @@ def test_gemm_rows_match_gemv_and_are_deterministic():
 
 
 def test_gemm_s64_scale_range():
-    """Scales across the fp16 range: large scales take the per-row range
-    shift, tiny and subnormal scales exercise the exact hi/lo split."""
+    """Scales across the fp16 range, rows of only large scales and subnormal
+    scales: the fp32 fold of each block's MFMA sum must keep them all."""
     n, k = 256, 1024
     rng = synth.rng_for(22)
     codes, _ = synth.q4_weights(rng, n, k)

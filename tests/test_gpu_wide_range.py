@@ -1,9 +1,11 @@
 """Activations whose values span more binades than a scaled fp16 copy holds.
 
-Every q4_0 and per-row kernel stages bf16 activations as fp16 scaled by one
-power of two per group (a 32-wide block for the S=1 GEMV, the fused GELU, the
-heads and the per-row formats; a whole vector for the multi-vector GEMV and
-head; a whole token for the S=64 GEMM and its head). A value more than 31
+The S=1 q4_0 and per-row kernels stage bf16 activations as fp16 scaled by
+one power of two per group (a 32-wide block for the S=1 GEMV, the fused GELU,
+the heads and the per-row formats; a whole vector for the multi-vector GEMV
+and head). The S=64 GEMM and its head feed the activations to the matrix
+cores as stored, so for them the same inputs check that nothing on that path
+narrows the range (a staged copy per token would fail them). A value more than 31
 binades below its group's largest (fewer on the per-row formats, whose staged
 values carry an extra field shift of 2^-8 for INT2 and 2^-4 for INT4) would
 lose significand bits there, so such a group sends the launch down the exact
@@ -211,9 +213,9 @@ def test_lmhead_multi_outlier():
 # --------------------------------------------------------- S=64 GEMM --
 @pytest.mark.parametrize("n,k,n_tok", [(3072, 2560, 64), (2560, 2048, 64), (20480, 2560, 17), (300, 1536, 5)])
 def test_gemm_s64_outlier_in_one_token(n, k, n_tok):
-    """A token with a 2^40 outlier whose code is zero on every row: with one
-    power of two per token, its other values would flush. Covers split-K
-    shapes (QKV, O) and an unsplit one (gate+up)."""
+    """A token with a 2^40 outlier whose code is zero on every row: a copy
+    scaled by one power of two per token would flush its other values. Covers
+    split-K shapes (QKV, O) and an unsplit one (gate+up)."""
     rng = synth.rng_for(608, n, k, n_tok)
     codes, sb = synth.q4_weights(rng, n, k)
     x = synth.bf16_normal(rng, (n_tok, k))
