@@ -67,49 +67,37 @@ enum GemmMode : int {
   kGemmHead = 2,    // per token, the tile's best (logit, row) into the workspace
 };
 
-// Row tile width and K split. The estimated time of a launch is the number
-// of workgroup rounds (two workgroups per CU at once) times the work of one
-// wave, plus the cost of writing and re-reading split partials (64 x n fp32
-// per slice) and of the reduce launch. Ties go to the wider tile, which reads
-// the activations fewer times.
+// Row tile width and K split, from timings of the model shapes on MI355X.
+// Very tall matrices (the heads) take two 16-row tiles per wave; otherwise
+// one. When the row tiles alone give fewer workgroups than CUs, K is split
+// across workgroups so that about one workgroup runs per CU (smaller splits
+// leave CUs idle; larger ones gain nothing and add partial-sum traffic).
 static GemmPlan gemm_plan(int64_t n, int64_t k, bool split = true) {
   const int64_t B = k / 32;
   const int64_t cus = std::max(1, device_cu_count());
-  const bool chunked = B % kChunk == 0;
-  GemmPlan best{};
-  best.chunked = chunked;
-  double best_cost = 0.0;
-  for (int sub : {4, 2, 1}) {
-    if (chunked && sub == 4) continue;
-    // chunked: 4 waves side by side over rows, each over the whole slice;
-    // otherwise one row tile per workgroup, its 4 waves over K quarters
-    const int64_t rows = chunked ? 64 * sub : 16 * sub;
-    const int64_t tiles = (n + rows - 1) / rows;
-    const int64_t unit = chunked ? kChunk : 1;
-    const int64_t smax = split ? std::max<int64_t>(1, std::min<int64_t>(16, B / (chunked ? 2 * kChunk : 8))) : 1;
-    for (int64_t s = 1; s <= smax; ++s) {
-      const int64_t bps = ((B + s - 1) / s + unit - 1) / unit * unit;
-      const int64_t slices = (B + bps - 1) / bps;
-      if (slices != s) continue;
-      const int64_t wgs = tiles * slices;
-      const int64_t rounds = (wgs + 2 * cus - 1) / (2 * cus);
-      const double per_wave = double(sub) * double(chunked ? bps : (bps + kGWaves - 1) / kGWaves);
-      // a u-block (16 rows x one block) costs about 300 cycles of one SIMD;
-      // partial traffic at about 4 TB/s, the reduce launch about 4 us
-      const double t_run = double(rounds) * 2.0 * per_wave * 300.0 / 2.4e3;  // us
-      const double t_part = slices > 1 ? double(slices) * 64.0 * double(n) * 8.0 / 4e6 + 4.0 : 0.0;
-      const double cost = t_run + t_part;
-      if (best.sub == 0 || cost < best_cost * 0.97) {
-        best_cost = cost;
-        best.sub = sub;
-        best.tiles = int(tiles);
-        best.slices = int(slices);
-        best.bps = int(bps);
-      }
-    }
+  GemmPlan p{};
+  p.chunked = B % kChunk == 0;
+  // rows per workgroup: chunked 64 * sub (4 waves side by side), otherwise
+  // 16 * sub (4 waves over K quarters)
+  const int64_t base = p.chunked ? 64 : 16;
+  const int subs[3] = {p.chunked ? 2 : 4, p.chunked ? 1 : 2, 1};
+  p.sub = subs[2];
+  if ((n + base * subs[0] - 1) / (base * subs[0]) >= 2 * cus)
+    p.sub = subs[0];
+  else if ((n + base * subs[1] - 1) / (base * subs[1]) >= cus)
+    p.sub = subs[1];
+  const int64_t rows = base * p.sub;
+  p.tiles = int((n + rows - 1) / rows);
+  int64_t want = 1;
+  if (split && p.tiles < cus) {
+    const int64_t smax = std::max<int64_t>(1, std::min<int64_t>(16, B / (p.chunked ? 2 * kChunk : 8)));
+    want = std::min<int64_t>(smax, std::max<int64_t>(1, (cus + p.tiles / 2) / p.tiles));
   }
-  best.total = best.slices > 1 ? align256(size_t(best.slices) * kTok * size_t(n) * 4) : 256;
-  return best;
+  const int64_t unit = p.chunked ? kChunk : 1;
+  p.bps = int(((B + want - 1) / want + unit - 1) / unit * unit);
+  p.slices = int((B + p.bps - 1) / p.bps);
+  p.total = p.slices > 1 ? align256(size_t(p.slices) * kTok * size_t(n) * 4) : 256;
+  return p;
 }
 
 // 16 * c for the 8 codes of one packed dword, in k order, as bf16.
@@ -569,26 +557,22 @@ static void launch_gemm(const GemmPlan& p, hipStream_t st, const uint8_t* nib, c
   }
 }
 
-// y[s, r] = sum over slices, in slice order.
+// y[s, r] = sum over slices, in slice order. Every slice's value is loaded
+// before the first add, so a thread has all of its loads in flight at once.
+constexpr int kMaxSlices = 16;
 __global__ __launch_bounds__(256) void gemm_reduce_kernel(const float* __restrict__ part, int slices, int n,
                                                           int n_tok, float* __restrict__ y) {
   const size_t total = size_t(n_tok) * size_t(n);
   const size_t stride = size_t(kTok) * size_t(n);
   for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < total; i += size_t(gridDim.x) * 256) {
-    // slices added left to right; the loads of four slices are issued
-    // before their adds so they are in flight together
-    float v = part[i];
-    int sl = 1;
-    for (; sl + 4 <= slices; sl += 4) {
-      const float a = part[size_t(sl) * stride + i], b = part[size_t(sl + 1) * stride + i];
-      const float c = part[size_t(sl + 2) * stride + i], d = part[size_t(sl + 3) * stride + i];
-      v += a;
-      v += b;
-      v += c;
-      v += d;
-    }
-    for (; sl < slices; ++sl) v += part[size_t(sl) * stride + i];
-    y[i] = v;
+    float v[kMaxSlices];
+#pragma unroll
+    for (int sl = 0; sl < kMaxSlices; ++sl) v[sl] = sl < slices ? part[size_t(sl) * stride + i] : 0.0f;
+    float acc = v[0];
+#pragma unroll
+    for (int sl = 1; sl < kMaxSlices; ++sl)
+      if (sl < slices) acc += v[sl];
+    y[i] = acc;
   }
 }
 
