@@ -923,9 +923,10 @@ def main():
                 desc = f"q4_rows_kernel GELU mode [{n}, {k}] (fused gate/up GELU, not in the step)"
             elif kind == "head":
                 n, k = wl.head_nk
-                # pass 1 (weights, x, partials) + pass 2; the call returns (index, value)
+                # weights and x; the last workgroup reduces the partials and
+                # the call returns (index, value)
                 b = weight_bytes(n, k) + 2 * k + 8
-                desc = f"q4_rows_kernel head mode [{n}, {k}] + lmhead_reduce_kernel (both passes)"
+                desc = f"q4_rows_kernel head mode [{n}, {k}] (both passes, one launch)"
             else:
                 n, k = shapes[kind]
                 b = q4_bytes(n, k)

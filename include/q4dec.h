@@ -126,8 +126,9 @@ int q4_gemv(const void* packed, int64_t n, int64_t k, const uint16_t* x,
 
 /* q4_gemv_multi: the S=1 matvec for m <= 8 activation vectors at once,
  * y[v, r] = sum_k c[r,k] * d[r,k/32] * x[v, k] (fp32 accumulation), with the
- * weights read once for all m (E2B card: a speculative verify of 4 rows reads
- * the weights once; mixed-bit page: the FFN and head dominate such a step).
+ * weights read once for all m ("Gemma-4 E2B mobile mixed-bit QAT weights",
+ * MTP speculative-decoding sections P5c/P5d: one S = 4 verify pass checks four
+ * draft rows against weights read once; the FFN and head dominate it).
  * m = 1 is q4_gemv. For m >= 2 the products run on the matrix cores: each
  * vector is converted once to fp16 scaled by one power of two (its largest
  * value lands in [2^14, 2^15)), codes times activations accumulate in fp32
@@ -340,16 +341,18 @@ size_t lmhead_workspace_bytes(int64_t vocab, int64_t k);
  * fused head + two-level argmax). Lowest index wins among equal maxima. The
  * cap is strictly increasing, so the argmax is taken on z (no per-row tanh)
  * and only the winning value is capped. Logits that are NaN never win; if no
- * logit compares, idx_out = -1 and val_out = NaN. Two launches on `stream`:
- * every workgroup of the first leaves its best (value, row) in ws, a
- * one-workgroup second launch reduces them.
+ * logit compares, idx_out = -1 and val_out = NaN. One launch on `stream`:
+ * every workgroup publishes its best (value, row) in ws and counts itself
+ * in on a counter in ws; the last workgroup to arrive reduces the partials,
+ * writes the result and sets the counter back to zero.
  *   packed   from q4_pack with (n = vocab, k); 16-byte aligned.
  *   x        bf16 [k], 16-byte aligned.
  *   cap      30.0 for Gemma 4; cap <= 0 returns the raw maximum logit.
  *   ws       device workspace of ws_bytes >= lmhead_workspace_bytes(vocab, k),
- *            8-byte aligned, owned by the caller; scratch for per-workgroup
- *            partials, no initial contents needed. Calls that share one ws
- *            must not overlap (use one stream or separate buffers).
+ *            8-byte aligned, owned by the caller: per-workgroup partials,
+ *            then the counter. Zero-fill ws once before its first use; every
+ *            call leaves the counter at zero. Calls that share one ws must
+ *            not overlap (use one stream or separate buffers).
  *   idx_out  device int32 [1]; val_out device fp32 [1].
  * Errors: NULL pointer, vocab <= 0 or >= 2^31, k constraints as q4_gemv,
  *         workspace too small, misalignment. */
@@ -361,14 +364,15 @@ int lmhead_softcap_argmax(const void* packed, int64_t vocab, int64_t k,
 /* lmhead_softcap_argmax_noalloc: lmhead_softcap_argmax with no workspace
  * argument, for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc). The
- * per-workgroup partials live in a device array inside the library: 8192
- * entries of 8 bytes (64 KiB) on every GPU the library runs on, held until
- * the process ends. The call itself allocates nothing; the first call on a
+ * per-workgroup partials and the arrival counter live in a device array
+ * inside the library: 8192 entries of 8 bytes and one 256-byte line (64.25
+ * KiB) on every GPU the library runs on, held until the process ends, zero
+ * when the library's code is loaded on the device; every call leaves the
+ * counter at zero. The call itself allocates nothing; the first call on a
  * device looks up that array's device address. All calls on one GPU share
  * the array, so calls that overlap in time on one GPU (several streams,
- * several host threads) race and must be serialised by the caller; the
- * array needs no initial contents. Same results as lmhead_softcap_argmax
- * (the same kernels).
+ * several host threads) race and must be serialised by the caller. Same
+ * results as lmhead_softcap_argmax (the same kernel).
  *   packed, vocab, k, x, cap, idx_out, val_out  as lmhead_softcap_argmax.
  * Errors: as lmhead_softcap_argmax (no workspace errors);
  *         Q4DEC_ERR_UNSUPPORTED if the head would need more than 8192
@@ -383,8 +387,9 @@ int lmhead_softcap_argmax_noalloc(const void* packed, int64_t vocab, int64_t k,
 size_t lmhead_multi_workspace_bytes(int64_t vocab, int64_t k, int64_t m);
 
 /* lmhead_softcap_argmax_multi: lmhead_softcap_argmax for m <= 8 activation
- * vectors with the head read once (E2B card: the speculative verify of 4
- * draft rows reads the head once and argmaxes each row). For each v < m:
+ * vectors with the head read once ("Gemma-4 E2B mobile mixed-bit QAT
+ * weights", MTP sections P5c/P5d: the verify pass reads the head once and
+ * takes each draft row's argmax). For each v < m:
  * idx_out[v], val_out[v] as lmhead_softcap_argmax on x[v]; the logits are
  * those of q4_gemv_multi (matrix cores, one power-of-two fp16 factor per
  * vector). Two launches on `stream`: the first leaves every workgroup's best

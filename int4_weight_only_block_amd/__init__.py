@@ -339,7 +339,7 @@ def lmhead_softcap_argmax(packed: torch.Tensor, vocab: int, k: int, x: torch.Ten
     px = _dev(x, "x", _U16, k)
     need = lmhead_workspace_bytes(vocab, k)
     if ws is None:
-        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+        ws = torch.zeros(need, dtype=torch.uint8, device=x.device)  # the arrival counter starts at zero
     pw = _dev(ws, "ws", _BYTES)
     if idx_out is None:
         idx_out = torch.empty(1, dtype=torch.int32, device=x.device)

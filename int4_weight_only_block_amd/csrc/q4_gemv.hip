@@ -25,6 +25,8 @@
 #include <mutex>
 #include <utility>
 
+#include <algorithm>
+
 #include "q4dec_internal.h"
 
 namespace q4dec {
@@ -117,8 +119,10 @@ struct Lane {
 // Most activation vectors one multi-vector GEMV launch takes.
 constexpr int kMaxVecs = 8;
 
-// Upper bound on head workgroups (one (value, row) partial each).
+// Upper bound on head workgroups (one (value, row) partial each), and the
+// partials each thread of the head's last workgroup loads at once.
 constexpr int kMaxPartials = 8192;
+constexpr int kReduceBatch = 16;
 
 // What a row kernel does with its row sums.
 enum RowMode : int {
@@ -127,11 +131,21 @@ enum RowMode : int {
   kGelu = 2,  // fused [gate; up] rows: a[j] = bf16(gelu_tanh(gate_j) * up_j)
 };
 
+// Where the head's last workgroup leaves its result: an arrival counter
+// (zero between calls), the capped maximum and its row.
+struct HeadOut {
+  uint32_t* counter;
+  int32_t* idx;
+  float* val;
+  float cap;
+};
+
 template <int LPR, int BPL, int MODE, bool FULL>
 __global__ __launch_bounds__(kThreads) void q4_rows_kernel(const uint8_t* __restrict__ nib,
                                                            const uint16_t* __restrict__ scl,
                                                            const uint16_t* __restrict__ x, int n, int k, int ipw,
-                                                           void* __restrict__ out, uint2* __restrict__ partials) {
+                                                           void* __restrict__ out, uint2* __restrict__ partials,
+                                                           HeadOut ho) {
   constexpr int RPW = 64 / LPR;  // rows per wave per iteration
   // GELU mode: lane groups r < RPW/2 take gate rows, the others the up rows
   // of the same outputs (n/2 apart), so each output's pair ends up 32 lanes
@@ -240,70 +254,72 @@ __global__ __launch_bounds__(kThreads) void q4_rows_kernel(const uint8_t* __rest
       si[wave] = bidx;
     }
     __syncthreads();
+    __shared__ int s_last;
     if (threadIdx.x == 0) {
       for (int w = 1; w < kWaves; ++w)
         if (better(sv[w], si[w], best, bidx)) {
           best = sv[w];
           bidx = si[w];
         }
-      partials[blockIdx.x] = make_uint2(__builtin_bit_cast(uint32_t, best), uint32_t(bidx));
+      // publish the partial at the coherence point, then count this
+      // workgroup in; the last one to arrive has every partial
+      const uint64_t pv = uint64_t(__builtin_bit_cast(uint32_t, best)) | (uint64_t(uint32_t(bidx)) << 32);
+      __hip_atomic_store(reinterpret_cast<uint64_t*>(partials) + blockIdx.x, pv, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(0);
+      const uint32_t old = __hip_atomic_fetch_add(ho.counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = old + 1u == gridDim.x;
     }
-  }
-}
-
-// Pass 2: one workgroup reduces the pass-1 partials. Each thread issues 16
-// loads before comparing, so up to 4096 partials cost one load latency (a
-// 256-thread workgroup starts and synchronises faster than a 1024-thread
-// one). The comparator is a total order on (value, row), so the result is
-// independent of the reduction order.
-constexpr int kReduceThreads = 256;
-constexpr int kReduceBatch = 16;
-
-__global__ __launch_bounds__(kReduceThreads) void lmhead_reduce_kernel(const uint2* __restrict__ partials, int g,
-                                                                       float cap, int32_t* __restrict__ idx_out,
-                                                                       float* __restrict__ val_out) {
-  float best = -INFINITY;
-  int bidx = INT_MAX;
-  for (int base = 0; base < g; base += kReduceThreads * kReduceBatch) {
-    uint2 p[kReduceBatch];
+    __syncthreads();
+    if (!s_last) return;
+    // pass 2 in the last workgroup: every thread loads its partials (up to
+    // kReduceBatch at once) before comparing; the comparator is a total order
+    // on (value, row), so the result does not depend on the order
+    best = -INFINITY;
+    bidx = INT_MAX;
+    const int g = gridDim.x;
+    for (int base = 0; base < g; base += kThreads * kReduceBatch) {
+      uint64_t pv[kReduceBatch];
 #pragma unroll
-    for (int j = 0; j < kReduceBatch; ++j) {
-      const int i = base + threadIdx.x + j * kReduceThreads;
-      p[j] = i < g ? partials[i] : make_uint2(__builtin_bit_cast(uint32_t, -INFINITY), uint32_t(INT_MAX));
-    }
+      for (int j = 0; j < kReduceBatch; ++j) {
+        const int i = base + int(threadIdx.x) + j * kThreads;
+        pv[j] = i < g ? __hip_atomic_load(reinterpret_cast<const uint64_t*>(partials) + i, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT)
+                      : (uint64_t(uint32_t(INT_MAX)) << 32) | __builtin_bit_cast(uint32_t, -INFINITY);
+      }
 #pragma unroll
-    for (int j = 0; j < kReduceBatch; ++j) {
-      const float v = __builtin_bit_cast(float, p[j].x);
-      const int ix = int(p[j].y);
-      if (better(v, ix, best, bidx)) {
-        best = v;
-        bidx = ix;
+      for (int j = 0; j < kReduceBatch; ++j) {
+        const float v = __builtin_bit_cast(float, uint32_t(pv[j]));
+        const int ix = int(uint32_t(pv[j] >> 32));
+        if (better(v, ix, best, bidx)) {
+          best = v;
+          bidx = ix;
+        }
       }
     }
-  }
-  wave_best(best, bidx);
-  constexpr int kW = kReduceThreads / 64;
-  __shared__ float sv[kW];
-  __shared__ int si[kW];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) {
-    sv[wave] = best;
-    si[wave] = bidx;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    for (int w = 1; w < kW; ++w)
-      if (better(sv[w], si[w], best, bidx)) {
-        best = sv[w];
-        bidx = si[w];
+    wave_best(best, bidx);
+    __syncthreads();  // the pass-1 slots are read before they are reused
+    if (lane == 0) {
+      sv[wave] = best;
+      si[wave] = bidx;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      for (int w = 1; w < kWaves; ++w)
+        if (better(sv[w], si[w], best, bidx)) {
+          best = sv[w];
+          bidx = si[w];
+        }
+      if (bidx == INT_MAX) {
+        *ho.idx = -1;
+        *ho.val = __builtin_nanf("");
+      } else {
+        *ho.idx = bidx;
+        // the cap is increasing: capping the winner alone gives the capped maximum
+        *ho.val = ho.cap > 0.0f ? ho.cap * tanhf(best / ho.cap) : best;
       }
-    if (bidx == INT_MAX) {
-      *idx_out = -1;
-      *val_out = __builtin_nanf("");
-    } else {
-      *idx_out = bidx;
-      // the cap is increasing: capping the winner alone gives the capped maximum
-      *val_out = cap > 0.0f ? cap * tanhf(best / cap) : best;
+      __hip_atomic_store(ho.counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -420,6 +436,19 @@ static Plan make_plan(int64_t n, int64_t k) {
     lpr = 32;
   }
   Plan p = plan_for<MODE>(n, B, lpr);
+  if constexpr (MODE == kHead) {
+    // About four workgroups per CU, each walking several row groups per
+    // wave: a whole number of workgroups per CU balances the stream (E2B
+    // head [262144, 1536]: 2 or 4 per CU 38.6-38.9 us, 2.7 or 3.2 per CU 41-46
+    // us), and fewer workgroups stage x fewer times and leave fewer partials.
+    if (p.fn) {
+      const int64_t target = 4 * int64_t(device_cu_count()) * kWaves;
+      p.ipw = int(std::max<int64_t>(1, (p.rg + target - 1) / target));
+      const int waves = (p.rg + p.ipw - 1) / p.ipw;
+      p.grid = (waves + kWaves - 1) / kWaves;
+    }
+    return p;
+  }
   // A matrix that fits one resident round at this split takes the widest
   // split up to 32 lanes that still fills every lane: shorter block chains
   // per wave and more waves to cover the load latency. (64-lane rows with
@@ -436,10 +465,10 @@ static Plan make_plan(int64_t n, int64_t k) {
 }
 
 static int launch_rows(const Plan& p, const uint8_t* nib, const uint16_t* scl, const uint16_t* x, int n, int k,
-                       void* out, uint2* partials, hipStream_t st) {
+                       void* out, uint2* partials, hipStream_t st, HeadOut ho = HeadOut{}) {
   if (!p.fn) return fail(Q4DEC_ERR_UNSUPPORTED, "no kernel for k=%d (lpr=%d, bpl=%d)", k, p.lpr, p.bpl);
   int ipw = p.ipw;
-  void* args[] = {&nib, &scl, &x, &n, &k, &ipw, &out, &partials};
+  void* args[] = {&nib, &scl, &x, &n, &k, &ipw, &out, &partials, &ho};
   hipError_t e = hipLaunchKernel(p.fn, dim3(p.grid), dim3(kThreads), args, 0, st);
   if (e != hipSuccess) return fail(Q4DEC_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return Q4DEC_OK;
@@ -477,7 +506,7 @@ extern "C" int q4_gemv(const void* packed, int64_t n, int64_t k, const uint16_t*
 extern "C" size_t lmhead_workspace_bytes(int64_t vocab, int64_t k) {
   (void)vocab;
   (void)k;
-  return size_t(q4dec::kMaxPartials) * sizeof(uint2);
+  return size_t(q4dec::kMaxPartials) * sizeof(uint2) + 256;  // partials, then the arrival counter's line
 }
 
 namespace q4dec {
@@ -494,8 +523,9 @@ static int head_check(const char* fn, const void* packed, int64_t vocab, int64_t
   return Q4DEC_OK;
 }
 
-// Both passes of the head, with the per-workgroup partials in `partials`
-// (at least kMaxPartials entries; the plan never needs more).
+// Both passes of the head in one launch, with the per-workgroup partials in
+// `partials` (kMaxPartials entries; the plan never needs more) followed by
+// the arrival counter (zero on entry, left zero).
 static int head_run(const char* fn, const void* packed, int64_t vocab, int64_t k, const uint16_t* x, float cap,
                     uint2* partials, int32_t* idx_out, float* val_out, hipStream_t st) {
   const Plan p = make_plan<kHead>(vocab, k);
@@ -504,20 +534,21 @@ static int head_run(const char* fn, const void* packed, int64_t vocab, int64_t k
                 p.grid, kMaxPartials);
   const uint8_t* nib = static_cast<const uint8_t*>(packed);
   const uint16_t* scl = reinterpret_cast<const uint16_t*>(nib + nib_plane_bytes(vocab, k));
-  int rc = launch_rows(p, nib, scl, x, int(vocab), int(k), nullptr, partials, st);
+  const HeadOut ho{reinterpret_cast<uint32_t*>(partials + kMaxPartials), idx_out, val_out, cap};
+  int rc = launch_rows(p, nib, scl, x, int(vocab), int(k), nullptr, partials, st, ho);
   if (rc) return rc;
-  hipLaunchKernelGGL(lmhead_reduce_kernel, dim3(1), dim3(kReduceThreads), 0, st, partials, p.grid, cap, idx_out,
-                     val_out);
   return launch_status(fn);
 }
 
 // Partials of lmhead_softcap_argmax_noalloc: a file-scope device array in
-// place of a caller workspace (kMaxPartials entries, 64 KiB on every GPU the
-// library runs on, held until the process ends). In host code `scratch`
+// place of a caller workspace (kMaxPartials entries and the arrival
+// counter's 256-byte line, 64.25 KiB on every GPU the library runs on, held
+// until the process ends; zero when the code object is loaded, and every
+// call leaves the counter at zero). In host code `scratch`
 // names a host-side stand-in, not the device memory: kernels get the device
 // address that hipGetSymbolAddress returns for the current device, looked
 // up once per device and kept.
-static __device__ __align__(256) uint2 scratch[kMaxPartials];
+static __device__ __align__(256) uint2 scratch[kMaxPartials + 32];
 
 static int scratch_partials(const char* fn, uint2** out) {
   static std::mutex mu;

@@ -1,7 +1,7 @@
 // q4_multi: multi-vector q4_0 GEMV on the matrix cores, y[v, r] = W[r, :] .
-// x[v, :] for 2 <= m <= 8 activation vectors ("visible-cx/gemma-4-E2B-CoreAI",
-// speculative verify: the weights are read once for the few rows a verify
-// step checks).
+// x[v, :] for 2 <= m <= 8 activation vectors ("Gemma-4 E2B mobile mixed-bit
+// QAT weights", MTP speculative-decoding sections P5c/P5d: a verify pass reads
+// the weights once for the few draft rows it checks).
 //
 // Mapping. v_mfma_f32_4x4x4_16b_f16 runs 16 independent 4x4x4 products per
 // wave; in 4-lane group g, lane 4g + i holds row i of A (four k values),

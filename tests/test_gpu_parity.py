@@ -795,7 +795,8 @@ def test_lmhead_s64_e4b_head_sampled_tokens():
 def test_lmhead_shared_workspace_and_graph_replays():
     """One workspace serves calls of different sizes back to back and the
     replays of a captured call; every call writes a fresh result (outputs are
-    preset to a sentinel before each call)."""
+    preset to a sentinel before each call), and every call leaves the arrival
+    counter in the workspace's last 256 bytes at zero."""
     ws = torch.zeros(q4.lmhead_workspace_bytes(262144, 2560), dtype=torch.uint8, device=DEV)
     idx = torch.empty(1, dtype=torch.int32, device=DEV)
     val = torch.empty(1, dtype=torch.float32, device=DEV)
@@ -841,6 +842,8 @@ def test_lmhead_shared_workspace_and_graph_replays():
         if oracle.top2_margin(c) >= 1e-3:
             assert gi == ri, (rep, gi, ri)
         assert abs(float(val.item()) - c[ri]) <= 1e-4 * a[0, ri] + 1e-6
+    torch.cuda.synchronize()
+    assert int(ws[-256:].count_nonzero().item()) == 0
 
 
 # -------------------------------------------------------------------- PLE --
@@ -1016,7 +1019,7 @@ def test_every_entry_point_replays_in_a_graph():
     pack_codes = torch.zeros((64, k), dtype=torch.int8, device=DEV)
     pack_scales = torch.zeros((64, k // 32), dtype=torch.int16, device=DEV)
     ws_g = torch.empty(q4.q4_gemm_workspace_bytes(2 * n, k), dtype=torch.uint8, device=DEV)
-    ws_h = torch.empty(q4.lmhead_workspace_bytes(2 * n, k), dtype=torch.uint8, device=DEV)
+    ws_h = torch.zeros(q4.lmhead_workspace_bytes(2 * n, k), dtype=torch.uint8, device=DEV)
     ws_m = torch.empty(q4.lmhead_multi_workspace_bytes(2 * n, k, m), dtype=torch.uint8, device=DEV)
     ws_s = torch.empty(q4.lmhead_s64_workspace_bytes(2 * n, k), dtype=torch.uint8, device=DEV)
     ws_r = torch.empty(q4.rowq_head_workspace_bytes(n, k, 2), dtype=torch.uint8, device=DEV)
