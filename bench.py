@@ -68,6 +68,10 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="skip the S=64 prefill step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--counters-summary", metavar="DIR",
+                    help="no GPU work: turn the rocprofv3 FETCH_SIZE / WRITE_SIZE csv output under DIR "
+                         "(pmc_FETCH_SIZE/, pmc_WRITE_SIZE/ over one decode step, cal_FETCH_SIZE/, "
+                         "cal_WRITE_SIZE/ over --copy-calibration) into profiles/hbm_counters.json")
     return ap.parse_args()
 
 
@@ -846,8 +850,74 @@ def load_traffic(shape: str):
     return k.get("hbm_bytes_per_launch")
 
 
+def counters_summary(d: str) -> dict:
+    """HBM bytes per launch of every decode-step launch shape from rocprofv3
+    counter csv files: the last complete step's dispatches (PLE gather, then
+    42 x {QKV, O, gate+up, down}, then the head) are matched to the shapes by
+    their order, FETCH_SIZE and WRITE_SIZE (KiB per dispatch) are scaled by
+    what the same counters read for a plain copy of known size, and each
+    shape's launches are averaged."""
+    import csv
+
+    import synth
+
+    def rows(sub):
+        files = [f for f in os.listdir(os.path.join(d, sub)) if f.endswith("counter_collection.csv")]
+        if len(files) != 1:
+            raise SystemExit(f"expected one counter_collection.csv under {sub}, found {files}")
+        with open(os.path.join(d, sub, files[0])) as f:
+            return list(csv.DictReader(f))
+
+    def step(sub):
+        rs = [r for r in rows(sub) if "q4dec::" in r["Kernel_Name"]
+              and ("q4_rows_kernel" in r["Kernel_Name"] or "ple_gather" in r["Kernel_Name"])]
+        starts = [i for i, r in enumerate(rs) if "ple_gather" in r["Kernel_Name"]]
+        mats = synth.stack_e4b_matrices()
+        for s0 in reversed(starts):
+            seq = rs[s0:s0 + 1 + len(mats)]
+            if len(seq) == 1 + len(mats) and ", 1, " in seq[-1]["Kernel_Name"]:  # ends in the head kernel
+                names = ["ple"] + [nm.split(".")[-1] for nm, _, _ in mats]
+                return [(nm, float(r["Counter_Value"])) for nm, r in zip(names, seq)]
+        raise SystemExit(f"no complete decode step under {sub}")
+
+    def copy_kib(sub):
+        vals = [float(r["Counter_Value"]) for r in rows(sub) if "copyBuffer" in r["Kernel_Name"]]
+        if not vals:
+            raise SystemExit(f"no copy dispatch under {sub}")
+        return sum(vals) / len(vals)
+
+    gib_kib = float(1 << 20)
+    fetch_scale = gib_kib / copy_kib("cal_FETCH_SIZE")
+    write_scale = gib_kib / copy_kib("cal_WRITE_SIZE")
+    fetch, write = step("pmc_FETCH_SIZE"), step("pmc_WRITE_SIZE")
+    shapes = {}
+    for (nm, fv), (nm2, wv) in zip(fetch, write):
+        assert nm == nm2
+        e = shapes.setdefault(nm, {"fetch_kib": [], "write_kib": []})
+        e["fetch_kib"].append(fv)
+        e["write_kib"].append(wv)
+    out = {}
+    for nm, e in shapes.items():
+        f = sum(e["fetch_kib"]) / len(e["fetch_kib"])
+        w = sum(e["write_kib"]) / len(e["write_kib"])
+        out[nm] = {"launches": len(e["fetch_kib"]), "fetch_kib_raw": round(f, 3), "write_kib_raw": round(w, 3),
+                   "hbm_bytes_per_launch": int(round((f * fetch_scale + w * write_scale) * 1024))}
+    return {"kernel_source_hash": kernel_source_hash(), "fetch_scale": round(fetch_scale, 6),
+            "write_scale": round(write_scale, 6),
+            "calibration": f"plain 1 GiB device copy: FETCH_SIZE {copy_kib('cal_FETCH_SIZE'):.1f} KiB, "
+                           f"WRITE_SIZE {copy_kib('cal_WRITE_SIZE'):.1f} KiB per dispatch",
+            "shapes": out}
+
+
 def main():
     args = parse()
+    if args.counters_summary:
+        c = counters_summary(args.counters_summary)
+        with open(COUNTERS_FILE, "w") as f:
+            json.dump(c, f, indent=1)
+            f.write("\n")
+        print(json.dumps(c))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(the hot path is built and measured on one GPU's share)",

@@ -265,12 +265,8 @@ __global__ __launch_bounds__(kCThreads) void q4_chain_kernel(const uint8_t* __re
       for (int qi = threadIdx.x; qi < 4 * B; qi += kCThreads) {
         const u32x4 v = src[qi];
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        uint32_t emax = 1, emin = 255;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          emax = max(emax, max((w[c] >> 7) & 0xFFu, (w[c] >> 23) & 0xFFu));
-          emin = min(emin, min(bf16_exp_nz(w[c] & 0xFFFFu), bf16_exp_nz(w[c] >> 16)));
-        }
+        uint32_t emax, emin;
+        block_exp_range(w, emax, emin);
         // the four quarters of a block sit in lanes 4j .. 4j+3 of one wave
         // (qi and threadIdx.x agree modulo 4 and kCThreads is a multiple of 64)
         emax = max(emax, uint32_t(__shfl_xor(int(emax), 1)));

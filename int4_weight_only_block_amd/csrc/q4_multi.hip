@@ -142,12 +142,8 @@ __global__ __launch_bounds__(kMThreads) void q4_multi_kernel(const uint8_t* __re
   auto take = [&](int idx, const uint4& w) {
     const int v = idx / k8, i = idx - v * k8;
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-    uint32_t e = 1, en = 255;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      e = max(e, max((ws[c] >> 7) & 0xFFu, (ws[c] >> 23) & 0xFFu));
-      en = min(en, min(bf16_exp_nz(ws[c] & 0xFFFFu), bf16_exp_nz(ws[c] >> 16)));
-    }
+    uint32_t e, en;
+    block_exp_range(ws, e, en);
 #pragma unroll
     for (int vv = 0; vv < kMultiVecs; ++vv)
       if (vv == v) {

@@ -109,11 +109,30 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h16) {
 // with a wider span is computed on the exact path instead.
 constexpr int kMaxSpan = 31;
 
-// Exponent field of a nonzero bf16 value (subnormals count as 1, whose last
-// significand bit they share); 255 for +-0, so it never lowers a minimum.
-__device__ __forceinline__ uint32_t bf16_exp_nz(uint32_t h16) {
-  const uint32_t e = (h16 >> 7) & 0xFFu;
-  return (h16 & 0x7FFFu) == 0u ? 255u : (e == 0u ? 1u : e);
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+// Exponent range of 2N bf16 values (N words): emax = largest exponent field
+// (at least 1), emin = smallest exponent field among the nonzero values
+// (subnormals count as 1, whose last significand bit they share; 255 when
+// all are zero, so a zero never lowers the minimum). Computed on the
+// magnitude bits (exponent above mantissa, so they order like the values'
+// magnitudes) with packed 16-bit integer ops: the largest magnitude has the
+// largest exponent, and subtracting 1 with wrap-around sends a zero
+// magnitude to 0xFFFF, out of the minimum.
+template <int N>
+__device__ __forceinline__ void block_exp_range(const uint32_t (&w)[N], uint32_t& emax, uint32_t& emin) {
+  u16x2 mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
+  const u16x2 one = {1, 1};
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const u16x2 z = __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu);
+    mx = __builtin_elementwise_max(mx, z);
+    mn = __builtin_elementwise_min(mn, u16x2(z - one));
+  }
+  const uint32_t big = max(uint32_t(mx[0]), uint32_t(mx[1]));
+  const uint32_t small = min(uint32_t(mn[0]), uint32_t(mn[1]));  // 0xFFFF: no nonzero value
+  emax = max(big >> 7, 1u);
+  emin = small == 0xFFFFu ? 255u : max((small + 1u) >> 7, 1u);
 }
 
 // sum_{j<32} c_j * x_j for one block with x as stored (bf16 [32], 16-byte
@@ -218,12 +237,8 @@ __device__ __forceinline__ bool stage_x_store(const uint4 (&v)[NXL], int B, uint
     const int qi = int(threadIdx.x) + u * NT;
     {
       const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-      uint32_t emax = 1, emin = 255;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        emax = max(emax, max((w[i] >> 7) & 0xFFu, (w[i] >> 23) & 0xFFu));
-        emin = min(emin, min(bf16_exp_nz(w[i] & 0xFFFFu), bf16_exp_nz(w[i] >> 16)));
-      }
+      uint32_t emax, emin;
+      block_exp_range(w, emax, emin);
       emax = max(emax, uint32_t(__shfl_xor(int(emax), 1)));
       emax = max(emax, uint32_t(__shfl_xor(int(emax), 2)));
       emin = min(emin, uint32_t(__shfl_xor(int(emin), 1)));

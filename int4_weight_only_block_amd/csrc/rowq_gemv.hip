@@ -161,12 +161,8 @@ __device__ __forceinline__ bool stage_block(const uint4 (&src)[4], uint32_t* __r
     const uint32_t v = raw[e >> 1];
     return __builtin_bit_cast(float, (e & 1) ? (v & 0xFFFF0000u) : (v << 16));
   };
-  uint32_t emax = 1, emin = 255;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    emax = max(emax, max((raw[i] >> 7) & 0xFFu, (raw[i] >> 23) & 0xFFu));
-    emin = min(emin, min(bf16_exp_nz(raw[i] & 0xFFFFu), bf16_exp_nz(raw[i] >> 16)));
-  }
+  uint32_t emax, emin;
+  block_exp_range(raw, emax, emin);
   // the span test right here (pinned by the empty asm), so the 32 exponent
   // fields die before the conversion instead of living across it
   int wide = int(emax) - int(emin) > kMaxSpan - kMaxShift<BITS>;
