@@ -411,9 +411,8 @@ def probe_quantize(torch, dev, seed: int, reps: int = 20):
 def probe_pack(torch, dev, seed: int, reps: int = 20):
     """q4_pack on an E4B gate+up sized matrix [20480, 2560] (load time, not
     part of a decode step): int8 codes and fp16 scales read, the packed
-    nibble, scale and row-exponent planes written, four distinct inputs in
-    rotation. The call is the nibble packing kernel plus the row-exponent
-    kernel."""
+    nibble and scale planes written, four distinct inputs in rotation; one
+    kernel per call."""
     import int4_weight_only_block_amd as q4
     import synth
 
@@ -437,7 +436,7 @@ def probe_pack(torch, dev, seed: int, reps: int = 20):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / (reps * len(ins))
-    b = n * k + n * (k // 32) * 2 + weight_bytes(n, k) + n
+    b = n * k + n * (k // 32) * 2 + weight_bytes(n, k)
     return {"shape": [n, k], "avg_call_us": round(us, 3), "bytes_per_call": b,
             "achieved_GBs": round(b / us / 1e3, 1), "frac_of_hbm_peak": round(b / us / 1e3 / HBM_PEAK_GBS, 4)}
 

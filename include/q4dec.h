@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define Q4DEC_ABI_VERSION 1
+#define Q4DEC_ABI_VERSION 2
 
 #define Q4DEC_OK 0
 #define Q4DEC_ERR_NULL -1        /* a required pointer is NULL */
@@ -65,9 +65,8 @@ int32_t q4dec_abi_version(void);
  * pointer stays valid until the next failing call on this thread. */
 const char* q4dec_last_error(void);
 
-/* Bytes of device memory a packed [n, k] q4_0 matrix occupies:
- * a nibble plane of n*k/2 bytes, an fp16 scale plane of n*(k/32)*2 bytes and
- * a per-row byte plane of n bytes (largest scale exponent of each row), each
+/* Bytes of device memory a packed [n, k] q4_0 matrix occupies: a nibble
+ * plane of n*k/2 bytes and an fp16 scale plane of n*(k/32)*2 bytes, each
  * padded to 256 bytes. Returns 0 if n <= 0, k <= 0 or k % 32 != 0. */
 size_t q4_packed_bytes(int64_t n, int64_t k);
 

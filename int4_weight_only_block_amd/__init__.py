@@ -22,7 +22,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libq4dec.so")
 HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "q4dec.h")
 
-ABI_VERSION = 1
+ABI_VERSION = 2
 OK = 0
 ERR_NULL = -1
 ERR_SHAPE = -2

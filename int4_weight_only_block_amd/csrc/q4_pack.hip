@@ -37,20 +37,6 @@ __global__ __launch_bounds__(256) void q4_pack_kernel(const int8_t* __restrict__
   if (bad && err) *err = 1;
 }
 
-// One wave per row: largest fp16 exponent field among the row's block scales
-// (lets the prefill GEMM keep c * d_hi inside the fp16 range, see q4_gemm).
-__global__ __launch_bounds__(256) void q4_row_exp_kernel(const uint16_t* __restrict__ scales, int64_t n, int nb,
-                                                         uint8_t* __restrict__ rexp) {
-  const int64_t row = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= n) return;
-  const int lane = threadIdx.x & 63;
-  const uint16_t* s = scales + row * nb;
-  int e = 0;
-  for (int b = lane; b < nb; b += 64) e = max(e, int((s[b] >> 10) & 0x1F));
-  for (int off = 32; off >= 1; off >>= 1) e = max(e, __shfl_xor(e, off));
-  if (lane == 0) rexp[row] = uint8_t(e);
-}
-
 }  // namespace q4dec
 
 extern "C" int q4_pack(const int8_t* codes, const uint16_t* scales, int64_t n, int64_t k, void* packed,
@@ -68,12 +54,8 @@ extern "C" int q4_pack(const int8_t* codes, const uint16_t* scales, int64_t n, i
   uint16_t* scl = reinterpret_cast<uint16_t*>(nib + nib_plane_bytes(n, k));
   const int64_t grid = (n_blocks + 255) / 256;
   if (grid > 0x7FFFFFFF) return fail(Q4DEC_ERR_SHAPE, "q4_pack: matrix too large");
-  uint8_t* rexp = nib + nib_plane_bytes(n, k) + scale_plane_bytes(n, k);
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(q4_pack_kernel, dim3(unsigned(grid)), dim3(256), 0, st, codes, scales, n_blocks, nib, scl,
                      err_flag);
-  const int64_t rgrid = (n + 3) / 4;
-  if (rgrid > 0x7FFFFFFF) return fail(Q4DEC_ERR_SHAPE, "q4_pack: matrix too large");
-  hipLaunchKernelGGL(q4_row_exp_kernel, dim3(unsigned(rgrid)), dim3(256), 0, st, scales, n, int(k / 32), rexp);
   return launch_status("q4_pack");
 }

@@ -44,7 +44,7 @@ const char* q4dec_last_error(void) { return q4dec::g_err; }
 
 size_t q4_packed_bytes(int64_t n, int64_t k) {
   if (n <= 0 || k <= 0 || (k % 32) != 0) return 0;
-  return q4dec::nib_plane_bytes(n, k) + q4dec::scale_plane_bytes(n, k) + q4dec::rexp_plane_bytes(n);
+  return q4dec::nib_plane_bytes(n, k) + q4dec::scale_plane_bytes(n, k);
 }
 
 }  // extern "C"

@@ -21,11 +21,9 @@ inline bool aligned(const void* p, size_t a) {
 }
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-// Planes of a packed [n, k] matrix, in order: nibbles, fp16 scales, and one
-// byte per row holding the largest fp16 exponent field among the row's scales.
+// Planes of a packed [n, k] matrix, in order: nibbles, then fp16 scales.
 inline size_t nib_plane_bytes(int64_t n, int64_t k) { return align256(size_t(n) * size_t(k) / 2); }
 inline size_t scale_plane_bytes(int64_t n, int64_t k) { return align256(size_t(n) * size_t(k / 32) * 2); }
-inline size_t rexp_plane_bytes(int64_t n) { return align256(size_t(n)); }
 
 // Multi-vector GEMV on the matrix cores (q4_multi.hip), for 2 <= m <= 8:
 // dynamic LDS it needs, and the launch (arguments already validated).

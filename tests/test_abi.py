@@ -30,9 +30,9 @@ def test_library_exports_every_header_symbol():
 
 
 def test_packed_bytes():
-    assert q4.q4_packed_bytes(1536, 1536) == 1536 * 768 + 1536 * 48 * 2 + 1536
-    assert q4.q4_packed_bytes(262144, 1536) == 226_492_416 + 262144
-    assert q4.q4_packed_bytes(3, 32) == 256 + 256 + 256  # each plane padded to 256 B
+    assert q4.q4_packed_bytes(1536, 1536) == 1536 * 768 + 1536 * 48 * 2
+    assert q4.q4_packed_bytes(262144, 1536) == 226_492_416
+    assert q4.q4_packed_bytes(3, 32) == 256 + 256  # each plane padded to 256 B
     assert q4.q4_packed_bytes(4, 33) == 0
     assert q4.q4_packed_bytes(0, 32) == 0
     assert q4.q4_packed_bytes(-1, 32) == 0
