@@ -155,9 +155,9 @@ int q4_gemv_multi(const void* packed, int64_t n, int64_t k, const uint16_t* x,
  * The raw packed bytes are the kernel's layout (no repacking). Within the
  * q4_gemv bar for every finite x: x is staged per 32-wide block as fp16
  * scaled by a power of two and by the field offset 2^-s the codes are read
- * at (s <= 8 for INT2, 4 for INT4, 0 for INT8); when a block's nonzero values
- * span more than 31 - s binades the call reads x as stored instead (exact
- * path, slower).
+ * at (s <= 8 for INT2, 4 for INT4, 0 for INT8); a block whose nonzero values
+ * span more than 31 - s binades is summed on its own from x as stored
+ * instead (each code * x exact in fp32).
  *   w          [n, k * bits / 8] bytes row-major, 16-byte aligned.
  *   row_scale  fp32 [n], 4-byte aligned.
  *   bits       2, 4 or 8; k a multiple of 64 (INT2) or 32 (INT4, INT8).

@@ -24,10 +24,13 @@
 // pre-multiplied by 2^-s, so each product in the dot is code * x exactly and
 // only the fp32 accumulation rounds.
 //
-// Staging scales each 32-wide block by one power of two; a block whose
+// Staging scales each 32-wide block by one power of two. A block whose
 // nonzero values span more binades than that copy holds exactly (31 minus
-// the largest field offset) sends the launch down an exact path that decodes
-// each code as a signed integer and reads x as stored.
+// the largest field offset) is "wide": it is staged as stored (bf16) and
+// enters the packed fp16 dot as zeros, and the lanes that hold it add its
+// sum separately, each code decoded as a signed integer and multiplied by x
+// in fp32, where every product is exact. A row step whose lanes hold no wide
+// block skips that branch.
 #include <limits.h>
 #include <math.h>
 
@@ -144,11 +147,12 @@ constexpr int kChunkLoads = BITS == 8 ? 2 : 1;
 template <int BITS>
 constexpr int kMaxShift = BITS == 2 ? 8 : BITS == 4 ? 4 : 0;
 
-// Returns true when the block is "wide": a nonzero value lies more than
-// kMaxSpan - kMaxShift binades below its largest exponent, so its scaled fp16
-// copy would lose bits; the kernel then reads x as stored (exact path).
+// A block is "wide" when a nonzero value lies more than kMaxSpan - kMaxShift
+// binades below its largest exponent, so its scaled fp16 copy would lose
+// bits. A wide block is stored as it came (bf16 pairs in element order) and
+// xe receives -1, which marks it.
 template <int BITS>
-__device__ __forceinline__ bool stage_block(const uint4 (&src)[4], uint32_t* __restrict__ dst, int sw,
+__device__ __forceinline__ void stage_block(const uint4 (&src)[4], uint32_t* __restrict__ dst, int sw,
                                             float* __restrict__ xe, bool store) {
   using F = Fields<BITS>;
   uint32_t raw[16];
@@ -178,13 +182,14 @@ __device__ __forceinline__ bool stage_block(const uint4 (&src)[4], uint32_t* __r
       out[d * F::kPairs + f] = __builtin_bit_cast(uint32_t, h);
     }
   }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) out[i] = wide ? raw[i] : out[i];
   if (store) {
     uint4* d4 = reinterpret_cast<uint4*>(dst);
 #pragma unroll
     for (int i = 0; i < 4; ++i) d4[i ^ (sw & 3)] = make_uint4(out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]);
-    *xe = ldexpf(1.0f, e);
+    *xe = wide ? -1.0f : ldexpf(1.0f, e);
   }
-  return wide != 0;
 }
 
 enum RowqMode { kRowqGemv = 0, kRowqGelu = 1, kRowqHead = 2 };
@@ -302,7 +307,6 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
 #pragma unroll
     for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(xr[u][i]));
 
-  bool wide_t = false;
 #pragma unroll
   for (int u = 0; u < NXB; ++u) {
     const int b = int(threadIdx.x) + u * kRThreads, bc = min(b, B - 1);
@@ -310,25 +314,18 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
                          make_uint4(xr[u][1].x, xr[u][1].y, xr[u][1].z, xr[u][1].w),
                          make_uint4(xr[u][2].x, xr[u][2].y, xr[u][2].z, xr[u][2].w),
                          make_uint4(xr[u][3].x, xr[u][3].y, xr[u][3].z, xr[u][3].w)};
-    wide_t |= stage_block<BITS>(v4, xs + 16 * bc, bc / BPC, xc + bc, b < B);
-  }
-  // a wide block anywhere in x puts every workgroup (all stage the same x)
-  // on the exact path
-  __shared__ int wide_w[kRWaves];
-  {
-    const bool wide_wave = __ballot(wide_t) != 0;
-    if (lane == 0) wide_w[wave] = wide_wave;
+    stage_block<BITS>(v4, xs + 16 * bc, bc / BPC, xc + bc, b < B);
   }
   // LDS writes done and visible; the weight loads above stay in flight
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  // uniform by construction; readfirstlane lets the compiler branch on it
-  // as a scalar, so the two paths do not hold registers at the same time
-  const bool exact = __builtin_amdgcn_readfirstlane(wide_w[0] | wide_w[1] | wide_w[2] | wide_w[3]) != 0;
 
+  // The lane's activation blocks, copied out of LDS into registers. A wide
+  // block l sets bit l of wbits: its packed dot (bf16 bits read as fp16
+  // pairs, meaningless) is dropped, and dot_wide adds its sum from the bf16
+  // copy in LDS instead.
   uint32_t xp[NB][16];
   float xf[NB];
-  // the lane's activation blocks, copied out of LDS (streaming path only)
-  auto fetch_x = [&]() {
+  uint32_t wbits = 0;
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     const int c = j * LPR + t;
@@ -339,17 +336,61 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
         const uint4* s4 = reinterpret_cast<const uint4*>(xs + 16 * b);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const uint4 v = s4[i ^ (c & 3)];
-          xp[l][4 * i] = v.x; xp[l][4 * i + 1] = v.y; xp[l][4 * i + 2] = v.z; xp[l][4 * i + 3] = v.w;
+          const uint4 q4 = s4[i ^ (c & 3)];
+          xp[l][4 * i] = q4.x; xp[l][4 * i + 1] = q4.y; xp[l][4 * i + 2] = q4.z; xp[l][4 * i + 3] = q4.w;
         }
         xf[l] = xc[b];
+        wbits |= uint32_t(xf[l] < 0.0f) << l;
       }
     }
   }
-  };
 
   uint32_t magic;
   asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+
+  // sum_e code_e * x_e over wide block j * BPC + bb of the lane: kDwords
+  // dwords of codes (first code in the lowest bits, two's complement) against
+  // x as stored (bf16 pairs in element order, read back from LDS); each code
+  // is sign-extended by a left and an arithmetic right shift (the sbfe
+  // builtin's result was converted to float as if unsigned), every product
+  // is exact in fp32 and only the sum rounds.
+  auto dot_wide = [&](const uint32_t* wd, int j, int bb) __attribute__((always_inline)) -> float {
+    constexpr int PER = 32 / BITS;  // codes per dword
+    // the LDS addresses are formed here from the lane index: hoisted out of
+    // the row loop as invariants, the four per block would each hold a
+    // register
+    int tt = t;
+    asm volatile("" : "+v"(tt));
+    const int sw = j * LPR + tt, b = sw * BPC + bb;
+    const uint4* s4 = reinterpret_cast<const uint4*>(xs + 16 * b);
+    float p = 0.0f;
+    // one 16-byte quarter (8 elements) at a time, so few registers are live
+    // beside the row loop's own
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = s4[i ^ (sw & 3)];
+      const uint32_t xw[4] = {v.x, v.y, v.z, v.w};
+      // the quarter's code words, tied by an empty asm to its x load: left
+      // free, the compiler decodes all 32 codes ahead of the first load and
+      // holds them at once
+      constexpr int NW = (8 + PER - 1) / PER;  // code words per quarter
+      uint32_t cw[NW];
+#pragma unroll
+      for (int m = 0; m < NW; ++m) {
+        cw[m] = wd[(8 * i) / PER + m];
+        asm volatile("" : "+v"(cw[m]) : "v"(v.x));
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int e = 8 * i + u;
+        const int code = int(cw[u / PER] << (32 - BITS - (e % PER) * BITS)) >> (32 - BITS);
+        const uint32_t xv = xw[u >> 1];
+        p = fmaf(float(code), __builtin_bit_cast(float, (u & 1) ? (xv & 0xFFFF0000u) : (xv << 16)), p);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return p;
+  };
 
   auto dot = [&](uint4(&q)[CPL][CH], float& sc, bool refill, int row_next) -> float {
     const u32x4* pn = reinterpret_cast<const u32x4*>(w + size_t(row_next) * row_bytes);
@@ -370,7 +411,16 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
           float p = 0.0f;
 #pragma unroll
           for (int d = 0; d < F::kDwords; ++d) p = F::dot(wd[bb * F::kDwords + d], &xp[l][d * F::kPairs], p, magic);
-          acc = fmaf(p, xf[l], acc);
+          const float a2 = fmaf(p, xf[l], acc);
+          acc = (wbits >> l) & 1u ? acc : a2;
+        }
+        // the chunk's wide blocks (lane-divergent, skipped by every wave
+        // whose lanes hold none; marked unlikely, so the code sits outside
+        // the loop)
+        if (__builtin_expect(((wbits >> (j * BPC)) & ((1u << BPC) - 1u)) != 0, 0)) {
+#pragma unroll
+          for (int bb = 0; bb < BPC; ++bb)
+            if ((wbits >> (j * BPC + bb)) & 1u) acc += dot_wide(&wd[bb * F::kDwords], j, bb);
         }
         // keep one chunk's work together so its temporaries die before the
         // next chunk's begin
@@ -416,47 +466,10 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
     const float acc = dot(q, sc, refill, row_next);
     emit(i, acc, s_i);
   };
-  // The exact path's row sum: each chunk loaded on its own, every code
-  // decoded as a signed integer (two's complement field, first code in the
-  // lowest bits) and multiplied by x as stored in fp32, where the product is
-  // exact; one chunk at a time.
-  auto dot_exact = [&](int row) -> float {
-    constexpr int NE = 128 * CH / BITS;  // codes per chunk
-    constexpr int PER = 32 / BITS;       // codes per dword
-    float acc = 0.0f;
-#pragma unroll 1
-    for (int j = 0; j < CPL; ++j) {
-      const int c = j * LPR + t;
-      if (FULL || c < U) {
-        const uint32_t* wp = reinterpret_cast<const uint32_t*>(w + size_t(row) * row_bytes + size_t(c) * 16 * CH);
-#pragma unroll 1
-        for (int d = 0; d < 4 * CH; ++d) {
-          const uint32_t word = wp[d];
-          const uint16_t* xd = x + size_t(c) * NE + d * PER;
-          // field f sign-extended by a left shift and an arithmetic right
-          // shift (the sbfe builtin's result was converted to float as if
-          // unsigned, so plain C is used)
-#pragma unroll
-          for (int f = 0; f < PER; ++f) {
-            const int code = int(word << (32 - BITS - f * BITS)) >> (32 - BITS);
-            acc = fmaf(float(code), bf16_to_f32(xd[f]), acc);
-          }
-        }
-      }
-    }
-    return acc;
-  };
-  if (exact) {
-    for (int i = 0; i < iters; ++i) {
-      const int row = row_of(i);
-      emit(i, dot_exact(row), row_scale[row]);
-    }
-  } else if constexpr (DEPTH == 1) {
-    fetch_x();
+  if constexpr (DEPTH == 1) {
     for (int i = 0; i + 1 < iters; ++i) step(i, qa, sa, true, row_of(i + 1));
     if (iters > 0) step(iters - 1, qa, sa, false, 0);
   } else {
-    fetch_x();
     // qa holds row group i, qb row group i + 1; each refills two ahead
     int i = 0;
     for (; i + 3 < iters; i += 2) {

@@ -8,8 +8,10 @@ cores as stored, so for them the same inputs check that nothing on that path
 narrows the range (a staged copy per token would fail them). A value more than 31
 binades below its group's largest (fewer on the per-row formats, whose staged
 values carry an extra field shift of 2^-8 for INT2 and 2^-4 for INT4) would
-lose significand bits there, so such a group sends the launch down the exact
-path, which reads x as stored. These cases are built so that the scaled path
+lose significand bits there. On the q4_0 kernels such a group sends the
+launch down the exact path, which reads x as stored; the per-row kernels
+stage such a block as stored and sum it on its own in fp32, beside the
+packed dot of the other blocks. These cases are built so that the scaled path
 would miss the GEMV bar |y - y_ref| <= 1e-4 sum|w x| + 1e-6: an outlier whose
 code is zero on every row (the rows' sums then come from values the scaled
 copy flushes), and a value exactly one binade past the limit whose last
@@ -30,8 +32,8 @@ pytestmark = pytest.mark.gpu
 
 DEV = torch.device("cuda:0")
 # one binade past this span (largest minus smallest exponent field of a
-# group's nonzero values) takes the exact path; per-row formats subtract
-# their largest field shift
+# group's nonzero values) takes the exact path (the per-row formats: the
+# block's own exact sum); per-row formats subtract their largest field shift
 SPAN = 31
 ROWQ_SPAN = {2: 23, 4: 27, 8: 31}
 
@@ -302,3 +304,34 @@ def test_rowq_span_threshold(bits, extra):
     y = q4.rowq_gemv(d(w), d(sc), n, k, bits, d(x)).cpu().numpy()
     yr, a = oracle.rowq_gemv(w, sc, bits, x)
     within(y, yr, a, f"rowq int{bits} span {s}")
+
+
+@pytest.mark.parametrize("pattern", ["all", "alternate"])
+@pytest.mark.parametrize("bits,k", [(2, 3072), (2, 2112), (4, 2080), (8, 2080)])
+def test_rowq_many_wide_blocks(bits, k, pattern):
+    """Wide blocks are summed one by one beside the packed dot: every block
+    (or every other one) carries an outlier of 2^40 whose code is zero on
+    every row, so lanes hold several wide blocks, both blocks of an INT2
+    chunk are wide, and k leaves a ragged last round of chunks."""
+    n = 300
+    rng = synth.rng_for(613, bits, k, pattern == "all")
+    w, sc = _rowq(rng, n, k, bits)
+    codes = oracle.rowq_unpack(w, n, k, bits)
+    blocks = range(0, k // 32, 1 if pattern == "all" else 2)
+    pos = [32 * b + int(rng.integers(0, 32)) for b in blocks]
+    codes[:, pos] = 0
+    w = oracle.rowq_pack(codes, bits)
+    x = synth.bf16_normal(rng, k)
+    x[pos] = bf16(2.0 ** 40)
+    y = q4.rowq_gemv(d(w), d(sc), n, k, bits, d(x)).cpu().numpy()
+    yr, a = oracle.rowq_gemv(w, sc, bits, x)
+    within(y, yr, a, f"rowq int{bits} k={k} {pattern} wide")
+    ref = oracle.rowq_lmhead(w, sc, bits, x, 30.0)
+    i, v = q4.rowq_softcap_argmax(d(w), d(sc), n, k, bits, d(x), 30.0)
+    if ref["margin"] >= 1e-3:
+        assert int(i.item()) == ref["idx"]
+    assert abs(float(v.item()) - ref["val"]) <= 1e-4 * ref["a_idx"] + 1e-6
+    got = q4.rowq_gemv_gelu_mul(d(w), d(sc), n, k, bits, d(x)).cpu().numpy().view(np.uint16)
+    a_ref, g, u, ag, au = oracle.rowq_gelu_mul(w, sc, bits, x)
+    tol = oracle.gelu_mul_tolerance(g, u, ag, au)
+    assert (np.abs(oracle.bf16_bits_to_f64(got) - a_ref) <= tol).all()
