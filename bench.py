@@ -68,6 +68,10 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="skip the S=64 prefill step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="no GPU work: per-shape launch durations of every complete decode step in the "
+                         "rocprofv3 kernel trace csv under DIR/ktr/, with the algorithmic bytes and the "
+                         "rate and fraction of the HBM peak they give (one JSON line)")
     ap.add_argument("--counters-summary", metavar="DIR",
                     help="no GPU work: turn the rocprofv3 FETCH_SIZE / WRITE_SIZE csv output under DIR "
                          "(pmc_FETCH_SIZE/, pmc_WRITE_SIZE/ over one decode step, cal_FETCH_SIZE/, "
@@ -908,8 +912,64 @@ def counters_summary(d: str) -> dict:
             "shapes": out}
 
 
+def trace_summary(d: str) -> dict:
+    """Per-shape durations (End - Start of each dispatch) of every complete
+    decode step in a rocprofv3 kernel trace: a PLE gather followed by the
+    step's 169 q4_0 launches in order (42 x {QKV, O, gate+up, down}, then the
+    head), matched to the shapes by that order."""
+    import csv
+    import statistics
+
+    import synth
+
+    sub = os.path.join(d, "ktr")
+    files = [f for f in os.listdir(sub) if f.endswith("kernel_trace.csv")]
+    if len(files) != 1:
+        raise SystemExit(f"expected one kernel_trace.csv under {sub}, found {files}")
+    with open(os.path.join(sub, files[0])) as f:
+        rs = [r for r in csv.DictReader(f) if "q4dec::" in r["Kernel_Name"]]
+    rs.sort(key=lambda r: int(r["Start_Timestamp"]))
+    mats = synth.stack_e4b_matrices()
+    kinds = ["ple"] + [nm.split(".")[-1] for nm, _, _ in mats]
+    durs = {kd: [] for kd in dict.fromkeys(kinds)}
+    steps, i = 0, 0
+    while i < len(rs):
+        seq = rs[i:i + len(kinds)]
+        ok = (len(seq) == len(kinds) and "ple_gather" in seq[0]["Kernel_Name"]
+              and all("q4_rows_kernel" in r["Kernel_Name"] for r in seq[1:])
+              and ", 1, " in seq[-1]["Kernel_Name"])  # the head mode
+        if not ok:
+            i += 1
+            continue
+        for kd, r in zip(kinds, seq):
+            durs[kd].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)
+        steps += 1
+        i += len(kinds)
+    if not steps:
+        raise SystemExit(f"no complete decode step in {files[0]}")
+    shapes = {}
+    for nm, n, k in mats:
+        shapes.setdefault(nm.split(".")[-1], (n, k))
+    out = {}
+    for kd, v in durs.items():
+        e = {"launches": len(v), "mean_us": round(statistics.fmean(v), 3),
+             "median_us": round(statistics.median(v), 3)}
+        if kd != "ple":
+            n, k = shapes[kd]
+            b = weight_bytes(n, k) + 2 * k + 8 if kd == "head" else q4_bytes(n, k)
+            gbs = b / (e["mean_us"] * 1e-6) / 1e9
+            e.update({"shape": [n, k], "bytes_per_launch": b, "achieved_GBs": round(gbs, 1),
+                      "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+        out[kd] = e
+    return {"kernel_source_hash": kernel_source_hash(), "trace": files[0], "decode_steps": steps,
+            "shapes": out}
+
+
 def main():
     args = parse()
+    if args.trace_summary:
+        print(json.dumps(trace_summary(args.trace_summary)))
+        return
     if args.counters_summary:
         c = counters_summary(args.counters_summary)
         with open(COUNTERS_FILE, "w") as f:
