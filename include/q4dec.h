@@ -65,6 +65,23 @@ int32_t q4dec_abi_version(void);
  * pointer stays valid until the next failing call on this thread. */
 const char* q4dec_last_error(void);
 
+/* Launch-contract checks of a debug build (built with Q4DEC_DEBUG=1; for
+ * developers changing the kernels or their plans). Every kernel then first
+ * checks that its launch fits what its code assumes (the activation staging
+ * holds every block, a plan marked full has no ragged lane, the grid covers
+ * every row, tile and K slice); a failed check sets a bit and that workgroup
+ * returns before touching memory.
+ * q4dec_debug_status synchronises the device, writes the OR of every bit
+ * set since the last call to *word (0: no check failed) and clears them.
+ * Bits: 0-2 q4_gemv family (staging, full plan, rows), 3-5 per-row kernels,
+ * 6-7 multi-vector GEMV (segments, rows), 9-11 S=64 GEMM (chunks, K slices,
+ * row tiles), 15 gathers, 17 q4_pack, 18 q4_quantize, 31 self-test.
+ * q4dec_debug_selftest launches a kernel whose check always fails (bit 31).
+ * Errors: NULL word; Q4DEC_ERR_UNSUPPORTED in a release build (word 0);
+ *         Q4DEC_ERR_HIP if the synchronisation reports an error. */
+int q4dec_debug_status(uint32_t* word);
+int q4dec_debug_selftest(void* stream);
+
 /* Bytes of device memory a packed [n, k] q4_0 matrix occupies: a nibble
  * plane of n*k/2 bytes and an fp16 scale plane of n*(k/32)*2 bytes, each
  * padded to 256 bytes. Returns 0 if n <= 0, k <= 0 or k % 32 != 0. */

@@ -19,7 +19,9 @@ import numpy as np
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libq4dec.so")
+# Q4DEC_LIB selects another build of the same library (libq4dec_asan.so, the
+# host-sanitizer build, for CPU runs of the host paths)
+LIB_PATH = os.environ.get("Q4DEC_LIB") or os.path.join(HERE, "libq4dec.so")
 HEADER_PATH = os.path.join(os.path.dirname(HERE), "include", "q4dec.h")
 
 ABI_VERSION = 2
@@ -40,6 +42,8 @@ _c_p = ctypes.c_void_p
 _SIGNATURES = {
     "q4dec_abi_version": (ctypes.c_int32, []),
     "q4dec_last_error": (ctypes.c_char_p, []),
+    "q4dec_debug_status": (ctypes.c_int, [_c_p]),
+    "q4dec_debug_selftest": (ctypes.c_int, [_c_p]),
     "q4_packed_bytes": (ctypes.c_size_t, [_c_i64, _c_i64]),
     "q4_pack": (ctypes.c_int, [_c_p, _c_p, _c_i64, _c_i64, _c_p, _c_p, _c_p]),
     "q4_quantize": (ctypes.c_int, [_c_p, _c_i64, _c_i64, ctypes.c_int32, _c_p, _c_p, _c_p, _c_p]),
@@ -164,6 +168,23 @@ def q4dec_abi_version() -> int:
 
 def q4dec_last_error() -> str:
     return lib().q4dec_last_error().decode()
+
+
+def debug_status() -> tuple[int, int]:
+    """(return code, word): the launch-contract bits set since the last call
+    (a debug build of the library), cleared by the call; a release build
+    returns ERR_UNSUPPORTED and 0."""
+    w = ctypes.c_uint32(0)
+    rc = int(lib().q4dec_debug_status(ctypes.byref(w)))
+    return rc, int(w.value)
+
+
+def debug_selftest(stream=None) -> int:
+    """Launch the debug build's always-failing check (bit 31)."""
+    import torch
+
+    st = stream if stream is not None else torch.cuda.current_stream()
+    return int(lib().q4dec_debug_selftest(ctypes.c_void_p(st.cuda_stream)))
 
 
 def q4_packed_bytes(n: int, k: int) -> int:

@@ -3,6 +3,16 @@
 Every .hip file under csrc/ is compiled to an object and the objects are linked
 into one shared library next to this file. Called by __graft_entry__.build()
 and usable as ``python -m int4_weight_only_block_amd.build``.
+
+``build(asan=True)`` builds libq4dec_asan.so: the same sources with the host
+code (argument checks, plans, launch set-up) instrumented by AddressSanitizer;
+device code is compiled as usual. It is for CPU runs of the host paths, with
+the sanitizer runtime preloaded (see ``asan_runtime()``).
+
+``build(debug=True)`` (or ``Q4DEC_DEBUG=1 python -m
+int4_weight_only_block_amd.build``) builds libq4dec_debug.so with
+-DQ4DEC_DEBUG=1: every kernel checks its launch contract on the device and
+records failures for q4dec_debug_status().
 """
 from __future__ import annotations
 
@@ -19,6 +29,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libq4dec.so")
+ASAN_LIB_PATH = os.path.join(HERE, "libq4dec_asan.so")
+DEBUG_LIB_PATH = os.path.join(HERE, "libq4dec_debug.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -35,6 +47,11 @@ HIPCC_FLAGS = [
 ]
 
 
+# host-only AddressSanitizer (each flag bound to the host pass)
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+ASAN_LINK_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-shared-libsan"]
+
+
 # per-file additions: the S=64 GEMM folds every MFMA result on the VALU, so
 # its MFMAs write VGPRs directly instead of going through AGPR copies
 FILE_FLAGS = {
@@ -49,9 +66,24 @@ def hipcc() -> str:
     return path
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
+def asan_runtime() -> str:
+    """Path of the clang AddressSanitizer runtime that libq4dec_asan.so links
+    against (to be preloaded into an uninstrumented python)."""
+    res = subprocess.run([os.path.join(os.path.dirname(os.path.realpath(hipcc())), "..", "lib", "llvm", "bin",
+                                       "clang"), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                         capture_output=True, text=True)
+    path = res.stdout.strip()
+    if res.returncode == 0 and os.path.isabs(path) and os.path.exists(path):
+        return path
+    found = sorted(glob.glob("/opt/rocm*/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not found:
+        raise RuntimeError("clang AddressSanitizer runtime not found")
+    return found[-1]
+
+
+def _compile(src: str, verbose: bool, build_dir: str, extra: list) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *HIPCC_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), *extra, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -64,24 +96,30 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, jobs: int | None = None, asan: bool = False, debug: bool = False) -> str:
+    if asan and debug:
+        raise ValueError("build one variant at a time")
+    build_dir = os.path.join(BUILD_DIR, "asan" if asan else "debug") if (asan or debug) else BUILD_DIR
+    lib_path = ASAN_LIB_PATH if asan else DEBUG_LIB_PATH if debug else LIB_PATH
+    os.makedirs(build_dir, exist_ok=True)
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if not sources:
         raise RuntimeError("no HIP sources found")
     jobs = jobs or min(len(sources), max(1, (os.cpu_count() or 4)))
+    extra = ASAN_FLAGS if asan else ["-DQ4DEC_DEBUG=1"] if debug else []
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), sources))
-    tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, extra), sources))
+    tmp = lib_path + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *(ASAN_LINK_FLAGS if asan else []), "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, asan="--asan" in sys.argv,
+                debug="--debug" in sys.argv or os.environ.get("Q4DEC_DEBUG", "0") not in ("", "0")))

@@ -20,6 +20,7 @@
 #include "q4dec_internal.h"
 
 namespace q4dec {
+Q4DEC_DEBUG_READER(ple_gather)
 
 __device__ __forceinline__ float round_product(int q, float s, double m) {
   const double p = double(q) * double(s);  // exact: 8 + 24 significant bits
@@ -46,6 +47,7 @@ __global__ __launch_bounds__(256) void ple_gather_kernel(const int8_t* __restric
                                                          const int32_t* __restrict__ ids, double mult,
                                                          float* __restrict__ out, int32_t* __restrict__ err,
                                                          int vec_ok) {
+  Q4_DCHECK(int64_t(gridDim.x) * 256 * 16 >= dim, kDbgGatherGrid);
   const int t = blockIdx.y;
   const int j0 = (blockIdx.x * 256 + threadIdx.x) * 16;
   if (j0 >= dim) return;
@@ -85,9 +87,10 @@ __global__ __launch_bounds__(256) void rowq_gather_kernel(const uint32_t* __rest
                                                           int group, const int32_t* __restrict__ ids, float mult,
                                                           float* __restrict__ out, int32_t* __restrict__ err) {
   constexpr int kPer = 32 / BITS;  // values per word
+  const int words = dim / kPer;
+  Q4_DCHECK(int64_t(gridDim.x) * 256 >= words, kDbgGatherGrid);
   const int t = blockIdx.y;
   const int c = blockIdx.x * 256 + threadIdx.x;
-  const int words = dim / kPer;
   if (c >= words) return;
   const int id = ids[t];
   float4* o4 = reinterpret_cast<float4*>(out + size_t(t) * size_t(dim) + size_t(c) * kPer);

@@ -51,6 +51,7 @@
 #include "q4dec_internal.h"
 
 namespace q4dec {
+Q4DEC_DEBUG_READER(q4_chain)
 namespace {
 
 constexpr int kCWaves = 16;                // waves per workgroup

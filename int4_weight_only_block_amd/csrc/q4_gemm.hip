@@ -42,6 +42,7 @@
 #include "q4dec_internal.h"
 
 namespace q4dec {
+Q4DEC_DEBUG_READER(q4_gemm)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
@@ -135,6 +136,8 @@ __global__ __launch_bounds__(kGThreads) void q4_gemm_kernel(const uint8_t* __res
   constexpr int kRows = 16 * SUB;
   __shared__ float4_t red[2][SUB * 4][64];  // two partial tiles (SUB = 4: 32 KB)
   const int B = k >> 5;
+  Q4_DCHECK(bps > 0 && int64_t(gridDim.y) * bps >= B && int64_t(gridDim.y - 1) * bps < B, kDbgGemmSlices);
+  Q4_DCHECK(int64_t(gridDim.x) * kRows >= n, kDbgGemmTiles);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4;    // lane group: k = 8q .. 8q+7 of a block; tokens 4q .. 4q+3 of a C tile
@@ -347,6 +350,9 @@ __global__ __launch_bounds__(kGThreads) void q4_gemm_chunk_kernel(const uint8_t*
                                                                   int n_tok, int bps, void* __restrict__ out) {
   __shared__ u32x4 xs[kChunk][kTok][4];  // [block][token][quarter, swizzled], 32 KB
   const int B = k >> 5;
+  Q4_DCHECK(B % kChunk == 0 && bps > 0 && bps % kChunk == 0, kDbgGemmChunks);
+  Q4_DCHECK(int64_t(gridDim.y) * bps >= B && int64_t(gridDim.y - 1) * bps < B, kDbgGemmSlices);
+  Q4_DCHECK(int64_t(gridDim.x) * 64 * SUB >= n, kDbgGemmTiles);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4;

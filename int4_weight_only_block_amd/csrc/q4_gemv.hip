@@ -30,6 +30,7 @@
 #include "q4dec_internal.h"
 
 namespace q4dec {
+Q4DEC_DEBUG_READER(q4_gemv)
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
@@ -169,6 +170,9 @@ __global__ __launch_bounds__(kThreads) void q4_rows_kernel(const uint8_t* __rest
   const size_t row_bytes = size_t(k) >> 1;
   // row groups this wave walks: rg_base, rg_base + kWaves, ... (uniform)
   const int iters = rg_base < RG ? min(ipw, (RG - rg_base + kWaves - 1) / kWaves) : 0;
+  Q4_DCHECK(B <= MAXB, kDbgGemvStaging);
+  Q4_DCHECK(!FULL || B == MAXB, kDbgGemvFull);
+  Q4_DCHECK(int64_t(gridDim.x) * kWaves * ipw >= RG, kDbgGemvRows);
   auto row_of = [&](int i) {
     if constexpr (MODE == kGelu) {
       const int v = (rg_base + i * kWaves) * UPW + (r % UPW);

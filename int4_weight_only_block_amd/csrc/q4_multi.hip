@@ -30,6 +30,7 @@
 #include "q4dec_internal.h"
 
 namespace q4dec {
+Q4DEC_DEBUG_READER(q4_multi)
 namespace {
 
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
@@ -90,6 +91,8 @@ __global__ __launch_bounds__(kMThreads) void q4_multi_kernel(const uint8_t* __re
   const int RG = (n + 3) / 4;
   const int rg_base = blockIdx.x * kMWaves * ipw + wave;
   const int iters = rg_base < RG ? min(ipw, (RG - rg_base + kMWaves - 1) / kMWaves) : 0;
+  Q4_DCHECK(nseg * 16 * BPL >= B && (!FULL || nseg * 16 * BPL == B), kDbgMultiStaging);
+  Q4_DCHECK(int64_t(gridDim.x) * kMWaves * ipw >= RG, kDbgMultiRows);
   const int units = iters * nseg;  // (row group, segment) steps this wave walks
   const size_t row_bytes = size_t(k) >> 1;
   auto row_of = [&](int u) {

@@ -4,11 +4,13 @@
 #include "q4dec_internal.h"
 
 namespace q4dec {
+Q4DEC_DEBUG_READER(q4_pack)
 
 __global__ __launch_bounds__(256) void q4_pack_kernel(const int8_t* __restrict__ codes,
                                                       const uint16_t* __restrict__ scales,
                                                       int64_t n_blocks, uint8_t* __restrict__ nib,
                                                       uint16_t* __restrict__ scl, int32_t* __restrict__ err) {
+  Q4_DCHECK(int64_t(gridDim.x) * blockDim.x >= n_blocks, kDbgPackGrid);
   const int64_t blk = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (blk >= n_blocks) return;
   // codes of a block are 32 contiguous bytes (row-major [n, k], k % 32 == 0)

@@ -8,10 +8,12 @@
 #include "q4dec_internal.h"
 
 namespace q4dec {
+Q4DEC_DEBUG_READER(q4_quantize)
 
 __global__ __launch_bounds__(256) void q4_quantize_kernel(const uint16_t* __restrict__ x, int64_t n_blocks, int rule,
                                                           int8_t* __restrict__ codes, uint16_t* __restrict__ scales,
                                                           int32_t* __restrict__ err) {
+  Q4_DCHECK(int64_t(gridDim.x) * blockDim.x >= n_blocks, kDbgQuantGrid);
   const int64_t blk = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (blk >= n_blocks) return;
   const uint4* src = reinterpret_cast<const uint4*>(x + blk * 32);

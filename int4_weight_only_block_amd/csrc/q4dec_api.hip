@@ -34,9 +34,36 @@ int device_cu_count() {
   return cache[dev];
 }
 
+Q4DEC_DEBUG_READER(api)
+
+// fails its one check on purpose, so a debug build's reporting can be tested
+__global__ void debug_selftest_kernel() { Q4_DCHECK(false, kDbgSelfTest); }
+
 }  // namespace q4dec
 
 extern "C" {
+
+int q4dec_debug_status(uint32_t* word) {
+  using namespace q4dec;
+  if (!word) return fail(Q4DEC_ERR_NULL, "q4dec_debug_status: word is NULL");
+  *word = 0;
+  if (!Q4DEC_DEBUG)
+    return fail(Q4DEC_ERR_UNSUPPORTED, "q4dec_debug_status: library built without Q4DEC_DEBUG");
+  const hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return fail(Q4DEC_ERR_HIP, "q4dec_debug_status: %s", hipGetErrorString(e));
+  *word = debug_take_q4_gemv() | debug_take_q4_multi() | debug_take_q4_chain() | debug_take_q4_gemm() |
+          debug_take_rowq_gemv() | debug_take_ple_gather() | debug_take_q4_pack() | debug_take_q4_quantize() |
+          debug_take_api();
+  return Q4DEC_OK;
+}
+
+int q4dec_debug_selftest(void* stream) {
+  using namespace q4dec;
+  if (!Q4DEC_DEBUG)
+    return fail(Q4DEC_ERR_UNSUPPORTED, "q4dec_debug_selftest: library built without Q4DEC_DEBUG");
+  hipLaunchKernelGGL(debug_selftest_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream));
+  return launch_status("q4dec_debug_selftest");
+}
 
 int32_t q4dec_abi_version(void) { return Q4DEC_ABI_VERSION; }
 

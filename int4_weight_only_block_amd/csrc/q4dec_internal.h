@@ -37,6 +37,72 @@ inline int launch_status(const char* what) {
   return Q4DEC_OK;
 }
 
+// ------------------------------------------------ launch-contract checks
+// Built with -DQ4DEC_DEBUG=1, each kernel first checks, uniformly across its
+// workgroup, that the launch fits what its code assumes: the activation
+// staging holds every block, a plan marked full has no ragged lane, the grid
+// covers every row, tile and K slice. A failed check sets its bit in the
+// translation unit's debug word and the workgroup returns before it touches
+// memory; q4dec_debug_status() collects and clears the words of every unit.
+// Release builds compile the checks away.
+#ifndef Q4DEC_DEBUG
+#define Q4DEC_DEBUG 0
+#endif
+
+// One bit per check; each translation unit owns its own bits.
+enum DebugBit : int {
+  kDbgGemvStaging = 0,   // q4_rows_kernel: B > staged blocks
+  kDbgGemvFull = 1,      // q4_rows_kernel: full plan with ragged lanes
+  kDbgGemvRows = 2,      // q4_rows_kernel: grid * waves * ipw < row groups
+  kDbgRowqStaging = 3,   // rowq_rows_kernel: blocks or chunks beyond the lanes
+  kDbgRowqFull = 4,      // rowq_rows_kernel: full plan with ragged lanes
+  kDbgRowqRows = 5,      // rowq_rows_kernel: grid does not cover the rows
+  kDbgMultiStaging = 6,  // q4_multi_kernel: lane segments do not cover k
+  kDbgMultiRows = 7,     // q4_multi_kernel: grid does not cover the rows
+  kDbgGemmChunks = 9,    // q4_gemm_chunk_kernel: k or the slice not whole chunks
+  kDbgGemmSlices = 10,   // q4_gemm kernels: slices miss or overrun K
+  kDbgGemmTiles = 11,    // q4_gemm kernels: tiles do not cover the rows
+  kDbgGatherGrid = 15,   // ple / rowq gather: grid does not cover the ids
+  kDbgPackGrid = 17,     // q4_pack_kernel: grid does not cover the blocks
+  kDbgQuantGrid = 18,    // q4_quantize_kernel: grid does not cover the blocks
+  kDbgSelfTest = 31,     // q4dec_debug_selftest: always fails
+};
+
+namespace {
+// this translation unit's debug word (device memory, zero at load)
+__device__ uint32_t g_debug_word;
+// reads and clears this unit's word (host; synchronous)
+inline uint32_t debug_take_local() {
+  uint32_t w = 0;
+  const uint32_t z = 0;
+  if (hipMemcpyFromSymbol(&w, HIP_SYMBOL(g_debug_word), sizeof(w), 0, hipMemcpyDeviceToHost) != hipSuccess) return 0;
+  (void)hipMemcpyToSymbol(HIP_SYMBOL(g_debug_word), &z, sizeof(z), 0, hipMemcpyHostToDevice);
+  return w;
+}
+}  // namespace
+
+// every unit's reader (defined by Q4DEC_DEBUG_READER in each .hip file)
+uint32_t debug_take_q4_gemv();
+uint32_t debug_take_q4_multi();
+uint32_t debug_take_q4_chain();
+uint32_t debug_take_q4_gemm();
+uint32_t debug_take_rowq_gemv();
+uint32_t debug_take_ple_gather();
+uint32_t debug_take_q4_pack();
+uint32_t debug_take_q4_quantize();
+uint32_t debug_take_api();
+#define Q4DEC_DEBUG_READER(unit) \
+  uint32_t debug_take_##unit() { return debug_take_local(); }
+
+// In a kernel, before any barrier or memory access: a uniform condition.
+#define Q4_DCHECK(cond, bit)                                                            \
+  do {                                                                                  \
+    if (Q4DEC_DEBUG && !(cond)) {                                                       \
+      if (threadIdx.x == 0) atomicOr(&::q4dec::g_debug_word, 1u << int(::q4dec::bit)); \
+      return;                                                                           \
+    }                                                                                   \
+  } while (0)
+
 // ------------------------------------------------------------- device side
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -42,6 +42,7 @@
 #include "q4dec_internal.h"
 
 namespace q4dec {
+Q4DEC_DEBUG_READER(rowq_gemv)
 namespace {
 
 constexpr int kRWaves = 4;
@@ -254,6 +255,9 @@ __global__ __launch_bounds__(kRThreads) void rowq_rows_kernel(const uint8_t* __r
   const int rg_base = blockIdx.x * kRWaves * ipw + wave;
   const size_t row_bytes = size_t(U) * 16 * CH;
   const int iters = rg_base < RG ? min(ipw, (RG - rg_base + kRWaves - 1) / kRWaves) : 0;
+  Q4_DCHECK(B <= MAXB && U <= LPR * CPL, kDbgRowqStaging);
+  Q4_DCHECK(!FULL || U == LPR * CPL, kDbgRowqFull);
+  Q4_DCHECK(int64_t(gridDim.x) * kRWaves * ipw >= RG, kDbgRowqRows);
   auto row_of = [&](int i) {
     if constexpr (MODE == kRowqGelu) {
       const int v = (rg_base + i * kRWaves) * UPW + (r % UPW);

@@ -11,7 +11,7 @@ import int4_weight_only_block_amd as q4
 pytestmark = pytest.mark.skipif(not os.path.exists(q4.LIB_PATH), reason="libq4dec.so not built")
 
 EXPECTED = {
-    "q4dec_abi_version", "q4dec_last_error", "q4_packed_bytes", "q4_pack", "q4_quantize", "q4_gemv", "q4_gemv_gelu_mul", "q4_gemv_multi", "rowq_gemv", "rowq_gemv_gelu_mul",
+    "q4dec_abi_version", "q4dec_last_error", "q4dec_debug_status", "q4dec_debug_selftest", "q4_packed_bytes", "q4_pack", "q4_quantize", "q4_gemv", "q4_gemv_gelu_mul", "q4_gemv_multi", "rowq_gemv", "rowq_gemv_gelu_mul",
     "rowq_head_workspace_bytes", "rowq_softcap_argmax",
     "q4_gemm_s64", "q4_gemm_workspace_bytes", "lmhead_workspace_bytes", "lmhead_softcap_argmax", "lmhead_softcap_argmax_noalloc", "lmhead_multi_workspace_bytes",
     "q4_chain_table_bytes", "q4_chain_workspace_bytes", "q4_chain_build", "q4_gemv_chain", "lmhead_softcap_argmax_multi", "lmhead_s64_workspace_bytes", "lmhead_softcap_argmax_s64", "ple_gather", "rowq_gather",
@@ -445,3 +445,14 @@ def test_chain_run_validation():
     assert L.q4_gemv_chain(host.ctypes.data, FAKE, FAKE + 64, ws_bytes, FAKE, FAKE, None) == q4.ERR_ALIGN
     # a table that q4_chain_build did not write
     assert L.q4_gemv_chain(host.ctypes.data, FAKE, FAKE, ws_bytes, FAKE, FAKE, None) == q4.ERR_SHAPE
+
+
+def test_debug_status_in_a_release_build():
+    """Only a build with Q4DEC_DEBUG=1 carries the launch-contract checks; a
+    release build says so (no GPU call is made)."""
+    if os.path.basename(q4.LIB_PATH) != "libq4dec.so":
+        pytest.skip("not the release library")
+    rc, word = q4.debug_status()
+    assert rc == q4.ERR_UNSUPPORTED and word == 0
+    assert "Q4DEC_DEBUG" in q4.q4dec_last_error()
+    assert q4.lib().q4dec_debug_status(None) == q4.ERR_NULL

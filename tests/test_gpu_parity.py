@@ -1121,6 +1121,24 @@ def test_gemm_rows_match_gemv_and_are_deterministic():
     assert (np.abs(y5.astype(np.float64) - y1[:5]) <= 2 * oracle.gemv_tolerance(a[:5])).all()
 
 
+def test_gemm_s64_shared_workspace_across_shapes():
+    """One workspace serves a sequence of split-K calls of different shapes
+    and token counts (the prefill step's pattern), twice over: no call may
+    read what an earlier one left in it."""
+    shapes = [(3072, 2560, 64), (2560, 2048, 64), (2560, 10240, 64), (300, 2560, 37), (2560, 2048, 7)]
+    need = max(q4.q4_gemm_workspace_bytes(n, k) for n, k, _ in shapes)
+    ws = torch.full((need,), 0x7F, dtype=torch.uint8, device=DEV)
+    rng = synth.rng_for(23)
+    for rep in range(2):
+        for n, k, t in shapes:
+            codes, sb = synth.q4_weights(rng, n, k)
+            xs = synth.bf16_normal(rng, (t, k))
+            y = torch.empty((t, n), dtype=torch.float32, device=DEV)
+            q4.q4_gemm_s64(pack(codes, sb), n, k, d(xs), y, ws)
+            yr, a = oracle.gemm(codes, sb, xs)
+            assert_within_tol(y.cpu().numpy().ravel(), yr.ravel(), a.ravel(), f"shared ws {n}x{k} s={t} rep {rep}")
+
+
 def test_gemm_s64_scale_range():
     """Scales across the fp16 range, rows of only large scales and subnormal
     scales: the fp32 fold of each block's MFMA sum must keep them all."""
