@@ -53,8 +53,9 @@ constexpr int kGWaves = 4;
 constexpr int kGThreads = 64 * kGWaves;
 
 struct GemmPlan {
-  bool chunked;  // k % 256 == 0: the chunked kernel (rows per workgroup = 64 * sub)
+  bool chunked;  // k % 256 == 0: the chunked kernel (rows per workgroup = 64 * sub + 16 * extra)
   int sub;       // 16-row MFMA tiles per wave
+  int extra;     // chunked, sub 1: a fifth 16-row tile whose blocks the four waves share
   int tiles;     // row tiles
   int slices;    // K slices across workgroups
   int bps;       // blocks per slice
@@ -73,7 +74,29 @@ enum GemmMode : int {
 // one. When the row tiles alone give fewer workgroups than CUs, K is split
 // across workgroups so that about one workgroup runs per CU (smaller splits
 // leave CUs idle; larger ones gain nothing and add partial-sum traffic).
+static GemmPlan gemm_plan_rows(int64_t n, int64_t k, bool split, int extra);
+
+// The chunked kernel with one 16-row tile per wave can take a fifth tile per
+// workgroup, its blocks shared out among the four waves (each wave 1.25 times
+// the work). Without a K split it is taken when it lowers the resident
+// rounds times the work per workgroup: the E4B gate+up runs 256 workgroups
+// of 80 rows in one round instead of 320 of 64 in two (27.7 to 24.6-25.0 us).
+// Split shapes keep 64 rows: the E4B down as 8 slices of 80-row tiles took
+// 19.6-19.8 us against 18.1 as 6 slices of 64-row tiles.
 static GemmPlan gemm_plan(int64_t n, int64_t k, bool split = true) {
+  const GemmPlan p0 = gemm_plan_rows(n, k, split, 0);
+  if (!p0.chunked || p0.sub != 1 || !split || p0.slices != 1) return p0;
+  const GemmPlan p1 = gemm_plan_rows(n, k, split, 1);
+  if (p1.slices != 1) return p0;
+  const int64_t cus = std::max(1, device_cu_count());
+  auto cost = [&](const GemmPlan& p) {
+    const int64_t rounds = (int64_t(p.tiles) * p.slices + cus - 1) / cus;
+    return double(rounds) * p.bps * (4 + p.extra);
+  };
+  return cost(p1) < cost(p0) ? p1 : p0;
+}
+
+static GemmPlan gemm_plan_rows(int64_t n, int64_t k, bool split, int extra) {
   const int64_t B = k / 32;
   const int64_t cus = std::max(1, device_cu_count());
   GemmPlan p{};
@@ -87,7 +110,8 @@ static GemmPlan gemm_plan(int64_t n, int64_t k, bool split = true) {
     p.sub = subs[0];
   else if ((n + base * subs[1] - 1) / (base * subs[1]) >= cus)
     p.sub = subs[1];
-  const int64_t rows = base * p.sub;
+  p.extra = extra;
+  const int64_t rows = base * p.sub + 16 * p.extra;
   p.tiles = int((n + rows - 1) / rows);
   int64_t want = 1;
   if (split && p.tiles < cus) {
@@ -337,13 +361,17 @@ __device__ __forceinline__ uint32_t fresh_copy(uint32_t v) {
   return o;
 }
 
-template <int SUB>
+template <int SUB, int EXTRA>
 struct ChunkW {
   u32x4 w[SUB][2];  // lane group q: block 4h + q of the lane's row, h = 0, 1
   u32x4 sc[SUB];    // the row's 8 fp16 scales of the chunk
+  // the shared fifth tile: the wave's blocks wave and wave + 4 of the chunk,
+  // dword q of the lane's row of that tile, and their fp16 scales
+  uint32_t ew[EXTRA ? 2 : 1];
+  uint16_t es[EXTRA ? 2 : 1];
 };
 
-template <int SUB, int MODE>
+template <int SUB, int MODE, int EXTRA>
 __global__ __launch_bounds__(kGThreads) void q4_gemm_chunk_kernel(const uint8_t* __restrict__ nib,
                                                                   const uint16_t* __restrict__ scl,
                                                                   const uint16_t* __restrict__ x, int n, int k,
@@ -352,14 +380,16 @@ __global__ __launch_bounds__(kGThreads) void q4_gemm_chunk_kernel(const uint8_t*
   const int B = k >> 5;
   Q4_DCHECK(B % kChunk == 0 && bps > 0 && bps % kChunk == 0, kDbgGemmChunks);
   Q4_DCHECK(int64_t(gridDim.y) * bps >= B && int64_t(gridDim.y - 1) * bps < B, kDbgGemmSlices);
-  Q4_DCHECK(int64_t(gridDim.x) * 64 * SUB >= n, kDbgGemmTiles);
+  Q4_DCHECK(int64_t(gridDim.x) * (64 * SUB + 16 * EXTRA) >= n, kDbgGemmTiles);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int q = lane >> 4;
   const int col = lane & 15;
   const int b_begin = blockIdx.y * bps;
   const int nch = (min(B, b_begin + bps) - b_begin) / kChunk;  // >= 1: B and bps are multiples of 8
-  const int r0 = (blockIdx.x * 4 + wave) * 16 * SUB;            // the wave's first row
+  const int rwg = blockIdx.x * (64 * SUB + 16 * EXTRA);          // the workgroup's first row
+  const int r0 = rwg + wave * 16 * SUB;                          // the wave's first row
+  const int re = rwg + 64 * SUB;                                 // the shared tile's first row
 
   const uint8_t* wrow[SUB];
   const uint8_t* srow[SUB];
@@ -369,17 +399,25 @@ __global__ __launch_bounds__(kGThreads) void q4_gemm_chunk_kernel(const uint8_t*
     wrow[u] = nib + size_t(rc) * size_t(k >> 1) + 16 * q;
     srow[u] = reinterpret_cast<const uint8_t*>(scl) + size_t(rc) * size_t(B) * 2;
   }
+  const int rce = min(re + col, n - 1);
+  const uint8_t* wrow_e = nib + size_t(rce) * size_t(k >> 1) + 4 * q;
+  const uint16_t* srow_e = scl + size_t(rce) * size_t(B);
   // activation staging: thread t holds token t / 4, quarter t % 4 of each block
   const int sx = threadIdx.x >> 2, qq = threadIdx.x & 3;
   const uint8_t* xrow = reinterpret_cast<const uint8_t*>(x) + size_t(min(sx, n_tok - 1)) * size_t(k) * 2 + 16 * qq;
 
-  auto load_w = [&](ChunkW<SUB>& R, int ci) {
+  auto load_w = [&](ChunkW<SUB, EXTRA>& R, int ci) {
     const size_t b0 = size_t(b_begin + ci * kChunk);
 #pragma unroll
     for (int u = 0; u < SUB; ++u) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) R.w[u][h] = *reinterpret_cast<const u32x4*>(wrow[u] + (b0 + 4 * h) * 16);
       R.sc[u] = *reinterpret_cast<const u32x4*>(srow[u] + b0 * 2);
+    }
+#pragma unroll
+    for (int h = 0; h < EXTRA * 2; ++h) {
+      R.ew[h] = *reinterpret_cast<const uint32_t*>(wrow_e + (b0 + 4 * h + wave) * 16);
+      R.es[h] = srow_e[b0 + 4 * h + wave];
     }
   };
   auto load_x = [&](ChunkX& X, int ci) {
@@ -393,6 +431,9 @@ __global__ __launch_bounds__(kGThreads) void q4_gemm_chunk_kernel(const uint8_t*
   for (int u = 0; u < SUB; ++u)
 #pragma unroll
     for (int m = 0; m < 4; ++m) acc[u][m] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  float4_t acc_e[EXTRA ? 4 : 1];
+#pragma unroll
+  for (int m = 0; m < (EXTRA ? 4 : 1); ++m) acc_e[m] = float4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   auto load_a = [&](u32x4 (&a)[4], int c) {
 #pragma unroll
@@ -405,7 +446,7 @@ __global__ __launch_bounds__(kGThreads) void q4_gemm_chunk_kernel(const uint8_t*
   // One chunk: stage its activations into LDS, take the weights out of the
   // register set (transposed), refill the set two chunks ahead and the
   // activation staging one chunk ahead, then run the 8 blocks.
-  auto run = [&](ChunkW<SUB>& R, ChunkX& X, int ci) {
+  auto run = [&](ChunkW<SUB, EXTRA>& R, ChunkX& X, int ci) {
     __syncthreads();  // every wave is done with the previous chunk
 #pragma unroll
     for (int c = 0; c < kChunk; ++c) xs[c][sx][xslot(sx, qq)] = X.v[c];
@@ -424,6 +465,12 @@ __global__ __launch_bounds__(kGThreads) void q4_gemm_chunk_kernel(const uint8_t*
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) sc[u][j] = fresh_copy(R.sc[u][j]);
+    }
+    uint32_t ewt[EXTRA ? 2 : 1], est[EXTRA ? 2 : 1];
+#pragma unroll
+    for (int h = 0; h < 2 * EXTRA; ++h) {
+      ewt[h] = fresh_copy(R.ew[h]);
+      est[h] = fresh_copy(R.es[h]);
     }
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
@@ -458,9 +505,25 @@ __global__ __launch_bounds__(kGThreads) void q4_gemm_chunk_kernel(const uint8_t*
       if (c + 2 < kChunk) load_a(a0, c + 2);
       block(a1, c + 1);
     }
+    // the wave's two blocks of the shared tile
+#pragma unroll
+    for (int h = 0; h < 2 * EXTRA; ++h) {
+      load_a(a0, 4 * h + wave);
+      const bf16x8_t bc = codes16_bf16(ewt[h]);
+      const float d = float(__builtin_bit_cast(_Float16, uint16_t(est[h])));
+      float4_t rr[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        rr[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0[m]), bc,
+                                                        float4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc_e[m][i] = fmaf(d, rr[m][i], acc_e[m][i]);
+    }
   };
 
-  ChunkW<SUB> ra, rb;
+  ChunkW<SUB, EXTRA> ra, rb;
   ChunkX xr;
   load_w(ra, 0);
   load_w(rb, nch > 1 ? 1 : 0);
@@ -535,6 +598,31 @@ __global__ __launch_bounds__(kGThreads) void q4_gemm_chunk_kernel(const uint8_t*
           if (s < n_tok) y[size_t(s) * size_t(n) + row] = acc[u][m][i] * 0.0625f;
         }
     }
+    if constexpr (EXTRA != 0) {
+      // the shared tile's four partial sums (one per wave), added in wave
+      // order through LDS (the activation buffer, free once every wave is
+      // past its last chunk)
+      float4_t* red = reinterpret_cast<float4_t*>(&xs[0][0][0]);  // [wave][m][lane]
+      __syncthreads();
+#pragma unroll
+      for (int m = 0; m < 4; ++m) red[(wave * 4 + m) * 64 + lane] = acc_e[m];
+      __syncthreads();
+      if (wave == 0) {
+        const int row = re + col;
+        if (row < n) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const float4_t v = ((red[m * 64 + lane] + red[(4 + m) * 64 + lane]) + red[(8 + m) * 64 + lane]) +
+                               red[(12 + m) * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int s = 16 * m + 4 * q + i;
+              if (s < n_tok) y[size_t(s) * size_t(n) + row] = v[i] * 0.0625f;
+            }
+          }
+        }
+      }
+    }
   }
 }
 
@@ -545,9 +633,14 @@ static void launch_gemm(const GemmPlan& p, hipStream_t st, const uint8_t* nib, c
   const dim3 block(kGThreads);
   if (p.chunked) {
     if (p.sub == 2)
-      hipLaunchKernelGGL((q4_gemm_chunk_kernel<2, MODE>), grid, block, 0, st, nib, scl, x, n, k, n_tok, p.bps, out);
+      hipLaunchKernelGGL((q4_gemm_chunk_kernel<2, MODE, 0>), grid, block, 0, st, nib, scl, x, n, k, n_tok, p.bps,
+                         out);
+    else if (MODE != kGemmHead && p.extra)
+      hipLaunchKernelGGL((q4_gemm_chunk_kernel<1, MODE == kGemmHead ? kGemmOut : MODE, 1>), grid, block, 0, st, nib,
+                         scl, x, n, k, n_tok, p.bps, out);
     else
-      hipLaunchKernelGGL((q4_gemm_chunk_kernel<1, MODE>), grid, block, 0, st, nib, scl, x, n, k, n_tok, p.bps, out);
+      hipLaunchKernelGGL((q4_gemm_chunk_kernel<1, MODE, 0>), grid, block, 0, st, nib, scl, x, n, k, n_tok, p.bps,
+                         out);
     return;
   }
   switch (p.sub) {

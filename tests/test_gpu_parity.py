@@ -1078,7 +1078,9 @@ def test_every_entry_point_replays_in_a_graph():
                                        (3072, 2560, 64), (2560, 2048, 64), (2560, 10240, 64), (77, 16384, 5),
                                        # many row tiles: one K slice, no reduce (E4B gate+up; a
                                        # ragged last tile; k not a multiple of 256)
-                                       (20480, 2560, 64), (16400, 512, 17)])
+                                       (20480, 2560, 64), (16400, 512, 17),
+                                       # 80-row workgroups whose shared fifth tile is ragged
+                                       (19990, 512, 64), (20470, 2560, 3)])
 def test_gemm_s64_tolerance(n, k, n_tok):
     rng = synth.rng_for(20, n, k, n_tok)
     codes, sb = synth.q4_weights(rng, n, k)
