@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="skip the S=64 prefill step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--gemm-shapes", metavar="NxK[,NxK...]",
+                    help="run only q4_gemm_s64 on 64 tokens for each shape (4 distinct matrices, one "
+                         "HIP graph per shape) and print us per launch (for counter runs)")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="no GPU work: per-shape launch durations of every complete decode step in the "
                          "rocprofv3 kernel trace csv under DIR/ktr/, with the algorithmic bytes and the "
@@ -965,6 +968,45 @@ def trace_summary(d: str) -> dict:
             "shapes": out}
 
 
+def gemm_shapes_only(torch, dev, spec: str, seed: int) -> dict:
+    """q4_gemm_s64 alone on 64 bf16 tokens for each NxK shape in spec: 4
+    distinct packed matrices, their 4 launches captured in one HIP graph and
+    replayed 5 times between HIP events; us per launch."""
+    import int4_weight_only_block_amd as q4
+    import synth
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed + 11)
+    out = {}
+    for item in spec.split(","):
+        n, k = (int(v) for v in item.lower().split("x"))
+        mats = [q4.q4_pack(*synth.torch_q4_weights(g, n, k, dev)) for _ in range(4)]
+        x = synth.torch_bf16_normal(g, (64, k), dev)
+        y = torch.empty((64, n), dtype=torch.float32, device=dev)
+        ws = torch.zeros(q4.q4_gemm_workspace_bytes(n, k), dtype=torch.uint8, device=dev)
+
+        def run():
+            for m in mats:
+                q4.q4_gemm_s64(m, n, k, x, y, ws)
+
+        run()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out[f"{n}x{k}"] = round(e0.elapsed_time(e1) * 1e3 / (5 * len(mats)), 3)
+        del graph, mats
+    return {"gemm_s64_us_per_launch": out}
+
+
 def main():
     args = parse()
     if args.trace_summary:
@@ -994,6 +1036,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": 1 << 30, "copy_bytes_written": 1 << 30, "copies": 3}))
+        return
+
+    if args.gemm_shapes:
+        print(json.dumps(gemm_shapes_only(torch, dev, args.gemm_shapes, args.seed)))
         return
 
     wl = Workload(dev, args.seed)

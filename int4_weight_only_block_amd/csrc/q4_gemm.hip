@@ -477,50 +477,63 @@ __global__ __launch_bounds__(kGThreads) void q4_gemm_chunk_kernel(const uint8_t*
     load_x(X, ci + 1 < nch ? ci + 1 : ci);  // past the end: this chunk again (cache hits, never used)
     load_w(R, ci + 2 < nch ? ci + 2 : ci);
     __builtin_amdgcn_sched_barrier(0);
-    // block c on the matrix cores; the activations of block c + 1 are read
-    // from LDS before block c's products are issued
-    auto block = [&](const u32x4 (&a)[4], int c) {
+    // The chunk as a fixed sequence of steps: its 8 blocks of the wave's own
+    // tiles, then (fifth tile) the wave's two blocks of the shared tile. The
+    // activations of step s + 2 are read from LDS while step s is issued,
+    // and step s's products are folded after step s + 1's MFMAs are issued,
+    // so the wave waits on neither the LDS nor the matrix cores' latency.
+    // Every accumulator still takes its blocks in K order.
+    constexpr int NS = kChunk + 2 * EXTRA;
+    u32x4 a[3][4];
+    float4_t pr[2][SUB][4];
+    float pd[2][SUB];
+    auto ablock = [&](int s) { return s < kChunk ? s : 4 * (s - kChunk) + wave; };
+    auto issue = [&](int s, float4_t (&r)[SUB][4], float (&d)[SUB]) {
+      const u32x4 (&av)[4] = a[s % 3];
+      if (s < kChunk) {
 #pragma unroll
-      for (int u = 0; u < SUB; ++u) {
-        const bf16x8_t bc = codes16_bf16(wt[u][c >> 2][c & 3]);
-        const uint32_t sw = sc[u][c >> 1];
-        const float d = float(__builtin_bit_cast(_Float16, uint16_t((c & 1) ? sw >> 16 : sw & 0xFFFFu)));
-        float4_t r[4];
+        for (int u = 0; u < SUB; ++u) {
+          const bf16x8_t bc = codes16_bf16(wt[u][s >> 2][s & 3]);
+          const uint32_t sw = sc[u][s >> 1];
+          d[u] = float(__builtin_bit_cast(_Float16, uint16_t((s & 1) ? sw >> 16 : sw & 0xFFFFu)));
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+            r[u][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[m]), bc,
+                                                              float4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+        }
+      } else {
+        const bf16x8_t bc = codes16_bf16(ewt[(s - kChunk) & 1]);
+        d[0] = float(__builtin_bit_cast(_Float16, uint16_t(est[(s - kChunk) & 1])));
 #pragma unroll
         for (int m = 0; m < 4; ++m)
-          r[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[m]), bc,
-                                                         float4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[u][m][i] = fmaf(d, r[m][i], acc[u][m][i]);
+          r[0][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av[m]), bc,
+                                                            float4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
       }
     };
-    u32x4 a0[4], a1[4];
-    load_a(a0, 0);
+    auto fold = [&](int s, const float4_t (&r)[SUB][4], const float (&d)[SUB]) {
+      if (s < kChunk) {
 #pragma unroll
-    for (int c = 0; c < kChunk; c += 2) {
-      load_a(a1, c + 1);
-      block(a0, c);
-      if (c + 2 < kChunk) load_a(a0, c + 2);
-      block(a1, c + 1);
+        for (int u = 0; u < SUB; ++u)
+#pragma unroll
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[u][m][i] = fmaf(d[u], r[u][m][i], acc[u][m][i]);
+      } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc_e[m][i] = fmaf(d[0], r[0][m][i], acc_e[m][i]);
+      }
+    };
+    load_a(a[0], ablock(0));
+    load_a(a[1], ablock(1));
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      if (s + 2 < NS) load_a(a[(s + 2) % 3], ablock(s + 2));
+      issue(s, pr[s & 1], pd[s & 1]);
+      if (s > 0) fold(s - 1, pr[(s - 1) & 1], pd[(s - 1) & 1]);
     }
-    // the wave's two blocks of the shared tile
-#pragma unroll
-    for (int h = 0; h < 2 * EXTRA; ++h) {
-      load_a(a0, 4 * h + wave);
-      const bf16x8_t bc = codes16_bf16(ewt[h]);
-      const float d = float(__builtin_bit_cast(_Float16, uint16_t(est[h])));
-      float4_t rr[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        rr[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a0[m]), bc,
-                                                        float4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc_e[m][i] = fmaf(d, rr[m][i], acc_e[m][i]);
-    }
+    fold(NS - 1, pr[(NS - 1) & 1], pd[(NS - 1) & 1]);
   };
 
   ChunkW<SUB, EXTRA> ra, rb;
