@@ -145,19 +145,17 @@ int q4_gemv(const void* packed, int64_t n, int64_t k, const uint16_t* x,
  * weights read once for all m ("Gemma-4 E2B mobile mixed-bit QAT weights",
  * MTP speculative-decoding sections P5c/P5d: one S = 4 verify pass checks four
  * draft rows against weights read once; the FFN and head dominate it).
- * m = 1 is q4_gemv. For m >= 2 the products run on the matrix cores: each
- * vector is converted once to fp16 scaled by one power of two (its largest
- * value lands in [2^14, 2^15)), codes times activations accumulate in fp32
- * per block, and each block sum is scaled by d; results are within the
- * q4_gemv bar of the exact sums for every finite x: when a vector's nonzero
- * values span more than 31 binades the call reads x as stored instead
- * (exact path, slower).
+ * m = 1 is q4_gemv. For m >= 2 the products run on the matrix cores: the
+ * vectors are used as stored (bf16) against the codes as exact bf16, so
+ * every code-activation product is exact, the products of a block
+ * accumulate in fp32 and each block sum is scaled by d in fp32; results are
+ * within the q4_gemv bar of the exact sums for every finite x.
  *   packed  from q4_pack with the same (n, k); 16-byte aligned.
  *   x       bf16 [m, k] row-major, 16-byte aligned.
  *   y       fp32 [m, n] row-major, 4-byte aligned, caller-owned.
  * Errors: NULL pointer, n or k as q4_gemv, m not in [1, 8], misalignment;
  *         unsupported when the staged vectors (4 * ceil(m / 4) rows of
- *         (k + 8) fp16 values) do not fit in one workgroup's LDS. */
+ *         (k + 8) bf16 values) do not fit in one workgroup's LDS. */
 int q4_gemv_multi(const void* packed, int64_t n, int64_t k, const uint16_t* x,
                   int64_t m, float* y, void* stream);
 
@@ -407,8 +405,7 @@ size_t lmhead_multi_workspace_bytes(int64_t vocab, int64_t k, int64_t m);
  * weights", MTP sections P5c/P5d: the verify pass reads the head once and
  * takes each draft row's argmax). For each v < m:
  * idx_out[v], val_out[v] as lmhead_softcap_argmax on x[v]; the logits are
- * those of q4_gemv_multi (matrix cores, one power-of-two fp16 factor per
- * vector). Two launches on `stream`: the first leaves every workgroup's best
+ * those of q4_gemv_multi (matrix cores, activations as stored). Two launches on `stream`: the first leaves every workgroup's best
  * (value, row) per vector in ws, the second (one workgroup per vector)
  * reduces them and caps the winner.
  *   packed   from q4_pack with (n = vocab, k); 16-byte aligned.
@@ -418,7 +415,7 @@ size_t lmhead_multi_workspace_bytes(int64_t vocab, int64_t k, int64_t m);
  *            sharing one ws must not overlap.
  *   idx_out  device int32 [m]; val_out device fp32 [m].
  * Errors: as lmhead_softcap_argmax, m not in [1, 8], and unsupported when
- *         the staged vectors (4 * ceil(m / 4) rows of (k + 8) fp16 values)
+ *         the staged vectors (4 * ceil(m / 4) rows of (k + 8) bf16 values)
  *         do not fit in one workgroup's LDS. */
 int lmhead_softcap_argmax_multi(const void* packed, int64_t vocab, int64_t k,
                                 const uint16_t* x, int64_t m, float cap,

@@ -39,12 +39,12 @@
 
 #include <algorithm>
 
+#include "q4_codes.h"
 #include "q4dec_internal.h"
 
 namespace q4dec {
 Q4DEC_DEBUG_READER(q4_gemm)
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kTok = 64;   // token slots
@@ -123,24 +123,6 @@ static GemmPlan gemm_plan_rows(int64_t n, int64_t k, bool split, int extra) {
   p.slices = int((B + p.bps - 1) / p.bps);
   p.total = p.slices > 1 ? align256(size_t(p.slices) * kTok * size_t(n) * 4) : 256;
   return p;
-}
-
-// 16 * c for the 8 codes of one packed dword, in k order, as bf16.
-__device__ __forceinline__ bf16x8_t codes16_bf16(uint32_t w) {
-  const uint32_t t = w ^ 0x88888888u;  // two's complement 4-bit codes
-  const uint32_t lo = (t << 4) & 0xF0F0F0F0u, hi = t & 0xF0F0F0F0u;
-  // byte j of the dword: low nibble k = 8q + {0, 4, 1, 5}[j], high nibble
-  // k = 8q + {2, 6, 3, 7}[j]; as signed bytes in the top half, 16 * c
-  bf16x8_t r;
-  r[0] = (__bf16)(float)(int8_t)(lo);
-  r[1] = (__bf16)(float)(int8_t)(lo >> 16);
-  r[2] = (__bf16)(float)(int8_t)(hi);
-  r[3] = (__bf16)(float)(int8_t)(hi >> 16);
-  r[4] = (__bf16)(float)(int8_t)(lo >> 8);
-  r[5] = (__bf16)(float)(int8_t)(lo >> 24);
-  r[6] = (__bf16)(float)(int8_t)(hi >> 8);
-  r[7] = (__bf16)(float)(int8_t)(hi >> 24);
-  return r;
 }
 
 // One block's registers for one lane: the activations of its 4 token tiles

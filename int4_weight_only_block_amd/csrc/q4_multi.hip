@@ -3,7 +3,7 @@
 // QAT weights", MTP speculative-decoding sections P5c/P5d: a verify pass reads
 // the weights once for the few draft rows it checks).
 //
-// Mapping. v_mfma_f32_4x4x4_16b_f16 runs 16 independent 4x4x4 products per
+// Mapping. v_mfma_f32_4x4x4_16b_bf16 runs 16 independent 4x4x4 products per
 // wave; in 4-lane group g, lane 4g + i holds row i of A (four k values),
 // lane 4g + i holds column i of B, and lane 4g + i receives column i of C.
 // So lane 4g + j takes weight row j of the wave's 4-row group as its B
@@ -14,11 +14,13 @@
 // row's lanes read 16 consecutive 16-byte blocks, 256 contiguous bytes), and
 // each lane walks its blocks t * 16 + g down the row.
 //
-// Codes. q4_pack's dword d of a block unpacks (fp16 magic number) into the
-// consecutive k pairs 8d .. 8d+7, so one MFMA takes 4 codes in k order and the
-// matching 4 activations straight from LDS, where each vector is stored as
-// fp16 in k order, scaled by one power of two per vector (its largest bf16
-// exponent lands at 2^14, as the prefill GEMM's per-token factor).
+// Numerics. q4_pack's dword d of a block holds the codes of k = 8d .. 8d+7;
+// they become 16 * c in bf16 (exact), so one MFMA takes 4 codes in k order
+// and the matching 4 activations straight from LDS, where each vector is
+// stored as given (bf16, no conversion). Every product is exact in fp32, the
+// matrix cores add a block's products in fp32, the block scale is folded in
+// fp32 and the factor 1/16 is applied once at the end (exact), as in the
+// S=64 GEMM: there is no range limit on x beyond fp32's own.
 #include <limits.h>
 #include <math.h>
 
@@ -27,13 +29,14 @@
 #include <tuple>
 #include <type_traits>
 
+#include "q4_codes.h"
 #include "q4dec_internal.h"
 
 namespace q4dec {
 Q4DEC_DEBUG_READER(q4_multi)
 namespace {
 
-typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef short short4_t __attribute__((ext_vector_type(4)));  // 4 bf16, the 4x4x4 MFMA operand
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kMWaves = 4;
@@ -80,9 +83,6 @@ __global__ __launch_bounds__(kMThreads) void q4_multi_kernel(const uint8_t* __re
   const int B = k >> 5;
   const int xsn = x_stride(k);
   _Float16* xs = reinterpret_cast<_Float16*>(dyn_lds);  // [4 * NG][xsn]
-  __shared__ uint32_t red[kMWaves][4 * NG];
-  __shared__ uint32_t redn[kMWaves][4 * NG];
-  __shared__ float ef[4 * NG];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -117,121 +117,45 @@ __global__ __launch_bounds__(kMThreads) void q4_multi_kernel(const uint8_t* __re
       }
     }
   };
-  // Stage x: the raw bf16 rows go to LDS while each vector's largest bf16
-  // exponent is found; then each row is rewritten in place as fp16 scaled by
-  // the power of two that puts its largest value at 2^14 (x is read from
-  // memory once). Rows v >= m are zeros. The first kMXLoads 16-byte pieces of
-  // each thread are loaded before the first weights (vector memory counters
-  // retire in order, so the staging then waits for these loads only); the
-  // loads are unconditional on a clamped index and an empty asm use after the
-  // weight loads keeps the compiler from moving them behind the weights.
+  // Stage x as stored: the m bf16 rows into LDS (row v at xs + v * xsn),
+  // rows m .. 4 * NG - 1 zero, with no conversion, so every code-activation
+  // product the matrix cores form is exact and x has no range limit beyond
+  // fp32's own. The first kMXLoads 16-byte pieces of each thread are loaded
+  // before the first weights (vector memory counters retire in order, so
+  // their stores then wait for these loads only); the loads are
+  // unconditional on a clamped index and an empty asm use after the weight
+  // loads keeps the compiler from moving them behind the weights.
   const int k8 = k >> 3;
-  const int tot = m * k8;  // 16-byte pieces of x
+  const int have = m * k8;        // 16-byte pieces of x
+  const int tot = 4 * NG * k8;    // 16-byte pieces of the LDS rows
   const uint4* xq = reinterpret_cast<const uint4*>(x);
+  auto put = [&](int idx, const uint4& w) {
+    const int v = idx / k8, i = idx - v * k8;
+    *reinterpret_cast<uint4*>(xs + size_t(v) * xsn + 8 * i) = idx < have ? w : make_uint4(0u, 0u, 0u, 0u);
+  };
   uint4 xr[kMXLoads];
 #pragma unroll
-  for (int u = 0; u < kMXLoads; ++u) xr[u] = xq[min(int(threadIdx.x) + u * kMThreads, tot - 1)];
+  for (int u = 0; u < kMXLoads; ++u) xr[u] = xq[min(int(threadIdx.x) + u * kMThreads, have - 1)];
   // (a wave with no rows loads the clamped last row and never uses it)
   load(0);
 #pragma unroll
   for (int u = 0; u < kMXLoads; ++u) asm volatile("" : "+v"(xr[u].x), "+v"(xr[u].y), "+v"(xr[u].z), "+v"(xr[u].w));
-
-  uint32_t emax[kMultiVecs], emin[kMultiVecs];
-#pragma unroll
-  for (int v = 0; v < kMultiVecs; ++v) {
-    emax[v] = 1;
-    emin[v] = 255;
-  }
-  auto take = [&](int idx, const uint4& w) {
-    const int v = idx / k8, i = idx - v * k8;
-    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-    uint32_t e, en;
-    block_exp_range(ws, e, en);
-#pragma unroll
-    for (int vv = 0; vv < kMultiVecs; ++vv)
-      if (vv == v) {
-        emax[vv] = max(emax[vv], e);
-        emin[vv] = min(emin[vv], en);
-      }
-    *reinterpret_cast<uint4*>(xs + size_t(v) * xsn + 8 * i) = w;
-  };
 #pragma unroll
   for (int u = 0; u < kMXLoads; ++u) {
     const int idx = int(threadIdx.x) + u * kMThreads;
-    if (idx < tot) take(idx, xr[u]);
+    if (idx < tot) put(idx, xr[u]);
   }
-  // the rest (long rows, many vectors) in batches of four loads in flight
-  for (int base = int(threadIdx.x) + kMXLoads * kMThreads; base < tot; base += 4 * kMThreads) {
-    uint4 r[4];
+  // the rest (long rows, many vectors) in batches of eight loads in flight
+  for (int base = int(threadIdx.x) + kMXLoads * kMThreads; base < tot; base += 8 * kMThreads) {
+    uint4 r[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) r[u] = xq[min(base + u * kMThreads, tot - 1)];
+    for (int u = 0; u < 8; ++u) r[u] = xq[min(base + u * kMThreads, have - 1)];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (base + u * kMThreads < tot) take(base + u * kMThreads, r[u]);
-  }
-  for (int v = 0; v < m; ++v) {
-    uint32_t e = emax[0], en = emin[0];
-#pragma unroll
-    for (int vv = 1; vv < kMultiVecs; ++vv)
-      if (vv == v) {
-        e = emax[vv];
-        en = emin[vv];
-      }
-    for (int off = 32; off >= 1; off >>= 1) {
-      e = max(e, uint32_t(__shfl_xor(int(e), off)));
-      en = min(en, uint32_t(__shfl_xor(int(en), off)));
-    }
-    if (lane == 0) {
-      red[wave][v] = e;
-      redn[wave][v] = en;
-    }
-  }
-  __syncthreads();
-  // A vector whose nonzero values span more binades than the scaled fp16
-  // copy keeps exactly puts every workgroup (all stage the same x) on the
-  // exact path: the rows stay raw bf16 in LDS and are read as stored.
-  int wide = 0;
-  for (int v = 0; v < m; ++v) {
-    const uint32_t e = max(max(red[0][v], red[1][v]), max(red[2][v], red[3][v]));
-    const uint32_t en = min(min(redn[0][v], redn[1][v]), min(redn[2][v], redn[3][v]));
-    wide |= int(e) - int(en) > kMaxSpan;
-  }
-  // uniform by construction; readfirstlane lets the compiler branch on it as
-  // a scalar, so the two paths do not hold registers at the same time
-  const bool exact = __builtin_amdgcn_readfirstlane(wide) != 0;
-  for (int idx = threadIdx.x; idx < 4 * NG * k8; idx += kMThreads) {
-    const int v = idx / k8, i = idx - v * k8;
-    uint4* slot = reinterpret_cast<uint4*>(xs + size_t(v) * xsn + 8 * i);
-    uint4 o = make_uint4(0u, 0u, 0u, 0u);
-    if (v < m && exact) {
-      o = *slot;  // raw bf16, read as stored
-      if (i == 0) ef[v] = 1.0f;
-    } else if (v < m) {
-      const uint32_t emax = max(max(red[0][v], red[1][v]), max(red[2][v], red[3][v]));
-      const int e = int(emax) - 127 - 14;
-      const uint4 w = *slot;
-      const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
-      uint32_t h[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const half2_t p = {(_Float16)ldexpf(bf16_to_f32(ws[c] & 0xFFFFu), -e),
-                           (_Float16)ldexpf(bf16_to_f32(ws[c] >> 16), -e)};
-        h[c] = __builtin_bit_cast(uint32_t, p);
-      }
-      o = make_uint4(h[0], h[1], h[2], h[3]);
-      if (i == 0) ef[v] = ldexpf(1.0f, e);
-    } else if (i == 0) {
-      ef[v] = 0.0f;
-    }
-    *slot = o;
+    for (int u = 0; u < 8; ++u)
+      if (base + u * kMThreads < tot) put(base + u * kMThreads, r[u]);
   }
   // LDS writes done and visible; the weight loads above stay in flight
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-
-  uint32_t m_lo, m_hi, magic;
-  asm volatile("v_mov_b32 %0, 0x000F000F" : "=v"(m_lo));
-  asm volatile("v_mov_b32 %0, 0x00F000F0" : "=v"(m_hi));
-  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 
   float acc[NG][4];
   float best[NG][4];  // head mode: best (sum, row) per vector over this lane's rows
@@ -262,9 +186,9 @@ __global__ __launch_bounds__(kMThreads) void q4_multi_kernel(const uint8_t* __re
           s += __shfl_xor(s, 32);
           const int v = 4 * g + i;
           if constexpr (MODE == kMultiGemv) {
-            if (grp == 0 && row < n && v < m) y[size_t(v) * size_t(n) + row] = s * ef[v];
+            if (grp == 0 && row < n && v < m) y[size_t(v) * size_t(n) + row] = s * 0.0625f;
           } else {
-            const float val = s * ef[v];
+            const float val = s * 0.0625f;
             if (row < n && v < m && better(val, row, best[g][i], bidx[g][i])) {
               best[g][i] = val;
               bidx[g][i] = row;
@@ -295,16 +219,17 @@ __global__ __launch_bounds__(kMThreads) void q4_multi_kernel(const uint8_t* __re
         for (int g = 0; g < NG; ++g) c[g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int dd = 0; dd < 4; ++dd) {
-          const CodePairs cp = unpack_dword(wd[dd], m_lo, m_hi, magic);  // k = 8dd .. 8dd+7 in order
-          const half4_t b_lo = {cp.p[0][0], cp.p[0][1], cp.p[1][0], cp.p[1][1]};
-          const half4_t b_hi = {cp.p[2][0], cp.p[2][1], cp.p[3][0], cp.p[3][1]};
+          // 16 * c for k = 8dd .. 8dd+7 in order, exact in bf16
+          const u32x4 bw = codes16_bf16_pairs(wd[dd]);
+          const short4_t b_lo = __builtin_bit_cast(short4_t, make_uint2(bw.x, bw.y));
+          const short4_t b_hi = __builtin_bit_cast(short4_t, make_uint2(bw.z, bw.w));
 #pragma unroll
           for (int g = 0; g < NG; ++g) {
             const uint4 xa = *reinterpret_cast<const uint4*>(xs + size_t(4 * g + j) * xsn + 32 * b + 8 * dd);
-            const half4_t a_lo = __builtin_bit_cast(half4_t, make_uint2(xa.x, xa.y));
-            const half4_t a_hi = __builtin_bit_cast(half4_t, make_uint2(xa.z, xa.w));
-            c[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(a_lo, b_lo, c[g], 0, 0, 0);
-            c[g] = __builtin_amdgcn_mfma_f32_4x4x4f16(a_hi, b_hi, c[g], 0, 0, 0);
+            const short4_t a_lo = __builtin_bit_cast(short4_t, make_uint2(xa.x, xa.y));
+            const short4_t a_hi = __builtin_bit_cast(short4_t, make_uint2(xa.z, xa.w));
+            c[g] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a_lo, b_lo, c[g], 0, 0, 0);
+            c[g] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a_hi, b_hi, c[g], 0, 0, 0);
           }
         }
 #pragma unroll
@@ -323,51 +248,8 @@ __global__ __launch_bounds__(kMThreads) void q4_multi_kernel(const uint8_t* __re
     }
     finish(u);
   };
-  // The exact path's step: each block loaded on its own (no refill, no
-  // unrolling) and summed per vector against the raw bf16 rows in fp32,
-  // where every code-activation product is exact.
-  auto step_exact = [&](int u) {
-    const int row = row_of(u);
-    const u32x4* np = reinterpret_cast<const u32x4*>(nib + size_t(row) * row_bytes);
-    const uint16_t* sp = scl + size_t(row) * size_t(B);
-#pragma unroll 1
-    for (int t = 0; t < BPL; ++t) {
-      const int b = block_of(u, t);
-      if (FULL || b < B) {
-        const u32x4 qv = np[b];
-        const uint32_t wd[4] = {qv.x, qv.y, qv.z, qv.w};
-        const float d = float(__builtin_bit_cast(_Float16, sp[b]));
-#pragma unroll 1
-        for (int v = 0; v < m; ++v) {
-          const uint4* xb = reinterpret_cast<const uint4*>(xs + size_t(v) * xsn + 32 * b);
-          float sum = 0.0f;
-#pragma unroll
-          for (int dd = 0; dd < 4; ++dd) {
-            const uint4 xv = xb[dd];  // bf16 k = 8dd .. 8dd+7
-            const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w};
-            const CodePairs cp = unpack_dword(wd[dd], m_lo, m_hi, magic);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-              sum = fmaf(float(cp.p[jj][0]), bf16_to_f32(xw[jj] & 0xFFFFu), sum);
-              sum = fmaf(float(cp.p[jj][1]), bf16_to_f32(xw[jj] >> 16), sum);
-            }
-          }
-#pragma unroll
-          for (int g = 0; g < NG; ++g)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              if (4 * g + i == v) acc[g][i] = fmaf(d, sum, acc[g][i]);
-        }
-      }
-    }
-    finish(u);
-  };
-  if (exact) {
-    for (int u = 0; u < units; ++u) step_exact(u);
-  } else {
-    for (int u = 0; u + 1 < units; ++u) step(u, std::true_type{});
-    if (units > 0) step(units - 1, std::false_type{});
-  }
+  for (int u = 0; u + 1 < units; ++u) step(u, std::true_type{});
+  if (units > 0) step(units - 1, std::false_type{});
 
   if constexpr (MODE == kMultiHead) {
     // the workgroup's best (value, row) per vector into its partial slots
@@ -514,15 +396,6 @@ MultiPlan multi_plan(int64_t n, int64_t k, int m) {
   const int cus = device_cu_count();
   const int waves_max = cus * multi_blocks_per_cu(p.fn, p.lds) * kMWaves;
   p.ipw = (rg + waves_max - 1) / waves_max;
-  // every workgroup stages all m vectors: a wave walks up to three row
-  // groups while the grid still covers 80% of the CUs, to spread that cost
-  for (int want = 3; want > p.ipw; --want) {
-    const int64_t g = ((rg + want - 1) / want + kMWaves - 1) / kMWaves;
-    if (g * 5 >= int64_t(cus) * 4) {
-      p.ipw = want;
-      break;
-    }
-  }
   const int waves = (rg + p.ipw - 1) / p.ipw;
   p.grid = (waves + kMWaves - 1) / kMWaves;
   return p;

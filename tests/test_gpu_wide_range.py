@@ -2,10 +2,10 @@
 
 The S=1 q4_0 and per-row kernels stage bf16 activations as fp16 scaled by
 one power of two per group (a 32-wide block for the S=1 GEMV, the fused GELU,
-the heads and the per-row formats; a whole vector for the multi-vector GEMV
-and head). The S=64 GEMM and its head feed the activations to the matrix
-cores as stored, so for them the same inputs check that nothing on that path
-narrows the range (a staged copy per token would fail them). A value more than 31
+the heads and the per-row formats). The S=64 GEMM, its head and the
+multi-vector GEMV and head feed the activations to the matrix cores as
+stored, so for them the same inputs check that nothing on that path narrows
+the range (a staged copy per token or per vector would fail them). A value more than 31
 binades below its group's largest (fewer on the per-row formats, whose staged
 values carry an extra field shift of 2^-8 for INT2 and 2^-4 for INT4) would
 lose significand bits there. On the q4_0 kernels such a group sends the
@@ -172,8 +172,8 @@ def test_lmhead_outlier(vocab, k):
 # ----------------------------------------------------- multi-vector GEMV --
 @pytest.mark.parametrize("m", [2, 4, 8])
 def test_gemv_multi_outlier_in_one_vector(m):
-    """One vector holds a 2^40 outlier with code zero on every row: with one
-    power of two per vector, its other values would flush."""
+    """One vector holds a 2^40 outlier with code zero on every row: a staged
+    copy with one power of two per vector would flush its other values."""
     n, k = 500, 2560
     rng = synth.rng_for(605, m)
     codes, sb = synth.q4_weights(rng, n, k)
