@@ -68,6 +68,9 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true", help="skip the S=64 prefill step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--verify-pass", action="store_true",
+                    help="build the decode workload and run one 4-token verify pass eagerly, untimed "
+                         "(for counter runs)")
     ap.add_argument("--gemm-shapes", metavar="NxK[,NxK...]",
                     help="run only q4_gemm_s64 on 64 tokens for each shape (4 distinct matrices, one "
                          "HIP graph per shape) and print us per launch (for counter runs)")
@@ -290,12 +293,14 @@ def probe_chain(torch, wl: Workload, graph, reps: int = 10):
     return out
 
 
-def probe_verify_m4(torch, wl: Workload, seed: int, reps: int = 10):
+def probe_verify_m4(torch, wl: Workload, seed: int, reps: int = 10, once: bool = False):
     """A 4-token verify pass: the 168 layer GEMVs with m = 4 activation
     vectors each (q4_gemv_multi: every weight read once for the 4 tokens)
     and the head for the same 4 vectors with softcap and per-vector argmax
     (lmhead_softcap_argmax_multi), one HIP graph; reported as ms per pass,
-    the head alone in us, and weight bytes/s. Not part of the decode step."""
+    the head alone in us, and weight bytes/s. Not part of the decode step.
+    With once, the pass runs one time, eagerly, and nothing is timed (for
+    counter runs, which then see each of its launches once)."""
     import int4_weight_only_block_amd as q4
     import synth
 
@@ -335,6 +340,10 @@ def probe_verify_m4(torch, wl: Workload, seed: int, reps: int = 10):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / r
 
+    if once:
+        run()
+        torch.cuda.synchronize()
+        return {"verify_pass_launches": len(mats) + 2}
     ms = time_graph(run, reps)
     head_us = time_graph(head, 10 * reps) * 1e3
     wb = sum(weight_bytes(n, k) for _, n, k in mats) + weight_bytes(vocab, kh)
@@ -1043,6 +1052,9 @@ def main():
         return
 
     wl = Workload(dev, args.seed)
+    if args.verify_pass:
+        print(json.dumps(probe_verify_m4(torch, wl, args.seed, once=True)))
+        return
     graph = capture_step(torch, wl)
     for _ in range(max(args.warmup, 0)):
         graph.replay()
