@@ -48,3 +48,13 @@ def test_traffic_is_gated_on_the_kernel_sources(tmp_path, monkeypatch):
 def test_host_cpu_model_is_named():
     m = bench.host_cpu_model()
     assert isinstance(m, str) and m
+
+
+def test_profiler_modes_parse(monkeypatch):
+    # the single-purpose runs that the rocprofv3 summaries are taken with
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--verify-pass"])
+    assert bench.parse().verify_pass
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--gemm-shapes", "16384x2560,20480x2560"])
+    a = bench.parse()
+    assert not a.verify_pass
+    assert [tuple(int(v) for v in s.split("x")) for s in a.gemm_shapes.split(",")] == [(16384, 2560), (20480, 2560)]
