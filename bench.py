@@ -71,6 +71,9 @@ def parse():
     ap.add_argument("--verify-pass", action="store_true",
                     help="build the decode workload and run one 4-token verify pass eagerly, untimed "
                          "(for counter runs)")
+    ap.add_argument("--heads-once", action="store_true",
+                    help="run the single-vector LM head once on an E2B- and once on an E4B-shaped matrix, "
+                         "untimed (for counter runs)")
     ap.add_argument("--gemm-shapes", metavar="NxK[,NxK...]",
                     help="run only q4_gemm_s64 on 64 tokens for each shape (4 distinct matrices, one "
                          "HIP graph per shape) and print us per launch (for counter runs)")
@@ -977,6 +980,27 @@ def trace_summary(d: str) -> dict:
             "shapes": out}
 
 
+def heads_once(torch, dev, seed: int) -> dict:
+    """The single-vector LM head (softcap + argmax, one launch) once on an
+    E2B-shaped [262144, 1536] and once on an E4B-shaped [262144, 2560] matrix,
+    eagerly and untimed (for counter runs, which then see each launch once)."""
+    import int4_weight_only_block_amd as q4
+    import synth
+
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed + 13)
+    out = {}
+    for vocab, k in ((262144, 1536), (262144, 2560)):
+        packed = q4.q4_pack(*synth.torch_q4_weights(g, vocab, k, dev))
+        x = synth.torch_bf16_normal(g, k, dev)
+        ws = torch.zeros(q4.lmhead_workspace_bytes(vocab, k), dtype=torch.uint8, device=dev)
+        idx, val = q4.lmhead_softcap_argmax(packed, vocab, k, x, 30.0, ws)
+        torch.cuda.synchronize()
+        out[f"{vocab}x{k}"] = {"idx": int(idx.item()), "val": float(val.item())}
+        del packed
+    return {"heads_once": out}
+
+
 def gemm_shapes_only(torch, dev, spec: str, seed: int) -> dict:
     """q4_gemm_s64 alone on 64 bf16 tokens for each NxK shape in spec: 4
     distinct packed matrices, their 4 launches captured in one HIP graph and
@@ -1049,6 +1073,9 @@ def main():
 
     if args.gemm_shapes:
         print(json.dumps(gemm_shapes_only(torch, dev, args.gemm_shapes, args.seed)))
+        return
+    if args.heads_once:
+        print(json.dumps(heads_once(torch, dev, args.seed)))
         return
 
     wl = Workload(dev, args.seed)
