@@ -54,6 +54,8 @@ def test_profiler_modes_parse(monkeypatch):
     # the single-purpose runs that the rocprofv3 summaries are taken with
     monkeypatch.setattr(sys, "argv", ["bench.py", "--verify-pass"])
     assert bench.parse().verify_pass
+    monkeypatch.setattr(sys, "argv", ["bench.py", "--heads-once"])
+    assert bench.parse().heads_once
     monkeypatch.setattr(sys, "argv", ["bench.py", "--gemm-shapes", "16384x2560,20480x2560"])
     a = bench.parse()
     assert not a.verify_pass
